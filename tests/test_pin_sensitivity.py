@@ -1,0 +1,91 @@
+"""Planted mistakes in the oracle (on the CPU) must each be caught by a pin."""
+import numpy as np
+import pytest
+
+from oracle import qref
+from tests import pins
+
+_orig_unpack = qref.unpack_codes
+_orig_pack = qref.pack_codes
+_orig_deq = qref.dequant_f32
+_orig_gemm = qref.qgemm_ref
+
+
+def _unpack_msb_first(words, N, K, fmt):
+    c = _orig_unpack(words, N, K, fmt)
+    cpw = 32 // qref.BITS[fmt]
+    return c.reshape(N, K // cpw, cpw)[:, :, ::-1].reshape(N, K).copy()
+
+
+def _pack_msb_first(codes, fmt):
+    cpw = 32 // qref.BITS[fmt]
+    N, K = codes.shape
+    return _orig_pack(np.asarray(codes).reshape(N, K // cpw, cpw)[:, :, ::-1].reshape(N, K), fmt)
+
+
+def _deq_sign(words, scales, zeros, N, K, group, fmt):
+    return -_orig_deq(words, scales, zeros, N, K, group, fmt)
+
+
+def _deq_no_zero(words, scales, zeros, N, K, group, fmt):
+    q = _orig_unpack(words, N, K, fmt).astype(np.float32)
+    s = np.asarray(scales, np.float16).reshape(N, K // group).astype(np.float32)
+    return s[:, np.arange(K) // group] * q
+
+
+def _deq_group_mod(words, scales, zeros, N, K, group, fmt):
+    q = _orig_unpack(words, N, K, fmt).astype(np.float32)
+    s, z = qref._group_params(scales, zeros, N, K, group, fmt)
+    g = np.arange(K) % (K // group)
+    return s[:, g] * (q - z[:, g])
+
+
+def _deq_q40_offset7(words, scales, zeros, N, K, group, fmt):
+    if fmt == qref.Q4_0:
+        q = _orig_unpack(words, N, K, fmt).astype(np.float32)
+        s = np.asarray(scales, np.float16).reshape(N, K // group).astype(np.float32)
+        return s[:, np.arange(K) // group] * (q - 7.0)
+    return _orig_deq(words, scales, zeros, N, K, group, fmt)
+
+
+def _deq_group_shift(words, scales, zeros, N, K, group, fmt):
+    q = _orig_unpack(words, N, K, fmt).astype(np.float32)
+    s, z = qref._group_params(scales, zeros, N, K, group, fmt)
+    g = np.minimum((np.arange(K) + 1) // group, K // group - 1)
+    return s[:, g] * (q - z[:, g])
+
+
+def _gemm_transposed(x, words, scales, zeros, M, N, K, group, fmt, residual=None):
+    x64 = np.asarray(x, np.float16).reshape(M, K).astype(np.float64)
+    w = _orig_deq(words, scales, zeros, N, K, group, fmt).astype(np.float64)
+    return x64 @ w.reshape(K, N)   # a transposed/reshaped operand
+
+
+def _gemm_fp16_accumulate(x, words, scales, zeros, M, N, K, group, fmt, residual=None):
+    x16 = np.asarray(x, np.float16).reshape(M, K)
+    w16 = _orig_deq(words, scales, zeros, N, K, group, fmt).astype(np.float16)
+    return (x16 @ w16.T).astype(np.float64)
+
+
+MUTANTS = {
+    "unpack_msb_first": [("unpack_codes", _unpack_msb_first), ("pack_codes", _pack_msb_first)],
+    "dequant_sign": [("dequant_f32", _deq_sign)],
+    "dropped_zero_point": [("dequant_f32", _deq_no_zero)],
+    "group_index_mod": [("dequant_f32", _deq_group_mod)],
+    "group_index_shift": [("dequant_f32", _deq_group_shift)],
+    "q4_0_offset_7": [("dequant_f32", _deq_q40_offset7)],
+    "transposed_operand": [("qgemm_ref", _gemm_transposed)],
+    "fp16_accumulation": [("qgemm_ref", _gemm_fp16_accumulate)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    for attr, fn in MUTANTS[name]:
+        monkeypatch.setattr(qref, attr, fn)
+    bad = pins.failing_pins(qref)
+    assert bad, f"planted mistake {name} passed every pin"
+
+
+def test_real_oracle_passes_all():
+    assert pins.failing_pins(qref) == []

@@ -1,0 +1,59 @@
+"""The seeded input generator: quantizer bounds, the q4_0 worked block, and
+agreement of its canonical packing with the oracle's unpack."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+def test_q4_0_worked_block():
+    # block [0.03, -0.05, 0.01, 0.049] (padded with zeros to 32): the extreme
+    # -0.05 maps to -8, so d = 0.00625 and the codes are [5, -8, 2, 7] (0.049
+    # would be 8 and clips to 7).
+    w = np.zeros((1, 32), np.float32)
+    w[0, :4] = [0.03, -0.05, 0.01, 0.049]
+    u, s = synth.quantize_q4_0(w)
+    assert float(s[0, 0]) == float(np.float16(0.00625))
+    assert list(u[0, :4].astype(int) - 8) == [5, -8, 2, 7]
+    assert np.all(u[0, 4:] == 8)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (2, 64), (2, 32)])
+def test_asym_quantizer_bounds(bits, group):
+    rng = np.random.default_rng(bits * 1000 + group)
+    w = synth.draw_weights(rng, 64, 512)
+    codes, s, z = synth.quantize_asym(w, bits, group)
+    qmax = (1 << bits) - 1
+    assert codes.max() <= qmax and z.max() <= qmax and z.min() >= 0
+    assert np.all(np.floor(z.astype(np.float32)) == z.astype(np.float32))
+    sf = s.astype(np.float32)[:, np.arange(512) // group]
+    zf = z.astype(np.float32)[:, np.arange(512) // group]
+    deq = sf * (codes.astype(np.float32) - zf)
+    unclipped = (codes > 0) & (codes < qmax)
+    # unclipped elements are within half a step of the dense weight
+    assert np.all(np.abs(w - deq)[unclipped] <= 0.5 * sf[unclipped] * (1 + 1e-3))
+    # the group extremes land at (or next to) the ends of the code range
+    wg = w.reshape(64, -1, group)
+    cg = codes.reshape(64, -1, group)
+    lo_code = np.take_along_axis(cg, wg.argmin(axis=2)[:, :, None], 2)
+    hi_code = np.take_along_axis(cg, wg.argmax(axis=2)[:, :, None], 2)
+    assert lo_code.max() <= 1 and hi_code.min() >= qmax - 1
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_generator_words_match_oracle_unpack(fmt):
+    c = synth.random_codes_case(9, fmt, 32 if fmt != 1 else 64, 48, 512, 2)
+    assert np.array_equal(oracle.unpack_codes(c.words, c.N, c.K, fmt), c.codes)
+
+
+def test_workloads_shapes_and_seeds():
+    c = synth.workload("tiny_int4_g32")
+    assert (c.N, c.K, c.M, c.group) == (256, 256, 4, 32)
+    assert c.words.shape == (256, 32) and c.scales.shape == (256, 8)
+    assert np.abs(c.x.astype(np.float32)).max() <= 1.0
+    c2 = synth.workload("tiny_int4_g32")
+    assert np.array_equal(c.words, c2.words) and np.array_equal(c.x, c2.x)
+    p = synth.WORKLOADS["int2_g64"]
+    q = synth.WORKLOADS["q4_0_b32"]
+    assert p["seed"] == q["seed"]     # the same W feeds both formats
