@@ -1,0 +1,278 @@
+"""Python binding of libqgemm.so: weight-only low-bit matmul on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``csrc/``; PyTorch provides device memory and the stream.  There is
+no CPU fallback: importing this package fails loudly when the library has not
+been built (``python bit_weight_only_dequant_amd/build.py``), and device calls
+reject tensors that are not on a GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+INT4_ASYM = 0
+INT2_ASYM = 1
+Q4_0 = 2
+BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python bit_weight_only_dequant_amd/build.py` "
+        "(or __graft_entry__.build()); there is no fallback path")
+
+# PyTorch-ROCm ships its own HIP runtime with the same soname as the system
+# one.  Loading torch first makes libqgemm bind to that already-loaded copy, so
+# the library and torch share one runtime (devices, streams, allocations).
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_I64 = ctypes.c_int64
+
+_SIGS = {
+    "qg_version": ([], _I),
+    "qg_status_str": ([_I], ctypes.c_char_p),
+    "qg_last_error": ([], ctypes.c_char_p),
+    "qg_packed_bytes": ([_I64, _I64, _I], _SZ),
+    "qpack": ([_P, _P, _I, _I, _I, _P], _I),
+    "qunpack": ([_P, _P, _I, _I, _I, _P], _I),
+    "qpack_host": ([_P, _P, _I, _I, _I], _I),
+    "qunpack_host": ([_P, _P, _I, _I, _I], _I),
+    "qgemm": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P], _I),
+    "qgemm_ex": ([_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _SZ, _P], _I),
+    "qgemm_workspace_bytes": ([_I, _I, _I, _I, _I], _SZ),
+    "qloop_block": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "qg_unpack_codes": ([_P, _P, _I, _I, _I, _P], _I),
+    "qg_dequant": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "qg_plan": ([_I, _I, _I, _I, _I, ctypes.POINTER(_I)], _I),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = int(status)
+        msg = status_str(status)
+        if self.status == 4:
+            msg += f" ({_lib.qg_last_error().decode()})"
+        super().__init__(f"{what}: {msg}" if what else msg)
+
+
+def status_str(status: int) -> str:
+    return _lib.qg_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise QGemmError(status, what)
+
+
+def version() -> int:
+    return _lib.qg_version()
+
+
+def cpw(fmt: int) -> int:
+    return 32 // BITS[fmt]
+
+
+def packed_bytes(N: int, K: int, fmt: int) -> int:
+    return int(_lib.qg_packed_bytes(N, K, fmt))
+
+
+def workspace_bytes(M: int, N: int, K: int, group: int, fmt: int) -> int:
+    return int(_lib.qgemm_workspace_bytes(M, N, K, group, fmt))
+
+
+def plan(M: int, N: int, K: int, group: int, fmt: int) -> dict:
+    out = (_I * 5)()
+    _check(_lib.qg_plan(M, N, K, group, fmt, out), "qg_plan")
+    return dict(path={1: "gemv", 2: "gemm"}.get(out[0], "none"), splits=out[1],
+                workgroups=out[2], tile_m=out[3], tile_n=out[4])
+
+
+# ----------------------------------------------------------------------------
+# host repack (numpy)
+# ----------------------------------------------------------------------------
+
+def qpack_host(canon: np.ndarray, N: int, K: int, fmt: int) -> np.ndarray:
+    canon = np.ascontiguousarray(canon, dtype=np.uint32)
+    out = np.zeros(packed_bytes(N, K, fmt) // 4, dtype=np.uint32)
+    _check(_lib.qpack_host(canon.ctypes.data, out.ctypes.data, N, K, fmt), "qpack_host")
+    return out
+
+
+def qunpack_host(packed: np.ndarray, N: int, K: int, fmt: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    out = np.zeros((N, K // cpw(fmt)), dtype=np.uint32)
+    _check(_lib.qunpack_host(packed.ctypes.data, out.ctypes.data, N, K, fmt), "qunpack_host")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# device calls (torch tensors on a GPU)
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, what):
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{what} must be a tensor on the GPU")
+    return t
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device, stream=None) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def to_words_tensor(words: np.ndarray, device="cuda"):
+    """uint32 numpy words -> int32 device tensor holding the same bits."""
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(words, dtype=np.uint32).view(np.int32)).to(device)
+
+
+def to_half_tensor(a: Optional[np.ndarray], device="cuda"):
+    if a is None:
+        return None
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16)).to(device)
+
+
+def qpack(canon, N: int, K: int, fmt: int, out=None, stream=None):
+    """canonical words (int32 bits, [N, K/cpw], device) -> packed buffer (int32, device)."""
+    torch = _torch()
+    _dev(canon, "canon")
+    n_words = packed_bytes(N, K, fmt) // 4
+    if out is None:
+        out = torch.empty(n_words, dtype=torch.int32, device=canon.device)
+    _check(_lib.qpack(_ptr(canon), _ptr(out), N, K, fmt, _stream(canon.device, stream)), "qpack")
+    return out
+
+
+def qunpack(packed, N: int, K: int, fmt: int, stream=None):
+    torch = _torch()
+    _dev(packed, "packed")
+    out = torch.empty((N, K // cpw(fmt)), dtype=torch.int32, device=packed.device)
+    _check(_lib.qunpack(_ptr(packed), _ptr(out), N, K, fmt, _stream(packed.device, stream)), "qunpack")
+    return out
+
+
+def unpack_codes(packed, N: int, K: int, fmt: int, stream=None):
+    torch = _torch()
+    _dev(packed, "packed")
+    out = torch.empty((N, K), dtype=torch.uint8, device=packed.device)
+    _check(_lib.qg_unpack_codes(_ptr(packed), _ptr(out), N, K, fmt, _stream(packed.device, stream)),
+           "qg_unpack_codes")
+    return out
+
+
+def dequant(packed, scales, zeros, N: int, K: int, group: int, fmt: int, stream=None):
+    torch = _torch()
+    _dev(packed, "packed"); _dev(scales, "scales"); _dev(zeros, "zeros")
+    out = torch.empty((N, K), dtype=torch.float16, device=packed.device)
+    _check(_lib.qg_dequant(_ptr(packed), _ptr(scales), _ptr(zeros), _ptr(out), N, K, group, fmt,
+                           _stream(packed.device, stream)), "qg_dequant")
+    return out
+
+
+def qgemm(x, packed, scales, zeros, N: int, K: int, group: int, fmt: int, out=None,
+          residual=None, workspace=None, stream=None):
+    """y = x . dequant(W)^T (+ residual).  x: fp16 [M, K] with unit column
+    stride (any row stride that is a multiple of 8); returns fp16 [M, N]."""
+    torch = _torch()
+    _dev(x, "x"); _dev(packed, "packed"); _dev(scales, "scales"); _dev(zeros, "zeros")
+    _dev(residual, "residual"); _dev(out, "out"); _dev(workspace, "workspace")
+    if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != K or (x.shape[0] > 1 and x.stride(1) != 1):
+        raise ValueError("x must be an fp16 [M, K] tensor with unit column stride")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    ldx = x.stride(0) if M > 1 else K
+    ldy = out.stride(0) if M > 1 else N
+    ldr = (residual.stride(0) if M > 1 else N) if residual is not None else N
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = _lib.qgemm_ex(_ptr(x), ldx, _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(residual), ldr,
+                       M, N, K, group, fmt, _ptr(out), ldy, ws_ptr, ws_bytes, _stream(x.device, stream))
+    _check(st, "qgemm")
+    return out
+
+
+def qgemm_plain(x, packed, scales, zeros, N: int, K: int, group: int, fmt: int, out, stream=None):
+    """The plain `qgemm` entry point (contiguous x and y, library workspace)."""
+    st = _lib.qgemm(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), x.shape[0], N, K, group, fmt,
+                    _ptr(out), _stream(x.device, stream))
+    _check(st, "qgemm")
+    return out
+
+
+class QuantLinear:
+    """One quantized weight matrix resident on the GPU in packed form."""
+
+    def __init__(self, words: np.ndarray, scales: np.ndarray, zeros: Optional[np.ndarray],
+                 N: int, K: int, group: int, fmt: int, device="cuda"):
+        self.N, self.K, self.group, self.fmt = N, K, group, fmt
+        canon = to_words_tensor(words, device)
+        self.packed = qpack(canon, N, K, fmt)
+        self.scales = to_half_tensor(scales, device)
+        self.zeros = to_half_tensor(zeros, device)
+        self.weight_bytes = (self.packed.numel() * 4 + self.scales.numel() * 2 +
+                             (0 if self.zeros is None else self.zeros.numel() * 2))
+
+    @classmethod
+    def from_case(cls, case, device="cuda"):
+        return cls(case.words, case.scales, case.zeros, case.N, case.K, case.group, case.fmt, device)
+
+    def __call__(self, x, out=None, residual=None, workspace=None, stream=None):
+        return qgemm(x, self.packed, self.scales, self.zeros, self.N, self.K, self.group, self.fmt,
+                     out=out, residual=residual, workspace=workspace, stream=stream)
+
+
+def loop_block(x, linears: Sequence[QuantLinear], L: int, scratch=None, events=None, stream=None):
+    """Run the looped shared block in place on x (fp16 [M, D]); see qloop_block."""
+    torch = _torch()
+    _dev(x, "x")
+    qkv, o, up, down = linears
+    M, D = x.shape
+    F = up.N
+    fmt, group = qkv.fmt, qkv.group
+    if scratch is None:
+        scratch = torch.empty(M * (3 * D + D + F), dtype=torch.float16, device=x.device)
+    arr = lambda vals: (ctypes.c_void_p * 4)(*vals)
+    packed4 = arr([l.packed.data_ptr() for l in linears])
+    scales4 = arr([l.scales.data_ptr() for l in linears])
+    zeros4 = arr([None if l.zeros is None else l.zeros.data_ptr() for l in linears])
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * (L + 1))(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in events])
+    st = _lib.qloop_block(_ptr(x), packed4, scales4, zeros4, M, D, F, group, fmt, L, _ptr(scratch),
+                          ev, _stream(x.device, stream))
+    _check(st, "qloop_block")
+    return x

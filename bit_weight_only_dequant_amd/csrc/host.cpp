@@ -1,0 +1,172 @@
+// host.cpp - pure host part of libqgemm: argument validation, launch planning,
+// the host repack, status strings.  Nothing here calls HIP, so every function
+// in this file works (and is tested) on a machine without a GPU.
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/qgemm.h"
+#include "internal.h"
+
+namespace qg {
+
+int check_format_group(int fmt, int group) {
+  if (fmt == QG_Q4_0) return group == 32 ? QG_OK : QG_E_ARG;
+  if (fmt == QG_INT4_ASYM || fmt == QG_INT2_ASYM)
+    return (group == 32 || group == 64 || group == 128) ? QG_OK : QG_E_ARG;
+  return QG_E_ARG;
+}
+
+int check_shape(int M, int N, int K, int group, int fmt) {
+  int st = check_format_group(fmt, group);
+  if (st != QG_OK) return st;
+  if (M < 0 || N < 0 || K < 0) return QG_E_ARG;
+  if (K % group != 0) return QG_E_ARG;
+  return QG_OK;
+}
+
+int check_align(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0 ? QG_OK : QG_E_ALIGN;
+}
+
+int check_ld(int ld, int minimum) { return ld >= minimum ? QG_OK : QG_E_ARG; }
+
+static int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+static bool force_is(const char* what) {
+  const char* v = getenv("QGEMM_FORCE");
+  return v && strcmp(v, what) == 0;
+}
+
+Plan make_plan(int M, int N, int K, int group, int fmt) {
+  (void)group;
+  Plan p;
+  if (M == 0 || N == 0) return p;  // no-op
+  p.rowblocks = (int)n_rowblocks(N);
+  p.wordtiles = (int)n_wordtiles(K, fmt);
+  if (K == 0) return p;             // zero fill
+  const int kt_width = ktile_width(fmt);
+  const bool gemv = force_is("gemm") ? false : (force_is("gemv") ? M <= GEMV_MAX_M : M <= GEMV_MAX_M);
+  const int split_env = env_int("QGEMM_SPLITK", 0);
+  if (gemv) {
+    p.path = 1;
+    p.mmax = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    const int tps_lds = std::max(1, GEMV_LDS_X_BYTES / (p.mmax * kt_width * 2));
+    const int tps_max = std::min(tps_lds, 4 * GEMV_TPW_MAX);
+    const int s_min = (int)ceil_div(p.wordtiles, tps_max);
+    const int s_par = (int)ceil_div(2 * GEMM_TARGET_WG, p.rowblocks);
+    const int s_fill = (int)ceil_div(p.wordtiles, 4);  // keep every wave busy
+    int s = std::max(s_min, std::min(s_par, s_fill));
+    if (split_env > 0) s = std::max(s_min, split_env);
+    s = std::min(std::max(s, 1), p.wordtiles);
+    if (p.rowblocks > WS_COUNTERS) s = s_min;  // counters would not fit
+    p.tps = (int)ceil_div(p.wordtiles, s);
+    p.splits = (int)ceil_div(p.wordtiles, p.tps);
+    if (p.splits > 1 && p.rowblocks > WS_COUNTERS) {
+      p.path = 0;  // K too long for one pass and too many row blocks to split
+      return p;
+    }
+    p.workgroups = (int64_t)p.rowblocks * p.splits;
+    if (p.splits > 1) p.ws_partial_bytes = (size_t)p.rowblocks * p.splits * p.mmax * 16 * sizeof(float);
+    return p;
+  }
+  p.path = 2;
+  p.tiles_n = (int)ceil_div(N, GEMM_TN);
+  p.tiles_m = (int)ceil_div(M, GEMM_TM);
+  const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
+  int s = (int)std::max<int64_t>(1, (GEMM_TARGET_WG + tiles / 2) / tiles);
+  if (split_env > 0) s = split_env;
+  s = std::min(std::max(s, 1), p.wordtiles);
+  if (tiles > WS_COUNTERS) s = 1;
+  p.tps = (int)ceil_div(p.wordtiles, s);
+  p.splits = (int)ceil_div(p.wordtiles, p.tps);
+  p.workgroups = tiles * p.splits;
+  if (p.splits > 1) p.ws_partial_bytes = (size_t)tiles * p.splits * GEMM_THREADS * 64 * sizeof(float);
+  return p;
+}
+
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" {
+
+int qg_version(void) { return 100; }  // 0.1.0
+
+const char* qg_status_str(int status) {
+  switch (status) {
+    case QG_OK: return "QG_OK";
+    case QG_E_ARG: return "QG_E_ARG: invalid size, format, group or pointer";
+    case QG_E_UNSUPPORTED: return "QG_E_UNSUPPORTED: request outside the implemented kernels";
+    case QG_E_ALIGN: return "QG_E_ALIGN: pointer or leading dimension misaligned";
+    case QG_E_DEVICE: return "QG_E_DEVICE: no usable HIP device or a HIP call failed";
+    case QG_E_NOMEM: return "QG_E_NOMEM: workspace allocation failed";
+    case QG_E_WORKSPACE: return "QG_E_WORKSPACE: caller workspace too small";
+    default: return "unknown qgemm status";
+  }
+}
+
+size_t qg_packed_bytes(int64_t N, int64_t K, int fmt) {
+  if (fmt < 0 || fmt > 2 || N < 0 || K < 0) return 0;
+  if (K % cpw_of(fmt) != 0) return 0;
+  return (size_t)n_rowblocks(N) * (size_t)n_wordtiles(K, fmt) * 64 * 4 * sizeof(uint32_t);
+}
+
+static int check_pack_args(const void* a, const void* b, int N, int K, int fmt) {
+  if (fmt < 0 || fmt > 2 || N < 0 || K < 0) return QG_E_ARG;
+  if (K % cpw_of(fmt) != 0) return QG_E_ARG;
+  if ((int64_t)N * K > 0 && (!a || !b)) return QG_E_ARG;
+  return QG_OK;
+}
+
+int qpack_host(const uint32_t* canon, uint32_t* packed, int N, int K, int fmt) {
+  int st = check_pack_args(canon, packed, N, K, fmt);
+  if (st != QG_OK) return st;
+  const int bits = bits_of(fmt);
+  const int64_t kw_n = K / cpw_of(fmt);
+  const int64_t wt = n_wordtiles(K, fmt);
+  const size_t total = qg_packed_bytes(N, K, fmt) / sizeof(uint32_t);
+  if (total) memset(packed, 0, total * sizeof(uint32_t));
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t kw = 0; kw < kw_n; ++kw)
+      packed[packed_index(n, kw, wt)] = perm_word(canon[n * kw_n + kw], bits);
+  return QG_OK;
+}
+
+int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt) {
+  int st = check_pack_args(packed, canon, N, K, fmt);
+  if (st != QG_OK) return st;
+  const int bits = bits_of(fmt);
+  const int64_t kw_n = K / cpw_of(fmt);
+  const int64_t wt = n_wordtiles(K, fmt);
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t kw = 0; kw < kw_n; ++kw)
+      canon[n * kw_n + kw] = unperm_word(packed[packed_index(n, kw, wt)], bits);
+  return QG_OK;
+}
+
+size_t qgemm_workspace_bytes(int M, int N, int K, int group, int fmt) {
+  if (check_shape(M, N, K, group, fmt) != QG_OK) return 0;
+  return make_plan(M, N, K, group, fmt).ws_bytes();
+}
+
+int qg_plan(int M, int N, int K, int group, int fmt, int out[5]) {
+  int st = check_shape(M, N, K, group, fmt);
+  if (st != QG_OK) return st;
+  if (!out) return QG_E_ARG;
+  Plan p = make_plan(M, N, K, group, fmt);
+  out[0] = p.path;
+  out[1] = p.splits;
+  out[2] = (int)p.workgroups;
+  out[3] = p.path == 2 ? GEMM_TM : p.mmax;
+  out[4] = p.path == 2 ? GEMM_TN : 16;
+  return QG_OK;
+}
+
+}  // extern "C"

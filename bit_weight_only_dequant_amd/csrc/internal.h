@@ -1,0 +1,52 @@
+// internal.h - host-side declarations shared by the validation/planning code
+// (host.cpp) and the launchers (kernels.hip).  Not part of the C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace qg {
+
+// Path choice: decode GEMV for M <= GEMV_MAX_M, MFMA GEMM above.
+constexpr int GEMV_MAX_M = 8;
+constexpr int GEMV_THREADS = 256;
+constexpr int GEMV_TPW_MAX = 8;          // word tiles one wave streams per launch
+constexpr int GEMV_LDS_X_BYTES = 32768;  // x slice staged per workgroup
+constexpr int GEMM_THREADS = 256;
+constexpr int GEMM_TM = 128;             // workgroup tile rows (M)
+constexpr int GEMM_TN = 128;             // workgroup tile columns (N)
+constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
+// Split-K arrival counters live in a fixed region at the start of every
+// workspace, so the partials of one problem never overwrite the counters of
+// another.  Problems with more tiles than counters run without split-K.
+constexpr int64_t WS_COUNTERS = 65536;
+constexpr size_t WS_COUNTER_BYTES = (size_t)WS_COUNTERS * 4;
+
+struct Plan {
+  int path = 0;        // 0 none (no-op / zero fill), 1 GEMV, 2 GEMM
+  int mmax = 0;        // GEMV: rows handled per launch (1, 2, 4, 8)
+  int splits = 1;      // K splits
+  int tps = 0;         // word tiles per split
+  int wordtiles = 0;   // total word tiles along K
+  int rowblocks = 0;   // N / 16 (rounded up)
+  int tiles_n = 0;     // GEMM tiles along N
+  int tiles_m = 0;     // GEMM tiles along M
+  int64_t workgroups = 0;
+  // workspace = [WS_COUNTER_BYTES of counters (zero between calls)][fp32 partials]
+  size_t ws_partial_bytes = 0;
+  size_t ws_bytes() const { return splits > 1 ? WS_COUNTER_BYTES + ws_partial_bytes : 0; }
+};
+
+// Validation (pure host, no HIP call).  Return QG_OK or an error status.
+int check_format_group(int fmt, int group);
+int check_shape(int M, int N, int K, int group, int fmt);
+int check_align(const void* p);
+int check_ld(int ld, int minimum);
+
+// Launch plan for a validated problem.  Environment overrides (for tuning and
+// tests): QGEMM_FORCE=gemv|gemm, QGEMM_SPLITK=<n>.
+Plan make_plan(int M, int N, int K, int group, int fmt);
+
+}  // namespace qg

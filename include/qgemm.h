@@ -1,0 +1,190 @@
+/*
+ * qgemm.h - C ABI of libqgemm.so: weight-only low-bit matrix multiply
+ *           y = x . dequant(W)^T on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the "dequantizing matmul" of the skyzh/tiny-llm feature
+ * list (items "Dequantizing Runtimes", "Quantized Matrix Multiplication",
+ * "Dequantization Matrix Multiplications"): low-bit weights are turned back
+ * into full precision inside the compute pass, so the fp16 weight matrix is
+ * never written to memory.  The weight formats are
+ *   - QG_INT4_ASYM: 4-bit codes with per-group fp16 scale and zero point (the
+ *     INT4 "GPTQ zero points" weights of the TinyLoop README, section "Status");
+ *   - QG_INT2_ASYM: 2-bit codes with per-group fp16 scale and zero point (the
+ *     INT2 body weights of the TinyLoop README, "Current Runtime Snapshot");
+ *   - QG_Q4_0: symmetric blocks of 32 with one fp16 scale and no zero point
+ *     (q4_0 of the torchnative guide "Inference with real transformers",
+ *     section "Quantise while loading"), codes stored offset-binary u = q + 8.
+ * For every format  w[n,k] = s[n, k/group] * (q[n,k] - z[n, k/group])  with
+ * z == 8 for q4_0, and  y[m,n] = sum_k x[m,k] * w[n,k].
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named "device" are device memory (hipMalloc or torch tensors on
+ *     the GPU) owned by the caller; the library never keeps or frees them.
+ *     Outputs are caller-allocated and written in place.
+ *   - fp16 buffers are passed as uint16_t (IEEE binary16 bit patterns).
+ *   - Matrices are row-major.  W is [N, K]: groups run along K in one row n.
+ *   - Canonical words: uint32 [N, K/cpw], cpw = 8 (INT4, q4_0) or 16 (INT2);
+ *     code k of row n sits at bits [b*(k%cpw), b*(k%cpw)+b) of word k/cpw.
+ *   - Scales (and zero points) are fp16 [N, K/group], canonical.  Zero points
+ *     hold integers in [0, 2^b - 1]; other values give unspecified results.
+ *   - "stream" is a hipStream_t (NULL = the default stream).  Every device
+ *     call is stream-ordered and asynchronous: QG_OK means "validated and
+ *     launched"; a kernel fault is reported by the caller's next sync.
+ *   - Arguments are validated on the host before any HIP call.  On error the
+ *     function returns a status and launches nothing; nothing aborts or prints.
+ *   - Shapes: group in {32, 64, 128} for INT4/INT2, group == 32 for q4_0;
+ *     K % group == 0; M, N, K >= 0.  Any N and any M are accepted.
+ *   - Device pointers to x, packed, scales, zeros, y and residual must be
+ *     16-byte aligned; leading dimensions must be multiples of 8 elements.
+ *   - Thread safety: calls are re-entrant.  Calls that use the library-owned
+ *     split-K workspace (qgemm, or qgemm_ex with workspace == NULL) must not
+ *     overlap on different streams of one device; give each concurrent stream
+ *     its own workspace through qgemm_ex.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QG_INT4_ASYM = 0,
+  QG_INT2_ASYM = 1,
+  QG_Q4_0 = 2
+} qg_format_t;
+
+typedef enum {
+  QG_OK = 0,
+  QG_E_ARG = 1,          /* a size, format, group or required pointer is invalid */
+  QG_E_UNSUPPORTED = 2,  /* valid request outside what the kernels implement    */
+  QG_E_ALIGN = 3,        /* pointer or leading dimension misaligned              */
+  QG_E_DEVICE = 4,       /* no usable HIP device, or a HIP call failed            */
+  QG_E_NOMEM = 5,        /* the library could not allocate its workspace          */
+  QG_E_WORKSPACE = 6     /* caller workspace too small                            */
+} qg_status_t;
+
+/* Library version as 10000*major + 100*minor + patch. */
+int qg_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qg_status_str(int status);
+
+/* Text of the last HIP error the library met on this thread (after a
+ * QG_E_DEVICE status); "no error" when there was none.  Static string. */
+const char* qg_last_error(void);
+
+/* Bytes of the packed (qpack) code buffer for an [N, K] weight in format fmt:
+ * N and K/cpw are rounded up to multiples of 16 (the tile of 16 rows by 16
+ * words); padding holds zero codes.  Returns 0 for an invalid request. */
+size_t qg_packed_bytes(int64_t N, int64_t K, int fmt);
+
+/*
+ * qpack: one-time repack of canonical words into the tile order the kernels
+ * stream (the analogue of the repack step the TinyLoop README, section
+ * "Status", describes for its tensor-core INT4 path).  A bijection on codes:
+ * qunpack(qpack(c)) == c bit for bit.
+ *   canon  [device, in]  uint32 [N, K/cpw] canonical words.
+ *   packed [device, out] qg_packed_bytes(N, K, fmt) bytes.
+ * Packed order: uint32 [ceil(N/16)][ceil(K/cpw/16)][64 lanes][4 words]; lane
+ * l = 16*g + r holds words 4g..4g+3 of the 16-word slice of row 16*rb + r,
+ * each word with its codes reordered so that even codes fill the low half and
+ * odd codes the high half (code j -> slot (j&1)*cpw/2 + j/2).
+ * Errors: QG_E_ARG (bad format, N or K < 0, K % cpw != 0, NULL with N*K > 0),
+ *         QG_E_ALIGN, QG_E_DEVICE.
+ */
+int qpack(const uint32_t* canon, uint32_t* packed, int N, int K, int fmt, void* stream);
+
+/* Inverse of qpack: packed -> canonical words [N, K/cpw] (device).  Same errors. */
+int qunpack(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt, void* stream);
+
+/* Host versions of qpack / qunpack on host memory (no HIP call): the same
+ * permutation, for offline packing.  Same errors except QG_E_DEVICE. */
+int qpack_host(const uint32_t* canon, uint32_t* packed, int N, int K, int fmt);
+int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt);
+
+/*
+ * qgemm: y[M,N] = x[M,K] . dequant(W)^T with fp32 accumulation and one
+ * round-to-nearest-even to fp16 at the end.
+ *   x      [device, in]  fp16 [M, K], row-major, leading dimension K.
+ *   packed [device, in]  qpack output for W [N, K].
+ *   scales [device, in]  fp16 [N, K/group].
+ *   zeros  [device, in]  fp16 [N, K/group]; must be NULL for QG_Q4_0 and
+ *                        non-NULL for the asymmetric formats.
+ *   y      [device, out] fp16 [M, N], row-major, leading dimension N.
+ * M <= 8 runs the decode GEMV (packed-fp16 dequant, fp32 dot products, no
+ * matrix cores); M > 8 runs the MFMA GEMM (dequant to fp16 in registers,
+ * fp16 MFMA with fp32 accumulation, split-K reduced in a fixed order, so the
+ * result is deterministic).  M == 0 or N == 0 is a no-op; K == 0 writes zeros.
+ * Uses a library-owned per-device workspace, allocated (hipMalloc) on first
+ * need and grown as needed; call once before capturing into a HIP graph.
+ * Errors: QG_E_ARG, QG_E_ALIGN, QG_E_DEVICE, QG_E_NOMEM.
+ */
+int qgemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+          const uint16_t* zeros, int M, int N, int K, int group, int fmt,
+          uint16_t* y, void* stream);
+
+/*
+ * qgemm_ex: qgemm with leading dimensions, an optional fused residual and an
+ * optional caller workspace:  y = x . dequant(W)^T + residual.
+ *   ldx, ldy, ldr  leading dimensions in elements (>= K, >= N, >= N; multiples of 8).
+ *   residual       [device, in] fp16 [M, N] with leading dimension ldr, or NULL.
+ *                  It may alias y only when ldr == ldy (in-place update).
+ *   workspace      [device] caller scratch of ws_bytes >= qgemm_workspace_bytes(),
+ *                  all zero before its first use (the library leaves it zero
+ *                  after every completed call), or NULL for the library's own.
+ * Errors: as qgemm, plus QG_E_WORKSPACE.
+ */
+int qgemm_ex(const uint16_t* x, int ldx, const uint32_t* packed, const uint16_t* scales,
+             const uint16_t* zeros, const uint16_t* residual, int ldr,
+             int M, int N, int K, int group, int fmt, uint16_t* y, int ldy,
+             void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes qgemm_ex needs for this problem (0 when none). */
+size_t qgemm_workspace_bytes(int M, int N, int K, int group, int fmt);
+
+/*
+ * qloop_block: the weight-shared looped block of the TinyLoop README (section
+ * "Why TinyLoop Exists": one block applied L times with the same weights).
+ * For l = 1..L, with D = K of the QKV linear:
+ *     qkv = x . Wqkv^T                  [M, 3D]
+ *     h   = x + qkv[:, 2D:3D] . Wo^T    [M, D]    (residual fused)
+ *     u   = h . Wup^T                   [M, F]
+ *     x   = h + u . Wdown^T             [M, D]    (residual fused)
+ * All four linears share one format and group.
+ *   x        [device, in/out] fp16 [M, D]: x_0 on entry, x_L on return.
+ *   packed4  host array of 4 device pointers (QKV, O, up, down), qpack output.
+ *   scales4, zeros4  host arrays of 4 device pointers (zeros4 entries NULL for q4_0).
+ *   F        the MLP width (N of up, K of down).
+ *   scratch  [device] fp16 buffer of at least M*(3D + D + F) elements.
+ *   events   NULL, or a host array of L+1 hipEvent_t recorded on the stream
+ *            before loop 1 and after each loop (per-loop timing).
+ * Errors: as qgemm_ex (the first failing call's status; nothing later runs).
+ */
+int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
+                const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt,
+                int L, uint16_t* scratch, void* const* events, void* stream);
+
+/* Debug: packed -> integer codes uint8 [N, K] (device), for the bit-exact
+ * check of the kernels' unpack.  Errors as qunpack. */
+int qg_unpack_codes(const uint32_t* packed, uint8_t* codes, int N, int K, int fmt,
+                    void* stream);
+
+/* Debug: packed + scales + zeros -> fp16 w [N, K] (device) through the same
+ * device dequant the GEMM uses: fp16_rne(s * (q - z)).  Errors as qgemm. */
+int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+               uint16_t* w, int N, int K, int group, int fmt, void* stream);
+
+/* Launch plan the library would use (for tracing and tests; no HIP call):
+ * out[0] = path (1 GEMV, 2 GEMM), out[1] = K splits, out[2] = workgroups,
+ * out[3] = tile rows (M), out[4] = tile columns (N).  Errors as qgemm. */
+int qg_plan(int M, int N, int K, int group, int fmt, int out[5]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

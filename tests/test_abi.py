@@ -1,0 +1,158 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/qgemm.h
+declares, validates arguments before any HIP call, and its host repack is the
+documented bijection (checked against the oracle's unpack).  No compute call
+reaches a GPU here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+qgm = pytest.importorskip("bit_weight_only_dequant_amd")
+lib = qgm._lib
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, E_ARG, E_UNSUP, E_ALIGN, E_DEVICE, E_NOMEM, E_WS = range(7)
+A = 0x10000  # a 16-byte aligned fake address: validation never dereferences it
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "qgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(qgm.EXPORTED) == names
+
+
+def gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def qgemm_status(x=A, packed=A, scales=A, zeros=A, M=1, N=16, K=128, group=32, fmt=0, y=A,
+                 ldx=None, ldy=None, resid=None, ldr=None, ws=None, ws_bytes=0):
+    return lib.qgemm_ex(x, K if ldx is None else ldx, packed, scales, zeros, resid,
+                        N if ldr is None else ldr, M, N, K, group, fmt, y,
+                        N if ldy is None else ldy, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(fmt=3), E_ARG),
+    (dict(fmt=-1), E_ARG),
+    (dict(group=48), E_ARG),
+    (dict(group=256), E_ARG),
+    (dict(fmt=2, zeros=None, group=64), E_ARG),      # q4_0 needs group 32
+    (dict(fmt=2, zeros=A, group=32), E_ARG),         # q4_0 takes no zero points
+    (dict(fmt=0, zeros=None), E_ARG),                # asymmetric needs zero points
+    (dict(K=100), E_ARG),                            # K % group
+    (dict(M=-1), E_ARG),
+    (dict(N=-5), E_ARG),
+    (dict(K=-32), E_ARG),
+    (dict(x=None), E_ARG),
+    (dict(packed=None), E_ARG),
+    (dict(scales=None), E_ARG),
+    (dict(y=None), E_ARG),
+    (dict(ldx=64), E_ARG),                           # ldx < K
+    (dict(ldy=8), E_ARG),                            # ldy < N
+    (dict(x=A + 2), E_ALIGN),
+    (dict(packed=A + 4), E_ALIGN),
+    (dict(y=A + 8), E_ALIGN),
+    (dict(ldx=132), E_ALIGN),                        # row starts not 16-byte aligned
+    (dict(resid=A, ldr=4), E_ARG),
+    (dict(resid=A, ldr=32, ldy=16), E_ARG),          # residual aliases y with another stride
+    (dict(M=128, N=1024, K=2048, ws=A, ws_bytes=16), E_WS),
+])
+def test_validation_before_any_hip_call(kw, expect):
+    if kw.get("resid") == A and kw.get("ldr") == 32:
+        kw = dict(kw, y=A)  # alias
+    assert qgemm_status(**kw) == expect
+
+
+def test_empty_calls_are_noops_without_hip():
+    assert qgemm_status(M=0) == OK
+    assert qgemm_status(N=0) == OK
+    assert lib.qgemm(None, None, None, None, 0, 16, 128, 32, 0, None, None) == OK
+
+
+@pytest.mark.skipif(gpu_present(), reason="checks the no-device status; a GPU is present")
+def test_no_device_status():
+    assert qgemm_status() == E_DEVICE
+    assert lib.qpack(A, A, 16, 128, 0, None) == E_DEVICE
+
+
+def test_status_strings():
+    for s in range(7):
+        assert qgm.status_str(s).startswith("QG_")
+    assert "unknown" in qgm.status_str(99)
+
+
+@pytest.mark.parametrize("N,K,fmt,expect", [
+    (16, 128, 0, 1024), (17, 128, 0, 2048), (16, 136, 0, 2048), (6144, 2048, 0, 6291456),
+    (8192, 2048, 1, 4194304), (8192, 2048, 2, 8388608), (0, 128, 0, 0), (16, 100, 0, 0),
+    (16, 128, 5, 0)])
+def test_packed_bytes(N, K, fmt, expect):
+    assert qgm.packed_bytes(N, K, fmt) == expect
+
+
+def decode_packed_by_formula(packed, N, K, fmt):
+    """The packed order as the header documents it, written out in Python."""
+    b = oracle.BITS[fmt]
+    cpw = 32 // b
+    kw_n = K // cpw
+    wt = -(-kw_n // 16)
+    codes = np.zeros((N, K), dtype=np.uint8)
+    for n in range(N):
+        for kw in range(kw_n):
+            rb, r, T, wi = n // 16, n % 16, kw // 16, kw % 16
+            g, t = wi // 4, wi % 4
+            word = int(packed[((rb * wt + T) * 64 + g * 16 + r) * 4 + t])
+            for j in range(cpw):
+                slot = (j & 1) * (cpw // 2) + (j >> 1)
+                codes[n, kw * cpw + j] = (word >> (b * slot)) & ((1 << b) - 1)
+    return codes
+
+
+@pytest.mark.parametrize("fmt,N,K", [(0, 16, 128), (0, 37, 96), (1, 20, 256), (1, 33, 160),
+                                     (2, 48, 64), (0, 5, 384)])
+def test_host_qpack_layout_and_roundtrip(fmt, N, K):
+    c = synth.random_codes_case(N * 7 + K + fmt, fmt, 32, N, K, 1)
+    packed = qgm.qpack_host(c.words, N, K, fmt)
+    assert packed.nbytes == qgm.packed_bytes(N, K, fmt)
+    assert np.array_equal(decode_packed_by_formula(packed, N, K, fmt),
+                          oracle.unpack_codes(c.words, N, K, fmt))
+    assert np.array_equal(qgm.qunpack_host(packed, N, K, fmt), c.words)
+    # padding is zero
+    nz = np.count_nonzero(packed)
+    assert nz <= np.count_nonzero(c.words)
+
+
+def test_host_repack_is_a_permutation_of_codes():
+    c = synth.random_codes_case(3, 0, 32, 64, 512, 1)
+    packed = qgm.qpack_host(c.words, 64, 512, 0)
+    a = np.sort(oracle.unpack_codes(c.words, 64, 512, 0).ravel())
+    b = np.sort(decode_packed_by_formula(packed, 64, 512, 0).ravel())
+    assert np.array_equal(a, b)
+
+
+def test_plans_for_the_workloads():
+    assert qgm.plan(1, 6144, 2048, 128, 0)["path"] == "gemv"
+    assert qgm.plan(8, 6144, 2048, 128, 0)["path"] == "gemv"
+    p = qgm.plan(128, 8192, 2048, 128, 0)
+    assert p["path"] == "gemm" and p["workgroups"] >= 128
+    assert qgm.plan(9, 64, 128, 32, 0)["path"] == "gemm"
+    assert qgm.workspace_bytes(1, 16, 128, 32, 0) == 0
+    assert qgm.workspace_bytes(128, 8192, 2048, 128, 0) > 0

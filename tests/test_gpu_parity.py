@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer work (repack, code unpack) is compared bit for bit; the dequantized
+fp16 weight bit for bit against fp16_rne(s*(q-z)); y within
+max|y - y_ref| <= 2e-3 * max|y_ref|, and bit for bit where the arithmetic is
+exact (one-hot x; x in {-1,0,1} with power-of-two scales).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible", allow_module_level=True)
+import bit_weight_only_dequant_amd as qgm  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev_half(a):
+    return qgm.to_half_tensor(a, DEV)
+
+
+def ref_y(case, x, residual=None):
+    return oracle.qgemm_ref(x, case.words, case.scales, case.zeros, x.shape[0], case.N, case.K,
+                            case.group, case.fmt, residual=residual)
+
+
+def run_gemm(lin, x_np, residual=None, **kw):
+    x = dev_half(x_np)
+    r = dev_half(residual) if residual is not None else None
+    y = lin(x, residual=r, **kw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def check_close(y, yr, what):
+    err = oracle.rel_error(y, yr)
+    say(f"  {what}: rel err {err:.3e}")
+    assert np.all(np.isfinite(y)), what
+    assert oracle.within_tolerance(y, yr), f"{what}: rel err {err}"
+
+
+@pytest.fixture(autouse=True)
+def _clean_env(monkeypatch):
+    monkeypatch.delenv("QGEMM_FORCE", raising=False)
+    monkeypatch.delenv("QGEMM_SPLITK", raising=False)
+    yield
+
+
+# ----------------------------------------------------------------------------
+# integer work: repack and unpack, bit-exact
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,group,N,K", [(0, 32, 256, 256), (0, 128, 6144, 2048), (1, 64, 8192, 2048),
+                                           (2, 32, 8192, 2048), (0, 32, 37, 96), (1, 32, 50, 160),
+                                           (2, 32, 3, 32)])
+def test_repack_and_codes_bit_exact(fmt, group, N, K):
+    say(f"repack fmt={fmt} N={N} K={K}")
+    c = synth.random_codes_case(N + K + fmt, fmt, group, N, K, 1)
+    canon = qgm.to_words_tensor(c.words, DEV)
+    packed = qgm.qpack(canon, N, K, fmt)
+    host = qgm.qpack_host(c.words, N, K, fmt)
+    assert np.array_equal(packed.cpu().numpy().view(np.uint32), host)
+    back = qgm.qunpack(packed, N, K, fmt)
+    assert np.array_equal(back.cpu().numpy().view(np.uint32), c.words)
+    codes = qgm.unpack_codes(packed, N, K, fmt)
+    assert np.array_equal(codes.cpu().numpy(), oracle.unpack_codes(c.words, N, K, fmt))
+
+
+@pytest.mark.parametrize("fmt,group,N,K", [(0, 32, 256, 256), (0, 128, 512, 2048), (1, 64, 256, 2048),
+                                           (1, 32, 64, 512), (2, 32, 256, 2048), (0, 64, 40, 192)])
+def test_dequant_bit_exact(fmt, group, N, K):
+    say(f"dequant fmt={fmt} g={group} N={N} K={K}")
+    c = synth.random_codes_case(7 * N + K + fmt, fmt, group, N, K, 1)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    w = qgm.dequant(lin.packed, lin.scales, lin.zeros, N, K, group, fmt)
+    expect = oracle.dequant_f16(c.words, c.scales, c.zeros, N, K, group, fmt)
+    got = w.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), expect.view(np.uint16))
+
+
+# ----------------------------------------------------------------------------
+# the five workloads
+# ----------------------------------------------------------------------------
+
+WL = [("tiny_int4_g32", 1), ("tiny_int4_g32", 4), ("decode_int4_g128", 1), ("decode_int4_g128", 8),
+      ("prefill_int4_g128", 128), ("int2_g64", 1), ("int2_g64", 128), ("q4_0_b32", 1), ("q4_0_b32", 128)]
+
+_cases = {}
+
+
+def get_case(name):
+    if name not in _cases:
+        c = synth.workload(name)
+        _cases[name] = (c, qgm.QuantLinear.from_case(c, DEV))
+    return _cases[name]
+
+
+@pytest.mark.parametrize("name,M", WL, ids=[f"{n}-M{m}" for n, m in WL])
+def test_workload_parity(name, M):
+    c, lin = get_case(name)
+    say(f"workload {name} M={M} plan={qgm.plan(M, c.N, c.K, c.group, c.fmt)}")
+    x = c.x[:M]
+    y = run_gemm(lin, x)
+    check_close(y, ref_y(c, x), f"{name} M={M}")
+    # codes of the packed buffer are the oracle's codes
+    codes = qgm.unpack_codes(lin.packed, c.N, c.K, c.fmt).cpu().numpy()
+    assert np.array_equal(codes, c.codes)
+
+
+def test_row0_consistency():
+    c, lin = get_case("decode_int4_g128")
+    y1 = run_gemm(lin, c.x[:1])
+    y8 = run_gemm(lin, c.x[:8])
+    check_close(y8[:1], ref_y(c, c.x[:1]), "row 0 of M=8")
+    assert oracle.rel_error(y8[:1], y1) <= 2e-3
+
+
+# ----------------------------------------------------------------------------
+# ragged shapes, forced paths, split-K variants
+# ----------------------------------------------------------------------------
+
+RAGGED = [
+    # fmt, group, N, K, M
+    (0, 32, 16, 32, 1), (0, 32, 100, 96, 3), (0, 64, 130, 192, 5), (0, 128, 1000, 384, 7),
+    (0, 128, 48, 2048, 8), (1, 32, 40, 160, 2), (1, 64, 272, 320, 6), (2, 32, 33, 224, 4),
+    (0, 32, 100, 96, 9), (0, 64, 130, 192, 17), (0, 128, 1000, 384, 100), (0, 128, 300, 2048, 129),
+    (1, 32, 40, 160, 33), (1, 64, 272, 320, 127), (2, 32, 33, 224, 200), (2, 32, 520, 1056, 257),
+    (0, 128, 2048, 8192, 130),
+]
+
+
+@pytest.mark.parametrize("fmt,group,N,K,M", RAGGED)
+def test_ragged_parity(fmt, group, N, K, M):
+    say(f"ragged fmt={fmt} g={group} N={N} K={K} M={M} plan={qgm.plan(M, N, K, group, fmt)}")
+    c = synth.random_codes_case(N * 31 + K * 7 + M + fmt, fmt, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    check_close(run_gemm(lin, c.x), ref_y(c, c.x), "ragged")
+
+
+@pytest.mark.parametrize("force,M", [("gemm", 1), ("gemm", 4), ("gemm", 8), ("gemv", 3)])
+@pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32)])
+def test_forced_path(monkeypatch, force, M, fmt, group):
+    monkeypatch.setenv("QGEMM_FORCE", force)
+    N, K = 272, 1024
+    say(f"forced {force} fmt={fmt} M={M} plan={qgm.plan(M, N, K, group, fmt)}")
+    c = synth.random_codes_case(11 + M + fmt, fmt, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    check_close(run_gemm(lin, c.x), ref_y(c, c.x), f"forced {force}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 16])
+@pytest.mark.parametrize("M", [2, 64])
+def test_split_k_variants(monkeypatch, splits, M):
+    monkeypatch.setenv("QGEMM_SPLITK", str(splits))
+    N, K, group, fmt = 384, 2048, 128, 0
+    say(f"splitk={splits} M={M} plan={qgm.plan(M, N, K, group, fmt)}")
+    c = synth.random_codes_case(splits * 100 + M, fmt, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    check_close(run_gemm(lin, c.x), ref_y(c, c.x), f"splitk {splits}")
+
+
+# ----------------------------------------------------------------------------
+# exact-arithmetic cases: bit-exact outputs whatever the order
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 5, 64, 130])
+@pytest.mark.parametrize("fmt,group", [(0, 32), (0, 128), (1, 64), (2, 32)])
+def test_one_hot_bit_exact(M, fmt, group):
+    N, K = 144, 512
+    say(f"one-hot fmt={fmt} g={group} M={M}")
+    c = synth.random_codes_case(M * 3 + fmt + group, fmt, group, N, K, 1)
+    rng = np.random.default_rng(M)
+    ks = rng.integers(0, K, size=M)
+    x = np.zeros((M, K), np.float16)
+    x[np.arange(M), ks] = 1.0
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    y = run_gemm(lin, x)
+    w16 = oracle.dequant_f16(c.words, c.scales, c.zeros, N, K, group, fmt)
+    expect = w16[:, ks].T
+    assert np.array_equal(y.view(np.uint16), expect.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 8, 128])
+@pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32)])
+def test_exact_regime_bit_exact(M, fmt, group):
+    # x in {-1, 0, 1}, power-of-two scales, integer zero points: every partial
+    # sum is an integer multiple of the smallest scale and exact in fp32
+    N, K = 256, 2048
+    say(f"exact regime fmt={fmt} M={M}")
+    rng = np.random.default_rng(fmt * 10 + M)
+    b = oracle.BITS[fmt]
+    codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
+    s = (2.0 ** rng.integers(-4, 0, size=(N, K // group))).astype(np.float16)
+    z = None if fmt == 2 else rng.integers(0, 1 << b, size=(N, K // group)).astype(np.float16)
+    x = rng.integers(-1, 2, size=(M, K)).astype(np.float16)
+    c = synth.QCase(fmt=fmt, group=group, N=N, K=K, codes=codes, words=synth.pack_words(codes, b),
+                    scales=s, zeros=z, x=x)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    y = run_gemm(lin, x)
+    yr = ref_y(c, x)
+    assert np.all(np.abs(yr) < 2048)
+    assert np.array_equal(y.astype(np.float64), yr.astype(np.float16).astype(np.float64))
+
+
+def test_closed_form_zero_codes():
+    N, K, group = 128, 1024, 128
+    codes = np.zeros((N, K), np.uint8)
+    s = np.full((N, K // group), 0.125, np.float16)
+    z = np.full((N, K // group), 7.0, np.float16)
+    for M in (1, 128):
+        x = np.random.default_rng(M).uniform(-1, 1, size=(M, K)).astype(np.float16)
+        c = synth.QCase(fmt=0, group=group, N=N, K=K, codes=codes, words=synth.pack_words(codes, 4),
+                        scales=s, zeros=z, x=x)
+        y = run_gemm(qgm.QuantLinear.from_case(c, DEV), x)
+        expect = -0.125 * 7.0 * x.astype(np.float64).sum(axis=1, keepdims=True) * np.ones((1, N))
+        check_close(y, expect, f"zero codes M={M}")
+
+
+def test_q4_0_all_eight_is_zero():
+    N, K = 64, 512
+    codes = np.full((N, K), 8, np.uint8)
+    s = np.random.default_rng(0).uniform(0.1, 2, size=(N, K // 32)).astype(np.float16)
+    for M in (1, 32):
+        x = np.random.default_rng(M).standard_normal((M, K)).astype(np.float16)
+        c = synth.QCase(fmt=2, group=32, N=N, K=K, codes=codes, words=synth.pack_words(codes, 4),
+                        scales=s, zeros=None, x=x)
+        y = run_gemm(qgm.QuantLinear.from_case(c, DEV), x)
+        assert np.array_equal(y, np.zeros_like(y))
+
+
+# ----------------------------------------------------------------------------
+# determinism, no stray writes, residual / strides / caller workspace
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,M", [("prefill_int4_g128", 128), ("decode_int4_g128", 1),
+                                    ("int2_g64", 128)])
+def test_deterministic(name, M):
+    c, lin = get_case(name)
+    x = dev_half(c.x[:M])
+    a = lin(x).clone()
+    b = lin(x).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 7, 100])
+def test_no_writes_outside_output(M):
+    N, K, group = 200, 640, 64
+    c = synth.random_codes_case(M + 5, 0, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    x = dev_half(c.x)
+    big = torch.full((M + 2, 256), float("nan"), dtype=torch.float16, device=DEV)
+    out = big[1:M + 1, :N]  # strided view, NaN guard rows and columns around it
+    lin(x, out=out)
+    torch.cuda.synchronize()
+    h = big.cpu().numpy()
+    assert np.all(np.isnan(h[0])) and np.all(np.isnan(h[M + 1])) and np.all(np.isnan(h[1:M + 1, N:]))
+    check_close(h[1:M + 1, :N], ref_y(c, c.x), "strided out")
+
+
+@pytest.mark.parametrize("M", [1, 8, 64])
+def test_residual_and_strided_input(M):
+    N, K, group = 256, 1024, 128
+    c = synth.random_codes_case(M + 77, 0, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    wide = np.random.default_rng(1).standard_normal((M, K + 64)).astype(np.float16)
+    wide[:, 32:32 + K] = c.x
+    xw = dev_half(wide)
+    x_view = xw[:, 32:32 + K]
+    res = np.random.default_rng(2).standard_normal((M, N)).astype(np.float16)
+    y = lin(x_view, residual=dev_half(res))
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), ref_y(c, c.x, residual=res), "residual+strided")
+
+
+def test_caller_workspace():
+    M, N, K, group = 128, 1024, 2048, 128
+    c = synth.random_codes_case(5, 0, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    nbytes = qgm.workspace_bytes(M, N, K, group, 0)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device=DEV)
+    x = dev_half(c.x)
+    y1 = lin(x, workspace=ws).clone()
+    y2 = lin(x, workspace=ws).clone()   # counters were left at zero
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    check_close(y1.cpu().numpy(), ref_y(c, c.x), "caller workspace")
+    with pytest.raises(qgm.QGemmError):
+        lin(x, workspace=torch.zeros(4, dtype=torch.int32, device=DEV))
+
+
+def test_plain_entry_point_and_empty():
+    c, lin = get_case("tiny_int4_g32")
+    x = dev_half(c.x)
+    y = torch.empty((4, c.N), dtype=torch.float16, device=DEV)
+    qgm.qgemm_plain(x, lin.packed, lin.scales, lin.zeros, c.N, c.K, c.group, c.fmt, y)
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), ref_y(c, c.x), "plain qgemm")
+    empty = lin(torch.empty((0, c.K), dtype=torch.float16, device=DEV))
+    assert empty.shape == (0, c.N)
+
+
+def test_k_zero_writes_zeros():
+    packed = torch.zeros(64, dtype=torch.int32, device=DEV)
+    s = torch.ones((16, 1), dtype=torch.float16, device=DEV)
+    x = torch.empty((3, 0), dtype=torch.float16, device=DEV)
+    y = torch.full((3, 16), 5.0, dtype=torch.float16, device=DEV)
+    qgm.qgemm(x, packed, s, s, 16, 0, 32, 0, out=y)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
