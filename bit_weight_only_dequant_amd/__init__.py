@@ -271,7 +271,15 @@ def loop_block(x, linears: Sequence[QuantLinear], L: int, scratch=None, events=N
     zeros4 = arr([None if l.zeros is None else l.zeros.data_ptr() for l in linears])
     ev = None
     if events is not None:
-        ev = (ctypes.c_void_p * (L + 1))(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in events])
+        handles = []
+        for e in events:
+            if hasattr(e, "cuda_event"):
+                if not e.cuda_event:      # torch creates the HIP event on first record
+                    e.record(torch.cuda.current_stream(x.device))
+                handles.append(e.cuda_event)
+            else:
+                handles.append(e)
+        ev = (ctypes.c_void_p * (L + 1))(*handles)
     st = _lib.qloop_block(_ptr(x), packed4, scales4, zeros4, M, D, F, group, fmt, L, _ptr(scratch),
                           ev, _stream(x.device, stream))
     _check(st, "qloop_block")

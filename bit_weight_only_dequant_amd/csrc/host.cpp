@@ -57,21 +57,19 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   if (gemv) {
     p.path = 1;
     p.mmax = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    const int nw = GEMV_THREADS / 64;
     const int tps_lds = std::max(1, GEMV_LDS_X_BYTES / (p.mmax * kt_width * 2));
-    const int tps_max = std::min(tps_lds, 4 * GEMV_TPW_MAX);
+    const int tps_max = std::min(tps_lds, nw * GEMV_TPW_MAX);
     const int s_min = (int)ceil_div(p.wordtiles, tps_max);
-    const int s_par = (int)ceil_div(2 * GEMM_TARGET_WG, p.rowblocks);
-    const int s_fill = (int)ceil_div(p.wordtiles, 4);  // keep every wave busy
+    // split only when there are too few row blocks to fill the chip: a split
+    // costs a second (reduce) launch
+    const int s_par = p.rowblocks >= GEMM_TARGET_WG ? 1 : (int)ceil_div(2 * GEMM_TARGET_WG, p.rowblocks);
+    const int s_fill = (int)ceil_div(p.wordtiles, nw);  // keep every wave busy
     int s = std::max(s_min, std::min(s_par, s_fill));
     if (split_env > 0) s = std::max(s_min, split_env);
     s = std::min(std::max(s, 1), p.wordtiles);
-    if (p.rowblocks > WS_COUNTERS) s = s_min;  // counters would not fit
     p.tps = (int)ceil_div(p.wordtiles, s);
     p.splits = (int)ceil_div(p.wordtiles, p.tps);
-    if (p.splits > 1 && p.rowblocks > WS_COUNTERS) {
-      p.path = 0;  // K too long for one pass and too many row blocks to split
-      return p;
-    }
     p.workgroups = (int64_t)p.rowblocks * p.splits;
     if (p.splits > 1) p.ws_partial_bytes = (size_t)p.rowblocks * p.splits * p.mmax * 16 * sizeof(float);
     return p;
@@ -80,14 +78,21 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   p.tiles_n = (int)ceil_div(N, GEMM_TN);
   p.tiles_m = (int)ceil_div(M, GEMM_TM);
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-  int s = (int)std::max<int64_t>(1, (GEMM_TARGET_WG + tiles / 2) / tiles);
+  // at most 4 word tiles per wave (16 per workgroup); split K across
+  // workgroups only when the tiles leave most compute units idle, since a
+  // split writes fp32 partials and costs a second (reduce) launch
+  const int s_min = (int)ceil_div(p.wordtiles, 4 * GEMM_TPW);
+  int s = tiles >= (GEMM_TARGET_WG * 5) / 8 ? 1 : (int)ceil_div(GEMM_TARGET_WG, tiles);
   if (split_env > 0) s = split_env;
-  s = std::min(std::max(s, 1), p.wordtiles);
-  if (tiles > WS_COUNTERS) s = 1;
+  s = std::min(std::max(s, s_min), p.wordtiles);
   p.tps = (int)ceil_div(p.wordtiles, s);
   p.splits = (int)ceil_div(p.wordtiles, p.tps);
+  if (p.tps > 4 * GEMM_TPW) {  // cannot happen: s >= s_min
+    p.path = 0;
+    return p;
+  }
   p.workgroups = tiles * p.splits;
-  if (p.splits > 1) p.ws_partial_bytes = (size_t)tiles * p.splits * GEMM_THREADS * 64 * sizeof(float);
+  if (p.splits > 1) p.ws_partial_bytes = (size_t)tiles * p.splits * GEMM_TM * GEMM_TN * sizeof(float);
   return p;
 }
 

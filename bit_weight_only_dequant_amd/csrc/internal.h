@@ -11,18 +11,14 @@ namespace qg {
 
 // Path choice: decode GEMV for M <= GEMV_MAX_M, MFMA GEMM above.
 constexpr int GEMV_MAX_M = 8;
-constexpr int GEMV_THREADS = 256;
+constexpr int GEMV_THREADS = 512;          // 8 waves per workgroup
 constexpr int GEMV_TPW_MAX = 8;          // word tiles one wave streams per launch
 constexpr int GEMV_LDS_X_BYTES = 32768;  // x slice staged per workgroup
 constexpr int GEMM_THREADS = 256;
 constexpr int GEMM_TM = 128;             // workgroup tile rows (M)
-constexpr int GEMM_TN = 128;             // workgroup tile columns (N)
+constexpr int GEMM_TN = 32;              // workgroup tile columns (N)
+constexpr int GEMM_TPW = 4;              // word tiles per wave (K per workgroup <= 16 tiles)
 constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
-// Split-K arrival counters live in a fixed region at the start of every
-// workspace, so the partials of one problem never overwrite the counters of
-// another.  Problems with more tiles than counters run without split-K.
-constexpr int64_t WS_COUNTERS = 65536;
-constexpr size_t WS_COUNTER_BYTES = (size_t)WS_COUNTERS * 4;
 
 struct Plan {
   int path = 0;        // 0 none (no-op / zero fill), 1 GEMV, 2 GEMM
@@ -34,9 +30,8 @@ struct Plan {
   int tiles_n = 0;     // GEMM tiles along N
   int tiles_m = 0;     // GEMM tiles along M
   int64_t workgroups = 0;
-  // workspace = [WS_COUNTER_BYTES of counters (zero between calls)][fp32 partials]
-  size_t ws_partial_bytes = 0;
-  size_t ws_bytes() const { return splits > 1 ? WS_COUNTER_BYTES + ws_partial_bytes : 0; }
+  size_t ws_partial_bytes = 0;  // fp32 split-K partials
+  size_t ws_bytes() const { return splits > 1 ? ws_partial_bytes : 0; }
 };
 
 // Validation (pure host, no HIP call).  Return QG_OK or an error status.

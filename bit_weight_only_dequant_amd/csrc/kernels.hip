@@ -16,14 +16,16 @@
 //                        pairs holding exact (q - z), v_dot2_f32_f16 against x
 //                        staged in LDS, fp32 scale per group, reduction over
 //                        lane groups and waves through LDS.
-//   gemm<FMT>            M > 8.  128x128 workgroup tile, 2x2 waves of 64x64.
-//                        x tiles staged in LDS (double-buffered); codes go
-//                        straight from HBM to VGPRs in the MFMA B-operand
-//                        layout, dequantized to fp16 s*(q-z) in registers and
-//                        fed to v_mfma_f32_16x16x32_f16 (fp32 accumulation).
-//   Split-K (both)       fp32 partials in a workspace; the last workgroup of a
-//                        tile to arrive sums them in split order (deterministic)
-//                        and resets the tile's counter.
+//   gemm<FMT>            M > 8.  128x32 workgroup tile; the 4 waves split K
+//                        and are summed through LDS.  x streams into per-wave
+//                        LDS stages with direct loads; codes go from HBM to
+//                        VGPRs in the MFMA B-operand layout, are dequantized
+//                        once to fp16 s*(q-z) in registers and fed to
+//                        v_mfma_f32_32x32x16_f16 (fp32 accumulation).
+//   Split-K (both)       fp32 partials in a workspace, summed in split order by a
+//                        second small kernel (deterministic).  A kernel boundary
+//                        orders the partials; an in-kernel device-scope fence
+//                        per workgroup would write back the whole L2 each time.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,6 +43,7 @@ typedef _Float16 f16;
 typedef f16 h2 __attribute__((ext_vector_type(2)));
 typedef f16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
@@ -187,19 +190,21 @@ __global__ void fill_zero_kernel(f16* __restrict__ y, int M, int N, int ldy,
 // ---------------------------------------------------------------------------
 struct GemvArgs {
   const f16* x; const uint32_t* packed; const f16* scales; const f16* zeros;
-  const f16* resid; f16* y; float* ws; uint32_t* cnt;
+  const f16* resid; f16* y; float* ws;
   int ldx, ldr, ldy, M, N, K, group;
   int wordtiles, rowblocks, splits, tps;
 };
 
-template <int FMT, int MMAX>
+template <int FMT, int MMAX, int TPW>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   using F = Fmt<FMT>;
-  constexpr int TPW = GEMV_TPW_MAX;
+  constexpr int NW = GEMV_THREADS / 64;                     // waves per workgroup
+  constexpr int KSMAX = NW * TPW * F::KT;                   // staged k range, upper bound
+  constexpr int NXC = (MMAX * KSMAX / 8 + GEMV_THREADS - 1) / GEMV_THREADS;  // x chunks per thread
+  static_assert(MMAX * KSMAX * 2 <= GEMV_LDS_X_BYTES, "x slice must fit the LDS stage");
   extern __shared__ __align__(16) uint8_t gemv_smem[];
-  f16* xs = reinterpret_cast<f16*>(gemv_smem);                       // [MMAX][KS]
-  float* red = reinterpret_cast<float*>(gemv_smem + GEMV_LDS_X_BYTES);  // [4 waves][4 g][MMAX][16]
-  __shared__ int last_flag;
+  f16* xs = reinterpret_cast<f16*>(gemv_smem);                          // [MMAX][KS]
+  float* red = reinterpret_cast<float*>(gemv_smem + GEMV_LDS_X_BYTES);  // [NW][4 g][MMAX][16]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
@@ -208,54 +213,63 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   const int T0 = split * a.tps;
   const int T1 = min(a.wordtiles, T0 + a.tps);
   const int ntile = T1 - T0;
-  const int tpw = (ntile + 3) >> 2;
+  const int tpw = (ntile + NW - 1) / NW;     // <= TPW (launch picks TPW)
   const int wt0 = T0 + wave * tpw;
   const int wt1 = min(T1, wt0 + tpw);
   const int KS = ntile * F::KT;             // k range staged for this workgroup
   const int ng = a.K / a.group;
-  const int n = rb * 16 + r;
-  const int nn = min(n, a.N - 1);
-
-  // 1. issue every code load of this wave first
+  const int nn = min(rb * 16 + r, a.N - 1);
+  const uint16_t* sp = reinterpret_cast<const uint16_t*>(a.scales);
+  const uint16_t* zp = reinterpret_cast<const uint16_t*>(a.zeros);
   const u4* pk = reinterpret_cast<const u4*>(a.packed);
-  u4 code[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int T = wt0 + i;
-    code[i] = u4{0u, 0u, 0u, 0u};
-    if (T < wt1) code[i] = pk[((int64_t)rb * a.wordtiles + T) * 64 + lane];
+
+  // 1. Issue every global load before any value is used, with no branches
+  //    (out-of-range indices clamped to a valid address, values masked
+  //    later): the residual this thread may add, the x slice, then tile by
+  //    tile codes and scales/zeros, so each wait covers only the next step.
+  const int om = tid >> 4, orow = tid & 15;
+  float res = 0.0f;
+  if (a.resid && a.splits == 1) {
+    const int mm = min(om, a.M - 1), nc = min(rb * 16 + orow, a.N - 1);
+    res = (float)a.resid[(int64_t)mm * a.ldr + nc];
   }
-  // 2. scales / zero points: one group per 32 codes of a lane
-  f16 sv[TPW][2], zv[TPW][2];
+  const int cpr = KS >> 3;                  // 16-byte chunks per staged row
+  u4 xr[NXC];
+#pragma unroll
+  for (int j = 0; j < NXC; ++j) {
+    const int c = tid + j * GEMV_THREADS;
+    const int m = c / cpr, k = T0 * F::KT + ((c - m * cpr) << 3);
+    const bool ok = c < MMAX * cpr && m < a.M && k < a.K;
+    xr[j] = *reinterpret_cast<const u4*>(ok ? a.x + (int64_t)m * a.ldx + k : a.x);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order: x first
+  u4 code[TPW];
+  uint32_t sraw[TPW][F::LS / 32], zraw[TPW][F::LS / 32];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
-    const int T = wt0 + i;
+    const int T = min(wt0 + i, T1 - 1);
+    code[i] = pk[((int64_t)rb * a.wordtiles + T) * 64 + lane];
 #pragma unroll
     for (int p = 0; p < F::LS / 32; ++p) {
-      sv[i][p] = (f16)0.0f;
-      zv[i][p] = (f16)8.0f;
-      if (T < wt1) {
-        const int grp = min((T * F::KT + g * F::LS + p * 32) / a.group, ng - 1);
-        sv[i][p] = a.scales[(int64_t)nn * ng + grp];
-        if constexpr (F::HAS_Z) zv[i][p] = a.zeros[(int64_t)nn * ng + grp];
-      }
+      const int grp = min((T * F::KT + g * F::LS + p * 32) / a.group, ng - 1);
+      sraw[i][p] = sp[(int64_t)nn * ng + grp];
+      if constexpr (F::HAS_Z) zraw[i][p] = zp[(int64_t)nn * ng + grp];
+      else zraw[i][p] = 0x4800;  // fp16 8.0
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // 3. stage x[0..MMAX)[T0*KT .. T1*KT) in LDS (zeros beyond M and K)
-  {
-    const int chunks_per_row = KS >> 3;
-    const int total = MMAX * chunks_per_row;
-    for (int c = tid; c < total; c += GEMV_THREADS) {
-      const int m = c / chunks_per_row, kk = (c - m * chunks_per_row) << 3;
-      const int k = T0 * F::KT + kk;
-      u4 v = u4{0u, 0u, 0u, 0u};
-      if (m < a.M && k < a.K) v = *reinterpret_cast<const u4*>(a.x + (int64_t)m * a.ldx + k);
-      *reinterpret_cast<u4*>(xs + m * KS + kk) = v;
-    }
+  // 2. stage x[0..MMAX)[T0*KT .. T1*KT) in LDS (zeros beyond M and K)
+#pragma unroll
+  for (int j = 0; j < NXC; ++j) {
+    const int c = tid + j * GEMV_THREADS;
+    const int m = c / cpr, kk = (c - m * cpr) << 3;
+    const bool ok = m < a.M && T0 * F::KT + kk < a.K;
+    if (c < MMAX * cpr) *reinterpret_cast<u4*>(xs + m * KS + kk) = ok ? xr[j] : u4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 
-  // 4. dot products: exact (q - z) pairs against fp16 x pairs, fp32 per group
+  // 3. dot products, tile by tile as the codes land: exact (q - z) pairs
+  //    against fp16 x pairs (v_dot2_f32_f16), fp32 scale once per 32 codes
   float acc[MMAX];
 #pragma unroll
   for (int m = 0; m < MMAX; ++m) acc[m] = 0.0f;
@@ -265,19 +279,20 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
     if (T < wt1) {
       const int kbase = (T - T0) * F::KT + g * F::LS;  // offset inside the staged slice
 #pragma unroll
-      for (int p = 0; p < F::LS / 32; ++p) {            // 32 codes = one group part
+      for (int p = 0; p < F::LS / 32; ++p) {
         float part[MMAX];
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) part[m] = 0.0f;
         h2 q[16];
+        const f16 z = __builtin_bit_cast(f16, (uint16_t)zraw[i][p]);
         if constexpr (FMT == INT2_ASYM) {
-          const ZC2 zc = make_zc2(zv[i][p]);
+          const ZC2 zc = make_zc2(z);
           qmz_int2_half(code[i][2 * p], 0, zc, q);
           qmz_int2_half(code[i][2 * p], 1, zc, q + 4);
           qmz_int2_half(code[i][2 * p + 1], 0, zc, q + 8);
           qmz_int2_half(code[i][2 * p + 1], 1, zc, q + 12);
         } else {
-          const ZC4 zc = make_zc4(zv[i][p]);
+          const ZC4 zc = make_zc4(z);
           qmz_int4(code[i][0], zc, q);
           qmz_int4(code[i][1], zc, q + 4);
           qmz_int4(code[i][2], zc, q + 8);
@@ -289,269 +304,321 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const h8 xv = xp[c];
-            float s = part[m];
-            s = __builtin_amdgcn_fdot2(q[4 * c + 0], h2{xv[0], xv[1]}, s, false);
-            s = __builtin_amdgcn_fdot2(q[4 * c + 1], h2{xv[2], xv[3]}, s, false);
-            s = __builtin_amdgcn_fdot2(q[4 * c + 2], h2{xv[4], xv[5]}, s, false);
-            s = __builtin_amdgcn_fdot2(q[4 * c + 3], h2{xv[6], xv[7]}, s, false);
-            part[m] = s;
+            float sacc = part[m];
+            sacc = __builtin_amdgcn_fdot2(q[4 * c + 0], h2{xv[0], xv[1]}, sacc, false);
+            sacc = __builtin_amdgcn_fdot2(q[4 * c + 1], h2{xv[2], xv[3]}, sacc, false);
+            sacc = __builtin_amdgcn_fdot2(q[4 * c + 2], h2{xv[4], xv[5]}, sacc, false);
+            sacc = __builtin_amdgcn_fdot2(q[4 * c + 3], h2{xv[6], xv[7]}, sacc, false);
+            part[m] = sacc;
           }
         }
-        const float sf = (float)sv[i][p];
+        const float sf = (float)__builtin_bit_cast(f16, (uint16_t)sraw[i][p]);
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) acc[m] = fmaf(sf, part[m], acc[m]);
       }
     }
   }
 
-  // 5. reduce over the 4 lane groups and 4 waves (fixed order)
+  // 4. reduce over the 4 lane groups and NW waves (fixed order)
 #pragma unroll
   for (int m = 0; m < MMAX; ++m) red[((wave * 4 + g) * MMAX + m) * 16 + r] = acc[m];
   __syncthreads();
+  if (tid >= MMAX * 16) return;
   float total = 0.0f;
-  const int om = tid >> 4, orow = tid & 15;
-  if (tid < MMAX * 16) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+  for (int w = 0; w < NW; ++w)
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) total += red[((w * 4 + gg) * MMAX + om) * 16 + orow];
-  }
+    for (int gg = 0; gg < 4; ++gg) total += red[((w * 4 + gg) * MMAX + om) * 16 + orow];
   const int on = rb * 16 + orow;
   if (a.splits == 1) {
-    if (tid < MMAX * 16 && om < a.M && on < a.N) {
-      float v = total;
-      if (a.resid) v += (float)a.resid[(int64_t)om * a.ldr + on];
-      a.y[(int64_t)om * a.ldy + on] = (f16)v;
-    }
+    if (om < a.M && on < a.N) a.y[(int64_t)om * a.ldy + on] = (f16)(total + res);
     return;
   }
-  // split-K: publish the partial, the last arrival reduces in split order
-  float* part = a.ws + ((int64_t)rb * a.splits) * MMAX * 16;
-  if (tid < MMAX * 16) part[split * MMAX * 16 + tid] = total;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&a.cnt[rb], 1u);
-    last_flag = (old == (uint32_t)(a.splits - 1));
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  if (tid < MMAX * 16) {
+  // split-K: this split's partial; gemv_reduce_kernel sums the splits in order
+  a.ws[((int64_t)rb * a.splits + split) * MMAX * 16 + tid] = total;
+}
+
+// Sums the split-K partials of the GEMV in split order (deterministic), adds
+// the residual and rounds once to fp16.  One thread per output.
+__global__ void gemv_reduce_kernel(const float* __restrict__ ws, const f16* __restrict__ resid,
+                                   f16* __restrict__ y, int M, int N, int ldr, int ldy, int splits,
+                                   int mmax) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i / N), n = (int)(i % N);
+    const int rb = n >> 4, r = n & 15;
+    const float* p = ws + ((int64_t)rb * splits) * mmax * 16 + m * 16 + r;
     float v = 0.0f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float ps = (s == split) ? total : __builtin_nontemporal_load(&part[s * MMAX * 16 + tid]);
-      v += ps;
-    }
-    if (om < a.M && on < a.N) {
-      if (a.resid) v += (float)a.resid[(int64_t)om * a.ldr + on];
-      a.y[(int64_t)om * a.ldy + on] = (f16)v;
-    }
+    for (int s = 0; s < splits; ++s) v += p[(int64_t)s * mmax * 16];
+    if (resid) v += (float)resid[(int64_t)m * ldr + n];
+    y[(int64_t)m * ldy + n] = (f16)v;
   }
-  if (tid == 0) a.cnt[rb] = 0u;
 }
 
 // ---------------------------------------------------------------------------
 // prefill GEMM (M > 8): fp16 MFMA on register-dequantized weights
 // ---------------------------------------------------------------------------
-constexpr int A_STRIDE = 272;             // bytes per staged x row (256 + 16 pad)
-constexpr int A_BUF = GEMM_TM * A_STRIDE;  // one stage: 128 rows x 128 k
-
 struct GemmArgs {
   const f16* x; const uint32_t* packed; const f16* scales; const f16* zeros;
-  const f16* resid; f16* y; float* ws; uint32_t* cnt;
+  const f16* resid; f16* y; float* ws;
   int ldx, ldr, ldy, M, N, K, group;
-  int wordtiles, rowblocks, tiles_n, splits, tps, xcd_remap;
+  int wordtiles, rowblocks, tiles_n, splits, tps;
 };
 
+// Output layout of v_mfma_f32_32x32x16_f16: lane l holds, in accumulator
+// element i (0..15), D[8*(i/4) + 4*(l/32) + i%4][l % 32].
+__device__ __forceinline__ int acc_row(int mb, int i, int lane) {
+  return mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// Staging of x for the GEMM, per wave.  A stage is 128 rows x 64 k of x (16
+// KiB): the two 32-k pieces that lane group 0 and lane group 1 supply to four
+// MFMA steps.  Each wave double-buffers its own stages in LDS with direct
+// global->LDS loads (16 per stage per lane), so waves never wait on each
+// other inside the K loop.  Inside a stage, row m holds 8 chunks of 16 bytes;
+// chunk c lands at c ^ (m % 8), so the fragment reads of 8 consecutive rows
+// fall in different banks.
+template <int FMT> struct GemmStage {
+  static constexpr int KT = Fmt<FMT>::KT;
+  static constexpr int SEG = Fmt<FMT>::LS / 32;     // 32-code segments per code chunk
+  static constexpr int STAGES = 2 * SEG;            // stages per word tile: (h, j) pairs
+  static constexpr int STAGE_BYTES = GEMM_TM * 64 * 2;
+  static constexpr int DMA = STAGE_BYTES / (64 * 16);  // direct loads per lane per stage (16)
+  static constexpr int TPW = GEMM_TPW;               // word tiles per wave, at most
+};
+
+template <int N> __device__ __forceinline__ void wait_vm() {
+  // s_waitcnt vmcnt(N) (GFX9 encoding), expcnt and lgkmcnt left at their maximum
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// prefill GEMM (M > 8).  Workgroup tile 128 (M) x 32 (N); the 4 waves split
+// the workgroup's K range and are summed through LDS at the end, so every code
+// is dequantized exactly once.  MFMA v_mfma_f32_32x32x16_f16: B operand lane l
+// = column l % 32, k-slots 8*(l/32)..+7.  Lane l reads its codes from two
+// 16-byte chunks of the packed tile: row block 2*(n0/32) + (l%32)/16, row
+// l%16, lane group g = l/32 + 2h (h = 0, 1), one packed word (8 codes) per
+// MFMA step; the A fragment of a step reads the matching 8 k of x, so A and
+// B agree on the k order.
 template <int FMT>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   using F = Fmt<FMT>;
-  constexpr int STAGES = F::LS / 32;        // 32-k stages per word tile (1 or 2)
-  __shared__ __align__(16) uint8_t smem[2 * A_BUF];
-  __shared__ int last_flag;
+  using S = GemmStage<FMT>;
+  constexpr int SEG = S::SEG;
+  __shared__ __align__(16) uint8_t smem[4 * 2 * S::STAGE_BYTES];   // 4 waves x 2 buffers
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int g = lane >> 4, r = lane & 15;
+  const int g2 = lane >> 5, r = lane & 15;
 
-  // workgroup -> (tile, split); with remap, one tile's splits share an XCD
-  int bid = blockIdx.x;
-  if (a.xcd_remap) bid = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
-  const int tile = bid / a.splits, split = bid - tile * a.splits;
+  const int tile = blockIdx.x / a.splits, split = blockIdx.x - (blockIdx.x / a.splits) * a.splits;
   const int tn = tile % a.tiles_n, tm = tile / a.tiles_n;
   const int m0 = tm * GEMM_TM, n0 = tn * GEMM_TN;
+  // this workgroup's word tiles, then this wave's share
   const int kt0 = split * a.tps;
   const int kt1 = min(a.wordtiles, kt0 + a.tps);
-  const int nst = (kt1 - kt0) * STAGES;
-  const int rbw = (n0 >> 4) + wn * 4;       // first row block of this wave
+  const int per = (kt1 - kt0 + 3) >> 2;
+  const int wt0 = kt0 + wave * per;
+  const int nt = max(0, min(kt1, wt0 + per) - wt0);     // <= S::TPW (plan guarantees)
+  const int nst = nt * S::STAGES;
+
+  const int rb = (n0 >> 4) + ((lane >> 4) & 1);         // this lane's row block
+  const int rbc = min(rb, a.rowblocks - 1);              // columns past N are never stored
+  const int nn = min(rb * 16 + r, a.N - 1);
   const int ng = a.K / a.group;
   const u4* pk = reinterpret_cast<const u4*>(a.packed);
+  const uint16_t* sp = reinterpret_cast<const uint16_t*>(a.scales);
+  const uint16_t* zp = reinterpret_cast<const uint16_t*>(a.zeros);
+  uint8_t* wbuf = smem + wave * 2 * S::STAGE_BYTES;
 
-  f4 acc[4][4];
+  // k offset (inside a word tile) of 32-code segment j of chunk h for lane group gg
+  auto seg_k = [](int gg, int h, int j) { return (gg + 2 * h) * F::LS + j * 32; };
+
+  // 1. codes and scales/zero points of all of this wave's tiles (clamped,
+  //    branch-free), waited for once before the x pipeline starts
+  u4 b[S::TPW][2];
+  uint32_t sv[S::TPW][2][SEG], zv[S::TPW][2][SEG];
+#pragma unroll
+  for (int t = 0; t < S::TPW; ++t) {
+    const int kt = min(wt0 + t, kt1 - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      b[t][h] = pk[((int64_t)rbc * a.wordtiles + kt) * 64 + (g2 + 2 * h) * 16 + r];
+#pragma unroll
+      for (int j = 0; j < SEG; ++j) {
+        const int grp = min((kt * F::KT + seg_k(g2, h, j)) / a.group, ng - 1);
+        sv[t][h][j] = sp[(int64_t)nn * ng + grp];
+        if constexpr (F::HAS_Z) zv[t][h][j] = zp[(int64_t)nn * ng + grp];
+        else zv[t][h][j] = 0x4800;  // fp16 8.0
+      }
+    }
+  }
+  // residual values this thread may add at the end (clamped, branch-free)
+  float res[16];
+  if (a.resid && a.splits == 1) {
+    const int colc = min(n0 + (lane & 31), a.N - 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = min(m0 + acc_row(wave, i, lane), a.M - 1);
+      res[i] = (float)a.resid[(int64_t)row * a.ldr + colc];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) res[i] = 0.0f;
+  }
+
+  // 2. direct x loads of stage st (tile kt, chunk h, segment j) into buffer buf
+  auto issue_stage = [&](int st, int buf) {
+    const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
+    const int kt = wt0 + t;
+    uint8_t* dst = wbuf + buf * S::STAGE_BYTES;
+#pragma unroll
+    for (int c = 0; c < S::DMA; ++c) {
+      const int slot = c * 64 + lane;                   // 16-byte slot this lane fills
+      const int m = slot >> 3, cs = slot & 7;
+      const int ch = cs ^ (m & 7);                      // source chunk: piece ch/4, 8 k at (ch%4)*8
+      const int row = min(m0 + m, a.M - 1);             // rows past M: any finite data
+      const int k = min(kt * F::KT + seg_k(ch >> 2, h, j) + (ch & 3) * 8, a.K - 8);  // past K: scale 0
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(a.x + (int64_t)row * a.ldx + k),
+          (void __attribute__((address_space(3)))*)(dst + c * 1024), 16, 0, 0);
+    }
+  };
+
+  f16v acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
 
-  u4 areg[8];
-  u4 bcur[4], bnext[4];
-  f16 scur[4], zcur[4], snext[4], znext[4];
-
-  auto load_a = [&](int st) {
-    const int kt = kt0 + st / STAGES, j = st % STAGES;
+  // 3. compute stage st from buffer buf: four MFMA steps x four m-blocks.
+  //    st is a compile-time constant after unrolling, so every register
+  //    array index below is static.
+  auto compute_stage = [&](int st, int buf) {
+    const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
+    const int kt = wt0 + t;
+    const uint8_t* abase = wbuf + buf * S::STAGE_BYTES;
+    const u4 bt = b[t][h];
+    const bool live = kt * F::KT + seg_k(g2, h, j) < a.K;   // segment past K: scale 0
+    const h2 s2 = splat(live ? __builtin_bit_cast(f16, (uint16_t)sv[t][h][j]) : (f16)0.0f);
+    const f16 z = __builtin_bit_cast(f16, (uint16_t)zv[t][h][j]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int chunk = tid + c * GEMM_THREADS;
-      const int m = chunk >> 4, seg = (chunk >> 2) & 3, q = chunk & 3;
-      const int k = kt * F::KT + seg * F::LS + j * 32 + q * 8;
-      const int row = m0 + m;
-      u4 v = u4{0u, 0u, 0u, 0u};
-      if (row < a.M && k < a.K) v = *reinterpret_cast<const u4*>(a.x + (int64_t)row * a.ldx + k);
-      areg[c] = v;
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int chunk = tid + c * GEMM_THREADS;
-      const int m = chunk >> 4, seg = (chunk >> 2) & 3, q = chunk & 3;
-      *reinterpret_cast<u4*>(smem + buf * A_BUF + m * A_STRIDE + seg * 64 + q * 16) = areg[c];
-    }
-  };
-  auto load_b = [&](int kt, u4* dst) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rb = rbw + i;
-      dst[i] = u4{0u, 0u, 0u, 0u};
-      if (rb < a.rowblocks) dst[i] = pk[((int64_t)rb * a.wordtiles + kt) * 64 + lane];
-    }
-  };
-  auto load_sz = [&](int st, f16* s, f16* z) {
-    const int kt = kt0 + st / STAGES, j = st % STAGES;
-    const int grp = min((kt * F::KT + g * F::LS + j * 32) / a.group, ng - 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int nn = min((rbw + i) * 16 + r, a.N - 1);
-      s[i] = a.scales[(int64_t)nn * ng + grp];
-      z[i] = F::HAS_Z ? a.zeros[(int64_t)nn * ng + grp] : (f16)8.0f;
-    }
-  };
-
-  load_a(0);
-  load_sz(0, scur, zcur);
-  load_b(kt0, bcur);
-  store_a(0);
-  __syncthreads();
-
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    const int j = st % STAGES;
-    const bool has_next = st + 1 < nst;
-    const bool next_new_tile = ((st + 1) % STAGES) == 0;
-    if (has_next) {
-      load_a(st + 1);
-      load_sz(st + 1, snext, znext);
-      if (next_new_tile) load_b(kt0 + (st + 1) / STAGES, bnext);
-    }
-    // dequant constants of this stage
-    h2 s2[4];
-    ZC4 zc4[4];
-    ZC2 zc2[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s2[i] = splat(scur[i]);
-      if constexpr (FMT == INT2_ASYM) zc2[i] = make_zc2(zcur[i]);
-      else zc4[i] = make_zc4(zcur[i]);
-    }
-    const uint8_t* abase = smem + buf * A_BUF;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      h8 af[4], bf[4];
+    for (int step = 0; step < 4; ++step) {
+      h2 q[4];
+      if constexpr (FMT == INT2_ASYM) qmz_int2_half(bt[2 * j + (step >> 1)], step & 1, make_zc2(z), q);
+      else qmz_int4(bt[step], make_zc4(z), q);
+      const h2 w0 = q[0] * s2, w1 = q[1] * s2, w2 = q[2] * s2, w3 = q[3] * s2;
+      const h8 bf = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+      const int c = g2 * 4 + step;                       // piece g2, 8 k at step*8
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const int m = wm * 64 + mb * 16 + r;
-        af[mb] = *reinterpret_cast<const h8*>(abase + m * A_STRIDE + g * 64 + t * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h2 q[4];
-        if constexpr (FMT == INT2_ASYM) {
-          qmz_int2_half(bcur[i][2 * j + (t >> 1)], t & 1, zc2[i], q);
-        } else {
-          qmz_int4(bcur[i][t], zc4[i], q);
-        }
-        const h2 w0 = q[0] * s2[i], w1 = q[1] * s2[i], w2 = q[2] * s2[i], w3 = q[3] * s2[i];
-        bf[i] = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
-      }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[mb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf[i], acc[mb][i], 0, 0, 0);
-    }
-    if (has_next) {
-      store_a(buf ^ 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        scur[i] = snext[i];
-        zcur[i] = znext[i];
-        if (next_new_tile) bcur[i] = bnext[i];
+        const int m = mb * 32 + (lane & 31);             // m % 8 == lane % 8
+        const h8 af = *reinterpret_cast<const h8*>(abase + (m * 8 + (c ^ (lane & 7))) * 16);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, acc[mb], 0, 0, 0);
       }
     }
-    __syncthreads();
-  }
-
-  // epilogue: lane holds D[4*g + e][r] of each 16x16 block
-  auto write_out = [&](f4 (&v)[4][4]) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = n0 + (wn * 4 + i) * 16 + r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = m0 + wm * 64 + mb * 16 + g * 4 + e;
-          if (row < a.M && col < a.N) {
-            float o = v[mb][i][e];
-            if (a.resid) o += (float)a.resid[(int64_t)row * a.ldr + col];
-            a.y[(int64_t)row * a.ldy + col] = (f16)o;
-          }
-        }
-      }
   };
 
-  if (a.splits == 1) {
-    write_out(acc);
-    return;
-  }
-  f4* wsp = reinterpret_cast<f4*>(a.ws);
-  const int64_t base = (int64_t)tile * a.splits;
+  // 4. x pipeline, two stages in flight per wave.  After the initial full
+  //    wait only direct loads are outstanding, all of one kind, so
+  //    "vmcnt <= 16" means every stage but the newest has landed.  The loop
+  //    is unrolled over the largest stage count; nst is wave-uniform.
+  if (nst > 0) issue_stage(0, 0);
+  if (nst > 1) issue_stage(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) wsp[((base + split) * 16 + q) * GEMM_THREADS + tid] = acc[q >> 2][q & 3];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&a.cnt[tile], 1u);
-    last_flag = (old == (uint32_t)(a.splits - 1));
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  f4 sum[4][4];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) sum[q >> 2][q & 3] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.splits; ++s) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      f4 v;
-      if (s == split) v = acc[q >> 2][q & 3];
-      else v = __builtin_nontemporal_load(&wsp[((base + s) * 16 + q) * GEMM_THREADS + tid]);
-      sum[q >> 2][q & 3] += v;
+  for (int st = 0; st < S::TPW * S::STAGES; ++st) {
+    if (st < nst) {
+      if (st > 0) {
+        if (st + 1 < nst) wait_vm<S::DMA>();
+        else wait_vm<0>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute_stage(st, st & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 2 < nst) {
+        __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0): this buffer's reads done
+        __builtin_amdgcn_sched_barrier(0);
+        issue_stage(st + 2, st & 1);
+      }
     }
   }
-  write_out(sum);
-  if (tid == 0) a.cnt[tile] = 0u;
+
+  // 5. sum the four waves' accumulators through LDS (fixed order)
+  __syncthreads();
+  f4* red = reinterpret_cast<f4*>(smem);                 // [wave][16 quads][64 lanes]
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    red[(wave * 16 + q) * 64 + lane] = f4{acc[q >> 2][4 * (q & 3)], acc[q >> 2][4 * (q & 3) + 1],
+                                          acc[q >> 2][4 * (q & 3) + 2], acc[q >> 2][4 * (q & 3) + 3]};
+  __syncthreads();
+  // wave w finishes m-block w
+  f4 tot[4];
+#pragma unroll
+  for (int quad = 0; quad < 4; ++quad) {
+    f4 v = red[(0 * 16 + wave * 4 + quad) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[(w * 16 + wave * 4 + quad) * 64 + lane];
+    tot[quad] = v;
+  }
+  if (a.splits == 1) {
+    const int col = n0 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = m0 + acc_row(wave, i, lane);
+      if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(tot[i >> 2][i & 3] + res[i]);
+    }
+    return;
+  }
+  // split-K: this split's 128 x 32 partial; gemm_reduce_kernel sums the splits
+  f4* wsp = reinterpret_cast<f4*>(a.ws);
+  const int64_t base = ((int64_t)tile * a.splits + split) * 16;
+#pragma unroll
+  for (int quad = 0; quad < 4; ++quad) wsp[(base + wave * 4 + quad) * 64 + lane] = tot[quad];
+}
+
+// Sums a tile's split partials in split order (deterministic), adds the
+// residual and rounds once to fp16.  One workgroup per 128 x 32 tile; thread
+// (wave w, lane) owns the four accumulator quads of m-block w; all loads are
+// issued first.
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_reduce_kernel(GemmArgs a) {
+  const int tile = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tn = tile % a.tiles_n, tm = tile / a.tiles_n;
+  const int m0 = tm * GEMM_TM, n0 = tn * GEMM_TN;
+  const f4* wsp = reinterpret_cast<const f4*>(a.ws);
+  const int col = n0 + (lane & 31);
+  const int colc = min(col, a.N - 1);
+  float res[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = min(m0 + acc_row(wave, i, lane), a.M - 1);
+    res[i] = a.resid ? (float)a.resid[(int64_t)row * a.ldr + colc] : 0.0f;
+  }
+  constexpr int SMAX = 4;
+  f4 sum[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sum[q] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < a.splits; s0 += SMAX) {
+    f4 v[SMAX][4];
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const int ss = min(s0 + s, a.splits - 1);
+      const int64_t base = ((int64_t)tile * a.splits + ss) * 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[s][q] = wsp[(base + wave * 4 + q) * 64 + lane];
+    }
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s)
+      if (s0 + s < a.splits)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] += v[s][q];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = m0 + acc_row(wave, i, lane);
+    if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(sum[i >> 2][i & 3] + res[i]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -622,19 +689,37 @@ static unsigned grid_for(int64_t total, int threads) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 65536));
 }
 
-template <int FMT, int MMAX>
+template <int FMT, int MMAX, int TPW>
 static void launch_gemv_t(const GemvArgs& a, int64_t wgs, hipStream_t s) {
-  const size_t shm = GEMV_LDS_X_BYTES + 4 * 4 * MMAX * 16 * sizeof(float);
-  hipLaunchKernelGGL((gemv_kernel<FMT, MMAX>), dim3((unsigned)wgs), dim3(GEMV_THREADS), shm, s, a);
+  const size_t shm = GEMV_LDS_X_BYTES + (GEMV_THREADS / 64) * 4 * MMAX * 16 * sizeof(float);
+  hipLaunchKernelGGL((gemv_kernel<FMT, MMAX, TPW>), dim3((unsigned)wgs), dim3(GEMV_THREADS), shm, s, a);
+}
+
+// TPW: word tiles per wave, rounded up to a power of two and capped so that
+// the x slice of MMAX * 4 * TPW tiles fits the 32 KiB LDS stage.  Returns
+// false when the plan asks for more tiles per wave than that (never, for plans
+// made by make_plan).
+template <int FMT, int MMAX>
+static bool launch_gemv_m(const GemvArgs& a, int tpw, int64_t wgs, hipStream_t s) {
+  constexpr int KT = Fmt<FMT>::KT;
+  constexpr int TMAX0 = GEMV_LDS_X_BYTES / (MMAX * (GEMV_THREADS / 64) * KT * 2);
+  constexpr int TMAX = TMAX0 < GEMV_TPW_MAX ? TMAX0 : GEMV_TPW_MAX;
+  constexpr int T2 = TMAX >= 2 ? 2 : 1, T4 = TMAX >= 4 ? 4 : T2, T8 = TMAX >= 8 ? 8 : T4;
+  if (tpw > TMAX) return false;
+  if (tpw <= 1) launch_gemv_t<FMT, MMAX, 1>(a, wgs, s);
+  else if (tpw <= 2) launch_gemv_t<FMT, MMAX, T2>(a, wgs, s);
+  else if (tpw <= 4) launch_gemv_t<FMT, MMAX, T4>(a, wgs, s);
+  else launch_gemv_t<FMT, MMAX, T8>(a, wgs, s);
+  return true;
 }
 
 template <int FMT>
-static void launch_gemv_f(const GemvArgs& a, int mmax, int64_t wgs, hipStream_t s) {
+static bool launch_gemv_f(const GemvArgs& a, int mmax, int tpw, int64_t wgs, hipStream_t s) {
   switch (mmax) {
-    case 1: launch_gemv_t<FMT, 1>(a, wgs, s); break;
-    case 2: launch_gemv_t<FMT, 2>(a, wgs, s); break;
-    case 4: launch_gemv_t<FMT, 4>(a, wgs, s); break;
-    default: launch_gemv_t<FMT, 8>(a, wgs, s); break;
+    case 1: return launch_gemv_m<FMT, 1>(a, tpw, wgs, s);
+    case 2: return launch_gemv_m<FMT, 2>(a, tpw, wgs, s);
+    case 4: return launch_gemv_m<FMT, 4>(a, tpw, wgs, s);
+    default: return launch_gemv_m<FMT, 8>(a, tpw, wgs, s);
   }
 }
 
@@ -682,8 +767,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
     st = library_ws(dev, p.ws_bytes(), &ws);
     if (st != QG_OK) return st;
   }
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws);
-  float* wsf = ws ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + WS_COUNTER_BYTES) : nullptr;
+  float* wsf = reinterpret_cast<float*>(ws);
   if (p.path == 1) {
     GemvArgs a;
     a.x = reinterpret_cast<const f16*>(x);
@@ -693,14 +777,22 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
     a.resid = reinterpret_cast<const f16*>(resid);
     a.y = reinterpret_cast<f16*>(y);
     a.ws = wsf;
-    a.cnt = cnt;
     a.ldx = ldx; a.ldr = ldr; a.ldy = ldy;
     a.M = M; a.N = N; a.K = K; a.group = group;
     a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.splits = p.splits; a.tps = p.tps;
+    const int tpw = (int)ceil_div(p.tps, GEMV_THREADS / 64);
+    bool launched;
     switch (fmt) {
-      case QG_INT4_ASYM: launch_gemv_f<INT4_ASYM>(a, p.mmax, p.workgroups, s); break;
-      case QG_INT2_ASYM: launch_gemv_f<INT2_ASYM>(a, p.mmax, p.workgroups, s); break;
-      default: launch_gemv_f<Q4_0>(a, p.mmax, p.workgroups, s); break;
+      case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, tpw, p.workgroups, s); break;
+      case QG_INT2_ASYM: launched = launch_gemv_f<INT2_ASYM>(a, p.mmax, tpw, p.workgroups, s); break;
+      default: launched = launch_gemv_f<Q4_0>(a, p.mmax, tpw, p.workgroups, s); break;
+    }
+    if (!launched) return QG_E_UNSUPPORTED;
+    if (p.splits > 1) {
+      st = launch_status();
+      if (st != QG_OK) return st;
+      hipLaunchKernelGGL(gemv_reduce_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, s, wsf,
+                         a.resid, a.y, M, N, ldr, ldy, p.splits, p.mmax);
     }
     return launch_status();
   }
@@ -712,17 +804,20 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
   a.resid = reinterpret_cast<const f16*>(resid);
   a.y = reinterpret_cast<f16*>(y);
   a.ws = wsf;
-  a.cnt = cnt;
   a.ldx = ldx; a.ldr = ldr; a.ldy = ldy;
   a.M = M; a.N = N; a.K = K; a.group = group;
   a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.tiles_n = p.tiles_n;
   a.splits = p.splits; a.tps = p.tps;
-  a.xcd_remap = (p.workgroups % 8 == 0) ? 1 : 0;
   const dim3 grid((unsigned)p.workgroups), block(GEMM_THREADS);
   switch (fmt) {
     case QG_INT4_ASYM: hipLaunchKernelGGL(gemm_kernel<INT4_ASYM>, grid, block, 0, s, a); break;
     case QG_INT2_ASYM: hipLaunchKernelGGL(gemm_kernel<INT2_ASYM>, grid, block, 0, s, a); break;
     default: hipLaunchKernelGGL(gemm_kernel<Q4_0>, grid, block, 0, s, a); break;
+  }
+  if (p.splits > 1) {
+    st = launch_status();
+    if (st != QG_OK) return st;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(p.workgroups / p.splits)), block, 0, s, a);
   }
   return launch_status();
 }

@@ -133,9 +133,9 @@ int qgemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
  *   ldx, ldy, ldr  leading dimensions in elements (>= K, >= N, >= N; multiples of 8).
  *   residual       [device, in] fp16 [M, N] with leading dimension ldr, or NULL.
  *                  It may alias y only when ldr == ldy (in-place update).
- *   workspace      [device] caller scratch of ws_bytes >= qgemm_workspace_bytes(),
- *                  all zero before its first use (the library leaves it zero
- *                  after every completed call), or NULL for the library's own.
+ *   workspace      [device] caller scratch of ws_bytes >= qgemm_workspace_bytes()
+ *                  (fp32 split-K partials; no initial contents needed), or NULL
+ *                  for the library's own.
  * Errors: as qgemm, plus QG_E_WORKSPACE.
  */
 int qgemm_ex(const uint16_t* x, int ldx, const uint32_t* packed, const uint16_t* scales,

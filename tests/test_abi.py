@@ -74,7 +74,7 @@ def qgemm_status(x=A, packed=A, scales=A, zeros=A, M=1, N=16, K=128, group=32, f
     (dict(ldx=132), E_ALIGN),                        # row starts not 16-byte aligned
     (dict(resid=A, ldr=4), E_ARG),
     (dict(resid=A, ldr=32, ldy=16), E_ARG),          # residual aliases y with another stride
-    (dict(M=128, N=1024, K=2048, ws=A, ws_bytes=16), E_WS),
+    (dict(M=128, N=1024, K=8192, ws=A, ws_bytes=16), E_WS),
 ])
 def test_validation_before_any_hip_call(kw, expect):
     if kw.get("resid") == A and kw.get("ldr") == 32:
@@ -155,4 +155,4 @@ def test_plans_for_the_workloads():
     assert p["path"] == "gemm" and p["workgroups"] >= 128
     assert qgm.plan(9, 64, 128, 32, 0)["path"] == "gemm"
     assert qgm.workspace_bytes(1, 16, 128, 32, 0) == 0
-    assert qgm.workspace_bytes(128, 8192, 2048, 128, 0) > 0
+    assert qgm.workspace_bytes(128, 2048, 8192, 128, 0) > 0   # split-K for small N

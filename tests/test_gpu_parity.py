@@ -321,3 +321,26 @@ def test_k_zero_writes_zeros():
     qgm.qgemm(x, packed, s, s, 16, 0, 32, 0, out=y)
     torch.cuda.synchronize()
     assert torch.count_nonzero(y).item() == 0
+
+
+@pytest.mark.parametrize("name,M", [("decode_int4_g128", 1), ("prefill_int4_g128", 128), ("int2_g64", 8)])
+def test_graph_replays_match_eager(name, M):
+    # the benchmark captures calls in a HIP graph: every replay, with eager
+    # work and synchronisation in between, must equal the eager result
+    c, lin = get_case(name)
+    x = dev_half(c.x[:M])
+    eager = lin(x).clone()
+    torch.cuda.synchronize()
+    y = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lin(x, out=y)
+        lin(x, out=y)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        other = lin(x)            # eager call between replays (same workspace)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(other.view(torch.int16), eager.view(torch.int16))
