@@ -178,14 +178,18 @@ def calibration_copy(torch, nbytes=512 << 20, reps=3):
     print(json.dumps(dict(calibration_copy_bytes=nbytes, reps=reps)), flush=True)
 
 
-def load_traffic(kernel, launches_unit="per launch"):
+def load_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the
+    kernel sources changed since the counters were taken."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except Exception:
         return None
     if t.get("kernel_src_sha") != kernel_hash():
         return None  # counters were taken on other kernel code
-    return t.get(kernel)
+    entry = t.get(kernel)
+    return None if entry is None else entry.get("bytes")
 
 
 def main():
