@@ -14,8 +14,9 @@
 //   gemv<FMT, MMAX>      M <= 8.  Bandwidth-bound.  One 16-byte code load per
 //                        lane per 16x16-word tile, unpack by mask into fp16
 //                        pairs holding exact (q - z), v_dot2_f32_f16 against x
-//                        staged in LDS, fp32 scale per group, reduction over
-//                        lane groups and waves through LDS.
+//                        that each wave stages for itself in LDS, fp32 scale
+//                        per group, lane groups summed by lane shuffles and
+//                        waves through LDS.
 //   gemm<FMT>            M > 8.  128x32 workgroup tile; the 4 waves split K
 //                        and are summed through LDS.  x streams into per-wave
 //                        LDS stages with direct loads; codes go from HBM to
@@ -195,140 +196,200 @@ struct GemvArgs {
   int wordtiles, rowblocks, splits, tps;
 };
 
+// (w & m) | c as one VOP3 instruction.  With both constants literal the
+// compiler emits v_and + v_or, since VOP3 on this target takes no literal;
+// here the mask sits in an SGPR and the magic in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(w), "s"(m), "v"(c));
+  return d;
+}
+
+// sum over lanes l, l^16, l^32, l^48 (result in every lane)
+__device__ __forceinline__ float sum_lane_groups(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// LDS bytes of gemv_kernel: per wave its x slice and (scale, zero) pairs, then
+// the cross-wave sums
+template <int FMT, int MMAX, int TPW> constexpr size_t gemv_lds_bytes() {
+  constexpr int KW = TPW * Fmt<FMT>::KT, NW = GEMV_THREADS / 64;
+  return (size_t)NW * (MMAX * KW * 2 + 16 * (KW / 32) * 4) + (size_t)NW * MMAX * 16 * sizeof(float);
+}
+
+// Decode GEMV (M <= 8).  Workgroup = one 16-row block (x one K split); its NW
+// waves take consecutive runs of word tiles.  Each wave stages only its own x
+// slice and (scale, zero) pairs in its own LDS region, so no wave waits for
+// another until the final sum.  Per lane and tile: one 16-byte code load,
+// masks into fp16 pairs holding exact (q - z) (one v_and_or_b32 plus one
+// packed add or fma per pair), v_dot2_f32_f16 against fp16 x pairs, the fp32
+// scale once per 32 (INT4) or 64 (INT2) codes.
 template <int FMT, int MMAX, int TPW>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   using F = Fmt<FMT>;
-  constexpr int NW = GEMV_THREADS / 64;                     // waves per workgroup
-  constexpr int KSMAX = NW * TPW * F::KT;                   // staged k range, upper bound
-  constexpr int NXC = (MMAX * KSMAX / 8 + GEMV_THREADS - 1) / GEMV_THREADS;  // x chunks per thread
-  static_assert(MMAX * KSMAX * 2 <= GEMV_LDS_X_BYTES, "x slice must fit the LDS stage");
-  extern __shared__ __align__(16) uint8_t gemv_smem[];
-  f16* xs = reinterpret_cast<f16*>(gemv_smem);                          // [MMAX][KS]
-  float* red = reinterpret_cast<float*>(gemv_smem + GEMV_LDS_X_BYTES);  // [NW][4 g][MMAX][16]
+  constexpr int NW = GEMV_THREADS / 64;
+  constexpr int KW = TPW * F::KT;              // k range of one wave
+  constexpr int GWMAX = KW / 32;               // groups per wave, at most (group >= 32)
+  constexpr int XCH = MMAX * KW / 8;           // 16-byte x chunks per wave
+  constexpr int NXC = (XCH + 63) / 64;
+  constexpr int NSZ = (16 * GWMAX + 63) / 64;  // (scale, zero) loads per lane, at most
+  constexpr int XB = MMAX * KW * 2, WB = XB + 16 * GWMAX * 4;
+  __shared__ __align__(16) uint8_t gemv_smem[gemv_lds_bytes<FMT, MMAX, TPW>()];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f16* xs = reinterpret_cast<f16*>(gemv_smem + wave * WB);                 // [MMAX][KW]
+  uint32_t* sz = reinterpret_cast<uint32_t*>(gemv_smem + wave * WB + XB);  // [16][GWMAX] s | z << 16
+  float* red = reinterpret_cast<float*>(gemv_smem + NW * WB);              // [NW][MMAX][16]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
-  const int rb = blockIdx.x % a.rowblocks;
-  const int split = blockIdx.x / a.rowblocks;
-  const int T0 = split * a.tps;
-  const int T1 = min(a.wordtiles, T0 + a.tps);
-  const int ntile = T1 - T0;
-  const int tpw = (ntile + NW - 1) / NW;     // <= TPW (launch picks TPW)
+  const int rb = blockIdx.x, split = blockIdx.y;
+  const int T0 = split * a.tps, T1 = min(a.wordtiles, T0 + a.tps);
+  const int tpw = (T1 - T0 + NW - 1) / NW;           // <= TPW (the launch picks TPW)
   const int wt0 = T0 + wave * tpw;
-  const int wt1 = min(T1, wt0 + tpw);
-  const int KS = ntile * F::KT;             // k range staged for this workgroup
-  const int ng = a.K / a.group;
-  const int nn = min(rb * 16 + r, a.N - 1);
-  const uint16_t* sp = reinterpret_cast<const uint16_t*>(a.scales);
-  const uint16_t* zp = reinterpret_cast<const uint16_t*>(a.zeros);
-  const u4* pk = reinterpret_cast<const u4*>(a.packed);
+  const int nt = max(0, min(T1, wt0 + tpw) - wt0);   // word tiles of this wave
+  const int k0 = wt0 * F::KT;                         // a group boundary (KT % group == 0)
+  const int lg = __builtin_ctz(a.group);
+  const int ng = a.K >> lg;
+  const int gstride = KW >> lg;                       // groups per full wave, a power of two
+  const int lgs = __builtin_ctz(gstride);
+  const int gs0 = k0 >> lg;
 
-  // 1. Issue every global load before any value is used, with no branches
-  //    (out-of-range indices clamped to a valid address, values masked
-  //    later): the residual this thread may add, the x slice, then tile by
-  //    tile codes and scales/zeros, so each wait covers only the next step.
+  // 1. Every global load first, with no branches (offsets of out-of-range
+  //    entries clamped to 0, values masked later): scales and zeros, the
+  //    residual, this wave's x slice, then its code tiles.
+  const int64_t szbase = (int64_t)rb * 16 * ng * 2;
+  const char* sp = reinterpret_cast<const char*>(a.scales) + szbase;
+  const char* zp = reinterpret_cast<const char*>(F::HAS_Z ? a.zeros : a.scales) + szbase;
+  uint32_t sraw[NSZ], zraw[NSZ];
+#pragma unroll
+  for (int j = 0; j < NSZ; ++j) {
+    const int e = lane + 64 * j;  // entry (row e >> lgs, group gs0 + e % gstride)
+    const int er = e >> lgs, eg = gs0 + (e & (gstride - 1));
+    const bool ok = e < 16 * gstride && rb * 16 + er < a.N && eg < ng;
+    const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
+    sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
+    if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+    else zraw[j] = 0x4800;  // fp16 8.0
+  }
   const int om = tid >> 4, orow = tid & 15;
   float res = 0.0f;
   if (a.resid && a.splits == 1) {
     const int mm = min(om, a.M - 1), nc = min(rb * 16 + orow, a.N - 1);
     res = (float)a.resid[(int64_t)mm * a.ldr + nc];
   }
-  const int cpr = KS >> 3;                  // 16-byte chunks per staged row
+  __builtin_amdgcn_sched_barrier(0);
   u4 xr[NXC];
 #pragma unroll
   for (int j = 0; j < NXC; ++j) {
-    const int c = tid + j * GEMV_THREADS;
-    const int m = c / cpr, k = T0 * F::KT + ((c - m * cpr) << 3);
-    const bool ok = c < MMAX * cpr && m < a.M && k < a.K;
-    xr[j] = *reinterpret_cast<const u4*>(ok ? a.x + (int64_t)m * a.ldx + k : a.x);
+    const int c = lane + 64 * j;
+    const int m = c / (KW / 8), k = k0 + (c % (KW / 8)) * 8;
+    const bool ok = c < XCH && m < a.M && k < a.K;
+    const uint32_t off = ok ? (uint32_t)(m * a.ldx + k) * 2u : 0u;
+    xr[j] = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(a.x) + off);
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep the issue order: x first
+  __builtin_amdgcn_sched_barrier(0);
   u4 code[TPW];
-  uint32_t sraw[TPW][F::LS / 32], zraw[TPW][F::LS / 32];
+  const char* pkrow = reinterpret_cast<const char*>(a.packed) + (int64_t)rb * a.wordtiles * 1024;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
-    const int T = min(wt0 + i, T1 - 1);
-    code[i] = pk[((int64_t)rb * a.wordtiles + T) * 64 + lane];
-#pragma unroll
-    for (int p = 0; p < F::LS / 32; ++p) {
-      const int grp = min((T * F::KT + g * F::LS + p * 32) / a.group, ng - 1);
-      sraw[i][p] = sp[(int64_t)nn * ng + grp];
-      if constexpr (F::HAS_Z) zraw[i][p] = zp[(int64_t)nn * ng + grp];
-      else zraw[i][p] = 0x4800;  // fp16 8.0
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    const int T = min(wt0 + i, a.wordtiles - 1);
+    code[i] = *reinterpret_cast<const u4*>(pkrow + (uint32_t)(T * 1024 + lane * 16));
   }
-  // 2. stage x[0..MMAX)[T0*KT .. T1*KT) in LDS (zeros beyond M and K)
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. Stage this wave's x (zeros beyond M and K) and its (scale, zero)
+  //    pairs.  Only this wave reads them: LDS operations of one wave complete
+  //    in order, so a wave-level barrier (no s_barrier) suffices.
 #pragma unroll
   for (int j = 0; j < NXC; ++j) {
-    const int c = tid + j * GEMV_THREADS;
-    const int m = c / cpr, kk = (c - m * cpr) << 3;
-    const bool ok = m < a.M && T0 * F::KT + kk < a.K;
-    if (c < MMAX * cpr) *reinterpret_cast<u4*>(xs + m * KS + kk) = ok ? xr[j] : u4{0u, 0u, 0u, 0u};
+    const int c = lane + 64 * j;
+    const int m = c / (KW / 8), kk = (c % (KW / 8)) * 8;
+    const bool ok = m < a.M && k0 + kk < a.K;
+    if (c < XCH) *reinterpret_cast<u4*>(xs + m * KW + kk) = ok ? xr[j] : u4{0u, 0u, 0u, 0u};
   }
-  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NSZ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < 16 * gstride) sz[(e >> lgs) * GWMAX + (e & (gstride - 1))] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // 3. dot products, tile by tile as the codes land: exact (q - z) pairs
-  //    against fp16 x pairs (v_dot2_f32_f16), fp32 scale once per 32 codes
+  // 3. Dot products, tile by tile and 32 codes at a time (a lane holds 32
+  //    INT4 or 64 INT2 codes, and a group may be 32 wide): exact (q - z)
+  //    pairs against fp16 x pairs (v_dot2_f32_f16, fp32 accumulation), fp32
+  //    scale once per 32 codes.
+  const uint32_t magic = 0x64006400u;
   float acc[MMAX];
 #pragma unroll
   for (int m = 0; m < MMAX; ++m) acc[m] = 0.0f;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
-    const int T = wt0 + i;
-    if (T < wt1) {
-      const int kbase = (T - T0) * F::KT + g * F::LS;  // offset inside the staged slice
+    if (i < nt) {
 #pragma unroll
       for (int p = 0; p < F::LS / 32; ++p) {
-        float part[MMAX];
-#pragma unroll
-        for (int m = 0; m < MMAX; ++m) part[m] = 0.0f;
+        const uint32_t szv = sz[r * GWMAX + ((i * F::KT + g * F::LS + p * 32) >> lg)];
+        const float sf = (float)__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu));
+        const f16 z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
         h2 q[16];
-        const f16 z = __builtin_bit_cast(f16, (uint16_t)zraw[i][p]);
         if constexpr (FMT == INT2_ASYM) {
           const ZC2 zc = make_zc2(z);
-          qmz_int2_half(code[i][2 * p], 0, zc, q);
-          qmz_int2_half(code[i][2 * p], 1, zc, q + 4);
-          qmz_int2_half(code[i][2 * p + 1], 0, zc, q + 8);
-          qmz_int2_half(code[i][2 * p + 1], 1, zc, q + 12);
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t w = code[i][2 * p + t], v = h ? (w >> 8) : w;
+              q[8 * t + 4 * h + 0] = as_h2(and_or(v, 0x00030003u, magic)) + zc.c0;
+              q[8 * t + 4 * h + 1] = as_h2(and_or(v, 0x000C000Cu, magic)) * splat((f16)0.25f) + zc.c1;
+              q[8 * t + 4 * h + 2] = as_h2(and_or(v, 0x00300030u, magic)) * splat((f16)0.0625f) + zc.c2;
+              q[8 * t + 4 * h + 3] = as_h2(and_or(v, 0x00C000C0u, magic)) * splat((f16)0.015625f) + zc.c3;
+            }
         } else {
           const ZC4 zc = make_zc4(z);
-          qmz_int4(code[i][0], zc, q);
-          qmz_int4(code[i][1], zc, q + 4);
-          qmz_int4(code[i][2], zc, q + 8);
-          qmz_int4(code[i][3], zc, q + 12);
+          const h2 inv16 = splat((f16)0.0625f);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t w = code[i][t], w8 = w >> 8;
+            q[4 * t + 0] = as_h2(and_or(w, 0x000F000Fu, magic)) + zc.c0;
+            q[4 * t + 1] = as_h2(and_or(w, 0x00F000F0u, magic)) * inv16 + zc.c1;
+            q[4 * t + 2] = as_h2(and_or(w8, 0x000F000Fu, magic)) + zc.c0;
+            q[4 * t + 3] = as_h2(and_or(w8, 0x00F000F0u, magic)) * inv16 + zc.c1;
+          }
         }
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) {
-          const h8* xp = reinterpret_cast<const h8*>(xs + m * KS + kbase + p * 32);
+          const h8* xp = reinterpret_cast<const h8*>(xs + m * KW + i * F::KT + g * F::LS + p * 32);
+          float A0 = 0.0f, A1 = 0.0f;  // two chains for issue overlap
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const h8 xv = xp[c];
-            float sacc = part[m];
-            sacc = __builtin_amdgcn_fdot2(q[4 * c + 0], h2{xv[0], xv[1]}, sacc, false);
-            sacc = __builtin_amdgcn_fdot2(q[4 * c + 1], h2{xv[2], xv[3]}, sacc, false);
-            sacc = __builtin_amdgcn_fdot2(q[4 * c + 2], h2{xv[4], xv[5]}, sacc, false);
-            sacc = __builtin_amdgcn_fdot2(q[4 * c + 3], h2{xv[6], xv[7]}, sacc, false);
-            part[m] = sacc;
+            float t0 = (c & 1) ? A1 : A0;
+            t0 = __builtin_amdgcn_fdot2(q[4 * c + 0], h2{xv[0], xv[1]}, t0, false);
+            t0 = __builtin_amdgcn_fdot2(q[4 * c + 1], h2{xv[2], xv[3]}, t0, false);
+            t0 = __builtin_amdgcn_fdot2(q[4 * c + 2], h2{xv[4], xv[5]}, t0, false);
+            t0 = __builtin_amdgcn_fdot2(q[4 * c + 3], h2{xv[6], xv[7]}, t0, false);
+            if (c & 1) A1 = t0; else A0 = t0;
           }
+          acc[m] = fmaf(sf, A0 + A1, acc[m]);
         }
-        const float sf = (float)__builtin_bit_cast(f16, (uint16_t)sraw[i][p]);
-#pragma unroll
-        for (int m = 0; m < MMAX; ++m) acc[m] = fmaf(sf, part[m], acc[m]);
       }
     }
   }
 
-  // 4. reduce over the 4 lane groups and NW waves (fixed order)
+  // 4. Sum the 4 lane groups across lanes, then the NW waves through LDS in
+  //    wave order (deterministic).
 #pragma unroll
-  for (int m = 0; m < MMAX; ++m) red[((wave * 4 + g) * MMAX + m) * 16 + r] = acc[m];
+  for (int m = 0; m < MMAX; ++m) {
+    const float v = sum_lane_groups(acc[m]);
+    if (g == 0) red[(wave * MMAX + m) * 16 + r] = v;
+  }
   __syncthreads();
   if (tid >= MMAX * 16) return;
   float total = 0.0f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w)
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) total += red[((w * 4 + gg) * MMAX + om) * 16 + orow];
+  for (int w = 0; w < NW; ++w) total += red[(w * MMAX + om) * 16 + orow];
   const int on = rb * 16 + orow;
   if (a.splits == 1) {
     if (om < a.M && on < a.N) a.y[(int64_t)om * a.ldy + on] = (f16)(total + res);
@@ -689,10 +750,12 @@ static unsigned grid_for(int64_t total, int threads) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 65536));
 }
 
+// grid: x = row blocks, y = K splits
 template <int FMT, int MMAX, int TPW>
-static void launch_gemv_t(const GemvArgs& a, int64_t wgs, hipStream_t s) {
-  const size_t shm = GEMV_LDS_X_BYTES + (GEMV_THREADS / 64) * 4 * MMAX * 16 * sizeof(float);
-  hipLaunchKernelGGL((gemv_kernel<FMT, MMAX, TPW>), dim3((unsigned)wgs), dim3(GEMV_THREADS), shm, s, a);
+static void launch_gemv_t(const GemvArgs& a, hipStream_t s) {
+  static_assert(gemv_lds_bytes<FMT, MMAX, TPW>() <= 80 * 1024, "GEMV LDS: at least two workgroups per CU");
+  hipLaunchKernelGGL((gemv_kernel<FMT, MMAX, TPW>), dim3((unsigned)a.rowblocks, (unsigned)a.splits),
+                     dim3(GEMV_THREADS), 0, s, a);
 }
 
 // TPW: word tiles per wave, rounded up to a power of two and capped so that
@@ -700,26 +763,26 @@ static void launch_gemv_t(const GemvArgs& a, int64_t wgs, hipStream_t s) {
 // false when the plan asks for more tiles per wave than that (never, for plans
 // made by make_plan).
 template <int FMT, int MMAX>
-static bool launch_gemv_m(const GemvArgs& a, int tpw, int64_t wgs, hipStream_t s) {
+static bool launch_gemv_m(const GemvArgs& a, int tpw, hipStream_t s) {
   constexpr int KT = Fmt<FMT>::KT;
   constexpr int TMAX0 = GEMV_LDS_X_BYTES / (MMAX * (GEMV_THREADS / 64) * KT * 2);
   constexpr int TMAX = TMAX0 < GEMV_TPW_MAX ? TMAX0 : GEMV_TPW_MAX;
   constexpr int T2 = TMAX >= 2 ? 2 : 1, T4 = TMAX >= 4 ? 4 : T2, T8 = TMAX >= 8 ? 8 : T4;
   if (tpw > TMAX) return false;
-  if (tpw <= 1) launch_gemv_t<FMT, MMAX, 1>(a, wgs, s);
-  else if (tpw <= 2) launch_gemv_t<FMT, MMAX, T2>(a, wgs, s);
-  else if (tpw <= 4) launch_gemv_t<FMT, MMAX, T4>(a, wgs, s);
-  else launch_gemv_t<FMT, MMAX, T8>(a, wgs, s);
+  if (tpw <= 1) launch_gemv_t<FMT, MMAX, 1>(a, s);
+  else if (tpw <= 2) launch_gemv_t<FMT, MMAX, T2>(a, s);
+  else if (tpw <= 4) launch_gemv_t<FMT, MMAX, T4>(a, s);
+  else launch_gemv_t<FMT, MMAX, T8>(a, s);
   return true;
 }
 
 template <int FMT>
-static bool launch_gemv_f(const GemvArgs& a, int mmax, int tpw, int64_t wgs, hipStream_t s) {
+static bool launch_gemv_f(const GemvArgs& a, int mmax, int tpw, hipStream_t s) {
   switch (mmax) {
-    case 1: return launch_gemv_m<FMT, 1>(a, tpw, wgs, s);
-    case 2: return launch_gemv_m<FMT, 2>(a, tpw, wgs, s);
-    case 4: return launch_gemv_m<FMT, 4>(a, tpw, wgs, s);
-    default: return launch_gemv_m<FMT, 8>(a, tpw, wgs, s);
+    case 1: return launch_gemv_m<FMT, 1>(a, tpw, s);
+    case 2: return launch_gemv_m<FMT, 2>(a, tpw, s);
+    case 4: return launch_gemv_m<FMT, 4>(a, tpw, s);
+    default: return launch_gemv_m<FMT, 8>(a, tpw, s);
   }
 }
 
@@ -780,12 +843,16 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
     a.ldx = ldx; a.ldr = ldr; a.ldy = ldy;
     a.M = M; a.N = N; a.K = K; a.group = group;
     a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.splits = p.splits; a.tps = p.tps;
+    // the kernel forms byte offsets of x and of one row block's codes in 32 bits
+    if ((int64_t)M * ldx * 2 >= (int64_t)1 << 32 || (int64_t)p.wordtiles * 1024 >= (int64_t)1 << 32 ||
+        p.splits > 65535)
+      return QG_E_UNSUPPORTED;
     const int tpw = (int)ceil_div(p.tps, GEMV_THREADS / 64);
     bool launched;
     switch (fmt) {
-      case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, tpw, p.workgroups, s); break;
-      case QG_INT2_ASYM: launched = launch_gemv_f<INT2_ASYM>(a, p.mmax, tpw, p.workgroups, s); break;
-      default: launched = launch_gemv_f<Q4_0>(a, p.mmax, tpw, p.workgroups, s); break;
+      case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, tpw, s); break;
+      case QG_INT2_ASYM: launched = launch_gemv_f<INT2_ASYM>(a, p.mmax, tpw, s); break;
+      default: launched = launch_gemv_f<Q4_0>(a, p.mmax, tpw, s); break;
     }
     if (!launched) return QG_E_UNSUPPORTED;
     if (p.splits > 1) {
