@@ -45,7 +45,6 @@ static bool force_is(const char* what) {
 }
 
 Plan make_plan(int M, int N, int K, int group, int fmt) {
-  (void)group;
   Plan p;
   if (M == 0 || N == 0) return p;  // no-op
   p.rowblocks = (int)n_rowblocks(N);
@@ -78,16 +77,19 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   p.tiles_n = (int)ceil_div(N, GEMM_TN);
   p.tiles_m = (int)ceil_div(M, GEMM_TM);
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-  // at most 4 word tiles per wave (16 per workgroup); split K across
-  // workgroups only when the tiles leave most compute units idle, since a
-  // split writes fp32 partials and costs a second (reduce) launch
-  const int s_min = (int)ceil_div(p.wordtiles, 4 * GEMM_TPW);
+  // at most GEMM_TPW word tiles per wave and GEMM_GCAP groups per workgroup;
+  // split K across workgroups only when the tiles leave most compute units
+  // idle, since a split writes fp32 partials and costs a second (reduce) launch
+  const int nw = GEMM_THREADS / 64;
+  const int s_tiles = (int)ceil_div(p.wordtiles, nw * GEMM_TPW);
+  const int s_groups = (int)ceil_div((int64_t)p.wordtiles * kt_width / group, GEMM_GCAP);
+  const int s_min = std::max(s_tiles, s_groups);
   int s = tiles >= (GEMM_TARGET_WG * 5) / 8 ? 1 : (int)ceil_div(GEMM_TARGET_WG, tiles);
   if (split_env > 0) s = split_env;
   s = std::min(std::max(s, s_min), p.wordtiles);
   p.tps = (int)ceil_div(p.wordtiles, s);
   p.splits = (int)ceil_div(p.wordtiles, p.tps);
-  if (p.tps > 4 * GEMM_TPW) {  // cannot happen: s >= s_min
+  if (p.tps > nw * GEMM_TPW || (int64_t)p.tps * kt_width / group > GEMM_GCAP) {  // cannot happen: s >= s_min
     p.path = 0;
     return p;
   }

@@ -14,10 +14,12 @@ constexpr int GEMV_MAX_M = 8;
 constexpr int GEMV_THREADS = 512;          // 8 waves per workgroup
 constexpr int GEMV_TPW_MAX = 8;          // word tiles one wave streams per launch
 constexpr int GEMV_LDS_X_BYTES = 32768;  // x slice staged per workgroup
-constexpr int GEMM_THREADS = 256;
-constexpr int GEMM_TM = 128;             // workgroup tile rows (M)
-constexpr int GEMM_TN = 32;              // workgroup tile columns (N)
-constexpr int GEMM_TPW = 4;              // word tiles per wave (K per workgroup <= 16 tiles)
+constexpr int GEMM_THREADS = 512;        // 8 waves; they split the workgroup's K range
+constexpr int GEMM_TM = 64;              // workgroup tile rows (M)
+constexpr int GEMM_TN = 64;              // workgroup tile columns (N)
+constexpr int GEMM_TPW = 2;              // word tiles per wave (K per workgroup <= 16 tiles)
+constexpr int GEMM_DEPTH = 1;            // x/code stages in flight per wave
+constexpr int GEMM_GCAP = 64;            // quantization groups per workgroup, at most
 constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
 
 struct Plan {

@@ -81,23 +81,32 @@ __device__ __forceinline__ ZC2 make_zc2(f16 z) {
   return r;
 }
 
+// (w & m) | c as one VOP3 instruction.  With both constants literal the
+// compiler emits v_and + v_or, since VOP3 on this target takes no literal;
+// here the mask sits in an SGPR and the magic in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(w), "s"(m), "v"(c));
+  return d;
+}
+
 // 4-bit packed word (8 codes) -> 4 pairs (c_2i - z, c_2i+1 - z), i = 0..3
 __device__ __forceinline__ void qmz_int4(uint32_t w, const ZC4& zc, h2 out[4]) {
+  const uint32_t magic = 0x64006400u, w8 = w >> 8;
   const h2 inv16 = splat((f16)0.0625f);
-  const uint32_t w8 = w >> 8;
-  out[0] = as_h2((w & 0x000F000Fu) | 0x64006400u) + zc.c0;
-  out[1] = as_h2((w & 0x00F000F0u) | 0x64006400u) * inv16 + zc.c1;
-  out[2] = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + zc.c0;
-  out[3] = as_h2((w8 & 0x00F000F0u) | 0x64006400u) * inv16 + zc.c1;
+  out[0] = as_h2(and_or(w, 0x000F000Fu, magic)) + zc.c0;
+  out[1] = as_h2(and_or(w, 0x00F000F0u, magic)) * inv16 + zc.c1;
+  out[2] = as_h2(and_or(w8, 0x000F000Fu, magic)) + zc.c0;
+  out[3] = as_h2(and_or(w8, 0x00F000F0u, magic)) * inv16 + zc.c1;
 }
 
 // 2-bit packed word, one half (8 codes): half 0 = codes 0..7, half 1 = 8..15
 __device__ __forceinline__ void qmz_int2_half(uint32_t w, int half, const ZC2& zc, h2 out[4]) {
-  const uint32_t v = half ? (w >> 8) : w;
-  out[0] = as_h2((v & 0x00030003u) | 0x64006400u) + zc.c0;
-  out[1] = as_h2((v & 0x000C000Cu) | 0x64006400u) * splat((f16)0.25f) + zc.c1;
-  out[2] = as_h2((v & 0x00300030u) | 0x64006400u) * splat((f16)0.0625f) + zc.c2;
-  out[3] = as_h2((v & 0x00C000C0u) | 0x64006400u) * splat((f16)0.015625f) + zc.c3;
+  const uint32_t magic = 0x64006400u, v = half ? (w >> 8) : w;
+  out[0] = as_h2(and_or(v, 0x00030003u, magic)) + zc.c0;
+  out[1] = as_h2(and_or(v, 0x000C000Cu, magic)) * splat((f16)0.25f) + zc.c1;
+  out[2] = as_h2(and_or(v, 0x00300030u, magic)) * splat((f16)0.0625f) + zc.c2;
+  out[3] = as_h2(and_or(v, 0x00C000C0u, magic)) * splat((f16)0.015625f) + zc.c3;
 }
 
 template <int FMT> struct Fmt;
@@ -195,15 +204,6 @@ struct GemvArgs {
   int ldx, ldr, ldy, M, N, K, group;
   int wordtiles, rowblocks, splits, tps;
 };
-
-// (w & m) | c as one VOP3 instruction.  With both constants literal the
-// compiler emits v_and + v_or, since VOP3 on this target takes no literal;
-// here the mask sits in an SGPR and the magic in a VGPR.
-__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t m, uint32_t c) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(w), "s"(m), "v"(c));
-  return d;
-}
 
 // sum over lanes l, l^16, l^32, l^48 (result in every lane)
 __device__ __forceinline__ float sum_lane_groups(float v) {
@@ -321,7 +321,6 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   //    INT4 or 64 INT2 codes, and a group may be 32 wide): exact (q - z)
   //    pairs against fp16 x pairs (v_dot2_f32_f16, fp32 accumulation), fp32
   //    scale once per 32 codes.
-  const uint32_t magic = 0x64006400u;
   float acc[MMAX];
 #pragma unroll
   for (int m = 0; m < MMAX; ++m) acc[m] = 0.0f;
@@ -339,24 +338,11 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 #pragma unroll
           for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const uint32_t w = code[i][2 * p + t], v = h ? (w >> 8) : w;
-              q[8 * t + 4 * h + 0] = as_h2(and_or(v, 0x00030003u, magic)) + zc.c0;
-              q[8 * t + 4 * h + 1] = as_h2(and_or(v, 0x000C000Cu, magic)) * splat((f16)0.25f) + zc.c1;
-              q[8 * t + 4 * h + 2] = as_h2(and_or(v, 0x00300030u, magic)) * splat((f16)0.0625f) + zc.c2;
-              q[8 * t + 4 * h + 3] = as_h2(and_or(v, 0x00C000C0u, magic)) * splat((f16)0.015625f) + zc.c3;
-            }
+            for (int h = 0; h < 2; ++h) qmz_int2_half(code[i][2 * p + t], h, zc, q + 8 * t + 4 * h);
         } else {
           const ZC4 zc = make_zc4(z);
-          const h2 inv16 = splat((f16)0.0625f);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t w = code[i][t], w8 = w >> 8;
-            q[4 * t + 0] = as_h2(and_or(w, 0x000F000Fu, magic)) + zc.c0;
-            q[4 * t + 1] = as_h2(and_or(w, 0x00F000F0u, magic)) * inv16 + zc.c1;
-            q[4 * t + 2] = as_h2(and_or(w8, 0x000F000Fu, magic)) + zc.c0;
-            q[4 * t + 3] = as_h2(and_or(w8, 0x00F000F0u, magic)) * inv16 + zc.c1;
-          }
+          for (int t = 0; t < 4; ++t) qmz_int4(code[i][t], zc, q + 4 * t);
         }
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) {
@@ -427,257 +413,324 @@ struct GemmArgs {
   int wordtiles, rowblocks, tiles_n, splits, tps;
 };
 
-// Output layout of v_mfma_f32_32x32x16_f16: lane l holds, in accumulator
-// element i (0..15), D[8*(i/4) + 4*(l/32) + i%4][l % 32].
-__device__ __forceinline__ int acc_row(int mb, int i, int lane) {
-  return mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-}
-
-// Staging of x for the GEMM, per wave.  A stage is 128 rows x 64 k of x (16
-// KiB): the two 32-k pieces that lane group 0 and lane group 1 supply to four
-// MFMA steps.  Each wave double-buffers its own stages in LDS with direct
-// global->LDS loads (16 per stage per lane), so waves never wait on each
-// other inside the K loop.  Inside a stage, row m holds 8 chunks of 16 bytes;
-// chunk c lands at c ^ (m % 8), so the fragment reads of 8 consecutive rows
-// fall in different banks.
-template <int FMT> struct GemmStage {
-  static constexpr int KT = Fmt<FMT>::KT;
-  static constexpr int SEG = Fmt<FMT>::LS / 32;     // 32-code segments per code chunk
-  static constexpr int STAGES = 2 * SEG;            // stages per word tile: (h, j) pairs
-  static constexpr int STAGE_BYTES = GEMM_TM * 64 * 2;
-  static constexpr int DMA = STAGE_BYTES / (64 * 16);  // direct loads per lane per stage (16)
-  static constexpr int TPW = GEMM_TPW;               // word tiles per wave, at most
-};
-
 template <int N> __device__ __forceinline__ void wait_vm() {
   // s_waitcnt vmcnt(N) (GFX9 encoding), expcnt and lgkmcnt left at their maximum
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ __forceinline__ void wait_lgkm0() {
+  // s_waitcnt lgkmcnt(0), vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
 
-// prefill GEMM (M > 8).  Workgroup tile 128 (M) x 32 (N); the 4 waves split
-// the workgroup's K range and are summed through LDS at the end, so every code
-// is dequantized exactly once.  MFMA v_mfma_f32_32x32x16_f16: B operand lane l
-// = column l % 32, k-slots 8*(l/32)..+7.  Lane l reads its codes from two
-// 16-byte chunks of the packed tile: row block 2*(n0/32) + (l%32)/16, row
-// l%16, lane group g = l/32 + 2h (h = 0, 1), one packed word (8 codes) per
-// MFMA step; the A fragment of a step reads the matching 8 k of x, so A and
-// B agree on the k order.
-template <int FMT>
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
+// Accumulator row of element i (0..15) of a 32 x 32 block for lane l: the
+// output layout of v_mfma_f32_32x32x16_f16 is D[8*(i/4) + 4*(l/32) + i%4][l%32].
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// Stage geometry: a stage is (word tile t, chunk h, 32-code segment j); for
+// lane half g2 it covers the 32 k at seg_k(g2, h, j) and feeds four MFMA
+// steps of 8 k each.  x part: 64 rows x 2 pieces of 32 k (8 KiB); code part:
+// chunk h of both 32-column blocks (2 KiB).
+template <int FMT> struct GemmStage {
+  static constexpr int KT = Fmt<FMT>::KT;
+  static constexpr int SEG = Fmt<FMT>::LS / 32;    // 32-code segments per 16-byte chunk
+  static constexpr int STAGES = 2 * SEG;           // stages per word tile
+  static constexpr int XB = GEMM_TM * 64 * 2;       // x bytes per stage
+  static constexpr int SB = XB + 2048;              // + code chunks of the two column blocks
+  static constexpr int DMA = XB / 1024 + 2;         // direct loads per lane per stage (10)
+};
+
+// Prefill GEMM (M > 8).  Workgroup tile 64 (M) x 64 (N) over the workgroup's
+// share of K; its NW waves split that share and are summed through LDS at the
+// end, so every code is dequantized once per workgroup.  Each wave owns 2 x 2
+// blocks of v_mfma_f32_32x32x16_f16 (B operand lane l = column l % 32,
+// k-slots 8*(l/32)..+7): lane l takes its codes from the 16-byte chunk of row
+// block n0/16 + 2*nb + (l%32)/16, row l%16, lane group l/32 + 2h, one packed
+// word (8 codes) per MFMA step, and the A fragment of the step reads the
+// matching 8 k of x, so A and B agree on the k order.
+//
+// Each wave streams its stages through a private DEPTH-deep LDS ring with
+// direct global->LDS loads (x and codes alike, so every wait is an explicit
+// vmcnt).  Inside a stage x sits as [piece][row][4 x 16 B]; sub-chunk u of
+// row m is stored at u ^ ((m >> 2) & 3), so the fragment reads of 16
+// consecutive rows hit 16 distinct bank groups.  All LDS operands of a stage
+// are read first; group barriers then interleave one MFMA with a few VALU of
+// the dequantization so the two pipes overlap.
+template <int FMT, int NW, int TPW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   using F = Fmt<FMT>;
   using S = GemmStage<FMT>;
   constexpr int SEG = S::SEG;
-  __shared__ __align__(16) uint8_t smem[4 * 2 * S::STAGE_BYTES];   // 4 waves x 2 buffers
+  constexpr int PIPE = NW * DEPTH * S::SB;
+  constexpr int RED = NW * 4 * 4 * 64 * 16;             // [wave][block][quad][lane] f4
+  constexpr int BIG = PIPE > RED ? PIPE : RED;
+  constexpr int SZB = GEMM_TN * GEMM_GCAP * 4;          // (s | z << 16) per column and group
+  static_assert(DEPTH >= 1 && DEPTH <= 3 && (DEPTH - 1) * S::DMA <= 63, "vmcnt range");
+  __shared__ __align__(16) uint8_t smem[BIG + SZB];
+  uint32_t* szl = reinterpret_cast<uint32_t*>(smem + BIG);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g2 = lane >> 5, r = lane & 15;
-
-  const int tile = blockIdx.x / a.splits, split = blockIdx.x - (blockIdx.x / a.splits) * a.splits;
-  const int tn = tile % a.tiles_n, tm = tile / a.tiles_n;
+  const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
   const int m0 = tm * GEMM_TM, n0 = tn * GEMM_TN;
-  // this workgroup's word tiles, then this wave's share
   const int kt0 = split * a.tps;
   const int kt1 = min(a.wordtiles, kt0 + a.tps);
-  const int per = (kt1 - kt0 + 3) >> 2;
+  const int per = (kt1 - kt0 + NW - 1) / NW;
   const int wt0 = kt0 + wave * per;
-  const int nt = max(0, min(kt1, wt0 + per) - wt0);     // <= S::TPW (plan guarantees)
+  const int nt = max(0, min(kt1, wt0 + per) - wt0);     // <= TPW (plan guarantees)
   const int nst = nt * S::STAGES;
+  const int lg = __builtin_ctz(a.group);
+  const int ng = a.K >> lg;
+  const int gw0 = (kt0 * F::KT) >> lg;                   // first group (KT % group == 0)
+  const int gwn = min(ng, ((kt1 * F::KT) + a.group - 1) >> lg) - gw0;  // <= GEMM_GCAP (plan)
+  uint8_t* wbuf = smem + wave * DEPTH * S::SB;
 
-  const int rb = (n0 >> 4) + ((lane >> 4) & 1);         // this lane's row block
-  const int rbc = min(rb, a.rowblocks - 1);              // columns past N are never stored
-  const int nn = min(rb * 16 + r, a.N - 1);
-  const int ng = a.K / a.group;
-  const u4* pk = reinterpret_cast<const u4*>(a.packed);
-  const uint16_t* sp = reinterpret_cast<const uint16_t*>(a.scales);
-  const uint16_t* zp = reinterpret_cast<const uint16_t*>(a.zeros);
-  uint8_t* wbuf = smem + wave * 2 * S::STAGE_BYTES;
-
-  // k offset (inside a word tile) of 32-code segment j of chunk h for lane group gg
   auto seg_k = [](int gg, int h, int j) { return (gg + 2 * h) * F::LS + j * 32; };
 
-  // 1. codes and scales/zero points of all of this wave's tiles (clamped,
-  //    branch-free), waited for once before the x pipeline starts
-  u4 b[S::TPW][2];
-  uint32_t sv[S::TPW][2][SEG], zv[S::TPW][2][SEG];
+  // 1. the workgroup's scales and zeros, loaded cooperatively (clamped) and
+  //    staged in LDS as [column][group]
+  constexpr int NSZ = GEMM_TN * GEMM_GCAP / (NW * 64);
+  const int gsr = gwn <= 1 ? 1 : 1 << (32 - __builtin_clz(gwn - 1));   // groups, rounded to a power of two
+  const int lgs = __builtin_ctz(gsr);
+  const int nsz = (GEMM_TN * gsr + NW * 64 - 1) / (NW * 64);
+  uint32_t sraw[NSZ], zraw[NSZ];
 #pragma unroll
-  for (int t = 0; t < S::TPW; ++t) {
-    const int kt = min(wt0 + t, kt1 - 1);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      b[t][h] = pk[((int64_t)rbc * a.wordtiles + kt) * 64 + (g2 + 2 * h) * 16 + r];
-#pragma unroll
-      for (int j = 0; j < SEG; ++j) {
-        const int grp = min((kt * F::KT + seg_k(g2, h, j)) / a.group, ng - 1);
-        sv[t][h][j] = sp[(int64_t)nn * ng + grp];
-        if constexpr (F::HAS_Z) zv[t][h][j] = zp[(int64_t)nn * ng + grp];
-        else zv[t][h][j] = 0x4800;  // fp16 8.0
-      }
+  for (int j = 0; j < NSZ; ++j) {
+    if (j < nsz) {
+      const int e = tid + NW * 64 * j;                   // column e >> lgs, group e % gsr
+      const int ec = e >> lgs, eg = e & (gsr - 1);
+      const bool ok = ec < GEMM_TN && eg < gwn && n0 + ec < a.N;
+      const int64_t off = ok ? ((int64_t)(n0 + ec) * ng + gw0 + eg) : 0;
+      sraw[j] = reinterpret_cast<const uint16_t*>(a.scales)[off];
+      if constexpr (F::HAS_Z) zraw[j] = reinterpret_cast<const uint16_t*>(a.zeros)[off];
+      else zraw[j] = 0x4800;  // fp16 8.0
     }
   }
-  // residual values this thread may add at the end (clamped, branch-free)
-  float res[16];
-  if (a.resid && a.splits == 1) {
-    const int colc = min(n0 + (lane & 31), a.N - 1);
+
+  // 2. per-lane byte offsets (fixed for all stages): x row quarters, code rows
+  uint32_t voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int m = q * 16 + (lane >> 2);
+    const int u = (lane & 3) ^ ((m >> 2) & 3);
+    voff[q] = (uint32_t)((min(m0 + m, a.M - 1) * a.ldx + u * 8) * 2);   // rows past M: any finite data
+  }
+  const char* cb[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int rb = min((n0 >> 4) + 2 * nb + ((lane >> 4) & 1), a.rowblocks - 1);  // columns past N: never stored
+    cb[nb] = reinterpret_cast<const char*>(a.packed) + (int64_t)rb * a.wordtiles * 1024 + (g2 * 16 + r) * 16;
+  }
+  auto issue_stage = [&](int st) {
+    const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
+    const int kt = wt0 + t;
+    uint8_t* dst = wbuf + (st % DEPTH) * S::SB;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int kp = kt * F::KT + seg_k(p, h, j);
+      const char* src = reinterpret_cast<const char*>(a.x) + (kp < a.K ? kp : 0) * 2;  // past K: scale 0
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(src + voff[q]),
+            (void __attribute__((address_space(3)))*)(dst + (p * 4 + q) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(cb[nb] + (int64_t)kt * 1024 + h * 512),
+          (void __attribute__((address_space(3)))*)(dst + S::XB + nb * 1024), 16, 0, 0);
+  };
+
+  f16v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.0f;
+
+  // byte offset of the A fragment (m-block mb, step) inside a stage
+  auto a_off = [&](int mb, int step) {
+    const int m = mb * 32 + (lane & 31);
+    return g2 * 4096 + m * 64 + ((step ^ ((m >> 2) & 3)) << 4);
+  };
+
+  // 3. one stage: every LDS operand first, then B operands (13 VALU per
+  //    word) interleaved with the 16 MFMAs
+  auto compute_stage = [&](int st) {
+    const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
+    const int kt = wt0 + t;
+    const uint8_t* sb = wbuf + (st % DEPTH) * S::SB;
+    const int kseg = kt * F::KT + seg_k(g2, h, j);
+    const bool live = kseg < a.K;                       // segment past K: scale 0
+    const int gi = min(max((kseg >> lg) - gw0, 0), gwn - 1);
+    uint32_t szv[2];
+    u4 bt[2];
+    h8 af[4][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      bt[nb] = *reinterpret_cast<const u4*>(sb + S::XB + nb * 1024 + lane * 16);
+      szv[nb] = szl[(nb * 32 + (lane & 31)) * GEMM_GCAP + gi];
+    }
+#pragma unroll
+    for (int step = 0; step < 4; ++step)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) af[step][mb] = *reinterpret_cast<const h8*>(sb + a_off(mb, step));
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the math
+    h2 s2[2];
+    f16 z[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      s2[nb] = splat(live ? __builtin_bit_cast(f16, (uint16_t)(szv[nb] & 0xffffu)) : (f16)0.0f);
+      z[nb] = __builtin_bit_cast(f16, (uint16_t)(szv[nb] >> 16));
+    }
+    h8 bf[4][2];
+#pragma unroll
+    for (int step = 0; step < 4; ++step)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        h2 q[4];
+        if constexpr (FMT == INT2_ASYM) qmz_int2_half(bt[nb][2 * j + (step >> 1)], step & 1, make_zc2(z[nb]), q);
+        else qmz_int4(bt[nb][step], make_zc4(z[nb]), q);
+        const h2 w0 = q[0] * s2[nb], w1 = q[1] * s2[nb], w2 = q[2] * s2[nb], w3 = q[3] * s2[nb];
+        bf[step][nb] = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+      }
+#pragma unroll
+    for (int step = 0; step < 4; ++step)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[step][mb], bf[step][nb], acc[mb][nb], 0, 0, 0);
+    // schedule: the first step's operands, then 16 x (one MFMA, six VALU)
+    __builtin_amdgcn_sched_group_barrier(0x002, 26, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = min(m0 + acc_row(wave, i, lane), a.M - 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+  };
+
+  // 4. first stages in flight, residual prefetch, then the scale/zero table
+  //    (waiting for the scale/zero loads only)
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nst) issue_stage(d);
+  float res[16];
+  const int fb = wave & 3;                               // block this wave finishes: (fb >> 1, fb & 1)
+  if (a.resid && a.splits == 1 && wave < 4) {
+    const int colc = min(n0 + (fb & 1) * 32 + (lane & 31), a.N - 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = min(m0 + (fb >> 1) * 32 + acc_row(i, lane), a.M - 1);
       res[i] = (float)a.resid[(int64_t)row * a.ldr + colc];
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) res[i] = 0.0f;
   }
-
-  // 2. direct x loads of stage st (tile kt, chunk h, segment j) into buffer buf
-  auto issue_stage = [&](int st, int buf) {
-    const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
-    const int kt = wt0 + t;
-    uint8_t* dst = wbuf + buf * S::STAGE_BYTES;
-#pragma unroll
-    for (int c = 0; c < S::DMA; ++c) {
-      const int slot = c * 64 + lane;                   // 16-byte slot this lane fills
-      const int m = slot >> 3, cs = slot & 7;
-      const int ch = cs ^ (m & 7);                      // source chunk: piece ch/4, 8 k at (ch%4)*8
-      const int row = min(m0 + m, a.M - 1);             // rows past M: any finite data
-      const int k = min(kt * F::KT + seg_k(ch >> 2, h, j) + (ch & 3) * 8, a.K - 8);  // past K: scale 0
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(a.x + (int64_t)row * a.ldx + k),
-          (void __attribute__((address_space(3)))*)(dst + c * 1024), 16, 0, 0);
-    }
-  };
-
-  f16v acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
-
-  // 3. compute stage st from buffer buf: four MFMA steps x four m-blocks.
-  //    st is a compile-time constant after unrolling, so every register
-  //    array index below is static.
-  auto compute_stage = [&](int st, int buf) {
-    const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
-    const int kt = wt0 + t;
-    const uint8_t* abase = wbuf + buf * S::STAGE_BYTES;
-    const u4 bt = b[t][h];
-    const bool live = kt * F::KT + seg_k(g2, h, j) < a.K;   // segment past K: scale 0
-    const h2 s2 = splat(live ? __builtin_bit_cast(f16, (uint16_t)sv[t][h][j]) : (f16)0.0f);
-    const f16 z = __builtin_bit_cast(f16, (uint16_t)zv[t][h][j]);
-#pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      h2 q[4];
-      if constexpr (FMT == INT2_ASYM) qmz_int2_half(bt[2 * j + (step >> 1)], step & 1, make_zc2(z), q);
-      else qmz_int4(bt[step], make_zc4(z), q);
-      const h2 w0 = q[0] * s2, w1 = q[1] * s2, w2 = q[2] * s2, w3 = q[3] * s2;
-      const h8 bf = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
-      const int c = g2 * 4 + step;                       // piece g2, 8 k at step*8
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int m = mb * 32 + (lane & 31);             // m % 8 == lane % 8
-        const h8 af = *reinterpret_cast<const h8*>(abase + (m * 8 + (c ^ (lane & 7))) * 16);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, acc[mb], 0, 0, 0);
-      }
-    }
-  };
-
-  // 4. x pipeline, two stages in flight per wave.  After the initial full
-  //    wait only direct loads are outstanding, all of one kind, so
-  //    "vmcnt <= 16" means every stage but the newest has landed.  The loop
-  //    is unrolled over the largest stage count; nst is wave-uniform.
-  if (nst > 0) issue_stage(0, 0);
-  if (nst > 1) issue_stage(1, 1);
-  __builtin_amdgcn_s_waitcnt(0);
+  {
+    const int ist = min(DEPTH, nst);
+    if (ist >= 3) wait_vm<(DEPTH >= 3 ? 3 : 0) * S::DMA>();
+    else if (ist == 2) wait_vm<(DEPTH >= 2 ? 2 : 0) * S::DMA>();
+    else if (ist == 1) wait_vm<S::DMA>();
+    else wait_vm<0>();
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int st = 0; st < S::TPW * S::STAGES; ++st) {
+  for (int j = 0; j < NSZ; ++j) {
+    const int e = tid + NW * 64 * j;
+    if (j < nsz && (e >> lgs) < GEMM_TN)
+      szl[(e >> lgs) * GEMM_GCAP + (e & (gsr - 1))] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+  }
+  __syncthreads();
+
+  // 5. the K loop: wait for stage st (newer stages may stay in flight),
+  //    compute it, refill its buffer with stage st + DEPTH
+#pragma unroll
+  for (int st = 0; st < TPW * S::STAGES; ++st) {
     if (st < nst) {
-      if (st > 0) {
-        if (st + 1 < nst) wait_vm<S::DMA>();
-        else wait_vm<0>();
-      }
+      const int newer = min(DEPTH - 1, nst - 1 - st);
+      if (newer >= 2) wait_vm<(DEPTH >= 3 ? 2 : 0) * S::DMA>();
+      else if (newer == 1) wait_vm<(DEPTH >= 2 ? 1 : 0) * S::DMA>();
+      else wait_vm<0>();
       __builtin_amdgcn_sched_barrier(0);
-      compute_stage(st, st & 1);
+      compute_stage(st);
       __builtin_amdgcn_sched_barrier(0);
-      if (st + 2 < nst) {
-        __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0): this buffer's reads done
+      if (st + DEPTH < nst) {
+        wait_lgkm0();  // this buffer's reads are back
         __builtin_amdgcn_sched_barrier(0);
-        issue_stage(st + 2, st & 1);
+        issue_stage(st + DEPTH);
       }
     }
   }
 
-  // 5. sum the four waves' accumulators through LDS (fixed order)
+  // 6. sum the NW waves' accumulators through LDS in wave order
+  //    (deterministic); wave w < 4 finishes block w
   __syncthreads();
-  f4* red = reinterpret_cast<f4*>(smem);                 // [wave][16 quads][64 lanes]
+  f4* red = reinterpret_cast<f4*>(smem);
 #pragma unroll
-  for (int q = 0; q < 16; ++q)
-    red[(wave * 16 + q) * 64 + lane] = f4{acc[q >> 2][4 * (q & 3)], acc[q >> 2][4 * (q & 3) + 1],
-                                          acc[q >> 2][4 * (q & 3) + 2], acc[q >> 2][4 * (q & 3) + 3]};
+  for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f16v& A = acc[blk >> 1][blk & 1];
+      red[((wave * 4 + blk) * 4 + q) * 64 + lane] = f4{A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]};
+    }
   __syncthreads();
-  // wave w finishes m-block w
+  if (wave >= 4) return;
   f4 tot[4];
 #pragma unroll
-  for (int quad = 0; quad < 4; ++quad) {
-    f4 v = red[(0 * 16 + wave * 4 + quad) * 64 + lane];
+  for (int q = 0; q < 4; ++q) {
+    f4 v = red[((0 * 4 + fb) * 4 + q) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) v += red[(w * 16 + wave * 4 + quad) * 64 + lane];
-    tot[quad] = v;
+    for (int w = 1; w < NW; ++w) v += red[((w * 4 + fb) * 4 + q) * 64 + lane];
+    tot[q] = v;
   }
+  const int col = n0 + (fb & 1) * 32 + (lane & 31);
   if (a.splits == 1) {
-    const int col = n0 + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = m0 + acc_row(wave, i, lane);
+      const int row = m0 + (fb >> 1) * 32 + acc_row(i, lane);
       if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(tot[i >> 2][i & 3] + res[i]);
     }
     return;
   }
-  // split-K: this split's 128 x 32 partial; gemm_reduce_kernel sums the splits
+  // split-K: this split's 64 x 64 partial; gemm_reduce_kernel sums the splits
   f4* wsp = reinterpret_cast<f4*>(a.ws);
-  const int64_t base = ((int64_t)tile * a.splits + split) * 16;
+  const int64_t tile = (int64_t)tm * a.tiles_n + tn;
+  const int64_t base = ((tile * a.splits + split) * 4 + fb) * 4;
 #pragma unroll
-  for (int quad = 0; quad < 4; ++quad) wsp[(base + wave * 4 + quad) * 64 + lane] = tot[quad];
+  for (int q = 0; q < 4; ++q) wsp[(base + q) * 64 + lane] = tot[q];
 }
 
-// Sums a tile's split partials in split order (deterministic), adds the
-// residual and rounds once to fp16.  One workgroup per 128 x 32 tile; thread
-// (wave w, lane) owns the four accumulator quads of m-block w; all loads are
-// issued first.
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_reduce_kernel(GemmArgs a) {
-  const int tile = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tn = tile % a.tiles_n, tm = tile / a.tiles_n;
+// Sums a 64 x 64 tile's split partials in split order (deterministic), adds
+// the residual and rounds once to fp16.  One workgroup of 4 waves per tile;
+// wave w owns block w in the GEMM's accumulator layout.
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
+  const int tn = blockIdx.x, tm = blockIdx.y, tid = threadIdx.x, lane = tid & 63, fb = tid >> 6;
   const int m0 = tm * GEMM_TM, n0 = tn * GEMM_TN;
+  const int64_t tile = (int64_t)tm * a.tiles_n + tn;
   const f4* wsp = reinterpret_cast<const f4*>(a.ws);
-  const int col = n0 + (lane & 31);
+  const int col = n0 + (fb & 1) * 32 + (lane & 31);
   const int colc = min(col, a.N - 1);
   float res[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int row = min(m0 + acc_row(wave, i, lane), a.M - 1);
+    const int row = min(m0 + (fb >> 1) * 32 + acc_row(i, lane), a.M - 1);
     res[i] = a.resid ? (float)a.resid[(int64_t)row * a.ldr + colc] : 0.0f;
   }
-  constexpr int SMAX = 4;
   f4 sum[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) sum[q] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < a.splits; s0 += SMAX) {
-    f4 v[SMAX][4];
+  for (int s = 0; s < a.splits; ++s) {
+    const int64_t base = ((tile * a.splits + s) * 4 + fb) * 4;
 #pragma unroll
-    for (int s = 0; s < SMAX; ++s) {
-      const int ss = min(s0 + s, a.splits - 1);
-      const int64_t base = ((int64_t)tile * a.splits + ss) * 16;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[s][q] = wsp[(base + wave * 4 + q) * 64 + lane];
-    }
-#pragma unroll
-    for (int s = 0; s < SMAX; ++s)
-      if (s0 + s < a.splits)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sum[q] += v[s][q];
+    for (int q = 0; q < 4; ++q) sum[q] += wsp[(base + q) * 64 + lane];
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int row = m0 + acc_row(wave, i, lane);
+    const int row = m0 + (fb >> 1) * 32 + acc_row(i, lane);
     if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(sum[i >> 2][i & 3] + res[i]);
   }
 }
@@ -875,16 +928,19 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
   a.M = M; a.N = N; a.K = K; a.group = group;
   a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.tiles_n = p.tiles_n;
   a.splits = p.splits; a.tps = p.tps;
-  const dim3 grid((unsigned)p.workgroups), block(GEMM_THREADS);
+  // the kernel forms byte offsets of x rows in 32 bits
+  if ((int64_t)M * ldx * 2 >= (int64_t)1 << 32 || p.tiles_m > 65535 || p.splits > 65535) return QG_E_UNSUPPORTED;
+  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.splits), block(GEMM_THREADS);
+  constexpr int NW = GEMM_THREADS / 64;
   switch (fmt) {
-    case QG_INT4_ASYM: hipLaunchKernelGGL(gemm_kernel<INT4_ASYM>, grid, block, 0, s, a); break;
-    case QG_INT2_ASYM: hipLaunchKernelGGL(gemm_kernel<INT2_ASYM>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(gemm_kernel<Q4_0>, grid, block, 0, s, a); break;
+    case QG_INT4_ASYM: hipLaunchKernelGGL((gemm_kernel<INT4_ASYM, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
+    case QG_INT2_ASYM: hipLaunchKernelGGL((gemm_kernel<INT2_ASYM, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((gemm_kernel<Q4_0, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
   }
   if (p.splits > 1) {
     st = launch_status();
     if (st != QG_OK) return st;
-    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(p.workgroups / p.splits)), block, 0, s, a);
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m), dim3(256), 0, s, a);
   }
   return launch_status();
 }
