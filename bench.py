@@ -43,8 +43,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=810)
     ap.add_argument("--warmup", type=int, default=81)
-    ap.add_argument("--only", choices=["all", "main", "gemm", "loop", "copy"], default="all",
-                    help="main/gemm/loop: run one leg (for profiler runs); copy: the calibration copy")
+    ap.add_argument("--only", choices=["all", "main", "gemm", "loop", "fp16", "copy"], default="all",
+                    help="main/gemm/loop/fp16: run one leg (for profiler runs); copy: the calibration copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
@@ -168,6 +168,72 @@ def loop_leg(qgm, torch, synth, L=8, flush=True):
                 weight_GBps_loop1_cold=round(wbytes / (cold[0] * 1e-3) / 1e9, 1))
 
 
+def graph_time(torch, step, steps, warmup):
+    """ms per step of `step(i)`, captured once in a HIP graph and replayed."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    start.record(stream)
+    g.replay()
+    stop.record(stream)
+    stop.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def fp16_leg(qgm, torch, synth, Ms=(1, 8, 32, 128, 512, 2048)):
+    """The fused qGEMM against two FP16 alternatives on the up-projection shape
+    (INT4 g128, N=8192, K=2048): dequantize-at-load (qg_dequant to an fp16 W,
+    then torch's fp16 GEMM, every call) and an FP16 body whose fp16 weights stay
+    resident (torch's fp16 GEMM alone).  Weights rotate over copies larger than
+    the on-die cache in all three, so each call reads its weights from HBM."""
+    c = synth.workload("prefill_int4_g128")
+    N, K = c.N, c.K
+    base = qgm.QuantLinear.from_case(c, "cuda")
+    w16 = qgm.dequant(base.packed, base.scales, base.zeros, N, K, c.group, c.fmt)
+    n16 = max(1, -(-2 * MALL_BYTES // (N * K * 2)))
+    w16s = [w16.clone() for _ in range(n16)]
+    wtmp = torch.empty_like(w16)
+    rows = []
+    for M in Ms:
+        xs = synth.draw_x(np.random.default_rng(7 + M), M, K)
+        x = qgm.to_half_tensor(xs, "cuda")
+        leg = Leg(qgm, torch, c, M)
+        leg.x = x
+        leg.y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        steps = 200 if M <= 128 else 50
+        t_fused = leg.time(steps, 10)
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+        def deq_step(i, leg=leg, x=x, y=y):
+            lin = leg.lins[i % leg.copies]
+            qgm.dequant_into(lin.packed, lin.scales, lin.zeros, N, K, c.group, c.fmt, wtmp)
+            torch.matmul(x, wtmp.t(), out=y)
+
+        def f16_step(i, x=x, y=y):
+            torch.matmul(x, w16s[i % n16].t(), out=y)
+
+        t_deq = graph_time(torch, deq_step, steps, 10)
+        t_f16 = graph_time(torch, f16_step, steps, 10)
+        fl = 2.0 * M * N * K
+        rows.append(dict(M=M, fused_us=round(t_fused * 1e3, 2), dequant_then_fp16_us=round(t_deq * 1e3, 2),
+                         fp16_resident_us=round(t_f16 * 1e3, 2),
+                         fused_TFLOPs=round(fl / (t_fused * 1e-3) / 1e12, 1),
+                         fp16_resident_TFLOPs=round(fl / (t_f16 * 1e-3) / 1e12, 1)))
+        del leg
+        torch.cuda.empty_cache()
+    return dict(leg="fp16_comparison_int4_g128_N8192_K2048", fp16_weight_copies=n16, rows=rows,
+                note="fp16 GEMM = torch.matmul (hipBLASLt), untuned, as a comparison only")
+
+
 def calibration_copy(torch, nbytes=512 << 20, reps=3):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     a = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda")
@@ -227,6 +293,9 @@ def main():
     if args.only == "loop":
         print(json.dumps(loop_leg(qgm, torch, synth)), flush=True)
         return
+    if args.only == "fp16":
+        print(json.dumps(fp16_leg(qgm, torch, synth)), flush=True)
+        return
 
     secondary = []
     leg8 = Leg(qgm, torch, main_case, 8)
@@ -245,6 +314,7 @@ def main():
     secondary.append(dict(leg_result("decode_int4_g128_M1_cache_resident", hot, hot.time(400, 40), 1)))
     del hot
     secondary.append(loop_leg(qgm, torch, synth))
+    secondary.append(fp16_leg(qgm, torch, synth, Ms=(1, 8, 128, 512)))
 
     leg, ms, main_r = out["main"]
     wbytes = leg.wbytes

@@ -193,9 +193,18 @@ def unpack_codes(packed, N: int, K: int, fmt: int, stream=None):
 
 
 def dequant(packed, scales, zeros, N: int, K: int, group: int, fmt: int, stream=None):
+    """fp16 [N, K] weights: fp16_rne(s * (q - z)), the GEMM's own dequant."""
     torch = _torch()
-    _dev(packed, "packed"); _dev(scales, "scales"); _dev(zeros, "zeros")
     out = torch.empty((N, K), dtype=torch.float16, device=packed.device)
+    return dequant_into(packed, scales, zeros, N, K, group, fmt, out, stream=stream)
+
+
+def dequant_into(packed, scales, zeros, N: int, K: int, group: int, fmt: int, out, stream=None):
+    """As `dequant`, into a caller-owned contiguous fp16 [N, K] tensor."""
+    torch = _torch()
+    _dev(packed, "packed"); _dev(scales, "scales"); _dev(zeros, "zeros"); _dev(out, "out")
+    if out.dtype != torch.float16 or tuple(out.shape) != (N, K) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp16 [N, K] tensor")
     _check(_lib.qg_dequant(_ptr(packed), _ptr(scales), _ptr(zeros), _ptr(out), N, K, group, fmt,
                            _stream(packed.device, stream)), "qg_dequant")
     return out

@@ -156,32 +156,51 @@ __global__ void unpack_codes_kernel(const uint32_t* __restrict__ packed, uint8_t
   }
 }
 
-// One thread per canonical word: the GEMM's register dequant, written out.
+// Dequantized weights written out (fp16 [N, K]), with the GEMM's register
+// dequant: one wave per (row block, word tile), so each wave reads 1 KiB of
+// codes contiguously; lane (g, r) turns its 16-byte chunk into 32 (INT4) or 64
+// (INT2) weights of row 16*rb + r and stores them contiguously.
 template <int FMT>
-__global__ void dequant_kernel(const uint32_t* __restrict__ packed, const f16* __restrict__ scales,
-                               const f16* __restrict__ zeros, f16* __restrict__ w,
-                               int N, int K, int group, int wordtiles) {
+__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ packed,
+                                                      const f16* __restrict__ scales,
+                                                      const f16* __restrict__ zeros, f16* __restrict__ w,
+                                                      int N, int K, int group, int wordtiles, int64_t units) {
   using F = Fmt<FMT>;
-  const int Kw = K / F::CPW, ng = K / group;
-  const int64_t total = (int64_t)N * Kw;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t n = i / Kw, kw = i % Kw;
-    const uint32_t word = packed[packed_index(n, kw, wordtiles)];
-    const int grp = (int)(kw * F::CPW / group);
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= units) return;
+  const int64_t rb = unit / wordtiles;
+  const int T = (int)(unit - rb * wordtiles);
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t n = rb * 16 + r;
+  const u4 c = reinterpret_cast<const u4*>(packed)[unit * 64 + lane];
+  if (n >= N) return;
+  const int ng = K / group;
+#pragma unroll
+  for (int p = 0; p < F::LS / 32; ++p) {
+    const int k = T * F::KT + g * F::LS + p * 32;  // first of this lane's 32 codes
+    if (k >= K) break;
+    const int grp = k / group;
     const h2 s2 = splat(scales[n * ng + grp]);
     const f16 z = F::HAS_Z ? zeros[n * ng + grp] : (f16)8.0f;
-    h2 out[8];
+    h2 q[16];
     if constexpr (FMT == INT2_ASYM) {
       const ZC2 zc = make_zc2(z);
-      qmz_int2_half(word, 0, zc, out);
-      qmz_int2_half(word, 1, zc, out + 4);
-    } else {
-      qmz_int4(word, make_zc4(z), out);
-    }
-    h2* dst = reinterpret_cast<h2*>(w + n * K + kw * F::CPW);
 #pragma unroll
-    for (int p = 0; p < F::CPW / 2; ++p) dst[p] = out[p] * s2;
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) qmz_int2_half(c[2 * p + t], h, zc, q + 8 * t + 4 * h);
+    } else {
+      const ZC4 zc = make_zc4(z);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qmz_int4(c[t], zc, q + 4 * t);
+    }
+    h8* dst = reinterpret_cast<h8*>(w + n * K + k);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const h2 a0 = q[4 * v] * s2, a1 = q[4 * v + 1] * s2, a2 = q[4 * v + 2] * s2, a3 = q[4 * v + 3] * s2;
+      dst[v] = h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+    }
   }
 }
 
@@ -1023,16 +1042,17 @@ int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* z
   if (st != QG_OK) return st;
   clear_pending_error();
   if (total == 0) return QG_OK;
-  const dim3 grid(grid_for(total, 256)), block(256);
+  const int wt = (int)n_wordtiles(K, fmt);
+  const int64_t units = n_rowblocks(N) * wt;
+  const dim3 grid((unsigned)ceil_div(units, 4)), block(256);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const f16* sc = reinterpret_cast<const f16*>(scales);
   const f16* zp = reinterpret_cast<const f16*>(zeros);
   f16* wo = reinterpret_cast<f16*>(w);
-  const int wt = (int)n_wordtiles(K, fmt);
   switch (fmt) {
-    case QG_INT4_ASYM: hipLaunchKernelGGL(dequant_kernel<INT4_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt); break;
-    case QG_INT2_ASYM: hipLaunchKernelGGL(dequant_kernel<INT2_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt); break;
-    default: hipLaunchKernelGGL(dequant_kernel<Q4_0>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt); break;
+    case QG_INT4_ASYM: hipLaunchKernelGGL(dequant_kernel<INT4_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
+    case QG_INT2_ASYM: hipLaunchKernelGGL(dequant_kernel<INT2_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
+    default: hipLaunchKernelGGL(dequant_kernel<Q4_0>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
   }
   return launch_status();
 }

@@ -344,3 +344,20 @@ def test_graph_replays_match_eager(name, M):
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
         assert torch.equal(other.view(torch.int16), eager.view(torch.int16))
+
+
+def test_dequant_into_caller_buffer_feeds_an_fp16_gemm():
+    # the dequantize-at-load comparison path: qg_dequant into a caller-owned
+    # fp16 [N, K] buffer (same bits as `dequant`), then a plain fp32 product
+    N, K, group, M = 200, 640, 64, 16
+    say("dequant_into + fp16 product")
+    c = synth.random_case(4242, 0, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    w = torch.full((N, K), float("nan"), dtype=torch.float16, device=DEV)
+    qgm.dequant_into(lin.packed, lin.scales, lin.zeros, N, K, group, 0, w)
+    ref_w = qgm.dequant(lin.packed, lin.scales, lin.zeros, N, K, group, 0)
+    assert torch.equal(w.view(torch.int16), ref_w.view(torch.int16))
+    y = (torch.from_numpy(c.x.astype(np.float32)) @ w.cpu().float().t()).numpy()
+    check_close(y, ref_y(c, c.x), "dequant then product")
+    with pytest.raises(ValueError):
+        qgm.dequant_into(lin.packed, lin.scales, lin.zeros, N, K, group, 0, w[:, :K - 8])
