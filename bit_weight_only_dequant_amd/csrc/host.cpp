@@ -55,10 +55,10 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   const int split_env = env_int("QGEMM_SPLITK", 0);
   if (gemv) {
     p.path = 1;
-    p.mmax = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    p.mmax = M <= 1 ? 1 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     const int nw = GEMV_THREADS / 64;
-    const int tps_lds = std::max(1, GEMV_LDS_X_BYTES / (p.mmax * kt_width * 2));
-    const int tps_max = std::min(tps_lds, nw * GEMV_TPW_MAX);
+    const int tps_lds = std::max(1, GEMV_LDS_X_BYTES / (kt_width * 2));
+    const int tps_max = p.mmax == 1 ? std::min(tps_lds, nw * GEMV_TPW_MAX) : nw * (GEMV_MFMA_KW / kt_width);
     const int s_min = (int)ceil_div(p.wordtiles, tps_max);
     // split only when there are too few row blocks to fill the chip: a split
     // costs a second (reduce) launch

@@ -9,8 +9,10 @@
 
 namespace qg {
 
-// Path choice: decode GEMV for M <= GEMV_MAX_M, MFMA GEMM above.
-constexpr int GEMV_MAX_M = 8;
+// Path choice: decode GEMV for M <= GEMV_MAX_M (v_dot2 for M = 1, 16 x 16 MFMA
+// blocks for 2..16 rows), MFMA GEMM above.
+constexpr int GEMV_MAX_M = 16;
+constexpr int GEMV_MFMA_KW = 256;        // K covered by one wave of the MFMA GEMV, at most
 constexpr int GEMV_THREADS = 512;          // 8 waves per workgroup
 constexpr int GEMV_TPW_MAX = 8;          // word tiles one wave streams per launch
 constexpr int GEMV_LDS_X_BYTES = 32768;  // x slice staged per workgroup
@@ -24,7 +26,7 @@ constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
 
 struct Plan {
   int path = 0;        // 0 none (no-op / zero fill), 1 GEMV, 2 GEMM
-  int mmax = 0;        // GEMV: rows handled per launch (1, 2, 4, 8)
+  int mmax = 0;        // GEMV: rows per launch (1: v_dot2 kernel; 4, 8, 16: MFMA kernel)
   int splits = 1;      // K splits
   int tps = 0;         // word tiles per split
   int wordtiles = 0;   // total word tiles along K

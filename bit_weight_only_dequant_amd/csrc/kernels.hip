@@ -11,18 +11,22 @@
 // Kernels
 //   qpack / qunpack      one-time permutation of codes into the tile order of
 //                        layout.h (HBM-bound, elementwise).
-//   gemv<FMT, MMAX>      M <= 8.  Bandwidth-bound.  One 16-byte code load per
+//   gemv<FMT, 1>         M == 1.  Bandwidth-bound.  One 16-byte code load per
 //                        lane per 16x16-word tile, unpack by mask into fp16
 //                        pairs holding exact (q - z), v_dot2_f32_f16 against x
 //                        that each wave stages for itself in LDS, fp32 scale
 //                        per group, lane groups summed by lane shuffles and
 //                        waves through LDS.
-//   gemm<FMT>            M > 8.  128x32 workgroup tile; the 4 waves split K
-//                        and are summed through LDS.  x streams into per-wave
-//                        LDS stages with direct loads; codes go from HBM to
-//                        VGPRs in the MFMA B-operand layout, are dequantized
-//                        once to fp16 s*(q-z) in registers and fed to
-//                        v_mfma_f32_32x32x16_f16 (fp32 accumulation).
+//   gemv_mfma<FMT, R>    2 <= M <= 16.  Same loads and staging; each packed
+//                        word, dequantized to fp16 s*(q-z), is one
+//                        v_mfma_f32_16x16x32_f16 step (the packed layout is
+//                        that MFMA's B operand), so the VALU work per code
+//                        does not grow with M.
+//   gemm<FMT>            M > 16.  64x64 workgroup tile; 8 waves split K and
+//                        are summed through LDS.  x and codes stream into
+//                        per-wave LDS rings with direct loads; codes are
+//                        dequantized once per workgroup to fp16 s*(q-z) in
+//                        registers and fed to v_mfma_f32_32x32x16_f16.
 //   Split-K (both)       fp32 partials in a workspace, summed in split order by a
 //                        second small kernel (deterministic).  A kernel boundary
 //                        orders the partials; an in-kernel device-scope fence
@@ -215,7 +219,7 @@ __global__ void fill_zero_kernel(f16* __restrict__ y, int M, int N, int ldy,
 }
 
 // ---------------------------------------------------------------------------
-// decode GEMV (M <= 8)
+// decode GEMV (M <= 16)
 // ---------------------------------------------------------------------------
 struct GemvArgs {
   const f16* x; const uint32_t* packed; const f16* scales; const f16* zeros;
@@ -237,7 +241,7 @@ template <int FMT, int MMAX, int TPW> constexpr size_t gemv_lds_bytes() {
   return (size_t)NW * (MMAX * KW * 2 + 16 * (KW / 32) * 4) + (size_t)NW * MMAX * 16 * sizeof(float);
 }
 
-// Decode GEMV (M <= 8).  Workgroup = one 16-row block (x one K split); its NW
+// Decode GEMV (used for M == 1).  Workgroup = one 16-row block (x one K split); its NW
 // waves take consecutive runs of word tiles.  Each wave stages only its own x
 // slice and (scale, zero) pairs in its own LDS region, so no wave waits for
 // another until the final sum.  Per lane and tile: one 16-byte code load,
@@ -404,6 +408,175 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   a.ws[((int64_t)rb * a.splits + split) * MMAX * 16 + tid] = total;
 }
 
+// LDS bytes of gemv_mfma_kernel: per wave its x rows (padded by 16 bytes so
+// that the A-fragment reads of 16 rows fall in distinct banks) and its
+// (scale, zero) pairs, then one 16 x 16 fp32 block per wave for the final sum
+template <int FMT, int MROWS, int TPW> constexpr size_t gemv_mfma_lds_bytes() {
+  constexpr int KW = TPW * Fmt<FMT>::KT, NW = GEMV_THREADS / 64;
+  return (size_t)NW * (MROWS * (KW + 8) * 2 + 16 * (KW / 32) * 4) + (size_t)NW * 64 * 16;
+}
+
+// Decode GEMV for 2 <= M <= 16 on the matrix cores.  Same workgroup and wave
+// layout as gemv_kernel (one 16-row block x a K range; 8 waves, each staging
+// its own x rows and (scale, zero) pairs), but the products run as
+// v_mfma_f32_16x16x32_f16.  In that operand layout lane l = 16g + r supplies
+// column r and k-slots 8g..8g+7 of B -- exactly the packed chunk of row r and
+// lane group g -- so once a word is dequantized to fp16 s*(q - z) (13 VALU per
+// 8 codes, the GEMM's dequant, whatever M is) it is one MFMA step; A is row r
+// of x (zero for r >= MROWS) at the same k.  The 16 x 16 accumulator holds
+// y[4g + i][16 rb + r] in lane 16g + r, element i.
+template <int FMT, int MROWS, int TPW>
+__global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
+  using F = Fmt<FMT>;
+  constexpr int NW = GEMV_THREADS / 64;
+  constexpr int KW = TPW * F::KT;              // k range of one wave
+  constexpr int KWP = KW + 8;                  // padded x row (halves)
+  constexpr int GWMAX = KW / 32;
+  constexpr int XCH = MROWS * KW / 8;          // 16-byte x chunks per wave
+  constexpr int NXC = (XCH + 63) / 64;
+  constexpr int NSZ = (16 * GWMAX + 63) / 64;
+  constexpr int XB = MROWS * KWP * 2, WB = XB + 16 * GWMAX * 4;
+  static_assert(MROWS == 4 || MROWS == 8 || MROWS == 16, "rows per MFMA block");
+  __shared__ __align__(16) uint8_t smem[gemv_mfma_lds_bytes<FMT, MROWS, TPW>()];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f16* xs = reinterpret_cast<f16*>(smem + wave * WB);                 // [MROWS][KWP]
+  uint32_t* sz = reinterpret_cast<uint32_t*>(smem + wave * WB + XB);  // [16][GWMAX] s | z << 16
+  f4* red = reinterpret_cast<f4*>(smem + NW * WB);                     // [NW][64 lanes]
+
+  const int g = lane >> 4, r = lane & 15;
+  const int rb = blockIdx.x, split = blockIdx.y;
+  const int T0 = split * a.tps, T1 = min(a.wordtiles, T0 + a.tps);
+  const int tpw = (T1 - T0 + NW - 1) / NW;
+  const int wt0 = T0 + wave * tpw;
+  const int nt = max(0, min(T1, wt0 + tpw) - wt0);
+  const int k0 = wt0 * F::KT;
+  const int lg = __builtin_ctz(a.group);
+  const int ng = a.K >> lg;
+  const int gstride = KW >> lg;
+  const int lgs = __builtin_ctz(gstride);
+  const int gs0 = k0 >> lg;
+
+  // 1. every global load first, branch-free: scales/zeros, residual, x, codes
+  const int64_t szbase = (int64_t)rb * 16 * ng * 2;
+  const char* sp = reinterpret_cast<const char*>(a.scales) + szbase;
+  const char* zp = reinterpret_cast<const char*>(F::HAS_Z ? a.zeros : a.scales) + szbase;
+  uint32_t sraw[NSZ], zraw[NSZ];
+#pragma unroll
+  for (int j = 0; j < NSZ; ++j) {
+    const int e = lane + 64 * j;
+    const int er = e >> lgs, eg = gs0 + (e & (gstride - 1));
+    const bool ok = e < 16 * gstride && rb * 16 + er < a.N && eg < ng;
+    const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
+    sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
+    if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+    else zraw[j] = 0x4800;  // fp16 8.0
+  }
+  float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (a.resid && a.splits == 1 && wave == 0) {
+    const int nc = min(rb * 16 + r, a.N - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) res[i] = (float)a.resid[(int64_t)min(4 * g + i, a.M - 1) * a.ldr + nc];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u4 xr[NXC];
+#pragma unroll
+  for (int j = 0; j < NXC; ++j) {
+    const int c = lane + 64 * j;
+    const int m = c / (KW / 8), k = k0 + (c % (KW / 8)) * 8;
+    const bool ok = c < XCH && m < a.M && k < a.K;
+    const uint32_t off = ok ? (uint32_t)(m * a.ldx + k) * 2u : 0u;
+    xr[j] = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(a.x) + off);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u4 code[TPW];
+  const char* pkrow = reinterpret_cast<const char*>(a.packed) + (int64_t)rb * a.wordtiles * 1024;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int T = min(wt0 + i, a.wordtiles - 1);
+    code[i] = *reinterpret_cast<const u4*>(pkrow + (uint32_t)(T * 1024 + lane * 16));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. stage this wave's x rows (zeros beyond M and K) and (scale, zero) pairs
+#pragma unroll
+  for (int j = 0; j < NXC; ++j) {
+    const int c = lane + 64 * j;
+    const int m = c / (KW / 8), kk = (c % (KW / 8)) * 8;
+    const bool ok = m < a.M && k0 + kk < a.K;
+    if (c < XCH) *reinterpret_cast<u4*>(xs + m * KWP + kk) = ok ? xr[j] : u4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int j = 0; j < NSZ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < 16 * gstride) sz[(e >> lgs) * GWMAX + (e & (gstride - 1))] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // 3. per 32-code segment: dequantize four words to fp16 s*(q - z), one MFMA each
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  const bool arow = r < MROWS;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (i < nt) {
+#pragma unroll
+      for (int p = 0; p < F::LS / 32; ++p) {
+        const int kl = i * F::KT + g * F::LS + p * 32;  // this lane's segment inside the wave's range
+        const uint32_t szv = sz[r * GWMAX + (kl >> lg)];
+        const h2 s2 = splat(__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu)));
+        const f16 z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
+        h8 av[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          av[t] = arow ? *reinterpret_cast<const h8*>(xs + (arow ? r : 0) * KWP + kl + 8 * t) : h8{};
+        h2 q[16];
+        if constexpr (FMT == INT2_ASYM) {
+          const ZC2 zc = make_zc2(z);
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) qmz_int2_half(code[i][2 * p + t], h, zc, q + 8 * t + 4 * h);
+        } else {
+          const ZC4 zc = make_zc4(z);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) qmz_int4(code[i][t], zc, q + 4 * t);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const h2 w0 = q[4 * t] * s2, w1 = q[4 * t + 1] * s2, w2 = q[4 * t + 2] * s2, w3 = q[4 * t + 3] * s2;
+          const h8 bf = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t], bf, acc, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // 4. sum the NW waves' blocks through LDS in wave order; wave 0 writes
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  f4 tot = red[lane];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) tot += red[w * 64 + lane];
+  const int n = rb * 16 + r;
+  if (a.splits == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (m < a.M && n < a.N) a.y[(int64_t)m * a.ldy + n] = (f16)(tot[i] + res[i]);
+    }
+    return;
+  }
+  // split-K: rows m < MROWS of this split's block, laid out as gemv_kernel's
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * g + i;
+    if (m < MROWS) a.ws[((int64_t)rb * a.splits + split) * MROWS * 16 + m * 16 + r] = tot[i];
+  }
+}
+
 // Sums the split-K partials of the GEMV in split order (deterministic), adds
 // the residual and rounds once to fp16.  One thread per output.
 __global__ void gemv_reduce_kernel(const float* __restrict__ ws, const f16* __restrict__ resid,
@@ -423,7 +596,7 @@ __global__ void gemv_reduce_kernel(const float* __restrict__ ws, const f16* __re
 }
 
 // ---------------------------------------------------------------------------
-// prefill GEMM (M > 8): fp16 MFMA on register-dequantized weights
+// prefill GEMM (M > 16): fp16 MFMA on register-dequantized weights
 // ---------------------------------------------------------------------------
 struct GemmArgs {
   const f16* x; const uint32_t* packed; const f16* scales; const f16* zeros;
@@ -458,7 +631,7 @@ template <int FMT> struct GemmStage {
   static constexpr int DMA = XB / 1024 + 2;         // direct loads per lane per stage (10)
 };
 
-// Prefill GEMM (M > 8).  Workgroup tile 64 (M) x 64 (N) over the workgroup's
+// Prefill GEMM (M > 16).  Workgroup tile 64 (M) x 64 (N) over the workgroup's
 // share of K; its NW waves split that share and are summed through LDS at the
 // end, so every code is dequantized once per workgroup.  Each wave owns 2 x 2
 // blocks of v_mfma_f32_32x32x16_f16 (B operand lane l = column l % 32,
@@ -831,30 +1004,44 @@ static void launch_gemv_t(const GemvArgs& a, hipStream_t s) {
 }
 
 // TPW: word tiles per wave, rounded up to a power of two and capped so that
-// the x slice of MMAX * 4 * TPW tiles fits the 32 KiB LDS stage.  Returns
-// false when the plan asks for more tiles per wave than that (never, for plans
-// made by make_plan).
-template <int FMT, int MMAX>
-static bool launch_gemv_m(const GemvArgs& a, int tpw, hipStream_t s) {
+// the x slice of 8 * TPW tiles fits the 32 KiB LDS stage.  Returns false when
+// the plan asks for more tiles per wave than that (never, for plans made by
+// make_plan).
+template <int FMT>
+static bool launch_gemv_dot(const GemvArgs& a, int tpw, hipStream_t s) {
   constexpr int KT = Fmt<FMT>::KT;
-  constexpr int TMAX0 = GEMV_LDS_X_BYTES / (MMAX * (GEMV_THREADS / 64) * KT * 2);
+  constexpr int TMAX0 = GEMV_LDS_X_BYTES / ((GEMV_THREADS / 64) * KT * 2);
   constexpr int TMAX = TMAX0 < GEMV_TPW_MAX ? TMAX0 : GEMV_TPW_MAX;
   constexpr int T2 = TMAX >= 2 ? 2 : 1, T4 = TMAX >= 4 ? 4 : T2, T8 = TMAX >= 8 ? 8 : T4;
   if (tpw > TMAX) return false;
-  if (tpw <= 1) launch_gemv_t<FMT, MMAX, 1>(a, s);
-  else if (tpw <= 2) launch_gemv_t<FMT, MMAX, T2>(a, s);
-  else if (tpw <= 4) launch_gemv_t<FMT, MMAX, T4>(a, s);
-  else launch_gemv_t<FMT, MMAX, T8>(a, s);
+  if (tpw <= 1) launch_gemv_t<FMT, 1, 1>(a, s);
+  else if (tpw <= 2) launch_gemv_t<FMT, 1, T2>(a, s);
+  else if (tpw <= 4) launch_gemv_t<FMT, 1, T4>(a, s);
+  else launch_gemv_t<FMT, 1, T8>(a, s);
   return true;
 }
 
+// grid: x = row blocks, y = K splits; a wave covers at most GEMV_MFMA_KW of K
+template <int FMT, int MROWS>
+static bool launch_gemv_mfma(const GemvArgs& a, int tpw, hipStream_t s) {
+  constexpr int TMAX = GEMV_MFMA_KW / Fmt<FMT>::KT;
+  static_assert(TMAX >= 1 && gemv_mfma_lds_bytes<FMT, MROWS, TMAX>() <= 80 * 1024,
+                "MFMA GEMV LDS: at least two workgroups per CU");
+  const dim3 grid((unsigned)a.rowblocks, (unsigned)a.splits), block(GEMV_THREADS);
+  if (tpw > TMAX) return false;
+  if (tpw <= 1) hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MROWS, 1>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MROWS, TMAX>), grid, block, 0, s, a);
+  return true;
+}
+
+// mmax 1: v_dot2 GEMV; 4, 8, 16: rows of the MFMA GEMV
 template <int FMT>
 static bool launch_gemv_f(const GemvArgs& a, int mmax, int tpw, hipStream_t s) {
   switch (mmax) {
-    case 1: return launch_gemv_m<FMT, 1>(a, tpw, s);
-    case 2: return launch_gemv_m<FMT, 2>(a, tpw, s);
-    case 4: return launch_gemv_m<FMT, 4>(a, tpw, s);
-    default: return launch_gemv_m<FMT, 8>(a, tpw, s);
+    case 1: return launch_gemv_dot<FMT>(a, tpw, s);
+    case 4: return launch_gemv_mfma<FMT, 4>(a, tpw, s);
+    case 8: return launch_gemv_mfma<FMT, 8>(a, tpw, s);
+    default: return launch_gemv_mfma<FMT, 16>(a, tpw, s);
   }
 }
 

@@ -115,10 +115,11 @@ int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt)
  *   zeros  [device, in]  fp16 [N, K/group]; must be NULL for QG_Q4_0 and
  *                        non-NULL for the asymmetric formats.
  *   y      [device, out] fp16 [M, N], row-major, leading dimension N.
- * M <= 8 runs the decode GEMV (packed-fp16 dequant, fp32 dot products, no
- * matrix cores); M > 8 runs the MFMA GEMM (dequant to fp16 in registers,
- * fp16 MFMA with fp32 accumulation, split-K reduced in a fixed order, so the
- * result is deterministic).  M == 0 or N == 0 is a no-op; K == 0 writes zeros.
+ * M == 1 runs the decode GEMV (packed-fp16 dequant, fp32 dot products);
+ * 2 <= M <= 16 the decode GEMV on 16 x 16 matrix-core blocks; M > 16 the
+ * MFMA GEMM.  All dequantize to fp16 in registers and accumulate in fp32;
+ * split-K partials are reduced in a fixed order, so the result is
+ * deterministic.  M == 0 or N == 0 is a no-op; K == 0 writes zeros.
  * Uses a library-owned per-device workspace, allocated (hipMalloc) on first
  * need and grown as needed; call once before capturing into a HIP graph.
  * Errors: QG_E_ARG, QG_E_ALIGN, QG_E_DEVICE, QG_E_NOMEM.

@@ -153,6 +153,7 @@ def test_plans_for_the_workloads():
     assert qgm.plan(8, 6144, 2048, 128, 0)["path"] == "gemv"
     p = qgm.plan(128, 8192, 2048, 128, 0)
     assert p["path"] == "gemm" and p["workgroups"] >= 128
-    assert qgm.plan(9, 64, 128, 32, 0)["path"] == "gemm"
+    assert qgm.plan(16, 64, 128, 32, 0)["path"] == "gemv"
+    assert qgm.plan(17, 64, 128, 32, 0)["path"] == "gemm"
     assert qgm.workspace_bytes(1, 16, 128, 32, 0) == 0
     assert qgm.workspace_bytes(128, 2048, 8192, 128, 0) > 0   # split-K for small N
