@@ -236,29 +236,28 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
 
 // LDS bytes of gemv_kernel: per wave its x slice and (scale, zero) pairs, then
 // the cross-wave sums
-template <int FMT, int MMAX, int TPW> constexpr size_t gemv_lds_bytes() {
-  constexpr int KW = TPW * Fmt<FMT>::KT, NW = GEMV_THREADS / 64;
+template <int FMT, int MMAX, int TPW, int NW> constexpr size_t gemv_lds_bytes() {
+  constexpr int KW = TPW * Fmt<FMT>::KT;
   return (size_t)NW * (MMAX * KW * 2 + 16 * (KW / 32) * 4) + (size_t)NW * MMAX * 16 * sizeof(float);
 }
 
 // Decode GEMV (used for M == 1).  Workgroup = one 16-row block (x one K split); its NW
-// waves take consecutive runs of word tiles.  Each wave stages only its own x
+// waves (8 or 16) take consecutive runs of word tiles.  Each wave stages only its own x
 // slice and (scale, zero) pairs in its own LDS region, so no wave waits for
 // another until the final sum.  Per lane and tile: one 16-byte code load,
 // masks into fp16 pairs holding exact (q - z) (one v_and_or_b32 plus one
 // packed add or fma per pair), v_dot2_f32_f16 against fp16 x pairs, the fp32
 // scale once per 32 (INT4) or 64 (INT2) codes.
-template <int FMT, int MMAX, int TPW>
-__global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
+template <int FMT, int MMAX, int TPW, int NW>
+__global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   using F = Fmt<FMT>;
-  constexpr int NW = GEMV_THREADS / 64;
   constexpr int KW = TPW * F::KT;              // k range of one wave
   constexpr int GWMAX = KW / 32;               // groups per wave, at most (group >= 32)
   constexpr int XCH = MMAX * KW / 8;           // 16-byte x chunks per wave
   constexpr int NXC = (XCH + 63) / 64;
   constexpr int NSZ = (16 * GWMAX + 63) / 64;  // (scale, zero) loads per lane, at most
   constexpr int XB = MMAX * KW * 2, WB = XB + 16 * GWMAX * 4;
-  __shared__ __align__(16) uint8_t gemv_smem[gemv_lds_bytes<FMT, MMAX, TPW>()];
+  __shared__ __align__(16) uint8_t gemv_smem[gemv_lds_bytes<FMT, MMAX, TPW, NW>()];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f16* xs = reinterpret_cast<f16*>(gemv_smem + wave * WB);                 // [MMAX][KW]
@@ -996,35 +995,44 @@ static unsigned grid_for(int64_t total, int threads) {
 }
 
 // grid: x = row blocks, y = K splits
-template <int FMT, int MMAX, int TPW>
+template <int FMT, int MMAX, int TPW, int NW>
 static void launch_gemv_t(const GemvArgs& a, hipStream_t s) {
-  static_assert(gemv_lds_bytes<FMT, MMAX, TPW>() <= 80 * 1024, "GEMV LDS: at least two workgroups per CU");
-  hipLaunchKernelGGL((gemv_kernel<FMT, MMAX, TPW>), dim3((unsigned)a.rowblocks, (unsigned)a.splits),
-                     dim3(GEMV_THREADS), 0, s, a);
+  static_assert(gemv_lds_bytes<FMT, MMAX, TPW, NW>() <= 80 * 1024, "GEMV LDS: at least two workgroups per CU");
+  hipLaunchKernelGGL((gemv_kernel<FMT, MMAX, TPW, NW>), dim3((unsigned)a.rowblocks, (unsigned)a.splits),
+                     dim3(NW * 64), 0, s, a);
 }
 
 // TPW: word tiles per wave, rounded up to a power of two and capped so that
-// the x slice of 8 * TPW tiles fits the 32 KiB LDS stage.  Returns false when
+// the x slice of NW * TPW tiles fits the 32 KiB LDS stage.  Returns false when
 // the plan asks for more tiles per wave than that (never, for plans made by
 // make_plan).
-template <int FMT>
-static bool launch_gemv_dot(const GemvArgs& a, int tpw, hipStream_t s) {
+template <int FMT, int NW>
+static bool launch_gemv_dot_w(const GemvArgs& a, int tps, hipStream_t s) {
   constexpr int KT = Fmt<FMT>::KT;
-  constexpr int TMAX0 = GEMV_LDS_X_BYTES / ((GEMV_THREADS / 64) * KT * 2);
+  constexpr int TMAX0 = GEMV_LDS_X_BYTES / (NW * KT * 2);
   constexpr int TMAX = TMAX0 < GEMV_TPW_MAX ? TMAX0 : GEMV_TPW_MAX;
   constexpr int T2 = TMAX >= 2 ? 2 : 1, T4 = TMAX >= 4 ? 4 : T2, T8 = TMAX >= 8 ? 8 : T4;
+  const int tpw = (tps + NW - 1) / NW;
   if (tpw > TMAX) return false;
-  if (tpw <= 1) launch_gemv_t<FMT, 1, 1>(a, s);
-  else if (tpw <= 2) launch_gemv_t<FMT, 1, T2>(a, s);
-  else if (tpw <= 4) launch_gemv_t<FMT, 1, T4>(a, s);
-  else launch_gemv_t<FMT, 1, T8>(a, s);
+  if (tpw <= 1) launch_gemv_t<FMT, 1, 1, NW>(a, s);
+  else if (tpw <= 2) launch_gemv_t<FMT, 1, T2, NW>(a, s);
+  else if (tpw <= 4) launch_gemv_t<FMT, 1, T4, NW>(a, s);
+  else launch_gemv_t<FMT, 1, T8, NW>(a, s);
   return true;
+}
+
+// 16 waves when a workgroup has at least 16 word tiles (more waves in flight,
+// one tile each at K = 2048), 8 otherwise
+template <int FMT>
+static bool launch_gemv_dot(const GemvArgs& a, int tps, hipStream_t s) {
+  return tps >= 16 ? launch_gemv_dot_w<FMT, 16>(a, tps, s) : launch_gemv_dot_w<FMT, 8>(a, tps, s);
 }
 
 // grid: x = row blocks, y = K splits; a wave covers at most GEMV_MFMA_KW of K
 template <int FMT, int MROWS>
-static bool launch_gemv_mfma(const GemvArgs& a, int tpw, hipStream_t s) {
+static bool launch_gemv_mfma(const GemvArgs& a, int tps, hipStream_t s) {
   constexpr int TMAX = GEMV_MFMA_KW / Fmt<FMT>::KT;
+  const int tpw = (tps + GEMV_THREADS / 64 - 1) / (GEMV_THREADS / 64);
   static_assert(TMAX >= 1 && gemv_mfma_lds_bytes<FMT, MROWS, TMAX>() <= 80 * 1024,
                 "MFMA GEMV LDS: at least two workgroups per CU");
   const dim3 grid((unsigned)a.rowblocks, (unsigned)a.splits), block(GEMV_THREADS);
@@ -1036,12 +1044,12 @@ static bool launch_gemv_mfma(const GemvArgs& a, int tpw, hipStream_t s) {
 
 // mmax 1: v_dot2 GEMV; 4, 8, 16: rows of the MFMA GEMV
 template <int FMT>
-static bool launch_gemv_f(const GemvArgs& a, int mmax, int tpw, hipStream_t s) {
+static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, hipStream_t s) {
   switch (mmax) {
-    case 1: return launch_gemv_dot<FMT>(a, tpw, s);
-    case 4: return launch_gemv_mfma<FMT, 4>(a, tpw, s);
-    case 8: return launch_gemv_mfma<FMT, 8>(a, tpw, s);
-    default: return launch_gemv_mfma<FMT, 16>(a, tpw, s);
+    case 1: return launch_gemv_dot<FMT>(a, tps, s);
+    case 4: return launch_gemv_mfma<FMT, 4>(a, tps, s);
+    case 8: return launch_gemv_mfma<FMT, 8>(a, tps, s);
+    default: return launch_gemv_mfma<FMT, 16>(a, tps, s);
   }
 }
 
@@ -1106,12 +1114,11 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
     if ((int64_t)M * ldx * 2 >= (int64_t)1 << 32 || (int64_t)p.wordtiles * 1024 >= (int64_t)1 << 32 ||
         p.splits > 65535)
       return QG_E_UNSUPPORTED;
-    const int tpw = (int)ceil_div(p.tps, GEMV_THREADS / 64);
     bool launched;
     switch (fmt) {
-      case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, tpw, s); break;
-      case QG_INT2_ASYM: launched = launch_gemv_f<INT2_ASYM>(a, p.mmax, tpw, s); break;
-      default: launched = launch_gemv_f<Q4_0>(a, p.mmax, tpw, s); break;
+      case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, p.tps, s); break;
+      case QG_INT2_ASYM: launched = launch_gemv_f<INT2_ASYM>(a, p.mmax, p.tps, s); break;
+      default: launched = launch_gemv_f<Q4_0>(a, p.mmax, p.tps, s); break;
     }
     if (!launched) return QG_E_UNSUPPORTED;
     if (p.splits > 1) {

@@ -138,6 +138,7 @@ RAGGED = [
     (0, 32, 100, 96, 9), (0, 64, 130, 192, 17), (0, 128, 1000, 384, 100), (0, 128, 300, 2048, 129),
     (1, 32, 40, 160, 33), (1, 64, 272, 320, 127), (2, 32, 33, 224, 200), (2, 32, 520, 1056, 257),
     (0, 128, 2048, 8192, 130),
+    (0, 128, 300, 2048, 16), (1, 32, 72, 512, 12), (2, 32, 48, 1024, 16), (0, 64, 520, 4352, 11),
 ]
 
 
