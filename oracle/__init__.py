@@ -5,7 +5,7 @@ Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 and never calls it.
 """
 from .qref import (  # noqa: F401
-    INT4_ASYM, INT2_ASYM, Q4_0, BITS,
+    INT4_ASYM, INT2_ASYM, Q4_0, Q8_0, BITS, IMPLICIT_ZERO,
     unpack_codes, pack_codes, dequant_f32, dequant_f16, qgemm_ref,
     rel_error, within_tolerance, TOLERANCE, loop_block_ref,
     fold_zero_point_ref,

@@ -13,19 +13,25 @@ What is computed, and where it comes from:
   w[n, k] = s[n, k // g] * (q[n, k] - z[n, k // g]).
 * The weight formats are the INT4 group weights with GPTQ zero points and the
   INT2 body weights of the TinyLoop README (sections "Status" and "Current
-  Runtime Snapshot") and q4_0 from the torchnative guide "Inference with real
-  transformers" (section "Quantise while loading").  The pages give names, not
-  layouts; the readings used are:
+  Runtime Snapshot") and q4_0 and q8_0 from the torchnative guide "Inference
+  with real transformers" (section "Quantise while loading").  The pages give
+  names, not layouts; the readings used are:
     - canonical words hold cpw = 32 / b codes, least significant bits first
       along K (code k of a row lives in word k // cpw at bit b * (k % cpw));
     - q4_0 stores u = q + 8 in a nibble, so w = s * (u - 8): the same formula
       with an implicit zero point of 8 and group 32;
+    - q8_0 stores u = q + 128 in a byte (signed 8-bit codes, offset binary),
+      so w = s * (u - 128): implicit zero point 128, group 32.  The guide says
+      this format loses nothing when the operands are integers; read here as:
+      a weight that already is a block scale times an integer in [-127, 127]
+      comes back exactly, and every code and every s * q is exact in fp32;
     - zero points are fp16 values holding integers in [0, 2^b - 1].
 * Precision: the dequantized weight is formed in fp32, which is exact (an
-  11-bit fp16 significand times an integer of at most 4 bits); the product is
-  taken in fp64.  The torchnative guide (section "float32 or bfloat16") notes
-  that a change of accumulation order alone changes low-precision results, so
-  parity is judged by a tolerance on y, and bit-exactly only on integer codes.
+  11-bit fp16 significand times an integer of at most 8 bits needs at most 19
+  significant bits); the product is taken in fp64.  The torchnative guide
+  (section "float32 or bfloat16") notes that a change of accumulation order
+  alone changes low-precision results, so parity is judged by a tolerance on
+  y, and bit-exactly only on integer codes.
 
 Every function here is pinned by tests/test_oracle_pins.py against closed
 forms, hand-worked values (tests/golden/), exact rational arithmetic and a
@@ -38,7 +44,10 @@ import numpy as np
 INT4_ASYM = 0
 INT2_ASYM = 1
 Q4_0 = 2
-BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4}
+Q8_0 = 3
+BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4, Q8_0: 8}
+# implicit zero points of the symmetric block formats (offset-binary codes)
+IMPLICIT_ZERO = {Q4_0: 8.0, Q8_0: 128.0}
 
 # max |y - y_ref| <= TOLERANCE * max |y_ref| over one call's output
 TOLERANCE = 2e-3
@@ -75,10 +84,10 @@ def pack_codes(codes: np.ndarray, fmt: int) -> np.ndarray:
 def _group_params(scales, zeros, N, K, group, fmt):
     ng = K // group
     s = np.asarray(scales, dtype=np.float16).reshape(N, ng).astype(np.float32)
-    if fmt == Q4_0:
+    if fmt in IMPLICIT_ZERO:
         if group != 32:
-            raise ValueError("q4_0 uses blocks of 32")
-        z = np.full((N, ng), 8.0, dtype=np.float32)
+            raise ValueError("q4_0 and q8_0 use blocks of 32")
+        z = np.full((N, ng), IMPLICIT_ZERO[fmt], dtype=np.float32)
     else:
         z = np.asarray(zeros, dtype=np.float16).reshape(N, ng).astype(np.float32)
     return s, z

@@ -21,6 +21,11 @@ DESIGN.md under "Readings"):
   point, signed codes in [-8, 7].  d = m / -8 where m is the signed element of
   largest magnitude; code = clip(rint(w / fp16(d)), -8, 7); stored as the
   offset-binary nibble u = code + 8.  An all-zero block has scale 0, u = 8.
+* q8_0 (same guide and section): blocks of 32, one fp16 scale, signed codes
+  in [-127, 127].  d = max|w| / 127; code = clip(rint(w / fp16(d)), -127, 127);
+  stored as the offset-binary byte u = code + 128.  An all-zero block has
+  scale 0, u = 128.  A block that already is d times integers in [-127, 127]
+  with one of magnitude 127 (d an fp16 value) is reproduced exactly.
 * Canonical packing: code (n, k) sits in word [n, k // cpw] at bits
   [b*(k % cpw), b*(k % cpw) + b), i.e. least significant bits first along K,
   cpw = 32 / b codes per uint32.
@@ -37,9 +42,11 @@ import numpy as np
 INT4_ASYM = 0
 INT2_ASYM = 1
 Q4_0 = 2
+Q8_0 = 3
 
-FORMAT_NAMES = {INT4_ASYM: "int4_asym", INT2_ASYM: "int2_asym", Q4_0: "q4_0"}
-FORMAT_BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4}
+FORMAT_NAMES = {INT4_ASYM: "int4_asym", INT2_ASYM: "int2_asym", Q4_0: "q4_0", Q8_0: "q8_0"}
+FORMAT_BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4, Q8_0: 8}
+SYMMETRIC = (Q4_0, Q8_0)   # block formats with no stored zero point
 
 
 def codes_per_word(fmt: int) -> int:
@@ -90,6 +97,23 @@ def quantize_q4_0(w: np.ndarray, block: int = 32):
     return u, s16
 
 
+def quantize_q8_0(w: np.ndarray, block: int = 32):
+    """Symmetric 8-bit block quantizer.  Returns (offset-binary codes uint8
+    [N,K] in [1, 255], scale fp16 [N,K/32])."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    assert k % block == 0
+    wb = w.reshape(n, k // block, block)
+    amax = np.abs(wb).max(axis=2)
+    s16 = (amax / np.float32(127.0)).astype(np.float32).astype(np.float16)
+    sf = s16.astype(np.float32)
+    safe = np.where(sf == 0, np.float32(1.0), sf)
+    q = np.clip(np.rint(wb / safe[:, :, None]), -127, 127)
+    q = np.where((sf == 0)[:, :, None], 0, q)
+    u = (q + 128).astype(np.uint8).reshape(n, k)
+    return u, s16
+
+
 def pack_words(codes: np.ndarray, bits: int) -> np.ndarray:
     """Canonical packing: least significant bits first along K."""
     codes = np.asarray(codes, dtype=np.uint32)
@@ -117,7 +141,7 @@ class QCase:
     codes: np.ndarray            # uint8 [N, K]
     words: np.ndarray            # uint32 [N, K / cpw], canonical order
     scales: np.ndarray           # fp16 [N, K / group]
-    zeros: Optional[np.ndarray]  # fp16 [N, K / group] or None for q4_0
+    zeros: Optional[np.ndarray]  # fp16 [N, K / group] or None for q4_0 / q8_0
     x: Optional[np.ndarray] = None  # fp16 [M, K]
 
     @property
@@ -137,6 +161,10 @@ def quantize(w: np.ndarray, fmt: int, group: int) -> QCase:
     if fmt == Q4_0:
         assert group == 32
         codes, s = quantize_q4_0(w, 32)
+        z = None
+    elif fmt == Q8_0:
+        assert group == 32
+        codes, s = quantize_q8_0(w, 32)
         z = None
     else:
         codes, s, z = quantize_asym(w, FORMAT_BITS[fmt], group)
@@ -176,7 +204,7 @@ def random_codes_case(seed: int, fmt: int, group: int, N: int, K: int, M: int) -
     codes = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
     s = (0.005 * rng.uniform(0.5, 1.5, size=(N, K // group))).astype(np.float16)
     z = None
-    if fmt != Q4_0:
+    if fmt not in SYMMETRIC:
         z = rng.integers(0, 1 << bits, size=(N, K // group)).astype(np.float16)
     x = draw_x(rng, M, K, "normal")
     return QCase(fmt=fmt, group=group, N=N, K=K, codes=codes,
@@ -190,6 +218,7 @@ WORKLOADS: Dict[str, dict] = {
     "prefill_int4_g128": dict(seed=1003, fmt=INT4_ASYM, group=128, N=8192, K=2048, M=128, xdist="normal", Ms=(128,)),
     "int2_g64":        dict(seed=1004, fmt=INT2_ASYM, group=64,  N=8192, K=2048, M=128, xdist="normal", Ms=(1, 128)),
     "q4_0_b32":        dict(seed=1004, fmt=Q4_0,      group=32,  N=8192, K=2048, M=128, xdist="normal", Ms=(1, 128)),
+    "q8_0_b32":        dict(seed=1004, fmt=Q8_0,      group=32,  N=8192, K=2048, M=128, xdist="normal", Ms=(1, 128)),
 }
 
 

@@ -15,8 +15,10 @@ from fractions import Fraction
 import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-FMT = {"int4": 0, "int2": 1, "q4_0": 2}
-BITS = {0: 4, 1: 2, 2: 4}
+FMT = {"int4": 0, "int2": 1, "q4_0": 2, "q8_0": 3}
+BITS = {0: 4, 1: 2, 2: 4, 3: 8}
+# implicit zero points of the block formats: q4_0 stores q + 8, q8_0 q + 128
+ZIMPL = {2: 8, 3: 128}
 
 
 # -- independent helpers (no oracle code) ------------------------------------
@@ -54,7 +56,7 @@ def brute_y(x, codes, scales, zeros, group, fmt):
             for k in range(K):
                 g = k // group
                 s = float(scales[n][g])
-                z = 8.0 if fmt == 2 else float(zeros[n][g])
+                z = float(ZIMPL[fmt]) if fmt in ZIMPL else float(zeros[n][g])
                 acc += float(x[m][k]) * (s * (float(codes[n][k]) - z))
             y[m][n] = acc
     return np.array(y)
@@ -73,7 +75,7 @@ def exact_y(x, codes, scales, zeros, group, fmt):
             for k in range(K):
                 g = k // group
                 s = Fraction(float(np.float16(scales[n][g])))
-                z = Fraction(8) if fmt == 2 else Fraction(float(np.float16(zeros[n][g])))
+                z = Fraction(ZIMPL[fmt]) if fmt in ZIMPL else Fraction(float(np.float16(zeros[n][g])))
                 acc += Fraction(float(x[m][k])) * s * (int(codes[n][k]) - z)
             row.append(acc)
         out.append(row)
@@ -85,7 +87,7 @@ def _rand_inputs(seed, fmt, N, K, M, group):
     b = BITS[fmt]
     codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
     s = (rng.uniform(0.01, 0.2, size=(N, K // group))).astype(np.float16)
-    z = None if fmt == 2 else rng.integers(0, 1 << b, size=(N, K // group)).astype(np.float16)
+    z = None if fmt in ZIMPL else rng.integers(0, 1 << b, size=(N, K // group)).astype(np.float16)
     x = rng.standard_normal((M, K)).astype(np.float16)
     return codes, s, z, x
 
@@ -115,8 +117,17 @@ def pin_handcases(O):
         fmt = FMT[c["fmt"]]
         K, g = c["K"], c["group"]
         rule = c["codes"]
-        codes = np.array([[(k % 16 if rule == "k%16" else k % 4 if rule == "k%4" else rule)
-                           for k in range(K)]], dtype=np.uint8)
+        def code(k):
+            if rule == "k%16":
+                return k % 16
+            if rule == "k%4":
+                return k % 4
+            if rule == "8k":
+                return 8 * k
+            if rule == "0/255":
+                return 255 * (k % 2)
+            return rule
+        codes = np.array([[code(k) for k in range(K)]], dtype=np.uint8)
         x = np.array([[1.0 if c["x"] == "ones" else (-1.0) ** k for k in range(K)]], dtype=np.float16)
         s = np.array([c["scales"]], dtype=np.float16)
         z = None if c["zeros"] is None else np.array([c["zeros"]], dtype=np.float16)
@@ -153,7 +164,7 @@ def pin_zero_codes_closed_form(O):
 
 def pin_one_hot(O):
     # x = e_k selects column k of the dequantized matrix: y[m, n] = s(q[n,k] - z)
-    for fmt, group in ((0, 32), (0, 128), (1, 32), (1, 64), (2, 32)):
+    for fmt, group in ((0, 32), (0, 128), (1, 32), (1, 64), (2, 32), (3, 32)):
         N, K = 24, 256     # N != K: a transposed operand cannot pass
         codes, s, z, _ = _rand_inputs(11 + fmt * 10 + group, fmt, N, K, 1, group)
         ks = [0, 1, 7, 8, 31, 32, 33, 100, 127, 128, 200, 255]
@@ -163,7 +174,7 @@ def pin_one_hot(O):
         y = O.qgemm_ref(x, pack_literal(codes, BITS[fmt]), s, z, len(ks), N, K, group, fmt)
         for i, k in enumerate(ks):
             for n in range(N):
-                zz = 8.0 if fmt == 2 else float(z[n, k // group])
+                zz = float(ZIMPL[fmt]) if fmt in ZIMPL else float(z[n, k // group])
                 exp = float(s[n, k // group]) * (int(codes[n, k]) - zz)
                 assert float(y[i, n]) == exp, (fmt, group, k, n, float(y[i, n]), exp)
 
@@ -178,11 +189,19 @@ def pin_format_identity(O):
     assert np.array_equal(a, b)
     uz = pack_literal(np.full((N, K), 8, dtype=np.uint8), 4)
     assert np.array_equal(O.qgemm_ref(x, uz, s, None, M, N, K, 32, 2), np.zeros((M, N)))
+    # q8_0 whose bytes are 120 + c for 4-bit c is q4_0 on the nibbles c
+    # (both decode to s * (c - 8)): one identity across the two block formats
+    u8 = codes.astype(np.uint8) + 120
+    c8 = O.qgemm_ref(x, pack_literal(u8, 8), s, None, M, N, K, 32, 3)
+    assert np.array_equal(a, c8)
+    u128 = pack_literal(np.full((N, K), 128, dtype=np.uint8), 8)
+    assert np.array_equal(O.qgemm_ref(x, u128, s, None, M, N, K, 32, 3), np.zeros((M, N)))
 
 
 def pin_bruteforce(O):
     for fmt, group, N, K, M in ((0, 32, 8, 64, 3), (0, 64, 16, 128, 2), (1, 32, 8, 64, 3),
-                                (1, 64, 16, 128, 1), (2, 32, 8, 64, 3), (2, 32, 16, 32, 2)):
+                                (1, 64, 16, 128, 1), (2, 32, 8, 64, 3), (2, 32, 16, 32, 2),
+                                (3, 32, 8, 64, 3), (3, 32, 16, 96, 2)):
         codes, s, z, x = _rand_inputs(100 + N + K + fmt, fmt, N, K, M, group)
         y = O.qgemm_ref(x, pack_literal(codes, BITS[fmt]), s, z, M, N, K, group, fmt)
         yb = brute_y(x, codes, s, z, group, fmt)
@@ -191,7 +210,7 @@ def pin_bruteforce(O):
 
 
 def pin_exact_rational(O):
-    for fmt, group in ((0, 32), (1, 64), (2, 32)):
+    for fmt, group in ((0, 32), (1, 64), (2, 32), (3, 32)):
         N, K, M = 6, 64, 2
         codes, s, z, x = _rand_inputs(300 + fmt, fmt, N, K, M, group)
         y = O.qgemm_ref(x, pack_literal(codes, BITS[fmt]), s, z, M, N, K, group, fmt)
@@ -204,7 +223,7 @@ def pin_exact_rational(O):
 
 def pin_dequant_exact(O):
     # the fp32 dequantized weight is exact, and its fp16 rounding is nearest-even
-    for fmt, group in ((0, 32), (1, 64), (2, 32)):
+    for fmt, group in ((0, 32), (1, 64), (2, 32), (3, 32)):
         N, K = 8, 128
         codes, s, z, _ = _rand_inputs(400 + fmt, fmt, N, K, 1, group)
         words = pack_literal(codes, BITS[fmt])
@@ -213,7 +232,7 @@ def pin_dequant_exact(O):
         assert w32.dtype == np.float32 and w16.dtype == np.float16
         for n in range(N):
             for k in range(K):
-                zz = Fraction(8) if fmt == 2 else Fraction(float(z[n, k // group]))
+                zz = Fraction(ZIMPL[fmt]) if fmt in ZIMPL else Fraction(float(z[n, k // group]))
                 e = Fraction(float(s[n, k // group])) * (int(codes[n, k]) - zz)
                 assert Fraction(float(w32[n, k])) == e, (fmt, n, k)
                 assert float(w16[n, k]) == half_rne(float(e)), (fmt, n, k)

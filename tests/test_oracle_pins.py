@@ -15,7 +15,7 @@ def test_pin(pin):
 
 
 @settings(max_examples=60, deadline=None)
-@given(fmt=st.sampled_from([0, 1, 2]), n=st.integers(1, 5), kw=st.integers(1, 6),
+@given(fmt=st.sampled_from([0, 1, 2, 3]), n=st.integers(1, 5), kw=st.integers(1, 6),
        seed=st.integers(0, 2**31 - 1))
 def test_word_roundtrip(fmt, n, kw, seed):
     rng = np.random.default_rng(seed)
@@ -28,7 +28,7 @@ def test_word_roundtrip(fmt, n, kw, seed):
 
 
 @settings(max_examples=40, deadline=None)
-@given(fmt=st.sampled_from([0, 1, 2]), n=st.integers(1, 4), kw=st.integers(1, 4),
+@given(fmt=st.sampled_from([0, 1, 2, 3]), n=st.integers(1, 4), kw=st.integers(1, 4),
        seed=st.integers(0, 2**31 - 1))
 def test_code_roundtrip(fmt, n, kw, seed):
     rng = np.random.default_rng(seed)

@@ -48,6 +48,19 @@ def _deq_q40_offset7(words, scales, zeros, N, K, group, fmt):
     return _orig_deq(words, scales, zeros, N, K, group, fmt)
 
 
+def _deq_q80_offset127(words, scales, zeros, N, K, group, fmt):
+    if fmt == qref.Q8_0:
+        q = _orig_unpack(words, N, K, fmt).astype(np.float32)
+        s = np.asarray(scales, np.float16).reshape(N, K // group).astype(np.float32)
+        return s[:, np.arange(K) // group] * (q - 127.0)
+    return _orig_deq(words, scales, zeros, N, K, group, fmt)
+
+
+def _unpack_q80_low7(words, N, K, fmt):
+    c = _orig_unpack(words, N, K, fmt)
+    return c & 0x7F if fmt == qref.Q8_0 else c   # a 7-bit mask drops the top bit
+
+
 def _deq_group_shift(words, scales, zeros, N, K, group, fmt):
     q = _orig_unpack(words, N, K, fmt).astype(np.float32)
     s, z = qref._group_params(scales, zeros, N, K, group, fmt)
@@ -74,6 +87,8 @@ MUTANTS = {
     "group_index_mod": [("dequant_f32", _deq_group_mod)],
     "group_index_shift": [("dequant_f32", _deq_group_shift)],
     "q4_0_offset_7": [("dequant_f32", _deq_q40_offset7)],
+    "q8_0_offset_127": [("dequant_f32", _deq_q80_offset127)],
+    "q8_0_seven_bit_mask": [("unpack_codes", _unpack_q80_low7)],
     "transposed_operand": [("qgemm_ref", _gemm_transposed)],
     "fp16_accumulation": [("qgemm_ref", _gemm_fp16_accumulate)],
 }

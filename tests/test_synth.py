@@ -19,6 +19,35 @@ def test_q4_0_worked_block():
     assert np.all(u[0, 4:] == 8)
 
 
+def test_q8_0_worked_block():
+    # block [0.5, -1.27, 0.004, 1.0] (padded with zeros to 32): max |w| = 1.27,
+    # d = 0.01 (fp16 0.010002136...), codes rint(w / d) = [50, -127, 0, 100]
+    w = np.zeros((1, 32), np.float32)
+    w[0, :4] = [0.5, -1.27, 0.004, 1.0]
+    u, s = synth.quantize_q8_0(w)
+    assert float(s[0, 0]) == float(np.float16(0.01))
+    assert list(u[0, :4].astype(int) - 128) == [50, -127, 0, 100]
+    assert np.all(u[0, 4:] == 128)
+    z, sz = synth.quantize_q8_0(np.zeros((2, 64), np.float32))
+    assert np.all(z == 128) and np.all(sz == 0)
+
+
+def test_q8_0_integer_operands_round_trip():
+    # a block that already is an fp16 scale times integers in [-127, 127] with
+    # one of magnitude 127 comes back exactly through quantizer and oracle
+    rng = np.random.default_rng(77)
+    N, K = 16, 256
+    q = rng.integers(-127, 128, size=(N, K // 32, 32))
+    q[:, :, 5] = np.where(rng.integers(0, 2, size=(N, K // 32)) == 1, 127, -127)
+    d = rng.uniform(1e-4, 0.1, size=(N, K // 32)).astype(np.float16).astype(np.float32)
+    w = (q * d[:, :, None]).astype(np.float32).reshape(N, K)
+    c = synth.quantize(w, synth.Q8_0, 32)
+    assert np.array_equal(c.scales.astype(np.float32), d)
+    assert np.array_equal(c.codes.astype(int) - 128, q.reshape(N, K))
+    back = oracle.dequant_f32(c.words, c.scales, None, N, K, 32, oracle.Q8_0)
+    assert np.array_equal(back, w)
+
+
 @pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (2, 64), (2, 32)])
 def test_asym_quantizer_bounds(bits, group):
     rng = np.random.default_rng(bits * 1000 + group)
@@ -41,7 +70,7 @@ def test_asym_quantizer_bounds(bits, group):
     assert lo_code.max() <= 1 and hi_code.min() >= qmax - 1
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_generator_words_match_oracle_unpack(fmt):
     c = synth.random_codes_case(9, fmt, 32 if fmt != 1 else 64, 48, 512, 2)
     assert np.array_equal(oracle.unpack_codes(c.words, c.N, c.K, fmt), c.codes)
