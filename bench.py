@@ -95,10 +95,13 @@ class Leg:
         return ms / steps
 
 
+FORMAT_NAMES = ("int4_asym", "int2_asym", "q4_0", "q8_0")
+
+
 def leg_result(name, leg, ms, M):
     c = leg.case
     flops = 2.0 * M * c.N * c.K
-    r = dict(leg=name, M=M, N=c.N, K=c.K, format=["int4_asym", "int2_asym", "q4_0"][c.fmt],
+    r = dict(leg=name, M=M, N=c.N, K=c.K, format=FORMAT_NAMES[c.fmt],
              group=c.group, us_per_call=round(ms * 1e3, 3),
              weight_GBps=round(leg.wbytes / (ms * 1e-3) / 1e9, 1),
              TFLOPs=round(flops / (ms * 1e-3) / 1e12, 2), weight_copies=leg.copies)
@@ -302,7 +305,7 @@ def main():
     secondary.append(leg_result("decode_int4_g128_M8", leg8, leg8.time(400, 40), 8))
     del leg8
     for name, M in (("prefill_int4_g128", 128), ("int2_g64", 1), ("int2_g64", 128),
-                    ("q4_0_b32", 1), ("q4_0_b32", 128)):
+                    ("q4_0_b32", 1), ("q4_0_b32", 128), ("q8_0_b32", 1), ("q8_0_b32", 128)):
         c = synth.workload(name)
         leg = Leg(qgm, torch, c, M)
         steps = 400 if M == 1 else 200

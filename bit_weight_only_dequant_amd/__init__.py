@@ -17,7 +17,8 @@ import numpy as np
 INT4_ASYM = 0
 INT2_ASYM = 1
 Q4_0 = 2
-BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4}
+Q8_0 = 3
+BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4, Q8_0: 8}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemm.so")

@@ -13,7 +13,7 @@
 namespace qg {
 
 int check_format_group(int fmt, int group) {
-  if (fmt == QG_Q4_0) return group == 32 ? QG_OK : QG_E_ARG;
+  if (fmt == QG_Q4_0 || fmt == QG_Q8_0) return group == 32 ? QG_OK : QG_E_ARG;
   if (fmt == QG_INT4_ASYM || fmt == QG_INT2_ASYM)
     return (group == 32 || group == 64 || group == 128) ? QG_OK : QG_E_ARG;
   return QG_E_ARG;
@@ -77,11 +77,12 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   p.tiles_n = (int)ceil_div(N, GEMM_TN);
   p.tiles_m = (int)ceil_div(M, GEMM_TM);
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-  // at most GEMM_TPW word tiles per wave and GEMM_GCAP groups per workgroup;
+  // at most gemm_tpw(fmt) word tiles per wave and GEMM_GCAP groups per workgroup;
   // split K across workgroups only when the tiles leave most compute units
   // idle, since a split writes fp32 partials and costs a second (reduce) launch
   const int nw = GEMM_THREADS / 64;
-  const int s_tiles = (int)ceil_div(p.wordtiles, nw * GEMM_TPW);
+  const int tpw = gemm_tpw(fmt);
+  const int s_tiles = (int)ceil_div(p.wordtiles, nw * tpw);
   const int s_groups = (int)ceil_div((int64_t)p.wordtiles * kt_width / group, GEMM_GCAP);
   const int s_min = std::max(s_tiles, s_groups);
   int s = tiles >= (GEMM_TARGET_WG * 5) / 8 ? 1 : (int)ceil_div(GEMM_TARGET_WG, tiles);
@@ -89,7 +90,7 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   s = std::min(std::max(s, s_min), p.wordtiles);
   p.tps = (int)ceil_div(p.wordtiles, s);
   p.splits = (int)ceil_div(p.wordtiles, p.tps);
-  if (p.tps > nw * GEMM_TPW || (int64_t)p.tps * kt_width / group > GEMM_GCAP) {  // cannot happen: s >= s_min
+  if (p.tps > nw * tpw || (int64_t)p.tps * kt_width / group > GEMM_GCAP) {  // cannot happen: s >= s_min
     p.path = 0;
     return p;
   }
@@ -120,13 +121,13 @@ const char* qg_status_str(int status) {
 }
 
 size_t qg_packed_bytes(int64_t N, int64_t K, int fmt) {
-  if (fmt < 0 || fmt > 2 || N < 0 || K < 0) return 0;
+  if (!valid_format(fmt) || N < 0 || K < 0) return 0;
   if (K % cpw_of(fmt) != 0) return 0;
   return (size_t)n_rowblocks(N) * (size_t)n_wordtiles(K, fmt) * 64 * 4 * sizeof(uint32_t);
 }
 
 static int check_pack_args(const void* a, const void* b, int N, int K, int fmt) {
-  if (fmt < 0 || fmt > 2 || N < 0 || K < 0) return QG_E_ARG;
+  if (!valid_format(fmt) || N < 0 || K < 0) return QG_E_ARG;
   if (K % cpw_of(fmt) != 0) return QG_E_ARG;
   if ((int64_t)N * K > 0 && (!a || !b)) return QG_E_ARG;
   return QG_OK;

@@ -20,9 +20,13 @@ constexpr int GEMM_THREADS = 512;        // 8 waves; they split the workgroup's 
 constexpr int GEMM_TM = 64;              // workgroup tile rows (M)
 constexpr int GEMM_TN = 64;              // workgroup tile columns (N)
 constexpr int GEMM_TPW = 2;              // word tiles per wave (K per workgroup <= 16 tiles)
+constexpr int GEMM_TPW_Q8 = 4;           // q8_0: a tile is 64 wide, so 4 per wave (256 of K)
 constexpr int GEMM_DEPTH = 1;            // x/code stages in flight per wave
 constexpr int GEMM_GCAP = 64;            // quantization groups per workgroup, at most
 constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
+
+// word tiles one GEMM wave covers, at most
+inline constexpr int gemm_tpw(int fmt) { return fmt == Q8_0 ? GEMM_TPW_Q8 : GEMM_TPW; }
 
 struct Plan {
   int path = 0;        // 0 none (no-op / zero fill), 1 GEMV, 2 GEMM

@@ -5,8 +5,8 @@
 // ("Dequantizing Runtimes", "Quantized Matrix Multiplication"): weights are
 // brought back to full precision inside the compute pass, never written out.
 // Formats: INT4 / INT2 with per-group fp16 scale and zero point (TinyLoop
-// README, "Status" and "Current Runtime Snapshot"), q4_0 (torchnative guide
-// "Inference with real transformers", "Quantise while loading").
+// README, "Status" and "Current Runtime Snapshot"), q4_0 and q8_0 (torchnative
+// guide "Inference with real transformers", "Quantise while loading").
 //
 // Kernels
 //   qpack / qunpack      one-time permutation of codes into the tile order of
@@ -69,6 +69,13 @@ __device__ __forceinline__ h2 splat(f16 v) { return h2{v, v}; }
 // Zero-point constants for one group: zc[i] = -(1024 * 2^-(b*i) + z)
 struct ZC4 { h2 c0, c1; };          // 4-bit: i = 0 (x1), 1 (x16)
 struct ZC2 { h2 c0, c1, c2, c3; };  // 2-bit: x1, x4, x16, x64
+struct ZC8 { h2 c0; };              // 8-bit: a byte fills the low 8 mantissa bits
+
+__device__ __forceinline__ ZC8 make_zc8(f16 z) {
+  ZC8 r;
+  r.c0 = splat((f16)-1024.0f - z);
+  return r;
+}
 
 __device__ __forceinline__ ZC4 make_zc4(f16 z) {
   ZC4 r;
@@ -113,10 +120,45 @@ __device__ __forceinline__ void qmz_int2_half(uint32_t w, int half, const ZC2& z
   out[3] = as_h2(and_or(v, 0x00C000C0u, magic)) * splat((f16)0.015625f) + zc.c3;
 }
 
+// 8-bit packed word (4 codes) -> 2 pairs (c_0 - z, c_1 - z), (c_2 - z, c_3 - z):
+// the word holds codes 0, 2, 1, 3 in bytes 0..3, so masking bytes 0 and 2
+// gives the first pair and, after a shift by 8, bytes 1 and 3 the second
+// (1024 + u is exact in fp16 for u <= 255)
+__device__ __forceinline__ void qmz_int8(uint32_t w, const ZC8& zc, h2 out[2]) {
+  const uint32_t magic = 0x64006400u;
+  out[0] = as_h2(and_or(w, 0x00FF00FFu, magic)) + zc.c0;
+  out[1] = as_h2(and_or(w >> 8, 0x00FF00FFu, magic)) + zc.c0;
+}
+
+// Per format: bits, codes per word, codes per 16-byte lane chunk (LS), K per
+// word tile (KT), codes per scale lookup (SW: a lane's chunk in runs of at
+// most 32, the smallest group), runs per chunk (NSEG), and the implicit zero
+// point of the block formats as fp16 bits (8.0 and 128.0).
 template <int FMT> struct Fmt;
-template <> struct Fmt<INT4_ASYM> { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128; static constexpr bool HAS_Z = true; };
-template <> struct Fmt<INT2_ASYM> { static constexpr int BITS = 2, CPW = 16, LS = 64, KT = 256; static constexpr bool HAS_Z = true; };
-template <> struct Fmt<Q4_0>      { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128; static constexpr bool HAS_Z = false; };
+template <> struct Fmt<INT4_ASYM> { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = true;  static constexpr uint32_t ZBITS = 0; };
+template <> struct Fmt<INT2_ASYM> { static constexpr int BITS = 2, CPW = 16, LS = 64, KT = 256, SW = 32, NSEG = 2; static constexpr bool HAS_Z = true;  static constexpr uint32_t ZBITS = 0; };
+template <> struct Fmt<Q4_0>      { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = false; static constexpr uint32_t ZBITS = 0x4800; };
+template <> struct Fmt<Q8_0>      { static constexpr int BITS = 8, CPW = 4,  LS = 16, KT = 64,  SW = 16, NSEG = 1; static constexpr bool HAS_Z = false; static constexpr uint32_t ZBITS = 0x5800; };
+
+// Exact (q - z) pairs, in k order, of run p (SW codes) of a lane's chunk c
+template <int FMT>
+__device__ __forceinline__ void run_qmz(const u4& c, int p, f16 z, h2* q) {
+  if constexpr (FMT == INT2_ASYM) {
+    const ZC2 zc = make_zc2(z);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) qmz_int2_half(c[2 * p + t], h, zc, q + 8 * t + 4 * h);
+  } else if constexpr (FMT == Q8_0) {
+    const ZC8 zc = make_zc8(z);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qmz_int8(c[t], zc, q + 2 * t);
+  } else {
+    const ZC4 zc = make_zc4(z);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qmz_int4(c[t], zc, q + 4 * t);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // repack kernels
@@ -162,8 +204,8 @@ __global__ void unpack_codes_kernel(const uint32_t* __restrict__ packed, uint8_t
 
 // Dequantized weights written out (fp16 [N, K]), with the GEMM's register
 // dequant: one wave per (row block, word tile), so each wave reads 1 KiB of
-// codes contiguously; lane (g, r) turns its 16-byte chunk into 32 (INT4) or 64
-// (INT2) weights of row 16*rb + r and stores them contiguously.
+// codes contiguously; lane (g, r) turns its 16-byte chunk into 32 (INT4), 64
+// (INT2) or 16 (q8_0) weights of row 16*rb + r and stores them contiguously.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ packed,
                                                       const f16* __restrict__ scales,
@@ -181,27 +223,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   if (n >= N) return;
   const int ng = K / group;
 #pragma unroll
-  for (int p = 0; p < F::LS / 32; ++p) {
-    const int k = T * F::KT + g * F::LS + p * 32;  // first of this lane's 32 codes
+  for (int p = 0; p < F::NSEG; ++p) {
+    const int k = T * F::KT + g * F::LS + p * F::SW;  // first of this lane's SW codes
     if (k >= K) break;
     const int grp = k / group;
     const h2 s2 = splat(scales[n * ng + grp]);
-    const f16 z = F::HAS_Z ? zeros[n * ng + grp] : (f16)8.0f;
-    h2 q[16];
-    if constexpr (FMT == INT2_ASYM) {
-      const ZC2 zc = make_zc2(z);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) qmz_int2_half(c[2 * p + t], h, zc, q + 8 * t + 4 * h);
-    } else {
-      const ZC4 zc = make_zc4(z);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) qmz_int4(c[t], zc, q + 4 * t);
-    }
+    const f16 z = F::HAS_Z ? zeros[n * ng + grp] : __builtin_bit_cast(f16, (uint16_t)F::ZBITS);
+    h2 q[F::SW / 2];
+    run_qmz<FMT>(c, p, z, q);
     h8* dst = reinterpret_cast<h8*>(w + n * K + k);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < F::SW / 8; ++v) {
       const h2 a0 = q[4 * v] * s2, a1 = q[4 * v + 1] * s2, a2 = q[4 * v + 2] * s2, a3 = q[4 * v + 3] * s2;
       dst[v] = h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
     }
@@ -247,7 +279,7 @@ template <int FMT, int MMAX, int TPW, int NW> constexpr size_t gemv_lds_bytes() 
 // another until the final sum.  Per lane and tile: one 16-byte code load,
 // masks into fp16 pairs holding exact (q - z) (one v_and_or_b32 plus one
 // packed add or fma per pair), v_dot2_f32_f16 against fp16 x pairs, the fp32
-// scale once per 32 (INT4) or 64 (INT2) codes.
+// scale once per run of SW codes (32; 16 for q8_0).
 template <int FMT, int MMAX, int TPW, int NW>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   using F = Fmt<FMT>;
@@ -292,7 +324,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
     const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
     sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
     if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
-    else zraw[j] = 0x4800;  // fp16 8.0
+    else zraw[j] = F::ZBITS;  // the implicit zero point
   }
   const int om = tid >> 4, orow = tid & 15;
   float res = 0.0f;
@@ -339,10 +371,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // 3. Dot products, tile by tile and 32 codes at a time (a lane holds 32
-  //    INT4 or 64 INT2 codes, and a group may be 32 wide): exact (q - z)
-  //    pairs against fp16 x pairs (v_dot2_f32_f16, fp32 accumulation), fp32
-  //    scale once per 32 codes.
+  // 3. Dot products, tile by tile and one run of SW codes at a time (a lane
+  //    holds 32 INT4, 64 INT2 or 16 q8_0 codes, and a group may be 32 wide):
+  //    exact (q - z) pairs against fp16 x pairs (v_dot2_f32_f16, fp32
+  //    accumulation), fp32 scale once per run.
   float acc[MMAX];
 #pragma unroll
   for (int m = 0; m < MMAX; ++m) acc[m] = 0.0f;
@@ -350,28 +382,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   for (int i = 0; i < TPW; ++i) {
     if (i < nt) {
 #pragma unroll
-      for (int p = 0; p < F::LS / 32; ++p) {
-        const uint32_t szv = sz[r * GWMAX + ((i * F::KT + g * F::LS + p * 32) >> lg)];
+      for (int p = 0; p < F::NSEG; ++p) {
+        const uint32_t szv = sz[r * GWMAX + ((i * F::KT + g * F::LS + p * F::SW) >> lg)];
         const float sf = (float)__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu));
         const f16 z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
-        h2 q[16];
-        if constexpr (FMT == INT2_ASYM) {
-          const ZC2 zc = make_zc2(z);
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) qmz_int2_half(code[i][2 * p + t], h, zc, q + 8 * t + 4 * h);
-        } else {
-          const ZC4 zc = make_zc4(z);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) qmz_int4(code[i][t], zc, q + 4 * t);
-        }
+        h2 q[F::SW / 2];
+        run_qmz<FMT>(code[i], p, z, q);
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) {
-          const h8* xp = reinterpret_cast<const h8*>(xs + m * KW + i * F::KT + g * F::LS + p * 32);
+          const h8* xp = reinterpret_cast<const h8*>(xs + m * KW + i * F::KT + g * F::LS + p * F::SW);
           float A0 = 0.0f, A1 = 0.0f;  // two chains for issue overlap
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < F::SW / 8; ++c) {
             const h8 xv = xp[c];
             float t0 = (c & 1) ? A1 : A0;
             t0 = __builtin_amdgcn_fdot2(q[4 * c + 0], h2{xv[0], xv[1]}, t0, false);
@@ -420,9 +442,9 @@ template <int FMT, int MROWS, int TPW> constexpr size_t gemv_mfma_lds_bytes() {
 // its own x rows and (scale, zero) pairs), but the products run as
 // v_mfma_f32_16x16x32_f16.  In that operand layout lane l = 16g + r supplies
 // column r and k-slots 8g..8g+7 of B -- exactly the packed chunk of row r and
-// lane group g -- so once a word is dequantized to fp16 s*(q - z) (13 VALU per
-// 8 codes, the GEMM's dequant, whatever M is) it is one MFMA step; A is row r
-// of x (zero for r >= MROWS) at the same k.  The 16 x 16 accumulator holds
+// lane group g -- so once 8 codes are dequantized to fp16 s*(q - z) (13 VALU
+// for 4-bit codes, the GEMM's dequant, whatever M is) they are one MFMA step;
+// A is row r of x (zero for r >= MROWS) at the same k.  The 16 x 16 accumulator holds
 // y[4g + i][16 rb + r] in lane 16g + r, element i.
 template <int FMT, int MROWS, int TPW>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
@@ -469,7 +491,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
     const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
     sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
     if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
-    else zraw[j] = 0x4800;  // fp16 8.0
+    else zraw[j] = F::ZBITS;  // the implicit zero point
   }
   float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (a.resid && a.splits == 1 && wave == 0) {
@@ -514,36 +536,26 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // 3. per 32-code segment: dequantize four words to fp16 s*(q - z), one MFMA each
+  // 3. per run of SW codes: dequantize to fp16 s*(q - z), one MFMA per 8 codes
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
   const bool arow = r < MROWS;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     if (i < nt) {
 #pragma unroll
-      for (int p = 0; p < F::LS / 32; ++p) {
-        const int kl = i * F::KT + g * F::LS + p * 32;  // this lane's segment inside the wave's range
+      for (int p = 0; p < F::NSEG; ++p) {
+        const int kl = i * F::KT + g * F::LS + p * F::SW;  // this lane's run inside the wave's range
         const uint32_t szv = sz[r * GWMAX + (kl >> lg)];
         const h2 s2 = splat(__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu)));
         const f16 z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
-        h8 av[4];
+        h8 av[F::SW / 8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < F::SW / 8; ++t)
           av[t] = arow ? *reinterpret_cast<const h8*>(xs + (arow ? r : 0) * KWP + kl + 8 * t) : h8{};
-        h2 q[16];
-        if constexpr (FMT == INT2_ASYM) {
-          const ZC2 zc = make_zc2(z);
+        h2 q[F::SW / 2];
+        run_qmz<FMT>(code[i], p, z, q);
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) qmz_int2_half(code[i][2 * p + t], h, zc, q + 8 * t + 4 * h);
-        } else {
-          const ZC4 zc = make_zc4(z);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) qmz_int4(code[i][t], zc, q + 4 * t);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < F::SW / 8; ++t) {
           const h2 w0 = q[4 * t] * s2, w1 = q[4 * t + 1] * s2, w2 = q[4 * t + 2] * s2, w3 = q[4 * t + 3] * s2;
           const h8 bf = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t], bf, acc, 0, 0, 0);
@@ -617,17 +629,23 @@ __device__ __forceinline__ void wait_lgkm0() {
 // output layout of v_mfma_f32_32x32x16_f16 is D[8*(i/4) + 4*(l/32) + i%4][l%32].
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
-// Stage geometry: a stage is (word tile t, chunk h, 32-code segment j); for
-// lane half g2 it covers the 32 k at seg_k(g2, h, j) and feeds four MFMA
-// steps of 8 k each.  x part: 64 rows x 2 pieces of 32 k (8 KiB); code part:
-// chunk h of both 32-column blocks (2 KiB).
+// Stage geometry.  A stage feeds four MFMA steps of 8 k per lane half g2
+// (32 k per half).  4- and 2-bit codes (WIDE: a lane's chunk holds 32 or more
+// codes): a stage is (word tile t, chunk h, 32-code run j) and lane half g2
+// takes its 32 k from lane group g2 + 2h, run j, at seg_k(g2, h, j).  8-bit
+// codes: a stage is a whole word tile and lane half g2 takes 16 k from each of
+// lane groups g2 (steps 0, 1) and g2 + 2 (steps 2, 3), i.e. chunk h = step / 2.
+// x part: 64 rows x 2 pieces (one per lane half) x 4 sub-chunks of 8 k
+// (8 KiB); code part: CH chunks of both 32-column blocks (2 KiB each).
 template <int FMT> struct GemmStage {
   static constexpr int KT = Fmt<FMT>::KT;
-  static constexpr int SEG = Fmt<FMT>::LS / 32;    // 32-code segments per 16-byte chunk
-  static constexpr int STAGES = 2 * SEG;           // stages per word tile
-  static constexpr int XB = GEMM_TM * 64 * 2;       // x bytes per stage
-  static constexpr int SB = XB + 2048;              // + code chunks of the two column blocks
-  static constexpr int DMA = XB / 1024 + 2;         // direct loads per lane per stage (10)
+  static constexpr bool WIDE = Fmt<FMT>::LS >= 32;
+  static constexpr int SEG = WIDE ? Fmt<FMT>::LS / 32 : 1;  // 32-code runs per chunk
+  static constexpr int CH = WIDE ? 1 : 2;                  // chunks per stage
+  static constexpr int STAGES = WIDE ? 2 * SEG : 1;        // stages per word tile
+  static constexpr int XB = GEMM_TM * 64 * 2;              // x bytes per stage
+  static constexpr int SB = XB + CH * 2048;                // + code chunks of the two column blocks
+  static constexpr int DMA = XB / 1024 + 2 * CH;           // direct loads per lane per stage (10, 12)
 };
 
 // Prefill GEMM (M > 16).  Workgroup tile 64 (M) x 64 (N) over the workgroup's
@@ -694,7 +712,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       const int64_t off = ok ? ((int64_t)(n0 + ec) * ng + gw0 + eg) : 0;
       sraw[j] = reinterpret_cast<const uint16_t*>(a.scales)[off];
       if constexpr (F::HAS_Z) zraw[j] = reinterpret_cast<const uint16_t*>(a.zeros)[off];
-      else zraw[j] = 0x4800;  // fp16 8.0
+      else zraw[j] = F::ZBITS;  // the implicit zero point
     }
   }
 
@@ -704,8 +722,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   for (int q = 0; q < 4; ++q) {
     const int m = q * 16 + (lane >> 2);
     const int u = (lane & 3) ^ ((m >> 2) & 3);
-    voff[q] = (uint32_t)((min(m0 + m, a.M - 1) * a.ldx + u * 8) * 2);   // rows past M: any finite data
+    const int ucol = S::WIDE ? u * 8 : 0;              // 8-bit codes: added per stage below
+    voff[q] = (uint32_t)((min(m0 + m, a.M - 1) * a.ldx + ucol) * 2);   // rows past M: any finite data
   }
+  // 8-bit codes: sub-chunk u of a piece sits 8 (u & 1) + 32 (u >> 1) past the
+  // piece's first k (the second half from lane group g2 + 2); u is the same
+  // for every q above, since q moves m by multiples of 16
+  const int usub = (lane & 3) ^ ((lane >> 4) & 3);
+  const int subk = 8 * (usub & 1) + 32 * (usub >> 1);
   const char* cb[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -718,8 +742,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     uint8_t* dst = wbuf + (st % DEPTH) * S::SB;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int kp = kt * F::KT + seg_k(p, h, j);
-      const char* src = reinterpret_cast<const char*>(a.x) + (kp < a.K ? kp : 0) * 2;  // past K: scale 0
+      const char* src;
+      if constexpr (S::WIDE) {
+        const int kp = kt * F::KT + seg_k(p, h, j);
+        src = reinterpret_cast<const char*>(a.x) + (kp < a.K ? kp : 0) * 2;  // past K: scale 0
+      } else {
+        const int kk = kt * F::KT + 16 * p + subk;                          // this lane's sub-chunk
+        src = reinterpret_cast<const char*>(a.x) + (kk < a.K ? kk : 0) * 2;
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         __builtin_amdgcn_global_load_lds(
@@ -727,10 +757,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
             (void __attribute__((address_space(3)))*)(dst + (p * 4 + q) * 1024), 16, 0, 0);
     }
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(cb[nb] + (int64_t)kt * 1024 + h * 512),
-          (void __attribute__((address_space(3)))*)(dst + S::XB + nb * 1024), 16, 0, 0);
+    for (int c = 0; c < S::CH; ++c)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(cb[nb] + (int64_t)kt * 1024 + (h + c) * 512),
+            (void __attribute__((address_space(3)))*)(dst + S::XB + (c * 2 + nb) * 1024), 16, 0, 0);
   };
 
   f16v acc[2][2];
@@ -748,43 +780,59 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   };
 
   // 3. one stage: every LDS operand first, then B operands (13 VALU per
-  //    word) interleaved with the 16 MFMAs
+  //    4-bit word, 14 per two 8-bit words) interleaved with the 16 MFMAs
   auto compute_stage = [&](int st) {
     const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
     const int kt = wt0 + t;
     const uint8_t* sb = wbuf + (st % DEPTH) * S::SB;
-    const int kseg = kt * F::KT + seg_k(g2, h, j);
-    const bool live = kseg < a.K;                       // segment past K: scale 0
-    const int gi = min(max((kseg >> lg) - gw0, 0), gwn - 1);
-    uint32_t szv[2];
-    u4 bt[2];
+    uint32_t szv[S::CH][2];
+    u4 bt[S::CH][2];
+    bool live[S::CH];
     h8 af[4][2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      bt[nb] = *reinterpret_cast<const u4*>(sb + S::XB + nb * 1024 + lane * 16);
-      szv[nb] = szl[(nb * 32 + (lane & 31)) * GEMM_GCAP + gi];
+    for (int c = 0; c < S::CH; ++c) {
+      // first k of this lane's codes in chunk c
+      const int kseg = kt * F::KT + (S::WIDE ? seg_k(g2, h, j) : 16 * (g2 + 2 * c));
+      live[c] = kseg < a.K;                             // codes past K: scale 0
+      const int gi = min(max((kseg >> lg) - gw0, 0), gwn - 1);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        bt[c][nb] = *reinterpret_cast<const u4*>(sb + S::XB + (c * 2 + nb) * 1024 + lane * 16);
+        szv[c][nb] = szl[(nb * 32 + (lane & 31)) * GEMM_GCAP + gi];
+      }
     }
 #pragma unroll
     for (int step = 0; step < 4; ++step)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) af[step][mb] = *reinterpret_cast<const h8*>(sb + a_off(mb, step));
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the math
-    h2 s2[2];
-    f16 z[2];
+    h2 s2[S::CH][2];
+    f16 z[S::CH][2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      s2[nb] = splat(live ? __builtin_bit_cast(f16, (uint16_t)(szv[nb] & 0xffffu)) : (f16)0.0f);
-      z[nb] = __builtin_bit_cast(f16, (uint16_t)(szv[nb] >> 16));
-    }
+    for (int c = 0; c < S::CH; ++c)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        s2[c][nb] = splat(live[c] ? __builtin_bit_cast(f16, (uint16_t)(szv[c][nb] & 0xffffu)) : (f16)0.0f);
+        z[c][nb] = __builtin_bit_cast(f16, (uint16_t)(szv[c][nb] >> 16));
+      }
     h8 bf[4][2];
 #pragma unroll
     for (int step = 0; step < 4; ++step)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
+        const int c = S::WIDE ? 0 : step >> 1;
         h2 q[4];
-        if constexpr (FMT == INT2_ASYM) qmz_int2_half(bt[nb][2 * j + (step >> 1)], step & 1, make_zc2(z[nb]), q);
-        else qmz_int4(bt[nb][step], make_zc4(z[nb]), q);
-        const h2 w0 = q[0] * s2[nb], w1 = q[1] * s2[nb], w2 = q[2] * s2[nb], w3 = q[3] * s2[nb];
+        if constexpr (FMT == INT2_ASYM) {
+          qmz_int2_half(bt[0][nb][2 * j + (step >> 1)], step & 1, make_zc2(z[0][nb]), q);
+        } else if constexpr (FMT == Q8_0) {
+          const ZC8 zc = make_zc8(z[c][nb]);
+          qmz_int8(bt[c][nb][2 * (step & 1)], zc, q);
+          qmz_int8(bt[c][nb][2 * (step & 1) + 1], zc, q + 2);
+        } else {
+          qmz_int4(bt[0][nb][step], make_zc4(z[0][nb]), q);
+        }
+        const h2 sc = s2[c][nb];
+        const h2 w0 = q[0] * sc, w1 = q[1] * sc, w2 = q[2] * sc, w3 = q[3] * sc;
         bf[step][nb] = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
       }
 #pragma unroll
@@ -1068,7 +1116,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
     if (check_align(y) != QG_OK || (resid && check_align(resid) != QG_OK)) return QG_E_ALIGN;
     if (K > 0) {
       if (!x || !packed || !scales) return QG_E_ARG;
-      if ((fmt == QG_Q4_0) != (zeros == nullptr)) return QG_E_ARG;
+      if (symmetric_format(fmt) != (zeros == nullptr)) return QG_E_ARG;
       if (check_ld(ldx, K) != QG_OK) return QG_E_ARG;
       if (ldx % 8 != 0) return QG_E_ALIGN;
       if (check_align(x) != QG_OK || check_align(packed) != QG_OK || check_align(scales) != QG_OK ||
@@ -1118,6 +1166,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
     switch (fmt) {
       case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, p.tps, s); break;
       case QG_INT2_ASYM: launched = launch_gemv_f<INT2_ASYM>(a, p.mmax, p.tps, s); break;
+      case QG_Q8_0: launched = launch_gemv_f<Q8_0>(a, p.mmax, p.tps, s); break;
       default: launched = launch_gemv_f<Q4_0>(a, p.mmax, p.tps, s); break;
     }
     if (!launched) return QG_E_UNSUPPORTED;
@@ -1148,6 +1197,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
   switch (fmt) {
     case QG_INT4_ASYM: hipLaunchKernelGGL((gemm_kernel<INT4_ASYM, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
     case QG_INT2_ASYM: hipLaunchKernelGGL((gemm_kernel<INT2_ASYM, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
+    case QG_Q8_0: hipLaunchKernelGGL((gemm_kernel<Q8_0, NW, GEMM_TPW_Q8, GEMM_DEPTH>), grid, block, 0, s, a); break;
     default: hipLaunchKernelGGL((gemm_kernel<Q4_0, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
   }
   if (p.splits > 1) {
@@ -1159,7 +1209,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
 }
 
 static int check_pack(const void* a, const void* b, int N, int K, int fmt) {
-  if (fmt < 0 || fmt > 2 || N < 0 || K < 0) return QG_E_ARG;
+  if (!valid_format(fmt) || N < 0 || K < 0) return QG_E_ARG;
   if (K % cpw_of(fmt) != 0) return QG_E_ARG;
   if ((int64_t)N * K > 0) {
     if (!a || !b) return QG_E_ARG;
@@ -1228,7 +1278,7 @@ int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* z
   const int64_t total = (int64_t)N * (K / cpw_of(fmt));
   if (total > 0) {
     if (!packed || !scales || !w) return QG_E_ARG;
-    if ((fmt == QG_Q4_0) != (zeros == nullptr)) return QG_E_ARG;
+    if (symmetric_format(fmt) != (zeros == nullptr)) return QG_E_ARG;
     if (check_align(packed) != QG_OK || check_align(w) != QG_OK) return QG_E_ALIGN;
   }
   int dev = 0;
@@ -1246,6 +1296,7 @@ int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* z
   switch (fmt) {
     case QG_INT4_ASYM: hipLaunchKernelGGL(dequant_kernel<INT4_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
     case QG_INT2_ASYM: hipLaunchKernelGGL(dequant_kernel<INT2_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
+    case QG_Q8_0: hipLaunchKernelGGL(dequant_kernel<Q8_0>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
     default: hipLaunchKernelGGL(dequant_kernel<Q4_0>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
   }
   return launch_status();

@@ -13,9 +13,11 @@
  *     INT2 body weights of the TinyLoop README, "Current Runtime Snapshot");
  *   - QG_Q4_0: symmetric blocks of 32 with one fp16 scale and no zero point
  *     (q4_0 of the torchnative guide "Inference with real transformers",
- *     section "Quantise while loading"), codes stored offset-binary u = q + 8.
+ *     section "Quantise while loading"), codes stored offset-binary u = q + 8;
+ *   - QG_Q8_0: the 8-bit sibling of q4_0 named in the same section: blocks of
+ *     32, one fp16 scale, signed 8-bit codes stored offset-binary u = q + 128.
  * For every format  w[n,k] = s[n, k/group] * (q[n,k] - z[n, k/group])  with
- * z == 8 for q4_0, and  y[m,n] = sum_k x[m,k] * w[n,k].
+ * z == 8 for q4_0, z == 128 for q8_0, and  y[m,n] = sum_k x[m,k] * w[n,k].
  *
  * Conventions shared by every entry point
  *   - Pointers named "device" are device memory (hipMalloc or torch tensors on
@@ -23,7 +25,8 @@
  *     Outputs are caller-allocated and written in place.
  *   - fp16 buffers are passed as uint16_t (IEEE binary16 bit patterns).
  *   - Matrices are row-major.  W is [N, K]: groups run along K in one row n.
- *   - Canonical words: uint32 [N, K/cpw], cpw = 8 (INT4, q4_0) or 16 (INT2);
+ *   - Canonical words: uint32 [N, K/cpw], cpw = 8 (INT4, q4_0), 16 (INT2) or
+ *     4 (q8_0);
  *     code k of row n sits at bits [b*(k%cpw), b*(k%cpw)+b) of word k/cpw.
  *   - Scales (and zero points) are fp16 [N, K/group], canonical.  Zero points
  *     hold integers in [0, 2^b - 1]; other values give unspecified results.
@@ -32,7 +35,8 @@
  *     launched"; a kernel fault is reported by the caller's next sync.
  *   - Arguments are validated on the host before any HIP call.  On error the
  *     function returns a status and launches nothing; nothing aborts or prints.
- *   - Shapes: group in {32, 64, 128} for INT4/INT2, group == 32 for q4_0;
+ *   - Shapes: group in {32, 64, 128} for INT4/INT2, group == 32 for q4_0 and
+ *     q8_0;
  *     K % group == 0; M, N, K >= 0.  Any N and any M are accepted.
  *   - Device pointers to x, packed, scales, zeros, y and residual must be
  *     16-byte aligned; leading dimensions must be multiples of 8 elements.
@@ -54,7 +58,8 @@ extern "C" {
 typedef enum {
   QG_INT4_ASYM = 0,
   QG_INT2_ASYM = 1,
-  QG_Q4_0 = 2
+  QG_Q4_0 = 2,
+  QG_Q8_0 = 3
 } qg_format_t;
 
 typedef enum {
@@ -113,7 +118,7 @@ int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt)
  *   packed [device, in]  qpack output for W [N, K].
  *   scales [device, in]  fp16 [N, K/group].
  *   zeros  [device, in]  fp16 [N, K/group]; must be NULL for QG_Q4_0 and
- *                        non-NULL for the asymmetric formats.
+ *                        QG_Q8_0 and non-NULL for the asymmetric formats.
  *   y      [device, out] fp16 [M, N], row-major, leading dimension N.
  * M == 1 runs the decode GEMV (packed-fp16 dequant, fp32 dot products);
  * 2 <= M <= 16 the decode GEMV on 16 x 16 matrix-core blocks; M > 16 the
@@ -158,7 +163,7 @@ size_t qgemm_workspace_bytes(int M, int N, int K, int group, int fmt);
  * All four linears share one format and group.
  *   x        [device, in/out] fp16 [M, D]: x_0 on entry, x_L on return.
  *   packed4  host array of 4 device pointers (QKV, O, up, down), qpack output.
- *   scales4, zeros4  host arrays of 4 device pointers (zeros4 entries NULL for q4_0).
+ *   scales4, zeros4  host arrays of 4 device pointers (zeros4 entries NULL for q4_0 and q8_0).
  *   F        the MLP width (N of up, K of down).
  *   scratch  [device] fp16 buffer of at least M*(3D + D + F) elements.
  *   events   NULL, or a host array of L+1 hipEvent_t recorded on the stream

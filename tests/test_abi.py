@@ -51,12 +51,14 @@ def qgemm_status(x=A, packed=A, scales=A, zeros=A, M=1, N=16, K=128, group=32, f
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(fmt=3), E_ARG),
+    (dict(fmt=4), E_ARG),
     (dict(fmt=-1), E_ARG),
     (dict(group=48), E_ARG),
     (dict(group=256), E_ARG),
     (dict(fmt=2, zeros=None, group=64), E_ARG),      # q4_0 needs group 32
     (dict(fmt=2, zeros=A, group=32), E_ARG),         # q4_0 takes no zero points
+    (dict(fmt=3, zeros=None, group=128), E_ARG),     # q8_0 needs group 32
+    (dict(fmt=3, zeros=A, group=32), E_ARG),         # q8_0 takes no zero points
     (dict(fmt=0, zeros=None), E_ARG),                # asymmetric needs zero points
     (dict(K=100), E_ARG),                            # K % group
     (dict(M=-1), E_ARG),
@@ -103,7 +105,7 @@ def test_status_strings():
 @pytest.mark.parametrize("N,K,fmt,expect", [
     (16, 128, 0, 1024), (17, 128, 0, 2048), (16, 136, 0, 2048), (6144, 2048, 0, 6291456),
     (8192, 2048, 1, 4194304), (8192, 2048, 2, 8388608), (0, 128, 0, 0), (16, 100, 0, 0),
-    (16, 128, 5, 0)])
+    (16, 128, 5, 0), (8192, 2048, 3, 16777216), (16, 96, 3, 2048), (16, 98, 3, 0)])
 def test_packed_bytes(N, K, fmt, expect):
     assert qgm.packed_bytes(N, K, fmt) == expect
 
@@ -127,7 +129,7 @@ def decode_packed_by_formula(packed, N, K, fmt):
 
 
 @pytest.mark.parametrize("fmt,N,K", [(0, 16, 128), (0, 37, 96), (1, 20, 256), (1, 33, 160),
-                                     (2, 48, 64), (0, 5, 384)])
+                                     (2, 48, 64), (0, 5, 384), (3, 16, 64), (3, 37, 96), (3, 20, 160)])
 def test_host_qpack_layout_and_roundtrip(fmt, N, K):
     c = synth.random_codes_case(N * 7 + K + fmt, fmt, 32, N, K, 1)
     packed = qgm.qpack_host(c.words, N, K, fmt)
@@ -157,3 +159,7 @@ def test_plans_for_the_workloads():
     assert qgm.plan(17, 64, 128, 32, 0)["path"] == "gemm"
     assert qgm.workspace_bytes(1, 16, 128, 32, 0) == 0
     assert qgm.workspace_bytes(128, 2048, 8192, 128, 0) > 0   # split-K for small N
+    # q8_0: 64-wide word tiles, 4 per GEMM wave, so K = 2048 needs no split
+    q = qgm.plan(128, 8192, 2048, 32, 3)
+    assert q["path"] == "gemm" and q["splits"] == 1
+    assert qgm.plan(1, 6144, 2048, 32, 3)["path"] == "gemv"

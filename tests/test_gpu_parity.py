@@ -64,7 +64,8 @@ def _clean_env(monkeypatch):
 
 @pytest.mark.parametrize("fmt,group,N,K", [(0, 32, 256, 256), (0, 128, 6144, 2048), (1, 64, 8192, 2048),
                                            (2, 32, 8192, 2048), (0, 32, 37, 96), (1, 32, 50, 160),
-                                           (2, 32, 3, 32)])
+                                           (2, 32, 3, 32), (3, 32, 8192, 2048), (3, 32, 37, 96),
+                                           (3, 32, 5, 32)])
 def test_repack_and_codes_bit_exact(fmt, group, N, K):
     say(f"repack fmt={fmt} N={N} K={K}")
     c = synth.random_codes_case(N + K + fmt, fmt, group, N, K, 1)
@@ -79,7 +80,8 @@ def test_repack_and_codes_bit_exact(fmt, group, N, K):
 
 
 @pytest.mark.parametrize("fmt,group,N,K", [(0, 32, 256, 256), (0, 128, 512, 2048), (1, 64, 256, 2048),
-                                           (1, 32, 64, 512), (2, 32, 256, 2048), (0, 64, 40, 192)])
+                                           (1, 32, 64, 512), (2, 32, 256, 2048), (0, 64, 40, 192),
+                                           (3, 32, 256, 2048), (3, 32, 40, 96)])
 def test_dequant_bit_exact(fmt, group, N, K):
     say(f"dequant fmt={fmt} g={group} N={N} K={K}")
     c = synth.random_codes_case(7 * N + K + fmt, fmt, group, N, K, 1)
@@ -95,7 +97,8 @@ def test_dequant_bit_exact(fmt, group, N, K):
 # ----------------------------------------------------------------------------
 
 WL = [("tiny_int4_g32", 1), ("tiny_int4_g32", 4), ("decode_int4_g128", 1), ("decode_int4_g128", 8),
-      ("prefill_int4_g128", 128), ("int2_g64", 1), ("int2_g64", 128), ("q4_0_b32", 1), ("q4_0_b32", 128)]
+      ("prefill_int4_g128", 128), ("int2_g64", 1), ("int2_g64", 128), ("q4_0_b32", 1), ("q4_0_b32", 128),
+      ("q8_0_b32", 1), ("q8_0_b32", 8), ("q8_0_b32", 128)]
 
 _cases = {}
 
@@ -139,6 +142,10 @@ RAGGED = [
     (1, 32, 40, 160, 33), (1, 64, 272, 320, 127), (2, 32, 33, 224, 200), (2, 32, 520, 1056, 257),
     (0, 128, 2048, 8192, 130),
     (0, 128, 300, 2048, 16), (1, 32, 72, 512, 12), (2, 32, 48, 1024, 16), (0, 64, 520, 4352, 11),
+    # q8_0: a word tile is 64 wide, so K = 32 mod 64 leaves half a tile
+    (3, 32, 16, 32, 1), (3, 32, 100, 96, 3), (3, 32, 33, 224, 4), (3, 32, 130, 160, 12),
+    (3, 32, 72, 544, 17), (3, 32, 300, 2048, 129), (3, 32, 520, 1056, 257), (3, 32, 1000, 4096, 64),
+    (3, 32, 48, 8192, 8), (3, 32, 40, 8224, 1), (3, 32, 64, 96, 100),
 ]
 
 
@@ -151,7 +158,7 @@ def test_ragged_parity(fmt, group, N, K, M):
 
 
 @pytest.mark.parametrize("force,M", [("gemm", 1), ("gemm", 4), ("gemm", 8), ("gemv", 3)])
-@pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32)])
+@pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32), (3, 32)])
 def test_forced_path(monkeypatch, force, M, fmt, group):
     monkeypatch.setenv("QGEMM_FORCE", force)
     N, K = 272, 1024
@@ -177,7 +184,7 @@ def test_split_k_variants(monkeypatch, splits, M):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M", [1, 5, 64, 130])
-@pytest.mark.parametrize("fmt,group", [(0, 32), (0, 128), (1, 64), (2, 32)])
+@pytest.mark.parametrize("fmt,group", [(0, 32), (0, 128), (1, 64), (2, 32), (3, 32)])
 def test_one_hot_bit_exact(M, fmt, group):
     N, K = 144, 512
     say(f"one-hot fmt={fmt} g={group} M={M}")
@@ -194,24 +201,25 @@ def test_one_hot_bit_exact(M, fmt, group):
 
 
 @pytest.mark.parametrize("M", [1, 8, 128])
-@pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32)])
+@pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32), (3, 32)])
 def test_exact_regime_bit_exact(M, fmt, group):
     # x in {-1, 0, 1}, power-of-two scales, integer zero points: every partial
     # sum is an integer multiple of the smallest scale and exact in fp32
-    N, K = 256, 2048
+    # (q8_0 at K = 512, so that |y| <= 512 * 128 / 2 stays inside fp16)
+    N, K = 256, 512 if fmt == 3 else 2048
     say(f"exact regime fmt={fmt} M={M}")
     rng = np.random.default_rng(fmt * 10 + M)
     b = oracle.BITS[fmt]
     codes = rng.integers(0, 1 << b, size=(N, K), dtype=np.uint8)
     s = (2.0 ** rng.integers(-4, 0, size=(N, K // group))).astype(np.float16)
-    z = None if fmt == 2 else rng.integers(0, 1 << b, size=(N, K // group)).astype(np.float16)
+    z = None if fmt in (2, 3) else rng.integers(0, 1 << b, size=(N, K // group)).astype(np.float16)
     x = rng.integers(-1, 2, size=(M, K)).astype(np.float16)
     c = synth.QCase(fmt=fmt, group=group, N=N, K=K, codes=codes, words=synth.pack_words(codes, b),
                     scales=s, zeros=z, x=x)
     lin = qgm.QuantLinear.from_case(c, DEV)
     y = run_gemm(lin, x)
     yr = ref_y(c, x)
-    assert np.all(np.abs(yr) < 2048)
+    assert np.all(np.abs(yr) < (2048 if b <= 4 else 32768))
     assert np.array_equal(y.astype(np.float64), yr.astype(np.float16).astype(np.float64))
 
 
@@ -229,13 +237,15 @@ def test_closed_form_zero_codes():
         check_close(y, expect, f"zero codes M={M}")
 
 
-def test_q4_0_all_eight_is_zero():
+@pytest.mark.parametrize("fmt,u,bits", [(2, 8, 4), (3, 128, 8)])
+def test_block_format_zero_code_is_zero(fmt, u, bits):
+    # q4_0 byte 8 and q8_0 byte 128 are the signed code 0: y is exactly 0
     N, K = 64, 512
-    codes = np.full((N, K), 8, np.uint8)
+    codes = np.full((N, K), u, np.uint8)
     s = np.random.default_rng(0).uniform(0.1, 2, size=(N, K // 32)).astype(np.float16)
-    for M in (1, 32):
+    for M in (1, 8, 32):
         x = np.random.default_rng(M).standard_normal((M, K)).astype(np.float16)
-        c = synth.QCase(fmt=2, group=32, N=N, K=K, codes=codes, words=synth.pack_words(codes, 4),
+        c = synth.QCase(fmt=fmt, group=32, N=N, K=K, codes=codes, words=synth.pack_words(codes, bits),
                         scales=s, zeros=None, x=x)
         y = run_gemm(qgm.QuantLinear.from_case(c, DEV), x)
         assert np.array_equal(y, np.zeros_like(y))
