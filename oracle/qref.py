@@ -25,10 +25,23 @@ What is computed, and where it comes from:
       this format loses nothing when the operands are integers; read here as:
       a weight that already is a block scale times an integer in [-127, 127]
       comes back exactly, and every code and every s * q is exact in fp32;
+    - q4k, the k-quant of the same guide, is only named there, with the
+      remark that layer widths must be multiples of 256.  Read as the
+      published k-quant scheme: super-blocks of 256 weights along K, each with
+      fp16 factors d and dmin, split into 8 sub-blocks of 32 whose 6-bit
+      integers sc and m (0..63) give the sub-block scale d * sc and the
+      sub-block offset dmin * m; 4-bit codes q in 0..15 (canonical INT4
+      words), w = d * sc * q - dmin * m.  The metadata layout is this
+      library's own: scales fp16 [N, K/256, 2] holding (d, dmin), zeros
+      uint16 [N, K/32] holding sc in the low byte and m in the high byte;
+      the group argument is the super-block, 256;
     - zero points are fp16 values holding integers in [0, 2^b - 1].
 * Precision: the dequantized weight is formed in fp32, which is exact (an
   11-bit fp16 significand times an integer of at most 8 bits needs at most 19
-  significant bits); the product is taken in fp64.  The torchnative guide
+  significant bits); the product is taken in fp64.  A q4k weight is the
+  difference of two such exact products (d * sc * q has at most 21
+  significant bits), formed in fp64, where it is exact whenever d and dmin
+  are within a factor 2^31 of each other; its fp32 copy is rounded once.  The torchnative guide
   (section "float32 or bfloat16") notes that a change of accumulation order
   alone changes low-precision results, so parity is judged by a tolerance on
   y, and bit-exactly only on integer codes.
@@ -45,7 +58,10 @@ INT4_ASYM = 0
 INT2_ASYM = 1
 Q4_0 = 2
 Q8_0 = 3
-BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4, Q8_0: 8}
+Q4K = 4
+BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4, Q8_0: 8, Q4K: 4}
+Q4K_SUPER = 256   # weights per q4k super-block (one (d, dmin) pair)
+Q4K_SUB = 32      # weights per q4k sub-block (one (sc, m) pair)
 # implicit zero points of the symmetric block formats (offset-binary codes)
 IMPLICIT_ZERO = {Q4_0: 8.0, Q8_0: 128.0}
 
@@ -93,24 +109,52 @@ def _group_params(scales, zeros, N, K, group, fmt):
     return s, z
 
 
-def dequant_f32(words, scales, zeros, N: int, K: int, group: int, fmt: int) -> np.ndarray:
-    """w[n, k] = s[n, k // g] * (q[n, k] - z[n, k // g]) in fp32 (exact)."""
+def q4k_subblock_params(scales, zeros, N: int, K: int):
+    """q4k: per sub-block scale d * sc and offset dmin * m, fp64 [N, K/32]
+    each (both exact: an fp16 value times a 6-bit integer)."""
+    if K % Q4K_SUPER != 0:
+        raise ValueError("q4k needs K divisible by 256")
+    ds = np.asarray(scales, dtype=np.float16).reshape(N, K // Q4K_SUPER, 2).astype(np.float64)
+    sm = np.asarray(zeros, dtype=np.uint16).reshape(N, K // Q4K_SUB)
+    sc = (sm & 0xFF).astype(np.float64)
+    m = (sm >> 8).astype(np.float64)
+    if sc.size and (sc.max() > 63 or m.max() > 63):
+        raise ValueError("q4k sub-block scales and offsets are 6-bit")
+    sup = np.arange(K // Q4K_SUB) // (Q4K_SUPER // Q4K_SUB)   # super-block of each sub-block
+    return ds[:, sup, 0] * sc, ds[:, sup, 1] * m
+
+
+def dequant_f64(words, scales, zeros, N: int, K: int, group: int, fmt: int) -> np.ndarray:
+    """The dequantized weight in fp64 (exact for every format)."""
+    if fmt == Q4K:
+        if group != Q4K_SUPER:
+            raise ValueError("q4k uses super-blocks of 256")
+        q = unpack_codes(words, N, K, fmt).astype(np.float64)
+        s, b = q4k_subblock_params(scales, zeros, N, K)
+        sidx = np.arange(K) // Q4K_SUB
+        return s[:, sidx] * q - b[:, sidx]
     q = unpack_codes(words, N, K, fmt).astype(np.float32)
     s, z = _group_params(scales, zeros, N, K, group, fmt)
     gidx = np.arange(K) // group
-    return s[:, gidx] * (q - z[:, gidx])
+    return (s[:, gidx] * (q - z[:, gidx])).astype(np.float64)
+
+
+def dequant_f32(words, scales, zeros, N: int, K: int, group: int, fmt: int) -> np.ndarray:
+    """w[n, k] = s[n, k // g] * (q[n, k] - z[n, k // g]) in fp32 (exact; for
+    q4k, d * sc * q - dmin * m rounded once to fp32)."""
+    return dequant_f64(words, scales, zeros, N, K, group, fmt).astype(np.float32)
 
 
 def dequant_f16(words, scales, zeros, N: int, K: int, group: int, fmt: int) -> np.ndarray:
     """The exact dequantized weight rounded once to fp16 (nearest-even)."""
-    return dequant_f32(words, scales, zeros, N, K, group, fmt).astype(np.float16)
+    return dequant_f64(words, scales, zeros, N, K, group, fmt).astype(np.float16)
 
 
 def qgemm_ref(x, words, scales, zeros, M: int, N: int, K: int, group: int, fmt: int,
               residual=None) -> np.ndarray:
     """y_ref = x . dequant(W)^T in fp64 (+ residual, when given)."""
     x64 = np.asarray(x, dtype=np.float16).reshape(M, K).astype(np.float64)
-    w64 = dequant_f32(words, scales, zeros, N, K, group, fmt).astype(np.float64)
+    w64 = dequant_f64(words, scales, zeros, N, K, group, fmt)
     y = x64 @ w64.T
     if residual is not None:
         y = y + np.asarray(residual, dtype=np.float16).reshape(M, N).astype(np.float64)

@@ -26,6 +26,14 @@ DESIGN.md under "Readings"):
   stored as the offset-binary byte u = code + 128.  An all-zero block has
   scale 0, u = 128.  A block that already is d times integers in [-127, 127]
   with one of magnitude 127 (d an fp16 value) is reproduced exactly.
+* q4k (same guide and section, named only, with widths divisible by 256):
+  the k-quant reading -- super-blocks of 256 with fp16 (d, dmin), sub-blocks
+  of 32 with 6-bit (sc, m), w = d * sc * q - dmin * m, q in 0..15.  Quantizer:
+  per sub-block, offset o = max(0, -min) and scale t = (max + o) / 15; per
+  super-block d = max t / 63 and dmin = max o / 63 in fp16; sc = rint(t / d),
+  m = rint(o / dmin), both clipped to 0..63; q = clip(rint((w + dmin m) /
+  (d sc)), 0, 15) with the stored values.  Metadata: scales fp16 [N, K/256, 2]
+  = (d, dmin), zeros uint16 [N, K/32] = sc | m << 8.
 * Canonical packing: code (n, k) sits in word [n, k // cpw] at bits
   [b*(k % cpw), b*(k % cpw) + b), i.e. least significant bits first along K,
   cpw = 32 / b codes per uint32.
@@ -43,9 +51,10 @@ INT4_ASYM = 0
 INT2_ASYM = 1
 Q4_0 = 2
 Q8_0 = 3
+Q4K = 4
 
-FORMAT_NAMES = {INT4_ASYM: "int4_asym", INT2_ASYM: "int2_asym", Q4_0: "q4_0", Q8_0: "q8_0"}
-FORMAT_BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4, Q8_0: 8}
+FORMAT_NAMES = {INT4_ASYM: "int4_asym", INT2_ASYM: "int2_asym", Q4_0: "q4_0", Q8_0: "q8_0", Q4K: "q4k"}
+FORMAT_BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4, Q8_0: 8, Q4K: 4}
 SYMMETRIC = (Q4_0, Q8_0)   # block formats with no stored zero point
 
 
@@ -114,6 +123,36 @@ def quantize_q8_0(w: np.ndarray, block: int = 32):
     return u, s16
 
 
+def quantize_q4k(w: np.ndarray):
+    """k-quant 4-bit quantizer.  Returns (codes uint8 [N,K] in [0, 15],
+    scales fp16 [N,K/256,2] = (d, dmin), zeros uint16 [N,K/32] = sc | m << 8)."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    assert k % 256 == 0
+    ns = k // 32
+    wb = w.reshape(n, ns, 32)
+    off = np.maximum(0.0, -wb.min(axis=2)).astype(np.float32)          # [n, ns]
+    t = ((wb.max(axis=2) + off) / np.float32(15.0)).astype(np.float32)
+    tS = t.reshape(n, k // 256, 8)
+    oS = off.reshape(n, k // 256, 8)
+    d = (tS.max(axis=2) / np.float32(63.0)).astype(np.float16)
+    dmin = (oS.max(axis=2) / np.float32(63.0)).astype(np.float16)
+    df = d.astype(np.float32)[:, :, None]
+    mf = dmin.astype(np.float32)[:, :, None]
+    sc = np.where(df > 0, np.clip(np.rint(tS / np.where(df > 0, df, 1)), 0, 63), 0).reshape(n, ns)
+    m = np.where(mf > 0, np.clip(np.rint(oS / np.where(mf > 0, mf, 1)), 0, 63), 0).reshape(n, ns)
+    sup = np.arange(ns) // 8
+    s_eff = d.astype(np.float32)[:, sup] * sc.astype(np.float32)      # [n, ns]
+    b_eff = dmin.astype(np.float32)[:, sup] * m.astype(np.float32)
+    safe = np.where(s_eff > 0, s_eff, 1.0)
+    q = np.clip(np.rint((wb + b_eff[:, :, None]) / safe[:, :, None]), 0, 15)
+    q = np.where((s_eff > 0)[:, :, None], q, 0)
+    codes = q.astype(np.uint8).reshape(n, k)
+    scales = np.stack([d, dmin], axis=-1)
+    zeros = (sc.astype(np.uint16) | (m.astype(np.uint16) << 8)).astype(np.uint16)
+    return codes, scales, zeros
+
+
 def pack_words(codes: np.ndarray, bits: int) -> np.ndarray:
     """Canonical packing: least significant bits first along K."""
     codes = np.asarray(codes, dtype=np.uint32)
@@ -142,6 +181,7 @@ class QCase:
     words: np.ndarray            # uint32 [N, K / cpw], canonical order
     scales: np.ndarray           # fp16 [N, K / group]
     zeros: Optional[np.ndarray]  # fp16 [N, K / group] or None for q4_0 / q8_0
+    #                              (q4k: scales fp16 [N, K/256, 2], zeros uint16 [N, K/32])
     x: Optional[np.ndarray] = None  # fp16 [M, K]
 
     @property
@@ -166,6 +206,9 @@ def quantize(w: np.ndarray, fmt: int, group: int) -> QCase:
         assert group == 32
         codes, s = quantize_q8_0(w, 32)
         z = None
+    elif fmt == Q4K:
+        assert group == 256
+        codes, s, z = quantize_q4k(w)
     else:
         codes, s, z = quantize_asym(w, FORMAT_BITS[fmt], group)
     return QCase(fmt=fmt, group=group, N=n, K=k, codes=codes,
@@ -202,6 +245,15 @@ def random_codes_case(seed: int, fmt: int, group: int, N: int, K: int, M: int) -
     rng = np.random.default_rng(seed)
     bits = FORMAT_BITS[fmt]
     codes = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    if fmt == Q4K:
+        # d, dmin ~ 3e-4 * U(0.5, 1.5); sc, m uniform over 0..63
+        ds = (3e-4 * rng.uniform(0.5, 1.5, size=(N, K // 256, 2))).astype(np.float16)
+        sc = rng.integers(0, 64, size=(N, K // 32))
+        m = rng.integers(0, 64, size=(N, K // 32))
+        z = (sc | (m << 8)).astype(np.uint16)
+        x = draw_x(rng, M, K, "normal")
+        return QCase(fmt=fmt, group=group, N=N, K=K, codes=codes,
+                     words=pack_words(codes, bits), scales=ds, zeros=z, x=x)
     s = (0.005 * rng.uniform(0.5, 1.5, size=(N, K // group))).astype(np.float16)
     z = None
     if fmt not in SYMMETRIC:
@@ -219,6 +271,7 @@ WORKLOADS: Dict[str, dict] = {
     "int2_g64":        dict(seed=1004, fmt=INT2_ASYM, group=64,  N=8192, K=2048, M=128, xdist="normal", Ms=(1, 128)),
     "q4_0_b32":        dict(seed=1004, fmt=Q4_0,      group=32,  N=8192, K=2048, M=128, xdist="normal", Ms=(1, 128)),
     "q8_0_b32":        dict(seed=1004, fmt=Q8_0,      group=32,  N=8192, K=2048, M=128, xdist="normal", Ms=(1, 128)),
+    "q4k_s256":        dict(seed=1004, fmt=Q4K,       group=256, N=8192, K=2048, M=128, xdist="normal", Ms=(1, 128)),
 }
 
 

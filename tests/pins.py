@@ -16,7 +16,8 @@ import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 FMT = {"int4": 0, "int2": 1, "q4_0": 2, "q8_0": 3}
-BITS = {0: 4, 1: 2, 2: 4, 3: 8}
+BITS = {0: 4, 1: 2, 2: 4, 3: 8, 4: 4}
+Q4K = 4
 # implicit zero points of the block formats: q4_0 stores q + 8, q8_0 q + 128
 ZIMPL = {2: 8, 3: 128}
 
@@ -90,6 +91,49 @@ def _rand_inputs(seed, fmt, N, K, M, group):
     z = None if fmt in ZIMPL else rng.integers(0, 1 << b, size=(N, K // group)).astype(np.float16)
     x = rng.standard_normal((M, K)).astype(np.float16)
     return codes, s, z, x
+
+
+def q4k_meta(d, dmin, sc, m):
+    """Metadata arrays of one q4k row set: scales fp16 [N, S, 2], zeros uint16
+    [N, 8S] with sc in the low byte and m in the high byte."""
+    d, dmin = np.asarray(d, np.float16), np.asarray(dmin, np.float16)
+    scales = np.stack([d, dmin], axis=-1)
+    zeros = (np.asarray(sc, np.uint16) | (np.asarray(m, np.uint16) << 8)).astype(np.uint16)
+    return scales, zeros
+
+
+def brute_y_q4k(x, codes, d, dmin, sc, m):
+    """Literal loops: w = d[S] * sc[j] * q - dmin[S] * m[j], S = k // 256, j = k // 32."""
+    x = np.asarray(x, dtype=np.float16).astype(float)
+    M, K = x.shape
+    N = len(codes)
+    y = np.zeros((M, N))
+    for mm in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                S, j = k // 256, k // 32
+                w = float(d[n][S]) * int(sc[n][j]) * int(codes[n][k]) - float(dmin[n][S]) * int(m[n][j])
+                acc += float(x[mm][k]) * w
+            y[mm, n] = acc
+    return y
+
+
+def exact_w_q4k(codes, d, dmin, sc, m, n, k):
+    S, j = k // 256, k // 32
+    return (Fraction(float(d[n][S])) * int(sc[n][j]) * int(codes[n][k])
+            - Fraction(float(dmin[n][S])) * int(m[n][j]))
+
+
+def _rand_q4k(seed, N, K, M):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    d = rng.uniform(1e-4, 2e-3, size=(N, K // 256)).astype(np.float16)
+    dmin = rng.uniform(1e-4, 2e-3, size=(N, K // 256)).astype(np.float16)
+    sc = rng.integers(0, 64, size=(N, K // 32))
+    m = rng.integers(0, 64, size=(N, K // 32))
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    return codes, d, dmin, sc, m, x
 
 
 # -- pins ---------------------------------------------------------------------
@@ -249,6 +293,81 @@ def pin_fold_identity(O):
     assert np.max(np.abs(y - yb)) <= 1e-12 * max(1.0, np.max(np.abs(yb)))
 
 
+def pin_q4k_handcases(O):
+    for line in open(os.path.join(GOLDEN, "q4k_handcases.jsonl")):
+        c = json.loads(line)
+        if "name" not in c:
+            continue
+        K, rule = c["K"], c["codes"]
+        codes = np.array([[(k % 16 if rule == "k%16" else rule) for k in range(K)]], dtype=np.uint8)
+        x = np.array([[1.0 if c["x"] == "ones" else (-1.0) ** k for k in range(K)]], dtype=np.float16)
+        scales, zeros = q4k_meta([c["d"]], [c["dmin"]], [c["sc"]], [c["m"]])
+        y = O.qgemm_ref(x, pack_literal(codes, 4), scales, zeros, 1, 1, K, 256, Q4K)
+        assert float(y[0, 0]) == c["y"], (c["name"], float(y[0, 0]), c["y"])
+
+
+def pin_q4k_bruteforce_and_exact(O):
+    for N, K, M in ((5, 256, 3), (3, 768, 2)):
+        codes, d, dmin, sc, m, x = _rand_q4k(600 + K, N, K, M)
+        scales, zeros = q4k_meta(d, dmin, sc, m)
+        words = pack_literal(codes, 4)
+        y = O.qgemm_ref(x, words, scales, zeros, M, N, K, 256, Q4K)
+        yb = brute_y_q4k(x, codes, d, dmin, sc, m)
+        assert y.shape == (M, N)
+        assert np.max(np.abs(y - yb)) <= 1e-12 * max(1.0, np.max(np.abs(yb))), (N, K, M)
+        w16 = O.dequant_f16(words, scales, zeros, N, K, 256, Q4K)
+        for n in range(N):
+            for k in range(0, K, 7):
+                e = exact_w_q4k(codes, d, dmin, sc, m, n, k)
+                assert float(w16[n, k]) == half_rne(float(e)), (n, k)
+        for mm in range(M):
+            for n in range(N):
+                ex = sum(Fraction(float(x[mm, k])) * exact_w_q4k(codes, d, dmin, sc, m, n, k) for k in range(K))
+                assert abs(float(y[mm, n]) - float(ex)) <= 1e-13 * max(1.0, abs(float(ex))), (mm, n)
+
+
+def pin_q4k_one_hot_and_zero_codes(O):
+    N, K = 24, 512       # N != K
+    codes, d, dmin, sc, m, _ = _rand_q4k(700, N, K, 1)
+    scales, zeros = q4k_meta(d, dmin, sc, m)
+    ks = [0, 1, 31, 32, 255, 256, 300, 511]
+    x = np.zeros((len(ks), K), np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    y = O.qgemm_ref(x, pack_literal(codes, 4), scales, zeros, len(ks), N, K, 256, Q4K)
+    for i, k in enumerate(ks):
+        for n in range(N):
+            assert Fraction(float(y[i, n])) == exact_w_q4k(codes, d, dmin, sc, m, n, k), (k, n)
+    # all codes 0: y = -sum_j dmin[S] m[j] sum_{k in j} x
+    xr = np.random.default_rng(5).standard_normal((2, K)).astype(np.float16)
+    y0 = O.qgemm_ref(xr, np.zeros((N, K // 8), np.uint32), scales, zeros, 2, N, K, 256, Q4K)
+    for mm in range(2):
+        for n in range(N):
+            ex = Fraction(0)
+            for j in range(K // 32):
+                sx = sum(Fraction(float(v)) for v in xr[mm, 32 * j:32 * j + 32])
+                ex -= Fraction(float(dmin[n, j // 8])) * int(m[n, j]) * sx
+            assert abs(float(y0[mm, n]) - float(ex)) <= 1e-12 * max(1.0, abs(float(ex))), (mm, n)
+
+
+def pin_q4k_matches_int4_g32(O):
+    # d a power of two, m = sc * z with integer z: w = d sc (q - z), i.e. INT4
+    # with group 32, scale d * sc (exact in fp16) and zero point z
+    rng = np.random.default_rng(800)
+    N, K, M = 8, 512, 3
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    sc = rng.integers(1, 5, size=(N, K // 32))
+    z = np.array([[rng.integers(0, min(15, 63 // int(v)) + 1) for v in row] for row in sc])
+    d = (2.0 ** rng.integers(-10, -4, size=(N, K // 256))).astype(np.float16)
+    scales, zeros = q4k_meta(d, d, sc, sc * z)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    words = pack_literal(codes, 4)
+    a = O.qgemm_ref(x, words, scales, zeros, M, N, K, 256, Q4K)
+    s32 = (d.astype(np.float64)[:, np.arange(K // 32) // 8] * sc).astype(np.float16)
+    b = O.qgemm_ref(x, words, s32, z.astype(np.float16), M, N, K, 32, 0)
+    assert np.array_equal(a, b)
+
+
 def pin_tolerance_rule(O):
     ref = np.array([[1.0, -4.0], [2.0, 0.5]])
     tol = O.TOLERANCE
@@ -267,7 +386,8 @@ def pin_tolerance_rule(O):
 
 ALL_PINS = [pin_worked_words, pin_handcases, pin_zero_codes_closed_form, pin_one_hot,
             pin_format_identity, pin_bruteforce, pin_exact_rational, pin_dequant_exact,
-            pin_fold_identity, pin_tolerance_rule]
+            pin_fold_identity, pin_tolerance_rule, pin_q4k_handcases, pin_q4k_bruteforce_and_exact,
+            pin_q4k_one_hot_and_zero_codes, pin_q4k_matches_int4_g32]
 
 
 def failing_pins(O):

@@ -7,7 +7,7 @@ from tests import pins
 
 _orig_unpack = qref.unpack_codes
 _orig_pack = qref.pack_codes
-_orig_deq = qref.dequant_f32
+_orig_deq = qref.dequant_f64
 _orig_gemm = qref.qgemm_ref
 
 
@@ -80,15 +80,71 @@ def _gemm_fp16_accumulate(x, words, scales, zeros, M, N, K, group, fmt, residual
     return (x16 @ w16.T).astype(np.float64)
 
 
+def _keep_q4k(fn):
+    """A mutant of the group formats that leaves q4k alone, so that only the
+    pins of the formats it breaks can catch it."""
+    def wrapped(words, scales, zeros, N, K, group, fmt):
+        if fmt == qref.Q4K:
+            return _orig_deq(words, scales, zeros, N, K, group, fmt)
+        return fn(words, scales, zeros, N, K, group, fmt)
+    return wrapped
+
+
+def _q4k_params(words, scales, zeros, N, K):
+    q = _orig_unpack(words, N, K, qref.Q4K).astype(np.float64)
+    ds = np.asarray(scales, np.float16).reshape(N, K // 256, 2).astype(np.float64)
+    sm = np.asarray(zeros, np.uint16).reshape(N, K // 32)
+    return q, ds, (sm & 0xFF).astype(np.float64), (sm >> 8).astype(np.float64)
+
+
+def _deq_q4k_no_offset(words, scales, zeros, N, K, group, fmt):
+    if fmt != qref.Q4K:
+        return _orig_deq(words, scales, zeros, N, K, group, fmt)
+    q, ds, sc, m = _q4k_params(words, scales, zeros, N, K)
+    sup = np.arange(K // 32) // 8
+    return (ds[:, sup, 0] * sc)[:, np.arange(K) // 32] * q
+
+
+def _deq_q4k_swapped_bytes(words, scales, zeros, N, K, group, fmt):
+    if fmt != qref.Q4K:
+        return _orig_deq(words, scales, zeros, N, K, group, fmt)
+    q, ds, sc, m = _q4k_params(words, scales, zeros, N, K)
+    sup = np.arange(K // 32) // 8
+    s, b = ds[:, sup, 0] * m, ds[:, sup, 1] * sc      # sc and m read from the wrong bytes
+    return s[:, np.arange(K) // 32] * q - b[:, np.arange(K) // 32]
+
+
+def _deq_q4k_super_index(words, scales, zeros, N, K, group, fmt):
+    if fmt != qref.Q4K:
+        return _orig_deq(words, scales, zeros, N, K, group, fmt)
+    q, ds, sc, m = _q4k_params(words, scales, zeros, N, K)
+    sup = np.arange(K // 32) % (K // 256)               # sub-block -> wrong super-block
+    s, b = ds[:, sup, 0] * sc, ds[:, sup, 1] * m
+    return s[:, np.arange(K) // 32] * q - b[:, np.arange(K) // 32]
+
+
+def _deq_q4k_dmin_for_d(words, scales, zeros, N, K, group, fmt):
+    if fmt != qref.Q4K:
+        return _orig_deq(words, scales, zeros, N, K, group, fmt)
+    q, ds, sc, m = _q4k_params(words, scales, zeros, N, K)
+    sup = np.arange(K // 32) // 8
+    s, b = ds[:, sup, 1] * sc, ds[:, sup, 0] * m        # d and dmin exchanged
+    return s[:, np.arange(K) // 32] * q - b[:, np.arange(K) // 32]
+
+
 MUTANTS = {
     "unpack_msb_first": [("unpack_codes", _unpack_msb_first), ("pack_codes", _pack_msb_first)],
-    "dequant_sign": [("dequant_f32", _deq_sign)],
-    "dropped_zero_point": [("dequant_f32", _deq_no_zero)],
-    "group_index_mod": [("dequant_f32", _deq_group_mod)],
-    "group_index_shift": [("dequant_f32", _deq_group_shift)],
-    "q4_0_offset_7": [("dequant_f32", _deq_q40_offset7)],
-    "q8_0_offset_127": [("dequant_f32", _deq_q80_offset127)],
+    "dequant_sign": [("dequant_f64", _keep_q4k(_deq_sign))],
+    "dropped_zero_point": [("dequant_f64", _keep_q4k(_deq_no_zero))],
+    "group_index_mod": [("dequant_f64", _keep_q4k(_deq_group_mod))],
+    "group_index_shift": [("dequant_f64", _keep_q4k(_deq_group_shift))],
+    "q4_0_offset_7": [("dequant_f64", _keep_q4k(_deq_q40_offset7))],
+    "q8_0_offset_127": [("dequant_f64", _keep_q4k(_deq_q80_offset127))],
     "q8_0_seven_bit_mask": [("unpack_codes", _unpack_q80_low7)],
+    "q4k_dropped_offset": [("dequant_f64", _deq_q4k_no_offset)],
+    "q4k_swapped_bytes": [("dequant_f64", _deq_q4k_swapped_bytes)],
+    "q4k_wrong_super_block": [("dequant_f64", _deq_q4k_super_index)],
+    "q4k_d_dmin_exchanged": [("dequant_f64", _deq_q4k_dmin_for_d)],
     "transposed_operand": [("qgemm_ref", _gemm_transposed)],
     "fp16_accumulation": [("qgemm_ref", _gemm_fp16_accumulate)],
 }

@@ -48,6 +48,35 @@ def test_q8_0_integer_operands_round_trip():
     assert np.array_equal(back, w)
 
 
+def test_q4k_quantizer_bounds_and_error():
+    rng = np.random.default_rng(31)
+    w = synth.draw_weights(rng, 32, 1024)
+    codes, scales, zeros = synth.quantize_q4k(w)
+    assert codes.max() <= 15 and scales.shape == (32, 4, 2) and zeros.shape == (32, 32)
+    assert (zeros & 0xFF).max() <= 63 and (zeros >> 8).max() <= 63
+    deq = oracle.dequant_f64(synth.pack_words(codes, 4), scales, zeros, 32, 1024, 256, oracle.Q4K)
+    # every weight within one sub-block step (d * sc) of its dequantized value
+    step = (scales[:, :, 0].astype(np.float64)[:, np.arange(32) // 8] * (zeros & 0xFF))[:, np.arange(1024) // 32]
+    assert np.all(np.abs(deq - w) <= step * 1.0 + 1e-7)
+    assert np.sqrt(np.mean((deq - w) ** 2)) < 0.1 * np.sqrt(np.mean(w.astype(np.float64) ** 2))
+
+
+def test_q4k_worked_sub_block():
+    # one super-block; sub-block 0 = [-0.3, 0.6, 0, ...], every other weight 0:
+    # offset 0.3, scale t0 = 0.9 / 15 = 0.06; all other sub-blocks t = o = 0.
+    # d = 0.06 / 63, dmin = 0.3 / 63 (fp16), so sc0 = m0 = 63 and the codes are
+    # rint((w + dmin*63) / (d*63)) = [0, 15, 5, 5, ...] in sub-block 0
+    w = np.zeros((1, 256), np.float32)
+    w[0, :2] = [-0.3, 0.6]
+    codes, scales, zeros = synth.quantize_q4k(w)
+    assert int(zeros[0, 0]) == 63 | (63 << 8)
+    assert np.all(zeros[0, 1:] == 0)
+    assert float(scales[0, 0, 0]) == float(np.float16(0.06 / 63))
+    assert float(scales[0, 0, 1]) == float(np.float16(0.3 / 63))
+    assert list(codes[0, :4]) == [0, 15, 5, 5]
+    assert np.all(codes[0, 32:] == 0)
+
+
 @pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (2, 64), (2, 32)])
 def test_asym_quantizer_bounds(bits, group):
     rng = np.random.default_rng(bits * 1000 + group)
@@ -70,9 +99,9 @@ def test_asym_quantizer_bounds(bits, group):
     assert lo_code.max() <= 1 and hi_code.min() >= qmax - 1
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_generator_words_match_oracle_unpack(fmt):
-    c = synth.random_codes_case(9, fmt, 32 if fmt != 1 else 64, 48, 512, 2)
+    c = synth.random_codes_case(9, fmt, {1: 64, 4: 256}.get(fmt, 32), 48, 512, 2)
     assert np.array_equal(oracle.unpack_codes(c.words, c.N, c.K, fmt), c.codes)
 
 
