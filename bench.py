@@ -95,7 +95,7 @@ class Leg:
         return ms / steps
 
 
-FORMAT_NAMES = ("int4_asym", "int2_asym", "q4_0", "q8_0")
+FORMAT_NAMES = ("int4_asym", "int2_asym", "q4_0", "q8_0", "q4k")
 
 
 def leg_result(name, leg, ms, M):
@@ -305,7 +305,8 @@ def main():
     secondary.append(leg_result("decode_int4_g128_M8", leg8, leg8.time(400, 40), 8))
     del leg8
     for name, M in (("prefill_int4_g128", 128), ("int2_g64", 1), ("int2_g64", 128),
-                    ("q4_0_b32", 1), ("q4_0_b32", 128), ("q8_0_b32", 1), ("q8_0_b32", 128)):
+                    ("q4_0_b32", 1), ("q4_0_b32", 128), ("q8_0_b32", 1), ("q8_0_b32", 128),
+                    ("q4k_s256", 1), ("q4k_s256", 128)):
         c = synth.workload(name)
         leg = Leg(qgm, torch, c, M)
         steps = 400 if M == 1 else 200

@@ -18,7 +18,8 @@ INT4_ASYM = 0
 INT2_ASYM = 1
 Q4_0 = 2
 Q8_0 = 3
-BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4, Q8_0: 8}
+Q4K = 4
+BITS = {INT4_ASYM: 4, INT2_ASYM: 2, Q4_0: 4, Q8_0: 8, Q4K: 4}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemm.so")
@@ -165,6 +166,15 @@ def to_half_tensor(a: Optional[np.ndarray], device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16)).to(device)
 
 
+def to_bits16_tensor(a: Optional[np.ndarray], device="cuda"):
+    """16-bit integer metadata (q4k's sc | m << 8) -> int16 device tensor
+    holding the same bits."""
+    if a is None:
+        return None
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(device)
+
+
 def qpack(canon, N: int, K: int, fmt: int, out=None, stream=None):
     """canonical words (int32 bits, [N, K/cpw], device) -> packed buffer (int32, device)."""
     torch = _torch()
@@ -252,7 +262,8 @@ class QuantLinear:
         canon = to_words_tensor(words, device)
         self.packed = qpack(canon, N, K, fmt)
         self.scales = to_half_tensor(scales, device)
-        self.zeros = to_half_tensor(zeros, device)
+        # q4k: zeros carries the (sc, m) bytes, not fp16 values
+        self.zeros = to_bits16_tensor(zeros, device) if fmt == Q4K else to_half_tensor(zeros, device)
         self.weight_bytes = (self.packed.numel() * 4 + self.scales.numel() * 2 +
                              (0 if self.zeros is None else self.zeros.numel() * 2))
 

@@ -14,6 +14,7 @@ namespace qg {
 
 int check_format_group(int fmt, int group) {
   if (fmt == QG_Q4_0 || fmt == QG_Q8_0) return group == 32 ? QG_OK : QG_E_ARG;
+  if (fmt == QG_Q4K) return group == 256 ? QG_OK : QG_E_ARG;
   if (fmt == QG_INT4_ASYM || fmt == QG_INT2_ASYM)
     return (group == 32 || group == 64 || group == 128) ? QG_OK : QG_E_ARG;
   return QG_E_ARG;
@@ -83,14 +84,15 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   const int nw = GEMM_THREADS / 64;
   const int tpw = gemm_tpw(fmt);
   const int s_tiles = (int)ceil_div(p.wordtiles, nw * tpw);
-  const int s_groups = (int)ceil_div((int64_t)p.wordtiles * kt_width / group, GEMM_GCAP);
+  const int mg = meta_group(fmt, group);   // scale entries the kernel stages per 'group'
+  const int s_groups = (int)ceil_div((int64_t)p.wordtiles * kt_width / mg, GEMM_GCAP);
   const int s_min = std::max(s_tiles, s_groups);
   int s = tiles >= (GEMM_TARGET_WG * 5) / 8 ? 1 : (int)ceil_div(GEMM_TARGET_WG, tiles);
   if (split_env > 0) s = split_env;
   s = std::min(std::max(s, s_min), p.wordtiles);
   p.tps = (int)ceil_div(p.wordtiles, s);
   p.splits = (int)ceil_div(p.wordtiles, p.tps);
-  if (p.tps > nw * tpw || (int64_t)p.tps * kt_width / group > GEMM_GCAP) {  // cannot happen: s >= s_min
+  if (p.tps > nw * tpw || (int64_t)p.tps * kt_width / mg > GEMM_GCAP) {  // cannot happen: s >= s_min
     p.path = 0;
     return p;
   }

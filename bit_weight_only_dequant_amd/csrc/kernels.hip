@@ -5,8 +5,9 @@
 // ("Dequantizing Runtimes", "Quantized Matrix Multiplication"): weights are
 // brought back to full precision inside the compute pass, never written out.
 // Formats: INT4 / INT2 with per-group fp16 scale and zero point (TinyLoop
-// README, "Status" and "Current Runtime Snapshot"), q4_0 and q8_0 (torchnative
-// guide "Inference with real transformers", "Quantise while loading").
+// README, "Status" and "Current Runtime Snapshot"), q4_0, q8_0 and the k-quant
+// q4k (torchnative guide "Inference with real transformers", "Quantise while
+// loading").
 //
 // Kernels
 //   qpack / qunpack      one-time permutation of codes into the tile order of
@@ -132,13 +133,40 @@ __device__ __forceinline__ void qmz_int8(uint32_t w, const ZC8& zc, h2 out[2]) {
 
 // Per format: bits, codes per word, codes per 16-byte lane chunk (LS), K per
 // word tile (KT), codes per scale lookup (SW: a lane's chunk in runs of at
-// most 32, the smallest group), runs per chunk (NSEG), and the implicit zero
-// point of the block formats as fp16 bits (8.0 and 128.0).
+// most 32, the smallest group), runs per chunk (NSEG), the implicit zero
+// point of the block formats as fp16 bits (8.0 and 128.0), and KQ for the
+// k-quant q4k (codes unpacked with zero point 0; per 32-code sub-block a
+// scale d*sc and an offset dmin*m instead of (s, z)).
 template <int FMT> struct Fmt;
-template <> struct Fmt<INT4_ASYM> { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = true;  static constexpr uint32_t ZBITS = 0; };
-template <> struct Fmt<INT2_ASYM> { static constexpr int BITS = 2, CPW = 16, LS = 64, KT = 256, SW = 32, NSEG = 2; static constexpr bool HAS_Z = true;  static constexpr uint32_t ZBITS = 0; };
-template <> struct Fmt<Q4_0>      { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = false; static constexpr uint32_t ZBITS = 0x4800; };
-template <> struct Fmt<Q8_0>      { static constexpr int BITS = 8, CPW = 4,  LS = 16, KT = 64,  SW = 16, NSEG = 1; static constexpr bool HAS_Z = false; static constexpr uint32_t ZBITS = 0x5800; };
+template <> struct Fmt<INT4_ASYM> { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = true,  KQ = false; static constexpr uint32_t ZBITS = 0; };
+template <> struct Fmt<INT2_ASYM> { static constexpr int BITS = 2, CPW = 16, LS = 64, KT = 256, SW = 32, NSEG = 2; static constexpr bool HAS_Z = true,  KQ = false; static constexpr uint32_t ZBITS = 0; };
+template <> struct Fmt<Q4_0>      { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = false, KQ = false; static constexpr uint32_t ZBITS = 0x4800; };
+template <> struct Fmt<Q8_0>      { static constexpr int BITS = 8, CPW = 4,  LS = 16, KT = 64,  SW = 16, NSEG = 1; static constexpr bool HAS_Z = false, KQ = false; static constexpr uint32_t ZBITS = 0x5800; };
+template <> struct Fmt<Q4K>       { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = false, KQ = true;  static constexpr uint32_t ZBITS = 0; };
+
+// q4k sub-block terms from the super-block pair ddm = d | dmin << 16 (fp16
+// bits) and the sub-block bytes scm = sc | m << 8.  In fp32 they are exact
+// (an fp16 value times a 6-bit integer): (d*sc, dmin*m).  For the fp16
+// weight w = fma(q, fp16(d*sc), -fp16(dmin*m)) each is rounded once to
+// fp16, returned as (bits of fp16(d*sc)) | (bits of -fp16(dmin*m)) << 16.
+__device__ __forceinline__ float2 kq_terms(uint32_t ddm, uint32_t scm) {
+  const float d = (float)__builtin_bit_cast(f16, (uint16_t)(ddm & 0xffffu));
+  const float dmin = (float)__builtin_bit_cast(f16, (uint16_t)(ddm >> 16));
+  return float2{d * (float)(scm & 0xffu), dmin * (float)((scm >> 8) & 0xffu)};
+}
+__device__ __forceinline__ uint32_t kq_half_pair(uint32_t ddm, uint32_t scm) {
+  const float2 t = kq_terms(ddm, scm);
+  const uint32_t ds = __builtin_bit_cast(uint16_t, (f16)t.x);
+  const uint32_t nb = __builtin_bit_cast(uint16_t, (f16)(-t.y));
+  return ds | (nb << 16);
+}
+// fp16 q4k weights of 4 pairs of exact codes: fma(q, ds, nb), one rounding
+__device__ __forceinline__ void kq_weights(const h2* q, uint32_t dsnb, h2* w, int n) {
+  const h2 ds = splat(__builtin_bit_cast(f16, (uint16_t)(dsnb & 0xffffu)));
+  const h2 nb = splat(__builtin_bit_cast(f16, (uint16_t)(dsnb >> 16)));
+#pragma unroll
+  for (int i = 0; i < n; ++i) w[i] = __builtin_elementwise_fma(q[i], ds, nb);
+}
 
 // Exact (q - z) pairs, in k order, of run p (SW codes) of a lane's chunk c
 template <int FMT>
@@ -221,21 +249,33 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   const int64_t n = rb * 16 + r;
   const u4 c = reinterpret_cast<const u4*>(packed)[unit * 64 + lane];
   if (n >= N) return;
-  const int ng = K / group;
+  const int ng = K / group;   // q4k: group = 32, the sub-block
 #pragma unroll
   for (int p = 0; p < F::NSEG; ++p) {
     const int k = T * F::KT + g * F::LS + p * F::SW;  // first of this lane's SW codes
     if (k >= K) break;
     const int grp = k / group;
-    const h2 s2 = splat(scales[n * ng + grp]);
-    const f16 z = F::HAS_Z ? zeros[n * ng + grp] : __builtin_bit_cast(f16, (uint16_t)F::ZBITS);
     h2 q[F::SW / 2];
-    run_qmz<FMT>(c, p, z, q);
     h8* dst = reinterpret_cast<h8*>(w + n * K + k);
+    if constexpr (F::KQ) {
+      const uint32_t ddm = reinterpret_cast<const uint32_t*>(scales)[n * (ng >> 3) + (grp >> 3)];
+      const uint32_t scm = reinterpret_cast<const uint16_t*>(zeros)[n * ng + grp];
+      run_qmz<FMT>(c, p, (f16)0.0f, q);
+      h2 wq[F::SW / 2];
+      kq_weights(q, kq_half_pair(ddm, scm), wq, F::SW / 2);
 #pragma unroll
-    for (int v = 0; v < F::SW / 8; ++v) {
-      const h2 a0 = q[4 * v] * s2, a1 = q[4 * v + 1] * s2, a2 = q[4 * v + 2] * s2, a3 = q[4 * v + 3] * s2;
-      dst[v] = h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+      for (int v = 0; v < F::SW / 8; ++v)
+        dst[v] = h8{wq[4 * v][0], wq[4 * v][1], wq[4 * v + 1][0], wq[4 * v + 1][1],
+                    wq[4 * v + 2][0], wq[4 * v + 2][1], wq[4 * v + 3][0], wq[4 * v + 3][1]};
+    } else {
+      const h2 s2 = splat(scales[n * ng + grp]);
+      const f16 z = F::HAS_Z ? zeros[n * ng + grp] : __builtin_bit_cast(f16, (uint16_t)F::ZBITS);
+      run_qmz<FMT>(c, p, z, q);
+#pragma unroll
+      for (int v = 0; v < F::SW / 8; ++v) {
+        const h2 a0 = q[4 * v] * s2, a1 = q[4 * v + 1] * s2, a2 = q[4 * v + 2] * s2, a3 = q[4 * v + 3] * s2;
+        dst[v] = h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+      }
     }
   }
 }
@@ -266,11 +306,14 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
   return v + __shfl_xor(v, 32);
 }
 
-// LDS bytes of gemv_kernel: per wave its x slice and (scale, zero) pairs, then
-// the cross-wave sums
+// LDS bytes of gemv_kernel: per wave its x slice, (scale, zero) pairs (q4k:
+// fp32 (d*sc, dmin*m)) and, for q4k, the x sum of each 32-wide run; then the
+// cross-wave sums
 template <int FMT, int MMAX, int TPW, int NW> constexpr size_t gemv_lds_bytes() {
   constexpr int KW = TPW * Fmt<FMT>::KT;
-  return (size_t)NW * (MMAX * KW * 2 + 16 * (KW / 32) * 4) + (size_t)NW * MMAX * 16 * sizeof(float);
+  constexpr int SZB = Fmt<FMT>::KQ ? 8 : 4;
+  constexpr int XSB = Fmt<FMT>::KQ ? MMAX * (KW / 32) * 4 : 0;
+  return (size_t)NW * (MMAX * KW * 2 + 16 * (KW / 32) * SZB + XSB) + (size_t)NW * MMAX * 16 * sizeof(float);
 }
 
 // Decode GEMV (used for M == 1).  Workgroup = one 16-row block (x one K split); its NW
@@ -279,7 +322,8 @@ template <int FMT, int MMAX, int TPW, int NW> constexpr size_t gemv_lds_bytes() 
 // another until the final sum.  Per lane and tile: one 16-byte code load,
 // masks into fp16 pairs holding exact (q - z) (one v_and_or_b32 plus one
 // packed add or fma per pair), v_dot2_f32_f16 against fp16 x pairs, the fp32
-// scale once per run of SW codes (32; 16 for q8_0).
+// scale once per run of SW codes (32; 16 for q8_0).  q4k: exact q, then
+// d*sc * (x . q) - dmin*m * sum(x) per 32-code sub-block, all in fp32.
 template <int FMT, int MMAX, int TPW, int NW>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   using F = Fmt<FMT>;
@@ -288,12 +332,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   constexpr int XCH = MMAX * KW / 8;           // 16-byte x chunks per wave
   constexpr int NXC = (XCH + 63) / 64;
   constexpr int NSZ = (16 * GWMAX + 63) / 64;  // (scale, zero) loads per lane, at most
-  constexpr int XB = MMAX * KW * 2, WB = XB + 16 * GWMAX * 4;
+  constexpr int SZB = F::KQ ? 8 : 4;
+  constexpr int XB = MMAX * KW * 2, SB = 16 * GWMAX * SZB;
+  constexpr int WB = XB + SB + (F::KQ ? MMAX * GWMAX * 4 : 0);
   __shared__ __align__(16) uint8_t gemv_smem[gemv_lds_bytes<FMT, MMAX, TPW, NW>()];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f16* xs = reinterpret_cast<f16*>(gemv_smem + wave * WB);                 // [MMAX][KW]
   uint32_t* sz = reinterpret_cast<uint32_t*>(gemv_smem + wave * WB + XB);  // [16][GWMAX] s | z << 16
+  float2* szk = reinterpret_cast<float2*>(gemv_smem + wave * WB + XB);     // q4k: [16][GWMAX] (d*sc, dmin*m)
+  float* xsum = reinterpret_cast<float*>(gemv_smem + wave * WB + XB + SB); // q4k: [MMAX][GWMAX]
   float* red = reinterpret_cast<float*>(gemv_smem + NW * WB);              // [NW][MMAX][16]
 
   const int g = lane >> 4, r = lane & 15;
@@ -313,8 +361,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   //    entries clamped to 0, values masked later): scales and zeros, the
   //    residual, this wave's x slice, then its code tiles.
   const int64_t szbase = (int64_t)rb * 16 * ng * 2;
-  const char* sp = reinterpret_cast<const char*>(a.scales) + szbase;
-  const char* zp = reinterpret_cast<const char*>(F::HAS_Z ? a.zeros : a.scales) + szbase;
+  // q4k: the (d, dmin) pair of each super-block (8 sub-blocks) as 32 bits,
+  // so a row block's pairs start at rb * 16 * (ng / 8) * 4 bytes
+  const char* sp = reinterpret_cast<const char*>(a.scales) + (F::KQ ? szbase / 4 : szbase);
+  const char* zp = reinterpret_cast<const char*>(F::HAS_Z || F::KQ ? a.zeros : a.scales) + szbase;
   uint32_t sraw[NSZ], zraw[NSZ];
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
@@ -322,9 +372,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
     const int er = e >> lgs, eg = gs0 + (e & (gstride - 1));
     const bool ok = e < 16 * gstride && rb * 16 + er < a.N && eg < ng;
     const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
-    sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
-    if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
-    else zraw[j] = F::ZBITS;  // the implicit zero point
+    if constexpr (F::KQ) {
+      sraw[j] = *reinterpret_cast<const uint32_t*>(sp + (ok ? (uint32_t)(er * (ng >> 3) + (eg >> 3)) * 4u : 0u));
+      zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+    } else {
+      sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
+      if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+      else zraw[j] = F::ZBITS;  // the implicit zero point
+    }
   }
   const int om = tid >> 4, orow = tid & 15;
   float res = 0.0f;
@@ -365,11 +420,33 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
     const int e = lane + 64 * j;
-    if (e < 16 * gstride) sz[(e >> lgs) * GWMAX + (e & (gstride - 1))] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+    if (e < 16 * gstride) {
+      const int idx = (e >> lgs) * GWMAX + (e & (gstride - 1));
+      if constexpr (F::KQ) szk[idx] = kq_terms(sraw[j], zraw[j]);
+      else sz[idx] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if constexpr (F::KQ) {
+    // x sum of every 32-wide run of the wave's range (zeros past K), one
+    // lane per (row, run)
+    for (int e = lane; e < MMAX * GWMAX; e += 64) {
+      const h8* xp = reinterpret_cast<const h8*>(xs + (e / GWMAX) * KW + (e % GWMAX) * 32);
+      float v = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const h8 xv = xp[c];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v = __builtin_amdgcn_fdot2(h2{xv[2 * t], xv[2 * t + 1]}, splat((f16)1.0f), v, false);
+      }
+      xsum[e] = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 
   // 3. Dot products, tile by tile and one run of SW codes at a time (a lane
   //    holds 32 INT4, 64 INT2 or 16 q8_0 codes, and a group may be 32 wide):
@@ -383,9 +460,19 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
     if (i < nt) {
 #pragma unroll
       for (int p = 0; p < F::NSEG; ++p) {
-        const uint32_t szv = sz[r * GWMAX + ((i * F::KT + g * F::LS + p * F::SW) >> lg)];
-        const float sf = (float)__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu));
-        const f16 z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
+        const int run = (i * F::KT + g * F::LS + p * F::SW) >> lg;
+        float sf, bk = 0.0f;
+        f16 z;
+        if constexpr (F::KQ) {
+          const float2 t = szk[r * GWMAX + run];
+          sf = t.x;
+          bk = t.y;
+          z = (f16)0.0f;
+        } else {
+          const uint32_t szv = sz[r * GWMAX + run];
+          sf = (float)__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu));
+          z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
+        }
         h2 q[F::SW / 2];
         run_qmz<FMT>(code[i], p, z, q);
 #pragma unroll
@@ -403,6 +490,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
             if (c & 1) A1 = t0; else A0 = t0;
           }
           acc[m] = fmaf(sf, A0 + A1, acc[m]);
+          if constexpr (F::KQ) acc[m] = fmaf(-bk, xsum[m * GWMAX + run], acc[m]);
         }
       }
     }
@@ -480,8 +568,10 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
 
   // 1. every global load first, branch-free: scales/zeros, residual, x, codes
   const int64_t szbase = (int64_t)rb * 16 * ng * 2;
-  const char* sp = reinterpret_cast<const char*>(a.scales) + szbase;
-  const char* zp = reinterpret_cast<const char*>(F::HAS_Z ? a.zeros : a.scales) + szbase;
+  // q4k: the (d, dmin) pair of each super-block (8 sub-blocks) as 32 bits,
+  // so a row block's pairs start at rb * 16 * (ng / 8) * 4 bytes
+  const char* sp = reinterpret_cast<const char*>(a.scales) + (F::KQ ? szbase / 4 : szbase);
+  const char* zp = reinterpret_cast<const char*>(F::HAS_Z || F::KQ ? a.zeros : a.scales) + szbase;
   uint32_t sraw[NSZ], zraw[NSZ];
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
@@ -489,9 +579,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
     const int er = e >> lgs, eg = gs0 + (e & (gstride - 1));
     const bool ok = e < 16 * gstride && rb * 16 + er < a.N && eg < ng;
     const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
-    sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
-    if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
-    else zraw[j] = F::ZBITS;  // the implicit zero point
+    if constexpr (F::KQ) {
+      sraw[j] = *reinterpret_cast<const uint32_t*>(sp + (ok ? (uint32_t)(er * (ng >> 3) + (eg >> 3)) * 4u : 0u));
+      zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+    } else {
+      sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
+      if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+      else zraw[j] = F::ZBITS;  // the implicit zero point
+    }
   }
   float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (a.resid && a.splits == 1 && wave == 0) {
@@ -530,7 +625,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
     const int e = lane + 64 * j;
-    if (e < 16 * gstride) sz[(e >> lgs) * GWMAX + (e & (gstride - 1))] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+    if (e < 16 * gstride)
+      sz[(e >> lgs) * GWMAX + (e & (gstride - 1))] =
+          F::KQ ? kq_half_pair(sraw[j], zraw[j]) : (sraw[j] & 0xffffu) | (zraw[j] << 16);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -547,16 +644,21 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
         const int kl = i * F::KT + g * F::LS + p * F::SW;  // this lane's run inside the wave's range
         const uint32_t szv = sz[r * GWMAX + (kl >> lg)];
         const h2 s2 = splat(__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu)));
-        const f16 z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
+        // q4k: the high half is -fp16(dmin*m), codes are unpacked with zero point 0
+        const f16 z = F::KQ ? (f16)0.0f : __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
         h8 av[F::SW / 8];
 #pragma unroll
         for (int t = 0; t < F::SW / 8; ++t)
           av[t] = arow ? *reinterpret_cast<const h8*>(xs + (arow ? r : 0) * KWP + kl + 8 * t) : h8{};
         h2 q[F::SW / 2];
         run_qmz<FMT>(code[i], p, z, q);
+        if constexpr (F::KQ) kq_weights(q, szv, q, F::SW / 2);   // fma(q, d*sc, -dmin*m)
 #pragma unroll
         for (int t = 0; t < F::SW / 8; ++t) {
-          const h2 w0 = q[4 * t] * s2, w1 = q[4 * t + 1] * s2, w2 = q[4 * t + 2] * s2, w3 = q[4 * t + 3] * s2;
+          h2 w0 = q[4 * t], w1 = q[4 * t + 1], w2 = q[4 * t + 2], w3 = q[4 * t + 3];
+          if constexpr (!F::KQ) {
+            w0 *= s2; w1 *= s2; w2 *= s2; w3 *= s2;
+          }
           const h8 bf = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t], bf, acc, 0, 0, 0);
         }
@@ -710,9 +812,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       const int ec = e >> lgs, eg = e & (gsr - 1);
       const bool ok = ec < GEMM_TN && eg < gwn && n0 + ec < a.N;
       const int64_t off = ok ? ((int64_t)(n0 + ec) * ng + gw0 + eg) : 0;
-      sraw[j] = reinterpret_cast<const uint16_t*>(a.scales)[off];
-      if constexpr (F::HAS_Z) zraw[j] = reinterpret_cast<const uint16_t*>(a.zeros)[off];
-      else zraw[j] = F::ZBITS;  // the implicit zero point
+      if constexpr (F::KQ) {   // (d, dmin) of the super-block, (sc, m) of the sub-block
+        const int64_t soff = ok ? ((int64_t)(n0 + ec) * (ng >> 3) + ((gw0 + eg) >> 3)) : 0;
+        sraw[j] = reinterpret_cast<const uint32_t*>(a.scales)[soff];
+        zraw[j] = reinterpret_cast<const uint16_t*>(a.zeros)[off];
+      } else {
+        sraw[j] = reinterpret_cast<const uint16_t*>(a.scales)[off];
+        if constexpr (F::HAS_Z) zraw[j] = reinterpret_cast<const uint16_t*>(a.zeros)[off];
+        else zraw[j] = F::ZBITS;  // the implicit zero point
+      }
     }
   }
 
@@ -808,12 +916,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the math
     h2 s2[S::CH][2];
     f16 z[S::CH][2];
+    uint32_t kqc[S::CH][2];   // q4k: fp16 (d*sc) | -fp16(dmin*m) << 16, 0 past K
 #pragma unroll
     for (int c = 0; c < S::CH; ++c)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         s2[c][nb] = splat(live[c] ? __builtin_bit_cast(f16, (uint16_t)(szv[c][nb] & 0xffffu)) : (f16)0.0f);
-        z[c][nb] = __builtin_bit_cast(f16, (uint16_t)(szv[c][nb] >> 16));
+        z[c][nb] = F::KQ ? (f16)0.0f : __builtin_bit_cast(f16, (uint16_t)(szv[c][nb] >> 16));
+        kqc[c][nb] = live[c] ? szv[c][nb] : 0u;
       }
     h8 bf[4][2];
 #pragma unroll
@@ -831,8 +941,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
         } else {
           qmz_int4(bt[0][nb][step], make_zc4(z[0][nb]), q);
         }
-        const h2 sc = s2[c][nb];
-        const h2 w0 = q[0] * sc, w1 = q[1] * sc, w2 = q[2] * sc, w3 = q[3] * sc;
+        h2 w0, w1, w2, w3;
+        if constexpr (F::KQ) {
+          h2 wq[4];
+          kq_weights(q, kqc[0][nb], wq, 4);
+          w0 = wq[0]; w1 = wq[1]; w2 = wq[2]; w3 = wq[3];
+        } else {
+          const h2 sc = s2[c][nb];
+          w0 = q[0] * sc; w1 = q[1] * sc; w2 = q[2] * sc; w3 = q[3] * sc;
+        }
         bf[step][nb] = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
       }
 #pragma unroll
@@ -881,7 +998,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   for (int j = 0; j < NSZ; ++j) {
     const int e = tid + NW * 64 * j;
     if (j < nsz && (e >> lgs) < GEMM_TN)
-      szl[(e >> lgs) * GEMM_GCAP + (e & (gsr - 1))] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+      szl[(e >> lgs) * GEMM_GCAP + (e & (gsr - 1))] =
+          F::KQ ? kq_half_pair(sraw[j], zraw[j]) : (sraw[j] & 0xffffu) | (zraw[j] << 16);
   }
   __syncthreads();
 
@@ -1054,11 +1172,22 @@ static void launch_gemv_t(const GemvArgs& a, hipStream_t s) {
 // the x slice of NW * TPW tiles fits the 32 KiB LDS stage.  Returns false when
 // the plan asks for more tiles per wave than that (never, for plans made by
 // make_plan).
+// largest power-of-two tiles per wave (<= GEMV_TPW_MAX) whose x slice fits the
+// x stage and whose whole LDS leaves room for two workgroups per CU
+template <int FMT, int NW> constexpr int gemv_dot_tmax() {
+  constexpr int KT = Fmt<FMT>::KT;
+  int t = GEMV_TPW_MAX;
+  while (t > 1 && (t * NW * KT * 2 > GEMV_LDS_X_BYTES ||
+                   (size_t)NW * (t * KT * 2 + 16 * (t * KT / 32) * (Fmt<FMT>::KQ ? 8 : 4) +
+                                 (Fmt<FMT>::KQ ? t * KT / 32 * 4 : 0)) + (size_t)NW * 16 * 4 > 80 * 1024))
+    t >>= 1;
+  return t;
+}
+
 template <int FMT, int NW>
 static bool launch_gemv_dot_w(const GemvArgs& a, int tps, hipStream_t s) {
-  constexpr int KT = Fmt<FMT>::KT;
-  constexpr int TMAX0 = GEMV_LDS_X_BYTES / (NW * KT * 2);
-  constexpr int TMAX = TMAX0 < GEMV_TPW_MAX ? TMAX0 : GEMV_TPW_MAX;
+  constexpr int TMAX = gemv_dot_tmax<FMT, NW>();
+  static_assert(gemv_lds_bytes<FMT, 1, TMAX, NW>() <= 80 * 1024, "tile cap and LDS size disagree");
   constexpr int T2 = TMAX >= 2 ? 2 : 1, T4 = TMAX >= 4 ? 4 : T2, T8 = TMAX >= 8 ? 8 : T4;
   const int tpw = (tps + NW - 1) / NW;
   if (tpw > TMAX) return false;
@@ -1156,7 +1285,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
     a.y = reinterpret_cast<f16*>(y);
     a.ws = wsf;
     a.ldx = ldx; a.ldr = ldr; a.ldy = ldy;
-    a.M = M; a.N = N; a.K = K; a.group = group;
+    a.M = M; a.N = N; a.K = K; a.group = meta_group(fmt, group);   // q4k: the 32-weight sub-block
     a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.splits = p.splits; a.tps = p.tps;
     // the kernel forms byte offsets of x and of one row block's codes in 32 bits
     if ((int64_t)M * ldx * 2 >= (int64_t)1 << 32 || (int64_t)p.wordtiles * 1024 >= (int64_t)1 << 32 ||
@@ -1167,6 +1296,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
       case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, p.tps, s); break;
       case QG_INT2_ASYM: launched = launch_gemv_f<INT2_ASYM>(a, p.mmax, p.tps, s); break;
       case QG_Q8_0: launched = launch_gemv_f<Q8_0>(a, p.mmax, p.tps, s); break;
+      case QG_Q4K: launched = launch_gemv_f<Q4K>(a, p.mmax, p.tps, s); break;
       default: launched = launch_gemv_f<Q4_0>(a, p.mmax, p.tps, s); break;
     }
     if (!launched) return QG_E_UNSUPPORTED;
@@ -1187,7 +1317,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
   a.y = reinterpret_cast<f16*>(y);
   a.ws = wsf;
   a.ldx = ldx; a.ldr = ldr; a.ldy = ldy;
-  a.M = M; a.N = N; a.K = K; a.group = group;
+  a.M = M; a.N = N; a.K = K; a.group = meta_group(fmt, group);   // q4k: the 32-weight sub-block
   a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.tiles_n = p.tiles_n;
   a.splits = p.splits; a.tps = p.tps;
   // the kernel forms byte offsets of x rows in 32 bits
@@ -1198,6 +1328,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
     case QG_INT4_ASYM: hipLaunchKernelGGL((gemm_kernel<INT4_ASYM, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
     case QG_INT2_ASYM: hipLaunchKernelGGL((gemm_kernel<INT2_ASYM, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
     case QG_Q8_0: hipLaunchKernelGGL((gemm_kernel<Q8_0, NW, GEMM_TPW_Q8, GEMM_DEPTH>), grid, block, 0, s, a); break;
+    case QG_Q4K: hipLaunchKernelGGL((gemm_kernel<Q4K, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
     default: hipLaunchKernelGGL((gemm_kernel<Q4_0, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
   }
   if (p.splits > 1) {
@@ -1288,16 +1419,18 @@ int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* z
   if (total == 0) return QG_OK;
   const int wt = (int)n_wordtiles(K, fmt);
   const int64_t units = n_rowblocks(N) * wt;
+  const int mg = meta_group(fmt, group);
   const dim3 grid((unsigned)ceil_div(units, 4)), block(256);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const f16* sc = reinterpret_cast<const f16*>(scales);
   const f16* zp = reinterpret_cast<const f16*>(zeros);
   f16* wo = reinterpret_cast<f16*>(w);
   switch (fmt) {
-    case QG_INT4_ASYM: hipLaunchKernelGGL(dequant_kernel<INT4_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
-    case QG_INT2_ASYM: hipLaunchKernelGGL(dequant_kernel<INT2_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
-    case QG_Q8_0: hipLaunchKernelGGL(dequant_kernel<Q8_0>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
-    default: hipLaunchKernelGGL(dequant_kernel<Q4_0>, grid, block, 0, s, packed, sc, zp, wo, N, K, group, wt, units); break;
+    case QG_INT4_ASYM: hipLaunchKernelGGL(dequant_kernel<INT4_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, mg, wt, units); break;
+    case QG_INT2_ASYM: hipLaunchKernelGGL(dequant_kernel<INT2_ASYM>, grid, block, 0, s, packed, sc, zp, wo, N, K, mg, wt, units); break;
+    case QG_Q8_0: hipLaunchKernelGGL(dequant_kernel<Q8_0>, grid, block, 0, s, packed, sc, zp, wo, N, K, mg, wt, units); break;
+    case QG_Q4K: hipLaunchKernelGGL(dequant_kernel<Q4K>, grid, block, 0, s, packed, sc, zp, wo, N, K, mg, wt, units); break;
+    default: hipLaunchKernelGGL(dequant_kernel<Q4_0>, grid, block, 0, s, packed, sc, zp, wo, N, K, mg, wt, units); break;
   }
   return launch_status();
 }

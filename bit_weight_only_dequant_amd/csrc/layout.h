@@ -24,10 +24,10 @@
 
 namespace qg {
 
-enum Format { INT4_ASYM = 0, INT2_ASYM = 1, Q4_0 = 2, Q8_0 = 3 };
+enum Format { INT4_ASYM = 0, INT2_ASYM = 1, Q4_0 = 2, Q8_0 = 3, Q4K = 4 };
 
 QG_HD int bits_of(int fmt) { return fmt == INT2_ASYM ? 2 : fmt == Q8_0 ? 8 : 4; }
-QG_HD bool valid_format(int fmt) { return fmt >= INT4_ASYM && fmt <= Q8_0; }
+QG_HD bool valid_format(int fmt) { return fmt >= INT4_ASYM && fmt <= Q4K; }
 // block formats with an implicit zero point (no zeros array)
 QG_HD bool symmetric_format(int fmt) { return fmt == Q4_0 || fmt == Q8_0; }
 QG_HD int cpw_of(int fmt) { return 32 / bits_of(fmt); }
@@ -38,6 +38,9 @@ QG_HD int64_t n_rowblocks(int64_t N) { return ceil_div(N, 16); }
 QG_HD int64_t n_wordtiles(int64_t K, int fmt) { return ceil_div(K / cpw_of(fmt), 16); }
 // K covered by one word tile: 16 words of cpw codes (128 for 4-bit, 256 for
 // 2-bit, 64 for 8-bit)
+// K covered by one scale/offset entry as the kernels see it: the group, or
+// for q4k the 32-weight sub-block (its super-block of 256 holds 8)
+QG_HD int meta_group(int fmt, int group) { return fmt == Q4K ? 32 : group; }
 QG_HD int ktile_width(int fmt) { return 16 * cpw_of(fmt); }
 
 // packed word index of canonical word (n, kw)

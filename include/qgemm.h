@@ -15,9 +15,13 @@
  *     (q4_0 of the torchnative guide "Inference with real transformers",
  *     section "Quantise while loading"), codes stored offset-binary u = q + 8;
  *   - QG_Q8_0: the 8-bit sibling of q4_0 named in the same section: blocks of
- *     32, one fp16 scale, signed 8-bit codes stored offset-binary u = q + 128.
- * For every format  w[n,k] = s[n, k/group] * (q[n,k] - z[n, k/group])  with
- * z == 8 for q4_0, z == 128 for q8_0, and  y[m,n] = sum_k x[m,k] * w[n,k].
+ *     32, one fp16 scale, signed 8-bit codes stored offset-binary u = q + 128;
+ *   - QG_Q4K: the 4-bit k-quant named in the same section (widths divisible
+ *     by 256), read as super-blocks of 256 weights with fp16 factors (d, dmin)
+ *     and sub-blocks of 32 with 6-bit integers (sc, m):
+ *     w = d * sc * q - dmin * m, q in 0..15.
+ * For the group formats  w[n,k] = s[n, k/group] * (q[n,k] - z[n, k/group])
+ * with z == 8 for q4_0 and z == 128 for q8_0; y[m,n] = sum_k x[m,k] * w[n,k].
  *
  * Conventions shared by every entry point
  *   - Pointers named "device" are device memory (hipMalloc or torch tensors on
@@ -25,18 +29,21 @@
  *     Outputs are caller-allocated and written in place.
  *   - fp16 buffers are passed as uint16_t (IEEE binary16 bit patterns).
  *   - Matrices are row-major.  W is [N, K]: groups run along K in one row n.
- *   - Canonical words: uint32 [N, K/cpw], cpw = 8 (INT4, q4_0), 16 (INT2) or
- *     4 (q8_0);
+ *   - Canonical words: uint32 [N, K/cpw], cpw = 8 (INT4, q4_0, q4k), 16 (INT2)
+ *     or 4 (q8_0);
  *     code k of row n sits at bits [b*(k%cpw), b*(k%cpw)+b) of word k/cpw.
  *   - Scales (and zero points) are fp16 [N, K/group], canonical.  Zero points
  *     hold integers in [0, 2^b - 1]; other values give unspecified results.
+ *     QG_Q4K (group = 256) instead takes scales = fp16 [N, K/256, 2], the
+ *     pair (d, dmin) of each super-block, and zeros = uint16 [N, K/32], sc in
+ *     the low byte and m in the high byte of each sub-block (both < 64).
  *   - "stream" is a hipStream_t (NULL = the default stream).  Every device
  *     call is stream-ordered and asynchronous: QG_OK means "validated and
  *     launched"; a kernel fault is reported by the caller's next sync.
  *   - Arguments are validated on the host before any HIP call.  On error the
  *     function returns a status and launches nothing; nothing aborts or prints.
  *   - Shapes: group in {32, 64, 128} for INT4/INT2, group == 32 for q4_0 and
- *     q8_0;
+ *     q8_0, group == 256 for q4k;
  *     K % group == 0; M, N, K >= 0.  Any N and any M are accepted.
  *   - Device pointers to x, packed, scales, zeros, y and residual must be
  *     16-byte aligned; leading dimensions must be multiples of 8 elements.
@@ -59,7 +66,8 @@ typedef enum {
   QG_INT4_ASYM = 0,
   QG_INT2_ASYM = 1,
   QG_Q4_0 = 2,
-  QG_Q8_0 = 3
+  QG_Q8_0 = 3,
+  QG_Q4K = 4
 } qg_format_t;
 
 typedef enum {
@@ -118,7 +126,8 @@ int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt)
  *   packed [device, in]  qpack output for W [N, K].
  *   scales [device, in]  fp16 [N, K/group].
  *   zeros  [device, in]  fp16 [N, K/group]; must be NULL for QG_Q4_0 and
- *                        QG_Q8_0 and non-NULL for the asymmetric formats.
+ *                        QG_Q8_0 and non-NULL for the asymmetric formats
+ *                        (QG_Q4K: the (sc, m) bytes, see above).
  *   y      [device, out] fp16 [M, N], row-major, leading dimension N.
  * M == 1 runs the decode GEMV (packed-fp16 dequant, fp32 dot products);
  * 2 <= M <= 16 the decode GEMV on 16 x 16 matrix-core blocks; M > 16 the
@@ -180,7 +189,9 @@ int qg_unpack_codes(const uint32_t* packed, uint8_t* codes, int N, int K, int fm
                     void* stream);
 
 /* Debug: packed + scales + zeros -> fp16 w [N, K] (device) through the same
- * device dequant the GEMM uses: fp16_rne(s * (q - z)).  Errors as qgemm. */
+ * device dequant the GEMM uses: fp16_rne(s * (q - z)); for QG_Q4K
+ * fp16_rne(fp16_rne(d*sc) * q - fp16_rne(dmin*m)) (one fused multiply-add).
+ * Errors as qgemm. */
 int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros,
                uint16_t* w, int N, int K, int group, int fmt, void* stream);
 

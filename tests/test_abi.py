@@ -51,7 +51,10 @@ def qgemm_status(x=A, packed=A, scales=A, zeros=A, M=1, N=16, K=128, group=32, f
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(fmt=4), E_ARG),
+    (dict(fmt=5), E_ARG),
+    (dict(fmt=4, group=128), E_ARG),                 # q4k: super-blocks of 256
+    (dict(fmt=4, group=256, K=384), E_ARG),          # K % 256
+    (dict(fmt=4, group=256, K=256, zeros=None), E_ARG),   # q4k needs its (sc, m) bytes
     (dict(fmt=-1), E_ARG),
     (dict(group=48), E_ARG),
     (dict(group=256), E_ARG),
@@ -105,7 +108,8 @@ def test_status_strings():
 @pytest.mark.parametrize("N,K,fmt,expect", [
     (16, 128, 0, 1024), (17, 128, 0, 2048), (16, 136, 0, 2048), (6144, 2048, 0, 6291456),
     (8192, 2048, 1, 4194304), (8192, 2048, 2, 8388608), (0, 128, 0, 0), (16, 100, 0, 0),
-    (16, 128, 5, 0), (8192, 2048, 3, 16777216), (16, 96, 3, 2048), (16, 98, 3, 0)])
+    (16, 128, 5, 0), (8192, 2048, 3, 16777216), (16, 96, 3, 2048), (16, 98, 3, 0),
+    (8192, 2048, 4, 8388608)])
 def test_packed_bytes(N, K, fmt, expect):
     assert qgm.packed_bytes(N, K, fmt) == expect
 
@@ -129,9 +133,10 @@ def decode_packed_by_formula(packed, N, K, fmt):
 
 
 @pytest.mark.parametrize("fmt,N,K", [(0, 16, 128), (0, 37, 96), (1, 20, 256), (1, 33, 160),
-                                     (2, 48, 64), (0, 5, 384), (3, 16, 64), (3, 37, 96), (3, 20, 160)])
+                                     (2, 48, 64), (0, 5, 384), (3, 16, 64), (3, 37, 96), (3, 20, 160),
+                                     (4, 21, 512)])
 def test_host_qpack_layout_and_roundtrip(fmt, N, K):
-    c = synth.random_codes_case(N * 7 + K + fmt, fmt, 32, N, K, 1)
+    c = synth.random_codes_case(N * 7 + K + fmt, fmt, 256 if fmt == 4 else 32, N, K, 1)
     packed = qgm.qpack_host(c.words, N, K, fmt)
     assert packed.nbytes == qgm.packed_bytes(N, K, fmt)
     assert np.array_equal(decode_packed_by_formula(packed, N, K, fmt),
@@ -163,3 +168,7 @@ def test_plans_for_the_workloads():
     q = qgm.plan(128, 8192, 2048, 32, 3)
     assert q["path"] == "gemm" and q["splits"] == 1
     assert qgm.plan(1, 6144, 2048, 32, 3)["path"] == "gemv"
+    # q4k: 4-bit tiles; its metadata comes per 32-weight sub-block
+    k = qgm.plan(128, 8192, 2048, 256, 4)
+    assert k["path"] == "gemm" and k["splits"] == 1
+    assert qgm.plan(1, 8192, 2048, 256, 4)["path"] == "gemv"

@@ -65,7 +65,7 @@ def _clean_env(monkeypatch):
 @pytest.mark.parametrize("fmt,group,N,K", [(0, 32, 256, 256), (0, 128, 6144, 2048), (1, 64, 8192, 2048),
                                            (2, 32, 8192, 2048), (0, 32, 37, 96), (1, 32, 50, 160),
                                            (2, 32, 3, 32), (3, 32, 8192, 2048), (3, 32, 37, 96),
-                                           (3, 32, 5, 32)])
+                                           (3, 32, 5, 32), (4, 256, 512, 2048), (4, 256, 17, 256)])
 def test_repack_and_codes_bit_exact(fmt, group, N, K):
     say(f"repack fmt={fmt} N={N} K={K}")
     c = synth.random_codes_case(N + K + fmt, fmt, group, N, K, 1)
@@ -98,7 +98,8 @@ def test_dequant_bit_exact(fmt, group, N, K):
 
 WL = [("tiny_int4_g32", 1), ("tiny_int4_g32", 4), ("decode_int4_g128", 1), ("decode_int4_g128", 8),
       ("prefill_int4_g128", 128), ("int2_g64", 1), ("int2_g64", 128), ("q4_0_b32", 1), ("q4_0_b32", 128),
-      ("q8_0_b32", 1), ("q8_0_b32", 8), ("q8_0_b32", 128)]
+      ("q8_0_b32", 1), ("q8_0_b32", 8), ("q8_0_b32", 128), ("q4k_s256", 1), ("q4k_s256", 8),
+      ("q4k_s256", 128)]
 
 _cases = {}
 
@@ -146,6 +147,10 @@ RAGGED = [
     (3, 32, 16, 32, 1), (3, 32, 100, 96, 3), (3, 32, 33, 224, 4), (3, 32, 130, 160, 12),
     (3, 32, 72, 544, 17), (3, 32, 300, 2048, 129), (3, 32, 520, 1056, 257), (3, 32, 1000, 4096, 64),
     (3, 32, 48, 8192, 8), (3, 32, 40, 8224, 1), (3, 32, 64, 96, 100),
+    # q4k: K a multiple of 256
+    (4, 256, 16, 256, 1), (4, 256, 100, 512, 3), (4, 256, 33, 768, 12), (4, 256, 130, 1280, 17),
+    (4, 256, 300, 2048, 129), (4, 256, 520, 4352, 257), (4, 256, 48, 8192, 8), (4, 256, 40, 8192, 1),
+    (4, 256, 64, 256, 100), (4, 256, 1000, 4096, 64),
 ]
 
 
@@ -158,7 +163,7 @@ def test_ragged_parity(fmt, group, N, K, M):
 
 
 @pytest.mark.parametrize("force,M", [("gemm", 1), ("gemm", 4), ("gemm", 8), ("gemv", 3)])
-@pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32), (3, 32)])
+@pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32), (3, 32), (4, 256)])
 def test_forced_path(monkeypatch, force, M, fmt, group):
     monkeypatch.setenv("QGEMM_FORCE", force)
     N, K = 272, 1024
@@ -177,6 +182,62 @@ def test_split_k_variants(monkeypatch, splits, M):
     c = synth.random_codes_case(splits * 100 + M, fmt, group, N, K, M)
     lin = qgm.QuantLinear.from_case(c, DEV)
     check_close(run_gemm(lin, c.x), ref_y(c, c.x), f"splitk {splits}")
+
+
+# ----------------------------------------------------------------------------
+# q4k: the fp16 weight of the matrix-core paths, bit for bit and against the
+# oracle's exact weight
+# ----------------------------------------------------------------------------
+
+def q4k_fp16_weight(c):
+    """fp16(fp16(d*sc) * q - fp16(dmin*m)) with one rounding of the fused
+    multiply-add: the documented dequant of the matrix-core paths, restated
+    here in NumPy (fp32 products are exact, fp64 holds the fma exactly)."""
+    N, K = c.N, c.K
+    ds = c.scales.reshape(N, K // 256, 2).astype(np.float32)
+    sc = (c.zeros & 0xFF).astype(np.float32)
+    m = (c.zeros >> 8).astype(np.float32)
+    sup = np.arange(K // 32) // 8
+    dsc = (ds[:, sup, 0] * sc).astype(np.float16).astype(np.float64)
+    nb = (-(ds[:, sup, 1] * m)).astype(np.float16).astype(np.float64)
+    idx = np.arange(K) // 32
+    return (dsc[:, idx] * c.codes.astype(np.float64) + nb[:, idx]).astype(np.float16)
+
+
+@pytest.mark.parametrize("N,K", [(256, 2048), (40, 512)])
+def test_q4k_dequant(N, K):
+    say(f"q4k dequant N={N} K={K}")
+    c = synth.random_codes_case(N + K, 4, 256, N, K, 1)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    got = qgm.dequant(lin.packed, lin.scales, lin.zeros, N, K, 256, 4).cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), q4k_fp16_weight(c).view(np.uint16))
+    # against the exact weight: one fp16 rounding of the result, of fp16(d*sc)
+    # (times q <= 15) and of fp16(dmin*m)
+    w = oracle.dequant_f64(c.words, c.scales, c.zeros, N, K, 256, 4)
+    s, b = oracle.q4k_subblock_params(c.scales, c.zeros, N, K)
+    idx = np.arange(K) // 32
+    ulp = lambda v: np.spacing(np.abs(v).astype(np.float16)).astype(np.float64)
+    bound = 0.5 * ulp(got) + 0.5 * 15 * ulp(s[:, idx]) + 0.5 * ulp(b[:, idx])
+    assert np.all(np.abs(got.astype(np.float64) - w) <= bound * (1 + 1e-9))
+
+
+@pytest.mark.parametrize("M", [1, 5, 64])
+def test_q4k_one_hot_bit_exact(M):
+    # x = e_k picks column k: M = 1 (fp32 terms) gives fp16(fp32(w)); the
+    # matrix-core paths give the fp16 weight above
+    N, K = 144, 512
+    say(f"q4k one-hot M={M}")
+    c = synth.random_codes_case(M * 5 + 3, 4, 256, N, K, 1)
+    ks = np.random.default_rng(M).integers(0, K, size=M)
+    x = np.zeros((M, K), np.float16)
+    x[np.arange(M), ks] = 1.0
+    y = run_gemm(qgm.QuantLinear.from_case(c, DEV), x)
+    if M == 1:
+        w = oracle.dequant_f64(c.words, c.scales, c.zeros, N, K, 256, 4)
+        expect = w[:, ks].T.astype(np.float32).astype(np.float16)
+    else:
+        expect = q4k_fp16_weight(c)[:, ks].T
+    assert np.array_equal(y.view(np.uint16), expect.view(np.uint16))
 
 
 # ----------------------------------------------------------------------------
