@@ -1062,33 +1062,30 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 }
 
 // Sums a 64 x 64 tile's split partials in split order (deterministic), adds
-// the residual and rounds once to fp16.  One workgroup of 4 waves per tile;
-// wave w owns block w in the GEMM's accumulator layout.
+// the residual and rounds once to fp16.  One workgroup of 4 waves per 32 x 32
+// block fb of the tile (grid: column tile, row tile, block), so the partials
+// are read by 4 workgroups per tile; wave q owns quad q of the block in the
+// GEMM's accumulator layout, 4 outputs per lane.
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
-  const int tn = blockIdx.x, tm = blockIdx.y, tid = threadIdx.x, lane = tid & 63, fb = tid >> 6;
+  const int tn = blockIdx.x, tm = blockIdx.y, fb = blockIdx.z;
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m0 = tm * GEMM_TM, n0 = tn * GEMM_TN;
   const int64_t tile = (int64_t)tm * a.tiles_n + tn;
   const f4* wsp = reinterpret_cast<const f4*>(a.ws);
   const int col = n0 + (fb & 1) * 32 + (lane & 31);
   const int colc = min(col, a.N - 1);
-  float res[16];
+  float res[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = min(m0 + (fb >> 1) * 32 + acc_row(i, lane), a.M - 1);
-    res[i] = a.resid ? (float)a.resid[(int64_t)row * a.ldr + colc] : 0.0f;
+  for (int e = 0; e < 4; ++e) {
+    const int row = min(m0 + (fb >> 1) * 32 + acc_row(4 * q + e, lane), a.M - 1);
+    res[e] = a.resid ? (float)a.resid[(int64_t)row * a.ldr + colc] : 0.0f;
   }
-  f4 sum[4];
+  f4 sum = f4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.splits; ++s) sum += wsp[(((tile * a.splits + s) * 4 + fb) * 4 + q) * 64 + lane];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) sum[q] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.splits; ++s) {
-    const int64_t base = ((tile * a.splits + s) * 4 + fb) * 4;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sum[q] += wsp[(base + q) * 64 + lane];
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = m0 + (fb >> 1) * 32 + acc_row(i, lane);
-    if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(sum[i >> 2][i & 3] + res[i]);
+  for (int e = 0; e < 4; ++e) {
+    const int row = m0 + (fb >> 1) * 32 + acc_row(4 * q + e, lane);
+    if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(sum[e] + res[e]);
   }
 }
 
@@ -1334,7 +1331,7 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
   if (p.splits > 1) {
     st = launch_status();
     if (st != QG_OK) return st;
-    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 4), dim3(256), 0, s, a);
   }
   return launch_status();
 }
