@@ -204,21 +204,22 @@ def fold_zero_point_ref(x, words, scales, zeros, M, N, K, group):
 
 def loop_block_ref(x0, lin, L: int, D: int = 2048):
     """Run the oracle's own chain.  ``lin`` is a list of 4 dicts with keys
-    words, scales, zeros, N, K, group (QKV, O, up, down).  Returns the list of
-    fp16 block outputs x_1..x_L."""
+    words, scales, zeros, N, K, group and optionally fmt (default INT4_ASYM)
+    for QKV, O, up, down.  Returns the list of fp16 block outputs x_1..x_L."""
     x = np.asarray(x0, dtype=np.float16)
     M = x.shape[0]
     outs = []
+
+    def lin_ref(a, l, residual=None):
+        return qgemm_ref(a, l["words"], l["scales"], l["zeros"], M, l["N"], l["K"], l["group"],
+                         l.get("fmt", INT4_ASYM), residual=residual).astype(np.float16)
+
     for _ in range(L):
         qkv, o, up, down = lin
-        y_qkv = qgemm_ref(x, qkv["words"], qkv["scales"], qkv["zeros"], M,
-                          qkv["N"], qkv["K"], qkv["group"], INT4_ASYM).astype(np.float16)
+        y_qkv = lin_ref(x, qkv)
         v = y_qkv[:, 2 * D:3 * D]
-        h = qgemm_ref(v, o["words"], o["scales"], o["zeros"], M, o["N"], o["K"],
-                      o["group"], INT4_ASYM, residual=x).astype(np.float16)
-        u = qgemm_ref(h, up["words"], up["scales"], up["zeros"], M, up["N"], up["K"],
-                      up["group"], INT4_ASYM).astype(np.float16)
-        x = qgemm_ref(u, down["words"], down["scales"], down["zeros"], M, down["N"],
-                      down["K"], down["group"], INT4_ASYM, residual=h).astype(np.float16)
+        h = lin_ref(v, o, residual=x)
+        u = lin_ref(h, up)
+        x = lin_ref(u, down, residual=h)
         outs.append(x)
     return outs

@@ -368,6 +368,34 @@ def pin_q4k_matches_int4_g32(O):
     assert np.array_equal(a, b)
 
 
+def exact_loop_linears(D):
+    """INT4 g32 weights with s = 1, z = 1, so w = q - 1 in {-1, 0, 1} exactly:
+    QKV = [0; -I; +I] (Q zero, K = -x, V = x), O = I, up = [I; -I] (F = 2D),
+    down = [I, 0].  One loop maps x to h = x + V = 2x and then to
+    h + down(up(h)) = 2h = 4x; any other slice of QKV, a missing residual or a
+    transposed operand gives something else."""
+    I = np.eye(D, dtype=np.int64)
+    Z = np.zeros((D, D), dtype=np.int64)
+    mats = [np.vstack([Z, -I, I]), I, np.vstack([I, -I]), np.hstack([I, Z])]
+    lins = []
+    for w in mats:
+        N, K = w.shape
+        codes = (w + 1).astype(np.uint8)
+        lins.append(dict(words=pack_literal(codes, 4), scales=np.ones((N, K // 32), np.float16),
+                         zeros=np.ones((N, K // 32), np.float16), N=N, K=K, group=32, fmt=0))
+    return lins
+
+
+def pin_loop_block_closed_form(O):
+    D, M, L = 64, 3, 3
+    x0 = (np.random.default_rng(9).integers(-8, 9, size=(M, D)) / 8.0).astype(np.float16)
+    outs = O.loop_block_ref(x0, exact_loop_linears(D), L, D=D)
+    assert len(outs) == L
+    for l, xl in enumerate(outs):
+        assert xl.dtype == np.float16 and xl.shape == (M, D)
+        assert np.array_equal(xl.astype(np.float64), x0.astype(np.float64) * 4.0 ** (l + 1)), l
+
+
 def pin_tolerance_rule(O):
     ref = np.array([[1.0, -4.0], [2.0, 0.5]])
     tol = O.TOLERANCE
@@ -387,7 +415,7 @@ def pin_tolerance_rule(O):
 ALL_PINS = [pin_worked_words, pin_handcases, pin_zero_codes_closed_form, pin_one_hot,
             pin_format_identity, pin_bruteforce, pin_exact_rational, pin_dequant_exact,
             pin_fold_identity, pin_tolerance_rule, pin_q4k_handcases, pin_q4k_bruteforce_and_exact,
-            pin_q4k_one_hot_and_zero_codes, pin_q4k_matches_int4_g32]
+            pin_q4k_one_hot_and_zero_codes, pin_q4k_matches_int4_g32, pin_loop_block_closed_form]
 
 
 def failing_pins(O):

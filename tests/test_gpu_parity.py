@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import synth
+from tests import pins
 
 pytestmark = pytest.mark.gpu
 
@@ -416,6 +417,56 @@ def test_graph_replays_match_eager(name, M):
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
         assert torch.equal(other.view(torch.int16), eager.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------
+# looped shared block: qloop_block against the oracle's chain
+# ----------------------------------------------------------------------------
+
+def _loop_lin_dicts(cases):
+    return [dict(words=c.words, scales=c.scales, zeros=c.zeros, N=c.N, K=c.K, group=c.group, fmt=c.fmt)
+            for c in cases]
+
+
+@pytest.mark.parametrize("fmt,group,M", [(0, 128, 1), (0, 128, 8), (0, 128, 40), (1, 64, 1), (2, 32, 40),
+                                         (3, 32, 8), (4, 256, 40), (4, 256, 1)])
+def test_loop_block_parity(fmt, group, M):
+    D, F, L = 256, 512, 3
+    say(f"loop fmt={fmt} g={group} M={M} D={D} F={F} L={L}")
+    cases = [synth.random_case(4000 + 10 * fmt + i, fmt, group, N, K, 1)
+             for i, (N, K) in enumerate(((3 * D, D), (D, D), (F, D), (D, F)))]
+    x0 = synth.draw_x(np.random.default_rng(4100 + M), M, D)
+    lins = [qgm.QuantLinear.from_case(c, DEV) for c in cases]
+    x = dev_half(x0)
+    qgm.loop_block(x, lins, L)
+    torch.cuda.synchronize()
+    ref = oracle.loop_block_ref(x0, _loop_lin_dicts(cases), L, D=D)
+    check_close(x.cpu().numpy(), ref[-1], f"loop x_{L}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 40])
+def test_loop_block_exact_chain(M):
+    # exact weights (see tests/pins.exact_loop_linears): every loop is x -> 4x
+    D, L = 64, 3
+    x0 = (np.random.default_rng(M).integers(-8, 9, size=(M, D)) / 8.0).astype(np.float16)
+    lins = [qgm.QuantLinear(l["words"], l["scales"], l["zeros"], l["N"], l["K"], l["group"], l["fmt"], DEV)
+            for l in pins.exact_loop_linears(D)]
+    x = dev_half(x0)
+    qgm.loop_block(x, lins, L)
+    torch.cuda.synchronize()
+    assert np.array_equal(x.cpu().numpy().astype(np.float64), x0.astype(np.float64) * 4.0 ** L)
+
+
+def test_loop_block_full_size():
+    # the benchmark's block: D = 2048, F = 8192, M = 128, INT4 g128, all 8 loops
+    lc = synth.loop_workload(M=128, L=8)
+    say("loop full size M=128 D=2048 F=8192 L=8")
+    lins = [qgm.QuantLinear.from_case(c, DEV) for c in lc.linears()]
+    x = dev_half(lc.x0)
+    qgm.loop_block(x, lins, lc.L)
+    torch.cuda.synchronize()
+    ref = oracle.loop_block_ref(lc.x0, _loop_lin_dicts(lc.linears()), lc.L)
+    check_close(x.cpu().numpy(), ref[-1], "loop x_8 full size")
 
 
 def test_dequant_into_caller_buffer_feeds_an_fp16_gemm():

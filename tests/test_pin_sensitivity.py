@@ -132,6 +132,33 @@ def _deq_q4k_dmin_for_d(words, scales, zeros, N, K, group, fmt):
     return s[:, np.arange(K) // 32] * q - b[:, np.arange(K) // 32]
 
 
+def _loop_wrong_slice(x0, lin, L, D=2048):
+    # O consumes the K third instead of V
+    x = np.asarray(x0, np.float16)
+    M, outs = x.shape[0], []
+    f = lambda a, l, r=None: _orig_gemm(a, l["words"], l["scales"], l["zeros"], M, l["N"], l["K"],
+                                       l["group"], l.get("fmt", 0), residual=r).astype(np.float16)
+    for _ in range(L):
+        qkv, o, up, down = lin
+        h = f(f(x, qkv)[:, D:2 * D], o, x)
+        x = f(f(h, up), down, h)
+        outs.append(x)
+    return outs
+
+
+def _loop_no_second_residual(x0, lin, L, D=2048):
+    x = np.asarray(x0, np.float16)
+    M, outs = x.shape[0], []
+    f = lambda a, l, r=None: _orig_gemm(a, l["words"], l["scales"], l["zeros"], M, l["N"], l["K"],
+                                       l["group"], l.get("fmt", 0), residual=r).astype(np.float16)
+    for _ in range(L):
+        qkv, o, up, down = lin
+        h = f(f(x, qkv)[:, 2 * D:3 * D], o, x)
+        x = f(f(h, up), down)
+        outs.append(x)
+    return outs
+
+
 MUTANTS = {
     "unpack_msb_first": [("unpack_codes", _unpack_msb_first), ("pack_codes", _pack_msb_first)],
     "dequant_sign": [("dequant_f64", _keep_q4k(_deq_sign))],
@@ -142,6 +169,8 @@ MUTANTS = {
     "q8_0_offset_127": [("dequant_f64", _keep_q4k(_deq_q80_offset127))],
     "q8_0_seven_bit_mask": [("unpack_codes", _unpack_q80_low7)],
     "q4k_dropped_offset": [("dequant_f64", _deq_q4k_no_offset)],
+    "loop_wrong_slice": [("loop_block_ref", _loop_wrong_slice)],
+    "loop_no_second_residual": [("loop_block_ref", _loop_no_second_residual)],
     "q4k_swapped_bytes": [("dequant_f64", _deq_q4k_swapped_bytes)],
     "q4k_wrong_super_block": [("dequant_f64", _deq_q4k_super_index)],
     "q4k_d_dmin_exchanged": [("dequant_f64", _deq_q4k_dmin_for_d)],
@@ -154,7 +183,8 @@ MUTANTS = {
 def test_mutant_is_caught(name, monkeypatch):
     for attr, fn in MUTANTS[name]:
         monkeypatch.setattr(qref, attr, fn)
-    bad = pins.failing_pins(qref)
+    with np.errstate(all="ignore"):   # some mutants overflow fp16 on purpose
+        bad = pins.failing_pins(qref)
     assert bad, f"planted mistake {name} passed every pin"
 
 
