@@ -318,7 +318,7 @@ def test_block_format_zero_code_is_zero(fmt, u, bits):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,M", [("prefill_int4_g128", 128), ("decode_int4_g128", 1),
-                                    ("int2_g64", 128)])
+                                    ("int2_g64", 128), ("q4k_s256", 8)])
 def test_deterministic(name, M):
     c, lin = get_case(name)
     x = dev_half(c.x[:M])
@@ -344,9 +344,10 @@ def test_no_writes_outside_output(M):
 
 
 @pytest.mark.parametrize("M", [1, 8, 64])
-def test_residual_and_strided_input(M):
-    N, K, group = 256, 1024, 128
-    c = synth.random_codes_case(M + 77, 0, group, N, K, M)
+@pytest.mark.parametrize("fmt,group", [(0, 128), (3, 32), (4, 256)])
+def test_residual_and_strided_input(M, fmt, group):
+    N, K = 256, 1024
+    c = synth.random_codes_case(M + 77 + fmt, fmt, group, N, K, M)
     lin = qgm.QuantLinear.from_case(c, DEV)
     wide = np.random.default_rng(1).standard_normal((M, K + 64)).astype(np.float16)
     wide[:, 32:32 + K] = c.x
@@ -396,7 +397,8 @@ def test_k_zero_writes_zeros():
     assert torch.count_nonzero(y).item() == 0
 
 
-@pytest.mark.parametrize("name,M", [("decode_int4_g128", 1), ("prefill_int4_g128", 128), ("int2_g64", 8)])
+@pytest.mark.parametrize("name,M", [("decode_int4_g128", 1), ("prefill_int4_g128", 128), ("int2_g64", 8),
+                                    ("q8_0_b32", 1), ("q4k_s256", 1), ("q4k_s256", 128)])
 def test_graph_replays_match_eager(name, M):
     # the benchmark captures calls in a HIP graph: every replay, with eager
     # work and synchronisation in between, must equal the eager result
