@@ -16,18 +16,21 @@
 //                        lane per 16x16-word tile, unpack by mask into fp16
 //                        pairs holding exact (q - z), v_dot2_f32_f16 against x
 //                        that each wave stages for itself in LDS, fp32 scale
-//                        per group, lane groups summed by lane shuffles and
-//                        waves through LDS.
-//   gemv_mfma<FMT, R>    2 <= M <= 16.  Same loads and staging; each packed
-//                        word, dequantized to fp16 s*(q-z), is one
+//                        per 32 codes (q8_0: 16; q4k: d*sc and the offset
+//                        dmin*m times the run's x sum), lane groups summed by
+//                        lane shuffles and waves through LDS.
+//   gemv_mfma<FMT, R>    2 <= M <= 16.  Same loads and staging; every 8 codes,
+//                        dequantized to fp16 weights, are one
 //                        v_mfma_f32_16x16x32_f16 step (the packed layout is
 //                        that MFMA's B operand), so the VALU work per code
 //                        does not grow with M.
 //   gemm<FMT>            M > 16.  64x64 workgroup tile; 8 waves split K and
 //                        are summed through LDS.  x and codes stream into
 //                        per-wave LDS rings with direct loads; codes are
-//                        dequantized once per workgroup to fp16 s*(q-z) in
+//                        dequantized once per workgroup to fp16 weights in
 //                        registers and fed to v_mfma_f32_32x32x16_f16.
+//   dequant<FMT>         the same fp16 weights written out (debug, and the
+//                        dequantize-at-load comparison).
 //   Split-K (both)       fp32 partials in a workspace, summed in split order by a
 //                        second small kernel (deterministic).  A kernel boundary
 //                        orders the partials; an in-kernel device-scope fence
@@ -160,7 +163,7 @@ __device__ __forceinline__ uint32_t kq_half_pair(uint32_t ddm, uint32_t scm) {
   const uint32_t nb = __builtin_bit_cast(uint16_t, (f16)(-t.y));
   return ds | (nb << 16);
 }
-// fp16 q4k weights of 4 pairs of exact codes: fma(q, ds, nb), one rounding
+// fp16 q4k weights of n pairs of exact codes: fma(q, ds, nb), one rounding
 __device__ __forceinline__ void kq_weights(const h2* q, uint32_t dsnb, h2* w, int n) {
   const h2 ds = splat(__builtin_bit_cast(f16, (uint16_t)(dsnb & 0xffffu)));
   const h2 nb = splat(__builtin_bit_cast(f16, (uint16_t)(dsnb >> 16)));
@@ -232,7 +235,7 @@ __global__ void unpack_codes_kernel(const uint32_t* __restrict__ packed, uint8_t
 
 // Dequantized weights written out (fp16 [N, K]), with the GEMM's register
 // dequant: one wave per (row block, word tile), so each wave reads 1 KiB of
-// codes contiguously; lane (g, r) turns its 16-byte chunk into 32 (INT4), 64
+// codes contiguously; lane (g, r) turns its 16-byte chunk into 32 (4-bit), 64
 // (INT2) or 16 (q8_0) weights of row 16*rb + r and stores them contiguously.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ packed,
@@ -309,11 +312,14 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
 // LDS bytes of gemv_kernel: per wave its x slice, (scale, zero) pairs (q4k:
 // fp32 (d*sc, dmin*m)) and, for q4k, the x sum of each 32-wide run; then the
 // cross-wave sums
+template <int FMT> constexpr size_t gemv_lds_bytes_for(int mmax, int tpw, int nw) {
+  const int KW = tpw * Fmt<FMT>::KT;
+  const int SZB = Fmt<FMT>::KQ ? 8 : 4;
+  const int XSB = Fmt<FMT>::KQ ? mmax * (KW / 32) * 4 : 0;
+  return (size_t)nw * (mmax * KW * 2 + 16 * (KW / 32) * SZB + XSB) + (size_t)nw * mmax * 16 * sizeof(float);
+}
 template <int FMT, int MMAX, int TPW, int NW> constexpr size_t gemv_lds_bytes() {
-  constexpr int KW = TPW * Fmt<FMT>::KT;
-  constexpr int SZB = Fmt<FMT>::KQ ? 8 : 4;
-  constexpr int XSB = Fmt<FMT>::KQ ? MMAX * (KW / 32) * 4 : 0;
-  return (size_t)NW * (MMAX * KW * 2 + 16 * (KW / 32) * SZB + XSB) + (size_t)NW * MMAX * 16 * sizeof(float);
+  return gemv_lds_bytes_for<FMT>(MMAX, TPW, NW);
 }
 
 // Decode GEMV (used for M == 1).  Workgroup = one 16-row block (x one K split); its NW
@@ -1165,22 +1171,18 @@ static void launch_gemv_t(const GemvArgs& a, hipStream_t s) {
                      dim3(NW * 64), 0, s, a);
 }
 
-// TPW: word tiles per wave, rounded up to a power of two and capped so that
-// the x slice of NW * TPW tiles fits the 32 KiB LDS stage.  Returns false when
-// the plan asks for more tiles per wave than that (never, for plans made by
-// make_plan).
-// largest power-of-two tiles per wave (<= GEMV_TPW_MAX) whose x slice fits the
-// x stage and whose whole LDS leaves room for two workgroups per CU
+// Largest power-of-two tiles per wave (<= GEMV_TPW_MAX) whose x slice fits
+// the 32 KiB x stage and whose whole LDS leaves room for two workgroups per CU
 template <int FMT, int NW> constexpr int gemv_dot_tmax() {
-  constexpr int KT = Fmt<FMT>::KT;
   int t = GEMV_TPW_MAX;
-  while (t > 1 && (t * NW * KT * 2 > GEMV_LDS_X_BYTES ||
-                   (size_t)NW * (t * KT * 2 + 16 * (t * KT / 32) * (Fmt<FMT>::KQ ? 8 : 4) +
-                                 (Fmt<FMT>::KQ ? t * KT / 32 * 4 : 0)) + (size_t)NW * 16 * 4 > 80 * 1024))
+  while (t > 1 && (t * NW * Fmt<FMT>::KT * 2 > GEMV_LDS_X_BYTES || gemv_lds_bytes_for<FMT>(1, t, NW) > 80 * 1024))
     t >>= 1;
   return t;
 }
 
+// TPW: word tiles per wave, rounded up to a power of two, at most
+// gemv_dot_tmax.  Returns false when the plan asks for more tiles per wave
+// than that (never, for plans made by make_plan).
 template <int FMT, int NW>
 static bool launch_gemv_dot_w(const GemvArgs& a, int tps, hipStream_t s) {
   constexpr int TMAX = gemv_dot_tmax<FMT, NW>();
