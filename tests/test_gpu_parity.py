@@ -174,6 +174,36 @@ def test_forced_path(monkeypatch, force, M, fmt, group):
     check_close(run_gemm(lin, c.x), ref_y(c, c.x), f"forced {force}")
 
 
+@pytest.mark.parametrize("fmt,group,N,K,M", [(0, 128, 16, 1 << 20, 1), (3, 32, 32, 1 << 19, 1),
+                                             (0, 32, 64, 1 << 18, 40), (4, 256, 16, 1 << 18, 8)])
+def test_very_long_k(fmt, group, N, K, M):
+    # hundreds of K splits (a single row block or column tile), through every path
+    say(f"long K fmt={fmt} N={N} K={K} M={M} plan={qgm.plan(M, N, K, group, fmt)}")
+    c = synth.random_codes_case(K + M + fmt, fmt, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    check_close(run_gemm(lin, c.x), ref_y(c, c.x), "long K")
+
+
+def test_offset_guards_reject_oversized_shapes():
+    # shapes whose byte offsets would not fit the kernels' 32-bit arithmetic are
+    # refused before any launch (the pointers are never dereferenced)
+    import ctypes
+    lib = qgm._lib
+    buf = torch.zeros(1 << 16, dtype=torch.int32, device=DEV)
+    p = buf.data_ptr()
+    st = torch.cuda.current_stream().cuda_stream
+    E_UNSUP = 2
+    # M * ldx * 2 >= 2^32: GEMV (M = 2) and GEMM (M = 17)
+    for M in (2, 17):
+        ldx = (1 << 32) // (2 * M) + 8
+        ldx -= ldx % 8
+        assert lib.qgemm_ex(p, ldx, p, p, p, None, 16, M, 16, 128, 128, 0, p, 16, None, 0, st) == E_UNSUP
+    # one row block's codes past 4 GiB: K = 2^29 INT4
+    K = 1 << 29
+    assert lib.qgemm_ex(p, K, p, p, p, None, 16, 1, 16, K, 128, 0, p, 16, None, 0, st) == E_UNSUP
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 5, 16])
 @pytest.mark.parametrize("M", [2, 64])
 def test_split_k_variants(monkeypatch, splits, M):
