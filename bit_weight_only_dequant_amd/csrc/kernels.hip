@@ -707,9 +707,21 @@ __global__ void gemv_reduce_kernel(const float* __restrict__ ws, const f16* __re
     const int m = (int)(i / N), n = (int)(i % N);
     const int rb = n >> 4, r = n & 15;
     const float* p = ws + ((int64_t)rb * splits) * mmax * 16 + m * 16 + r;
+    const int64_t ps = (int64_t)mmax * 16;
+    uint32_t rv = 0u;   // fp16 bits, in a register of its own (no wait before the partial loads)
+    if (resid) rv = reinterpret_cast<const uint16_t*>(resid)[(int64_t)m * ldr + n];
+    // partials eight splits at a time, all loads before the adds, split order kept
     float v = 0.0f;
-    for (int s = 0; s < splits; ++s) v += p[(int64_t)s * mmax * 16];
-    if (resid) v += (float)resid[(int64_t)m * ldr + n];
+    int s = 0;
+    for (; s + 8 <= splits; s += 8) {
+      float t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = p[(s + j) * ps];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += t[j];
+    }
+    for (; s < splits; ++s) v += p[s * ps];
+    if (resid) v += (float)__builtin_bit_cast(f16, (uint16_t)rv);
     y[(int64_t)m * ldy + n] = (f16)v;
   }
 }
@@ -1080,14 +1092,30 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
   const f4* wsp = reinterpret_cast<const f4*>(a.ws);
   const int col = n0 + (fb & 1) * 32 + (lane & 31);
   const int colc = min(col, a.N - 1);
+  // every load is issued before the first use: residual, then the partials
+  // four splits at a time, added in split order (deterministic)
+  uint32_t rr[4] = {0u, 0u, 0u, 0u};   // fp16 bits, one per register (no packing wait)
+  if (a.resid) {   // uniform branch: the four loads go out together
+    const uint16_t* rb16 = reinterpret_cast<const uint16_t*>(a.resid);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = min(m0 + (fb >> 1) * 32 + acc_row(4 * q + e, lane), a.M - 1);
+      rr[e] = rb16[(int64_t)row * a.ldr + colc];
+    }
+  }
+  const f4* pp = wsp + ((tile * a.splits * 4 + fb) * 4 + q) * 64 + lane;
+  const int64_t pstride = 4 * 4 * 64;           // one split, in f4
+  f4 sum = f4{0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= a.splits; s += 4) {
+    const f4 p0 = pp[(s + 0) * pstride], p1 = pp[(s + 1) * pstride];
+    const f4 p2 = pp[(s + 2) * pstride], p3 = pp[(s + 3) * pstride];
+    sum += p0; sum += p1; sum += p2; sum += p3;
+  }
+  for (; s < a.splits; ++s) sum += pp[s * pstride];
   float res[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = min(m0 + (fb >> 1) * 32 + acc_row(4 * q + e, lane), a.M - 1);
-    res[e] = a.resid ? (float)a.resid[(int64_t)row * a.ldr + colc] : 0.0f;
-  }
-  f4 sum = f4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.splits; ++s) sum += wsp[(((tile * a.splits + s) * 4 + fb) * 4 + q) * 64 + lane];
+  for (int e = 0; e < 4; ++e) res[e] = (float)__builtin_bit_cast(f16, (uint16_t)rr[e]);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = m0 + (fb >> 1) * 32 + acc_row(4 * q + e, lane);
