@@ -792,7 +792,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   constexpr int PIPE = NW * DEPTH * S::SB;
   constexpr int RED = NW * 4 * 4 * 64 * 16;             // [wave][block][quad][lane] f4
   constexpr int BIG = PIPE > RED ? PIPE : RED;
-  constexpr int SZB = GEMM_TN * GEMM_GCAP * 4;          // (s | z << 16) per column and group
+  // (s | z << 16) per column and group; a column's row is padded by one
+  // word so that the 32 columns one lookup reads fall in 32 distinct banks
+  constexpr int SZS = GEMM_GCAP + 1;
+  constexpr int SZB = GEMM_TN * SZS * 4;
   static_assert(DEPTH >= 1 && DEPTH <= 3 && (DEPTH - 1) * S::DMA <= 63, "vmcnt range");
   __shared__ __align__(16) uint8_t smem[BIG + SZB];
   uint32_t* szl = reinterpret_cast<uint32_t*>(smem + BIG);
@@ -817,7 +820,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   auto seg_k = [](int gg, int h, int j) { return (gg + 2 * h) * F::LS + j * 32; };
 
   // 1. the workgroup's scales and zeros, loaded cooperatively (clamped) and
-  //    staged in LDS as [column][group]
+  //    staged in LDS as [column][group] (rows padded by one word)
   constexpr int NSZ = GEMM_TN * GEMM_GCAP / (NW * 64);
   const int gsr = gwn <= 1 ? 1 : 1 << (32 - __builtin_clz(gwn - 1));   // groups, rounded to a power of two
   const int lgs = __builtin_ctz(gsr);
@@ -924,7 +927,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         bt[c][nb] = *reinterpret_cast<const u4*>(sb + S::XB + (c * 2 + nb) * 1024 + lane * 16);
-        szv[c][nb] = szl[(nb * 32 + (lane & 31)) * GEMM_GCAP + gi];
+        szv[c][nb] = szl[(nb * 32 + (lane & 31)) * SZS + gi];
       }
     }
 #pragma unroll
@@ -1016,7 +1019,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   for (int j = 0; j < NSZ; ++j) {
     const int e = tid + NW * 64 * j;
     if (j < nsz && (e >> lgs) < GEMM_TN)
-      szl[(e >> lgs) * GEMM_GCAP + (e & (gsr - 1))] =
+      szl[(e >> lgs) * SZS + (e & (gsr - 1))] =
           F::KQ ? kq_half_pair(sraw[j], zraw[j]) : (sraw[j] & 0xffffu) | (zraw[j] << 16);
   }
   __syncthreads();
