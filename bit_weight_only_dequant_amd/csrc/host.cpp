@@ -75,8 +75,10 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     return p;
   }
   p.path = 2;
-  p.tiles_n = (int)ceil_div(N, GEMM_TN);
-  p.tiles_m = (int)ceil_div(M, GEMM_TM);
+  p.tm = M <= GEMM_SMALL_M ? 32 : GEMM_TM;
+  p.tn = M <= GEMM_SMALL_M ? 32 : GEMM_TN;
+  p.tiles_n = (int)ceil_div(N, p.tn);
+  p.tiles_m = (int)ceil_div(M, p.tm);
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
   // at most gemm_tpw(fmt) word tiles per wave and GEMM_GCAP groups per workgroup;
   // split K across workgroups only when the tiles leave most compute units
@@ -97,7 +99,7 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     return p;
   }
   p.workgroups = tiles * p.splits;
-  if (p.splits > 1) p.ws_partial_bytes = (size_t)tiles * p.splits * GEMM_TM * GEMM_TN * sizeof(float);
+  if (p.splits > 1) p.ws_partial_bytes = (size_t)tiles * p.splits * p.tm * p.tn * sizeof(float);
   return p;
 }
 
@@ -174,8 +176,8 @@ int qg_plan(int M, int N, int K, int group, int fmt, int out[5]) {
   out[0] = p.path;
   out[1] = p.splits;
   out[2] = (int)p.workgroups;
-  out[3] = p.path == 2 ? GEMM_TM : p.mmax;
-  out[4] = p.path == 2 ? GEMM_TN : 16;
+  out[3] = p.path == 2 ? p.tm : p.mmax;
+  out[4] = p.path == 2 ? p.tn : 16;
   return QG_OK;
 }
 

@@ -755,23 +755,25 @@ __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 
 // takes its 32 k from lane group g2 + 2h, run j, at seg_k(g2, h, j).  8-bit
 // codes: a stage is a whole word tile and lane half g2 takes 16 k from each of
 // lane groups g2 (steps 0, 1) and g2 + 2 (steps 2, 3), i.e. chunk h = step / 2.
-// x part: 64 rows x 2 pieces (one per lane half) x 4 sub-chunks of 8 k
-// (8 KiB); code part: CH chunks of both 32-column blocks (2 KiB each).
-template <int FMT> struct GemmStage {
+// x part: 32*MB rows x 2 pieces (one per lane half) x 4 sub-chunks of 8 k
+// (4 KiB per 32 rows); code part: CH chunks of the NB 32-column blocks
+// (1 KiB per block and chunk).
+template <int FMT, int MB, int NB> struct GemmStage {
   static constexpr int KT = Fmt<FMT>::KT;
   static constexpr bool WIDE = Fmt<FMT>::LS >= 32;
   static constexpr int SEG = WIDE ? Fmt<FMT>::LS / 32 : 1;  // 32-code runs per chunk
   static constexpr int CH = WIDE ? 1 : 2;                  // chunks per stage
   static constexpr int STAGES = WIDE ? 2 * SEG : 1;        // stages per word tile
-  static constexpr int XB = GEMM_TM * 64 * 2;              // x bytes per stage
-  static constexpr int SB = XB + CH * 2048;                // + code chunks of the two column blocks
-  static constexpr int DMA = XB / 1024 + 2 * CH;           // direct loads per lane per stage (10, 12)
+  static constexpr int XB = 32 * MB * 64 * 2;              // x bytes per stage
+  static constexpr int SB = XB + CH * NB * 1024;           // + code chunks of the column blocks
+  static constexpr int DMA = XB / 1024 + NB * CH;          // direct loads per lane per stage (10, 12 at 2 x 2)
 };
 
-// Prefill GEMM (M > 16).  Workgroup tile 64 (M) x 64 (N) over the workgroup's
-// share of K; its NW waves split that share and are summed through LDS at the
-// end, so every code is dequantized once per workgroup.  Each wave owns 2 x 2
-// blocks of v_mfma_f32_32x32x16_f16 (B operand lane l = column l % 32,
+// Prefill GEMM (M > 16).  Workgroup tile 32*MB (M) x 32*NB (N) -- 64 x 64,
+// or 32 x 32 when M <= 32 -- over the workgroup's share of K; its NW waves
+// split that share and are summed through LDS at the end, so every code is
+// dequantized once per workgroup.  Each wave owns MB x NB blocks of
+// v_mfma_f32_32x32x16_f16 (B operand lane l = column l % 32,
 // k-slots 8*(l/32)..+7): lane l takes its codes from the 16-byte chunk of row
 // block n0/16 + 2*nb + (l%32)/16, row l%16, lane group l/32 + 2h, one packed
 // word (8 codes) per MFMA step, and the A fragment of the step reads the
@@ -784,18 +786,19 @@ template <int FMT> struct GemmStage {
 // consecutive rows hit 16 distinct bank groups.  All LDS operands of a stage
 // are read first; group barriers then interleave one MFMA with a few VALU of
 // the dequantization so the two pipes overlap.
-template <int FMT, int NW, int TPW, int DEPTH>
+template <int FMT, int NW, int TPW, int DEPTH, int MB, int NB>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   using F = Fmt<FMT>;
-  using S = GemmStage<FMT>;
+  using S = GemmStage<FMT, MB, NB>;
   constexpr int SEG = S::SEG;
+  constexpr int TM = 32 * MB, TN = 32 * NB, NBLK = MB * NB;
   constexpr int PIPE = NW * DEPTH * S::SB;
-  constexpr int RED = NW * 4 * 4 * 64 * 16;             // [wave][block][quad][lane] f4
+  constexpr int RED = NW * NBLK * 4 * 64 * 16;          // [wave][block][quad][lane] f4
   constexpr int BIG = PIPE > RED ? PIPE : RED;
   // (s | z << 16) per column and group; a column's row is padded by one
   // word so that the 32 columns one lookup reads fall in 32 distinct banks
   constexpr int SZS = GEMM_GCAP + 1;
-  constexpr int SZB = GEMM_TN * SZS * 4;
+  constexpr int SZB = TN * SZS * 4;
   static_assert(DEPTH >= 1 && DEPTH <= 3 && (DEPTH - 1) * S::DMA <= 63, "vmcnt range");
   __shared__ __align__(16) uint8_t smem[BIG + SZB];
   uint32_t* szl = reinterpret_cast<uint32_t*>(smem + BIG);
@@ -804,7 +807,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g2 = lane >> 5, r = lane & 15;
   const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
-  const int m0 = tm * GEMM_TM, n0 = tn * GEMM_TN;
+  const int m0 = tm * TM, n0 = tn * TN;
   const int kt0 = split * a.tps;
   const int kt1 = min(a.wordtiles, kt0 + a.tps);
   const int per = (kt1 - kt0 + NW - 1) / NW;
@@ -821,17 +824,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 
   // 1. the workgroup's scales and zeros, loaded cooperatively (clamped) and
   //    staged in LDS as [column][group] (rows padded by one word)
-  constexpr int NSZ = GEMM_TN * GEMM_GCAP / (NW * 64);
+  constexpr int NSZ = (TN * GEMM_GCAP + NW * 64 - 1) / (NW * 64);
   const int gsr = gwn <= 1 ? 1 : 1 << (32 - __builtin_clz(gwn - 1));   // groups, rounded to a power of two
   const int lgs = __builtin_ctz(gsr);
-  const int nsz = (GEMM_TN * gsr + NW * 64 - 1) / (NW * 64);
+  const int nsz = (TN * gsr + NW * 64 - 1) / (NW * 64);
   uint32_t sraw[NSZ], zraw[NSZ];
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
     if (j < nsz) {
       const int e = tid + NW * 64 * j;                   // column e >> lgs, group e % gsr
       const int ec = e >> lgs, eg = e & (gsr - 1);
-      const bool ok = ec < GEMM_TN && eg < gwn && n0 + ec < a.N;
+      const bool ok = ec < TN && eg < gwn && n0 + ec < a.N;
       const int64_t off = ok ? ((int64_t)(n0 + ec) * ng + gw0 + eg) : 0;
       if constexpr (F::KQ) {   // (d, dmin) of the super-block, (sc, m) of the sub-block
         const int64_t soff = ok ? ((int64_t)(n0 + ec) * (ng >> 3) + ((gw0 + eg) >> 3)) : 0;
@@ -846,9 +849,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   }
 
   // 2. per-lane byte offsets (fixed for all stages): x row quarters, code rows
-  uint32_t voff[4];
+  uint32_t voff[2 * MB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 2 * MB; ++q) {
     const int m = q * 16 + (lane >> 2);
     const int u = (lane & 3) ^ ((m >> 2) & 3);
     const int ucol = S::WIDE ? u * 8 : 0;              // 8-bit codes: added per stage below
@@ -859,9 +862,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   // for every q above, since q moves m by multiples of 16
   const int usub = (lane & 3) ^ ((lane >> 4) & 3);
   const int subk = 8 * (usub & 1) + 32 * (usub >> 1);
-  const char* cb[2];
+  const char* cb[NB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int rb = min((n0 >> 4) + 2 * nb + ((lane >> 4) & 1), a.rowblocks - 1);  // columns past N: never stored
     cb[nb] = reinterpret_cast<const char*>(a.packed) + (int64_t)rb * a.wordtiles * 1024 + (g2 * 16 + r) * 16;
   }
@@ -880,44 +883,45 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
         src = reinterpret_cast<const char*>(a.x) + (kk < a.K ? kk : 0) * 2;
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 2 * MB; ++q)
         __builtin_amdgcn_global_load_lds(
             (const void __attribute__((address_space(1)))*)(src + voff[q]),
-            (void __attribute__((address_space(3)))*)(dst + (p * 4 + q) * 1024), 16, 0, 0);
+            (void __attribute__((address_space(3)))*)(dst + (p * 2 * MB + q) * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < S::CH; ++c)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
         __builtin_amdgcn_global_load_lds(
             (const void __attribute__((address_space(1)))*)(cb[nb] + (int64_t)kt * 1024 + (h + c) * 512),
-            (void __attribute__((address_space(3)))*)(dst + S::XB + (c * 2 + nb) * 1024), 16, 0, 0);
+            (void __attribute__((address_space(3)))*)(dst + S::XB + (c * NB + nb) * 1024), 16, 0, 0);
   };
 
-  f16v acc[2][2];
+  f16v acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn)
+    for (int jn = 0; jn < NB; ++jn)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.0f;
 
-  // byte offset of the A fragment (m-block mb, step) inside a stage
+  // byte offset of the A fragment (m-block mb, step) inside a stage: piece
+  // g2 holds TM rows of 64 bytes
   auto a_off = [&](int mb, int step) {
     const int m = mb * 32 + (lane & 31);
-    return g2 * 4096 + m * 64 + ((step ^ ((m >> 2) & 3)) << 4);
+    return g2 * (TM * 64) + m * 64 + ((step ^ ((m >> 2) & 3)) << 4);
   };
 
   // 3. one stage: every LDS operand first, then B operands (13 VALU per
-  //    4-bit word, 14 per two 8-bit words) interleaved with the 16 MFMAs
+  //    4-bit word, 14 per two 8-bit words) interleaved with the 4*MB*NB MFMAs
   auto compute_stage = [&](int st) {
     const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
     const int kt = wt0 + t;
     const uint8_t* sb = wbuf + (st % DEPTH) * S::SB;
-    uint32_t szv[S::CH][2];
-    u4 bt[S::CH][2];
+    uint32_t szv[S::CH][NB];
+    u4 bt[S::CH][NB];
     bool live[S::CH];
-    h8 af[4][2];
+    h8 af[4][MB];
 #pragma unroll
     for (int c = 0; c < S::CH; ++c) {
       // first k of this lane's codes in chunk c
@@ -925,32 +929,32 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       live[c] = kseg < a.K;                             // codes past K: scale 0
       const int gi = min(max((kseg >> lg) - gw0, 0), gwn - 1);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        bt[c][nb] = *reinterpret_cast<const u4*>(sb + S::XB + (c * 2 + nb) * 1024 + lane * 16);
+      for (int nb = 0; nb < NB; ++nb) {
+        bt[c][nb] = *reinterpret_cast<const u4*>(sb + S::XB + (c * NB + nb) * 1024 + lane * 16);
         szv[c][nb] = szl[(nb * 32 + (lane & 31)) * SZS + gi];
       }
     }
 #pragma unroll
     for (int step = 0; step < 4; ++step)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) af[step][mb] = *reinterpret_cast<const h8*>(sb + a_off(mb, step));
+      for (int mb = 0; mb < MB; ++mb) af[step][mb] = *reinterpret_cast<const h8*>(sb + a_off(mb, step));
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the math
-    h2 s2[S::CH][2];
-    f16 z[S::CH][2];
-    uint32_t kqc[S::CH][2];   // q4k: fp16 (d*sc) | -fp16(dmin*m) << 16, 0 past K
+    h2 s2[S::CH][NB];
+    f16 z[S::CH][NB];
+    uint32_t kqc[S::CH][NB];   // q4k: fp16 (d*sc) | -fp16(dmin*m) << 16, 0 past K
 #pragma unroll
     for (int c = 0; c < S::CH; ++c)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         s2[c][nb] = splat(live[c] ? __builtin_bit_cast(f16, (uint16_t)(szv[c][nb] & 0xffffu)) : (f16)0.0f);
         z[c][nb] = F::KQ ? (f16)0.0f : __builtin_bit_cast(f16, (uint16_t)(szv[c][nb] >> 16));
         kqc[c][nb] = live[c] ? szv[c][nb] : 0u;
       }
-    h8 bf[4][2];
+    h8 bf[4][NB];
 #pragma unroll
     for (int step = 0; step < 4; ++step)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const int c = S::WIDE ? 0 : step >> 1;
         h2 q[4];
         if constexpr (FMT == INT2_ASYM) {
@@ -976,16 +980,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int step = 0; step < 4; ++step)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[step][mb], bf[step][nb], acc[mb][nb], 0, 0, 0);
-    // schedule: the first step's operands, then 16 x (one MFMA, six VALU)
-    __builtin_amdgcn_sched_group_barrier(0x002, 26, 0);
+    // schedule: the first step's operands, then per MFMA a share of the VALU
+    // (2 x 2 blocks: 26, then 16 x (one MFMA, six VALU))
+    constexpr int VFIRST = 13 * NB, VPER = NBLK == 4 ? 6 : 13 * NB / MB;
+    __builtin_amdgcn_sched_group_barrier(0x002, VFIRST, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4 * NBLK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
     }
   };
 
@@ -995,12 +1001,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   for (int d = 0; d < DEPTH; ++d)
     if (d < nst) issue_stage(d);
   float res[16];
-  const int fb = wave & 3;                               // block this wave finishes: (fb >> 1, fb & 1)
-  if (a.resid && a.splits == 1 && wave < 4) {
-    const int colc = min(n0 + (fb & 1) * 32 + (lane & 31), a.N - 1);
+  const int fb = wave < NBLK ? wave : 0;                 // block this wave finishes: (fb / NB, fb % NB)
+  if (a.resid && a.splits == 1 && wave < NBLK) {
+    const int colc = min(n0 + (fb % NB) * 32 + (lane & 31), a.N - 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = min(m0 + (fb >> 1) * 32 + acc_row(i, lane), a.M - 1);
+      const int row = min(m0 + (fb / NB) * 32 + acc_row(i, lane), a.M - 1);
       res[i] = (float)a.resid[(int64_t)row * a.ldr + colc];
     }
   } else {
@@ -1018,7 +1024,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
     const int e = tid + NW * 64 * j;
-    if (j < nsz && (e >> lgs) < GEMM_TN)
+    if (j < nsz && (e >> lgs) < TN)
       szl[(e >> lgs) * SZS + (e & (gsr - 1))] =
           F::KQ ? kq_half_pair(sraw[j], zraw[j]) : (sraw[j] & 0xffffu) | (zraw[j] << 16);
   }
@@ -1045,55 +1051,57 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   }
 
   // 6. sum the NW waves' accumulators through LDS in wave order
-  //    (deterministic); wave w < 4 finishes block w
+  //    (deterministic); wave w < NBLK finishes block w
   __syncthreads();
   f4* red = reinterpret_cast<f4*>(smem);
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk)
+  for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f16v& A = acc[blk >> 1][blk & 1];
-      red[((wave * 4 + blk) * 4 + q) * 64 + lane] = f4{A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]};
+      const f16v& A = acc[blk / NB][blk % NB];
+      red[((wave * NBLK + blk) * 4 + q) * 64 + lane] = f4{A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]};
     }
   __syncthreads();
-  if (wave >= 4) return;
+  if (wave >= NBLK) return;
   f4 tot[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    f4 v = red[((0 * 4 + fb) * 4 + q) * 64 + lane];
+    f4 v = red[((0 * NBLK + fb) * 4 + q) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) v += red[((w * 4 + fb) * 4 + q) * 64 + lane];
+    for (int w = 1; w < NW; ++w) v += red[((w * NBLK + fb) * 4 + q) * 64 + lane];
     tot[q] = v;
   }
-  const int col = n0 + (fb & 1) * 32 + (lane & 31);
+  const int col = n0 + (fb % NB) * 32 + (lane & 31);
   if (a.splits == 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = m0 + (fb >> 1) * 32 + acc_row(i, lane);
+      const int row = m0 + (fb / NB) * 32 + acc_row(i, lane);
       if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(tot[i >> 2][i & 3] + res[i]);
     }
     return;
   }
-  // split-K: this split's 64 x 64 partial; gemm_reduce_kernel sums the splits
+  // split-K: this split's TM x TN partial; gemm_reduce_kernel sums the splits
   f4* wsp = reinterpret_cast<f4*>(a.ws);
   const int64_t tile = (int64_t)tm * a.tiles_n + tn;
-  const int64_t base = ((tile * a.splits + split) * 4 + fb) * 4;
+  const int64_t base = ((tile * a.splits + split) * NBLK + fb) * 4;
 #pragma unroll
   for (int q = 0; q < 4; ++q) wsp[(base + q) * 64 + lane] = tot[q];
 }
 
-// Sums a 64 x 64 tile's split partials in split order (deterministic), adds
-// the residual and rounds once to fp16.  One workgroup of 4 waves per 32 x 32
+// Sums a tile's split partials in split order (deterministic), adds the
+// residual and rounds once to fp16.  One workgroup of 4 waves per 32 x 32
 // block fb of the tile (grid: column tile, row tile, block), so the partials
-// are read by 4 workgroups per tile; wave q owns quad q of the block in the
-// GEMM's accumulator layout, 4 outputs per lane.
+// are read by MB * NB workgroups per tile; wave q owns quad q of the block in
+// the GEMM's accumulator layout, 4 outputs per lane.
+template <int MB, int NB>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
+  constexpr int NBLK = MB * NB;
   const int tn = blockIdx.x, tm = blockIdx.y, fb = blockIdx.z;
   const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int m0 = tm * GEMM_TM, n0 = tn * GEMM_TN;
+  const int m0 = tm * 32 * MB, n0 = tn * 32 * NB;
   const int64_t tile = (int64_t)tm * a.tiles_n + tn;
   const f4* wsp = reinterpret_cast<const f4*>(a.ws);
-  const int col = n0 + (fb & 1) * 32 + (lane & 31);
+  const int col = n0 + (fb % NB) * 32 + (lane & 31);
   const int colc = min(col, a.N - 1);
   // every load is issued before the first use: residual, then the partials
   // four splits at a time, added in split order (deterministic)
@@ -1102,12 +1110,12 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
     const uint16_t* rb16 = reinterpret_cast<const uint16_t*>(a.resid);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = min(m0 + (fb >> 1) * 32 + acc_row(4 * q + e, lane), a.M - 1);
+      const int row = min(m0 + (fb / NB) * 32 + acc_row(4 * q + e, lane), a.M - 1);
       rr[e] = rb16[(int64_t)row * a.ldr + colc];
     }
   }
-  const f4* pp = wsp + ((tile * a.splits * 4 + fb) * 4 + q) * 64 + lane;
-  const int64_t pstride = 4 * 4 * 64;           // one split, in f4
+  const f4* pp = wsp + ((tile * a.splits * NBLK + fb) * 4 + q) * 64 + lane;
+  const int64_t pstride = NBLK * 4 * 64;        // one split, in f4
   f4 sum = f4{0.f, 0.f, 0.f, 0.f};
   int s = 0;
   for (; s + 4 <= a.splits; s += 4) {
@@ -1121,7 +1129,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
   for (int e = 0; e < 4; ++e) res[e] = (float)__builtin_bit_cast(f16, (uint16_t)rr[e]);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int row = m0 + (fb >> 1) * 32 + acc_row(4 * q + e, lane);
+    const int row = m0 + (fb / NB) * 32 + acc_row(4 * q + e, lane);
     if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(sum[e] + res[e]);
   }
 }
@@ -1260,6 +1268,20 @@ static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, hipStream_t s) {
   }
 }
 
+// grid: x = column tiles, y = row tiles, z = K splits; MB x NB blocks of 32 x 32
+template <int MB, int NB>
+static void launch_gemm_tiles(const GemmArgs& a, const Plan& p, int fmt, hipStream_t s) {
+  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.splits), block(GEMM_THREADS);
+  constexpr int NW = GEMM_THREADS / 64;
+  switch (fmt) {
+    case QG_INT4_ASYM: hipLaunchKernelGGL((gemm_kernel<INT4_ASYM, NW, GEMM_TPW, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
+    case QG_INT2_ASYM: hipLaunchKernelGGL((gemm_kernel<INT2_ASYM, NW, GEMM_TPW, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
+    case QG_Q8_0: hipLaunchKernelGGL((gemm_kernel<Q8_0, NW, GEMM_TPW_Q8, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
+    case QG_Q4K: hipLaunchKernelGGL((gemm_kernel<Q4K, NW, GEMM_TPW, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((gemm_kernel<Q4_0, NW, GEMM_TPW, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
+  }
+}
+
 static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const uint16_t* scales,
                      const uint16_t* zeros, const uint16_t* resid, int ldr, int M, int N, int K,
                      int group, int fmt, uint16_t* y, int ldy, void* workspace, size_t ws_bytes,
@@ -1352,19 +1374,15 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
   a.splits = p.splits; a.tps = p.tps;
   // the kernel forms byte offsets of x rows in 32 bits
   if ((int64_t)M * ldx * 2 >= (int64_t)1 << 32 || p.tiles_m > 65535 || p.splits > 65535) return QG_E_UNSUPPORTED;
-  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.splits), block(GEMM_THREADS);
-  constexpr int NW = GEMM_THREADS / 64;
-  switch (fmt) {
-    case QG_INT4_ASYM: hipLaunchKernelGGL((gemm_kernel<INT4_ASYM, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
-    case QG_INT2_ASYM: hipLaunchKernelGGL((gemm_kernel<INT2_ASYM, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
-    case QG_Q8_0: hipLaunchKernelGGL((gemm_kernel<Q8_0, NW, GEMM_TPW_Q8, GEMM_DEPTH>), grid, block, 0, s, a); break;
-    case QG_Q4K: hipLaunchKernelGGL((gemm_kernel<Q4K, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_kernel<Q4_0, NW, GEMM_TPW, GEMM_DEPTH>), grid, block, 0, s, a); break;
-  }
+  if (p.tm == 32) launch_gemm_tiles<1, 1>(a, p, fmt, s);
+  else launch_gemm_tiles<2, 2>(a, p, fmt, s);
   if (p.splits > 1) {
     st = launch_status();
     if (st != QG_OK) return st;
-    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 4), dim3(256), 0, s, a);
+    if (p.tm == 32)
+      hipLaunchKernelGGL((gemm_reduce_kernel<1, 1>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_reduce_kernel<2, 2>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 4), dim3(256), 0, s, a);
   }
   return launch_status();
 }

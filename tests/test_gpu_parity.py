@@ -152,6 +152,9 @@ RAGGED = [
     (4, 256, 16, 256, 1), (4, 256, 100, 512, 3), (4, 256, 33, 768, 12), (4, 256, 130, 1280, 17),
     (4, 256, 300, 2048, 129), (4, 256, 520, 4352, 257), (4, 256, 48, 8192, 8), (4, 256, 40, 8192, 1),
     (4, 256, 64, 256, 100), (4, 256, 1000, 4096, 64),
+    # 17 <= M <= 32: 32 x 32 GEMM tiles (with and without split-K)
+    (0, 128, 300, 2048, 32), (1, 64, 272, 320, 24), (2, 32, 520, 1056, 20), (3, 32, 100, 96, 32),
+    (4, 256, 64, 512, 30), (0, 128, 2048, 8192, 32), (0, 32, 33, 96, 31), (3, 32, 2048, 2048, 18),
 ]
 
 
@@ -163,7 +166,7 @@ def test_ragged_parity(fmt, group, N, K, M):
     check_close(run_gemm(lin, c.x), ref_y(c, c.x), "ragged")
 
 
-@pytest.mark.parametrize("force,M", [("gemm", 1), ("gemm", 4), ("gemm", 8), ("gemv", 3)])
+@pytest.mark.parametrize("force,M", [("gemm", 1), ("gemm", 4), ("gemm", 8), ("gemm", 16), ("gemv", 3)])
 @pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32), (3, 32), (4, 256)])
 def test_forced_path(monkeypatch, force, M, fmt, group):
     monkeypatch.setenv("QGEMM_FORCE", force)
@@ -205,7 +208,7 @@ def test_offset_guards_reject_oversized_shapes():
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 5, 16])
-@pytest.mark.parametrize("M", [2, 64])
+@pytest.mark.parametrize("M", [2, 24, 64])
 def test_split_k_variants(monkeypatch, splits, M):
     monkeypatch.setenv("QGEMM_SPLITK", str(splits))
     N, K, group, fmt = 384, 2048, 128, 0
@@ -275,7 +278,7 @@ def test_q4k_one_hot_bit_exact(M):
 # exact-arithmetic cases: bit-exact outputs whatever the order
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M", [1, 5, 64, 130])
+@pytest.mark.parametrize("M", [1, 5, 24, 64, 130])
 @pytest.mark.parametrize("fmt,group", [(0, 32), (0, 128), (1, 64), (2, 32), (3, 32)])
 def test_one_hot_bit_exact(M, fmt, group):
     N, K = 144, 512
@@ -292,7 +295,7 @@ def test_one_hot_bit_exact(M, fmt, group):
     assert np.array_equal(y.view(np.uint16), expect.view(np.uint16))
 
 
-@pytest.mark.parametrize("M", [1, 8, 128])
+@pytest.mark.parametrize("M", [1, 8, 32, 128])
 @pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32), (3, 32)])
 def test_exact_regime_bit_exact(M, fmt, group):
     # x in {-1, 0, 1}, power-of-two scales, integer zero points: every partial
