@@ -75,8 +75,10 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     return p;
   }
   p.path = 2;
+  // tile rows follow M (32 or 64); 64-row tiles are 32 columns wide up to
+  // M = 64, so a single row of tiles still spreads over the CUs without a split
   p.tm = M <= GEMM_SMALL_M ? 32 : GEMM_TM;
-  p.tn = M <= GEMM_SMALL_M ? 32 : GEMM_TN;
+  p.tn = M <= 2 * GEMM_SMALL_M ? 32 : GEMM_TN;
   p.tiles_n = (int)ceil_div(N, p.tn);
   p.tiles_m = (int)ceil_div(M, p.tm);
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;

@@ -19,7 +19,7 @@ constexpr int GEMV_LDS_X_BYTES = 32768;  // x slice staged per workgroup
 constexpr int GEMM_THREADS = 512;        // 8 waves; they split the workgroup's K range
 constexpr int GEMM_TM = 64;              // workgroup tile rows (M)
 constexpr int GEMM_TN = 64;              // workgroup tile columns (N)
-constexpr int GEMM_SMALL_M = 32;         // M <= this: 32 x 32 tiles (half the x rows per workgroup)
+constexpr int GEMM_SMALL_M = 32;         // M <= this: 32 x 32 tiles; M <= 2x this: 64 x 32
 constexpr int GEMM_TPW = 2;              // word tiles per wave (K per workgroup <= 16 tiles)
 constexpr int GEMM_TPW_Q8 = 4;           // q8_0: a tile is 64 wide, so 4 per wave (256 of K)
 constexpr int GEMM_DEPTH = 1;            // x/code stages in flight per wave
@@ -36,7 +36,7 @@ struct Plan {
   int tps = 0;         // word tiles per split
   int wordtiles = 0;   // total word tiles along K
   int rowblocks = 0;   // N / 16 (rounded up)
-  int tm = 0, tn = 0;  // GEMM tile rows and columns (64 x 64, or 32 x 32 for small M)
+  int tm = 0, tn = 0;  // GEMM tile rows and columns (64 x 64; 64 x 32 or 32 x 32 for small M)
   int tiles_n = 0;     // GEMM tiles along N
   int tiles_m = 0;     // GEMM tiles along M
   int64_t workgroups = 0;

@@ -770,7 +770,7 @@ template <int FMT, int MB, int NB> struct GemmStage {
 };
 
 // Prefill GEMM (M > 16).  Workgroup tile 32*MB (M) x 32*NB (N) -- 64 x 64,
-// or 32 x 32 when M <= 32 -- over the workgroup's share of K; its NW waves
+// 64 x 32 when M <= 64, 32 x 32 when M <= 32 -- over the workgroup's share of K; its NW waves
 // split that share and are summed through LDS at the end, so every code is
 // dequantized once per workgroup.  Each wave owns MB x NB blocks of
 // v_mfma_f32_32x32x16_f16 (B operand lane l = column l % 32,
@@ -1375,12 +1375,15 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
   // the kernel forms byte offsets of x rows in 32 bits
   if ((int64_t)M * ldx * 2 >= (int64_t)1 << 32 || p.tiles_m > 65535 || p.splits > 65535) return QG_E_UNSUPPORTED;
   if (p.tm == 32) launch_gemm_tiles<1, 1>(a, p, fmt, s);
+  else if (p.tn == 32) launch_gemm_tiles<2, 1>(a, p, fmt, s);
   else launch_gemm_tiles<2, 2>(a, p, fmt, s);
   if (p.splits > 1) {
     st = launch_status();
     if (st != QG_OK) return st;
     if (p.tm == 32)
       hipLaunchKernelGGL((gemm_reduce_kernel<1, 1>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1), dim3(256), 0, s, a);
+    else if (p.tn == 32)
+      hipLaunchKernelGGL((gemm_reduce_kernel<2, 1>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 2), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((gemm_reduce_kernel<2, 2>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 4), dim3(256), 0, s, a);
   }

@@ -162,9 +162,10 @@ def test_plans_for_the_workloads():
     assert p["path"] == "gemm" and p["workgroups"] >= 128
     assert qgm.plan(16, 64, 128, 32, 0)["path"] == "gemv"
     assert qgm.plan(17, 64, 128, 32, 0)["path"] == "gemm"
-    # 17..32 rows: 32 x 32 tiles; above: 64 x 64
+    # 17..32 rows: 32 x 32 tiles; 33..64: 64 x 32; above: 64 x 64
     assert (qgm.plan(32, 8192, 2048, 128, 0)["tile_m"], qgm.plan(32, 8192, 2048, 128, 0)["tile_n"]) == (32, 32)
-    assert (qgm.plan(33, 8192, 2048, 128, 0)["tile_m"], qgm.plan(33, 8192, 2048, 128, 0)["tile_n"]) == (64, 64)
+    assert (qgm.plan(33, 8192, 2048, 128, 0)["tile_m"], qgm.plan(33, 8192, 2048, 128, 0)["tile_n"]) == (64, 32)
+    assert (qgm.plan(65, 8192, 2048, 128, 0)["tile_m"], qgm.plan(65, 8192, 2048, 128, 0)["tile_n"]) == (64, 64)
     assert qgm.plan(32, 8192, 2048, 128, 0)["workgroups"] == 256
     assert qgm.workspace_bytes(1, 16, 128, 32, 0) == 0
     assert qgm.workspace_bytes(128, 2048, 8192, 128, 0) > 0   # split-K for small N

@@ -155,6 +155,9 @@ RAGGED = [
     # 17 <= M <= 32: 32 x 32 GEMM tiles (with and without split-K)
     (0, 128, 300, 2048, 32), (1, 64, 272, 320, 24), (2, 32, 520, 1056, 20), (3, 32, 100, 96, 32),
     (4, 256, 64, 512, 30), (0, 128, 2048, 8192, 32), (0, 32, 33, 96, 31), (3, 32, 2048, 2048, 18),
+    # 33 <= M <= 64: 64 x 32 tiles
+    (0, 128, 300, 2048, 48), (4, 256, 130, 1280, 40), (2, 32, 520, 1056, 64), (1, 64, 2048, 8192, 60),
+    (3, 32, 72, 544, 33),
 ]
 
 
@@ -208,7 +211,7 @@ def test_offset_guards_reject_oversized_shapes():
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 5, 16])
-@pytest.mark.parametrize("M", [2, 24, 64])
+@pytest.mark.parametrize("M", [2, 24, 64, 100])
 def test_split_k_variants(monkeypatch, splits, M):
     monkeypatch.setenv("QGEMM_SPLITK", str(splits))
     N, K, group, fmt = 384, 2048, 128, 0
