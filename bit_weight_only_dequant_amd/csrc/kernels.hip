@@ -236,50 +236,69 @@ __global__ void unpack_codes_kernel(const uint32_t* __restrict__ packed, uint8_t
 // Dequantized weights written out (fp16 [N, K]), with the GEMM's register
 // dequant: one wave per (row block, word tile), so each wave reads 1 KiB of
 // codes contiguously; lane (g, r) turns its 16-byte chunk into 32 (4-bit), 64
-// (INT2) or 16 (q8_0) weights of row 16*rb + r and stores them contiguously.
+// (INT2) or 16 (q8_0) weights of row 16*rb + r.  The wave's 16-row tile goes
+// through LDS (rows padded by 16 bytes against bank conflicts) and is stored
+// row by row, 16 bytes per lane, so each store instruction writes whole
+// 64-to-256-byte row segments instead of 16 bytes per 64.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ packed,
                                                       const f16* __restrict__ scales,
                                                       const f16* __restrict__ zeros, f16* __restrict__ w,
                                                       int N, int K, int group, int wordtiles, int64_t units) {
   using F = Fmt<FMT>;
-  const int lane = threadIdx.x & 63;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= units) return;
+  constexpr int KTP = F::KT + 8;                 // padded tile row, in halves
+  constexpr int TB = 16 * KTP * 2;               // tile bytes per wave
+  constexpr int LPR = F::KT / 8;                 // lanes per row when storing (16 bytes each)
+  constexpr int ROUNDS = 16 * LPR / 64;          // store instructions per lane
+  __shared__ __align__(16) uint8_t deq_smem[4 * TB];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + wv;
+  if (unit >= units) return;                     // the whole wave
   const int64_t rb = unit / wordtiles;
   const int T = (int)(unit - rb * wordtiles);
   const int g = lane >> 4, r = lane & 15;
   const int64_t n = rb * 16 + r;
+  f16* tl = reinterpret_cast<f16*>(deq_smem + wv * TB);   // [16 rows][KTP]
   const u4 c = reinterpret_cast<const u4*>(packed)[unit * 64 + lane];
-  if (n >= N) return;
   const int ng = K / group;   // q4k: group = 32, the sub-block
 #pragma unroll
   for (int p = 0; p < F::NSEG; ++p) {
-    const int k = T * F::KT + g * F::LS + p * F::SW;  // first of this lane's SW codes
-    if (k >= K) break;
+    const int kl = g * F::LS + p * F::SW;          // this lane's first code inside the tile
+    const int k = T * F::KT + kl;
+    if (n >= N || k >= K) continue;
     const int grp = k / group;
     h2 q[F::SW / 2];
-    h8* dst = reinterpret_cast<h8*>(w + n * K + k);
+    h2 wq[F::SW / 2];
     if constexpr (F::KQ) {
       const uint32_t ddm = reinterpret_cast<const uint32_t*>(scales)[n * (ng >> 3) + (grp >> 3)];
       const uint32_t scm = reinterpret_cast<const uint16_t*>(zeros)[n * ng + grp];
       run_qmz<FMT>(c, p, (f16)0.0f, q);
-      h2 wq[F::SW / 2];
       kq_weights(q, kq_half_pair(ddm, scm), wq, F::SW / 2);
-#pragma unroll
-      for (int v = 0; v < F::SW / 8; ++v)
-        dst[v] = h8{wq[4 * v][0], wq[4 * v][1], wq[4 * v + 1][0], wq[4 * v + 1][1],
-                    wq[4 * v + 2][0], wq[4 * v + 2][1], wq[4 * v + 3][0], wq[4 * v + 3][1]};
     } else {
       const h2 s2 = splat(scales[n * ng + grp]);
       const f16 z = F::HAS_Z ? zeros[n * ng + grp] : __builtin_bit_cast(f16, (uint16_t)F::ZBITS);
       run_qmz<FMT>(c, p, z, q);
 #pragma unroll
-      for (int v = 0; v < F::SW / 8; ++v) {
-        const h2 a0 = q[4 * v] * s2, a1 = q[4 * v + 1] * s2, a2 = q[4 * v + 2] * s2, a3 = q[4 * v + 3] * s2;
-        dst[v] = h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-      }
+      for (int i = 0; i < F::SW / 2; ++i) wq[i] = q[i] * s2;
     }
+    h8* dst = reinterpret_cast<h8*>(tl + r * KTP + kl);
+#pragma unroll
+    for (int v = 0; v < F::SW / 8; ++v)
+      dst[v] = h8{wq[4 * v][0], wq[4 * v][1], wq[4 * v + 1][0], wq[4 * v + 1][1],
+                  wq[4 * v + 2][0], wq[4 * v + 2][1], wq[4 * v + 3][0], wq[4 * v + 3][1]};
+  }
+  // only this wave reads its tile: a wave-level barrier orders the LDS traffic
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int v = 0; v < ROUNDS; ++v) {
+    const int idx = v * 64 + lane;
+    const int row = idx / LPR, ch = idx % LPR;
+    const int64_t nn = rb * 16 + row;
+    const int kk = T * F::KT + ch * 8;
+    if (nn < N && kk < K)
+      *reinterpret_cast<h8*>(w + nn * K + kk) = *reinterpret_cast<const h8*>(tl + row * KTP + ch * 8);
   }
 }
 
