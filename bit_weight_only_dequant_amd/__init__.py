@@ -153,6 +153,45 @@ def _stream(device, stream=None) -> int:
     return stream.cuda_stream
 
 
+def _meta_shapes(N: int, K: int, group: int, fmt: int):
+    """Element counts the kernels read: (scales, zeros or None)."""
+    if fmt == Q4K:
+        return N * (K // 256) * 2, N * (K // 32)
+    if fmt in (Q4_0, Q8_0):
+        return N * (K // group), None
+    return N * (K // group), N * (K // group)
+
+
+def _check_weights(packed, scales, zeros, N: int, K: int, group: int, fmt: int, device):
+    """The packed codes and metadata hold at least what the kernels read, on
+    x's device, with the element types the kernels take."""
+    torch = _torch()
+    if fmt not in BITS or group <= 0 or K % group or N < 0 or K < 0:
+        return   # the library reports the bad argument itself
+    for t, what in ((packed, "packed"), (scales, "scales"), (zeros, "zeros")):
+        if t is not None and t.device != device:
+            raise ValueError(f"{what} is on {t.device}, x on {device}")
+    need = packed_bytes(N, K, fmt)
+    if packed is not None and packed.numel() * packed.element_size() < need:
+        raise ValueError(f"packed holds {packed.numel() * packed.element_size()} bytes, needs {need}")
+    ns, nz = _meta_shapes(N, K, group, fmt)
+    if scales is not None and (scales.dtype != torch.float16 or scales.numel() < ns):
+        raise ValueError(f"scales must be fp16 with at least {ns} elements")
+    if zeros is not None and nz is not None:
+        zt = torch.int16 if fmt == Q4K else torch.float16
+        if zeros.dtype != zt or zeros.numel() < nz:
+            raise ValueError(f"zeros must be {zt} with at least {nz} elements")
+
+
+def _check_out(t, M: int, N: int, what: str, device):
+    """An fp16 [M, N] tensor with unit column stride on x's device."""
+    torch = _torch()
+    if t.dtype != torch.float16 or t.dim() != 2 or tuple(t.shape) != (M, N) or t.device != device:
+        raise ValueError(f"{what} must be an fp16 [{M}, {N}] tensor on {device}")
+    if N > 1 and M > 0 and t.stride(1) != 1:
+        raise ValueError(f"{what} must have unit column stride")
+
+
 def to_words_tensor(words: np.ndarray, device="cuda"):
     """uint32 numpy words -> int32 device tensor holding the same bits."""
     torch = _torch()
@@ -216,6 +255,7 @@ def dequant_into(packed, scales, zeros, N: int, K: int, group: int, fmt: int, ou
     _dev(packed, "packed"); _dev(scales, "scales"); _dev(zeros, "zeros"); _dev(out, "out")
     if out.dtype != torch.float16 or tuple(out.shape) != (N, K) or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp16 [N, K] tensor")
+    _check_weights(packed, scales, zeros, N, K, group, fmt, out.device)
     _check(_lib.qg_dequant(_ptr(packed), _ptr(scales), _ptr(zeros), _ptr(out), N, K, group, fmt,
                            _stream(packed.device, stream)), "qg_dequant")
     return out
@@ -231,8 +271,12 @@ def qgemm(x, packed, scales, zeros, N: int, K: int, group: int, fmt: int, out=No
     if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != K or (x.shape[0] > 1 and x.stride(1) != 1):
         raise ValueError("x must be an fp16 [M, K] tensor with unit column stride")
     M = x.shape[0]
+    _check_weights(packed, scales, zeros, N, K, group, fmt, x.device)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _check_out(out, M, N, "out", x.device)
+    if residual is not None:
+        _check_out(residual, M, N, "residual", x.device)
     ldx = x.stride(0) if M > 1 else K
     ldy = out.stride(0) if M > 1 else N
     ldr = (residual.stride(0) if M > 1 else N) if residual is not None else N
@@ -247,6 +291,14 @@ def qgemm(x, packed, scales, zeros, N: int, K: int, group: int, fmt: int, out=No
 
 def qgemm_plain(x, packed, scales, zeros, N: int, K: int, group: int, fmt: int, out, stream=None):
     """The plain `qgemm` entry point (contiguous x and y, library workspace)."""
+    torch = _torch()
+    _dev(x, "x"); _dev(out, "out")
+    if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp16 [M, K] tensor")
+    _check_weights(packed, scales, zeros, N, K, group, fmt, x.device)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    _check_out(out, x.shape[0], N, "out", x.device)
     st = _lib.qgemm(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), x.shape[0], N, K, group, fmt,
                     _ptr(out), _stream(x.device, stream))
     _check(st, "qgemm")
@@ -281,11 +333,25 @@ def loop_block(x, linears: Sequence[QuantLinear], L: int, scratch=None, events=N
     torch = _torch()
     _dev(x, "x")
     qkv, o, up, down = linears
+    if x.dtype != torch.float16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp16 [M, D] tensor")
     M, D = x.shape
     F = up.N
     fmt, group = qkv.fmt, qkv.group
+    shapes = [(l.N, l.K) for l in linears]
+    if shapes != [(3 * D, D), (D, D), (F, D), (D, F)]:
+        raise ValueError(f"linears must be QKV [3D, D], O [D, D], up [F, D], down [D, F] for D = {D}; got {shapes}")
+    if any(l.fmt != fmt or l.group != group for l in linears):
+        raise ValueError("the four linears must share one format and group")
+    if L < 0:
+        raise ValueError("L must be >= 0")
+    need = M * (3 * D + D + F)
     if scratch is None:
-        scratch = torch.empty(M * (3 * D + D + F), dtype=torch.float16, device=x.device)
+        scratch = torch.empty(need, dtype=torch.float16, device=x.device)
+    elif scratch.dtype != torch.float16 or scratch.numel() < need or scratch.device != x.device:
+        raise ValueError(f"scratch must be fp16 with at least {need} elements on {x.device}")
+    if events is not None and len(events) != L + 1:
+        raise ValueError("events must hold L + 1 events")
     arr = lambda vals: (ctypes.c_void_p * 4)(*vals)
     packed4 = arr([l.packed.data_ptr() for l in linears])
     scales4 = arr([l.scales.data_ptr() for l in linears])

@@ -423,6 +423,42 @@ def test_plain_entry_point_and_empty():
     assert empty.shape == (0, c.N)
 
 
+def test_binding_rejects_mismatched_tensors():
+    # the binding checks what the C ABI cannot see (tensor sizes, dtypes,
+    # devices) before any launch
+    c, lin = get_case("tiny_int4_g32")
+    x = dev_half(c.x)
+    M, N, K = x.shape[0], c.N, c.K
+    bad_out = [torch.empty((M - 1, N), dtype=torch.float16, device=DEV),       # too few rows
+               torch.empty((M, N), dtype=torch.float32, device=DEV),           # wrong dtype
+               torch.empty((N, M), dtype=torch.float16, device=DEV).t()]       # column stride != 1
+    for out in bad_out:
+        with pytest.raises(ValueError):
+            lin(x, out=out)
+    with pytest.raises(ValueError):
+        lin(x, residual=torch.zeros((M, N - 1), dtype=torch.float16, device=DEV))
+    with pytest.raises(ValueError):   # packed codes too short for [N, K]
+        qgm.qgemm(x, lin.packed[:-1], lin.scales, lin.zeros, N, K, c.group, c.fmt)
+    with pytest.raises(ValueError):   # scales for a smaller N
+        qgm.qgemm(x, lin.packed, lin.scales[:-1], lin.zeros, N, K, c.group, c.fmt)
+    with pytest.raises(ValueError):   # fp16 zero points given as int16 bits
+        qgm.qgemm(x, lin.packed, lin.scales, lin.zeros.view(torch.int16), N, K, c.group, c.fmt)
+    with pytest.raises(ValueError):
+        qgm.dequant(lin.packed[:10], lin.scales, lin.zeros, N, K, c.group, c.fmt)
+    # the looped block checks its four shapes and the scratch size
+    D, F = 64, 128
+    cases = [synth.random_codes_case(70 + i, 0, 32, n, k, 1)
+             for i, (n, k) in enumerate(((3 * D, D), (D, D), (F, D), (D, F)))]
+    lins = [qgm.QuantLinear.from_case(cc, DEV) for cc in cases]
+    xl = dev_half(np.zeros((4, D), np.float16))
+    with pytest.raises(ValueError):
+        qgm.loop_block(xl, [lins[0], lins[1], lins[3], lins[2]], 1)   # up and down swapped
+    with pytest.raises(ValueError):
+        qgm.loop_block(xl, lins, 1, scratch=torch.empty(10, dtype=torch.float16, device=DEV))
+    qgm.loop_block(xl, lins, 1)   # the right shapes run
+    torch.cuda.synchronize()
+
+
 def test_k_zero_writes_zeros():
     packed = torch.zeros(64, dtype=torch.int32, device=DEV)
     s = torch.ones((16, 1), dtype=torch.float16, device=DEV)
