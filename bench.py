@@ -261,6 +261,12 @@ def load_traffic(kernel):
     return None if entry is None else entry.get("bytes")
 
 
+def gemv_kernel_name(qgm, c):
+    """The M = 1 kernel the library's plan picks: 16-row or 8-row workgroups."""
+    rows = qgm.plan(1, c.N, c.K, c.group, c.fmt)["tile_n"]
+    return "gemv_half_kernel<INT4> (8-row workgroups)" if rows == 8 else "gemv_kernel<INT4,1>"
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -344,7 +350,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "gemv_kernel<INT4,1>",
+                     "kernel": gemv_kernel_name(qgm, main_case),
                      "algorithmic_bytes_per_launch": wbytes},
         "secondary": secondary,
     }

@@ -72,6 +72,20 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     p.splits = (int)ceil_div(p.wordtiles, p.tps);
     p.workgroups = (int64_t)p.rowblocks * p.splits;
     if (p.splits > 1) p.ws_partial_bytes = (size_t)p.rowblocks * p.splits * p.mmax * 16 * sizeof(float);
+    // M = 1: 8-row workgroups (twice as many) when they spread over the
+    // compute units more evenly, e.g. 384 row blocks -> 768 = 3 per CU
+    if (p.mmax == 1 && fmt != Q4K && p.tps <= 8 * GEMV_HALF_TPW) {
+      const auto fill = [](int64_t w) {   // busy share of the last round of workgroups
+        return (double)w / (double)(ceil_div(w, GEMM_TARGET_WG) * GEMM_TARGET_WG);
+      };
+      bool half = fill(2 * p.workgroups) > fill(p.workgroups);
+      const int rows_env = env_int("QGEMM_GEMV_ROWS", 0);
+      if (rows_env == 8 || rows_env == 16) half = rows_env == 8;
+      if (half) {
+        p.rows = 8;
+        p.workgroups *= 2;
+      }
+    }
     return p;
   }
   p.path = 2;
@@ -179,7 +193,7 @@ int qg_plan(int M, int N, int K, int group, int fmt, int out[5]) {
   out[1] = p.splits;
   out[2] = (int)p.workgroups;
   out[3] = p.path == 2 ? p.tm : p.mmax;
-  out[4] = p.path == 2 ? p.tn : 16;
+  out[4] = p.path == 2 ? p.tn : p.rows;
   return QG_OK;
 }
 

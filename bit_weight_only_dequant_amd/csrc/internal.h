@@ -16,6 +16,7 @@ constexpr int GEMV_MFMA_KW = 256;        // K covered by one wave of the MFMA GE
 constexpr int GEMV_THREADS = 512;          // 8 waves per workgroup
 constexpr int GEMV_TPW_MAX = 8;          // word tiles one wave streams per launch
 constexpr int GEMV_LDS_X_BYTES = 32768;  // x slice staged per workgroup
+constexpr int GEMV_HALF_TPW = 4;        // word tiles per wave of the half-row-block GEMV, at most
 constexpr int GEMM_THREADS = 512;        // 8 waves; they split the workgroup's K range
 constexpr int GEMM_TM = 64;              // workgroup tile rows (M)
 constexpr int GEMM_TN = 64;              // workgroup tile columns (N)
@@ -36,6 +37,7 @@ struct Plan {
   int tps = 0;         // word tiles per split
   int wordtiles = 0;   // total word tiles along K
   int rowblocks = 0;   // N / 16 (rounded up)
+  int rows = 16;       // GEMV: W rows per workgroup (16; 8 for the half-row-block kernel)
   int tm = 0, tn = 0;  // GEMM tile rows and columns (64 x 64; 64 x 32 or 32 x 32 for small M)
   int tiles_n = 0;     // GEMM tiles along N
   int tiles_m = 0;     // GEMM tiles along M
@@ -51,7 +53,7 @@ int check_align(const void* p);
 int check_ld(int ld, int minimum);
 
 // Launch plan for a validated problem.  Environment overrides (for tuning and
-// tests): QGEMM_FORCE=gemv|gemm, QGEMM_SPLITK=<n>.
+// tests): QGEMM_FORCE=gemv|gemm, QGEMM_SPLITK=<n>, QGEMM_GEMV_ROWS=8|16 (M = 1).
 Plan make_plan(int M, int N, int K, int group, int fmt);
 
 }  // namespace qg

@@ -542,6 +542,143 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   a.ws[((int64_t)rb * a.splits + split) * MMAX * 16 + tid] = total;
 }
 
+// Decode GEMV on half row blocks (M = 1, used when the row blocks alone would
+// leave the compute units unevenly loaded, e.g. 384 blocks on 256 CUs): a
+// workgroup takes rows 8 hb .. 8 hb + 7 of row block blockIdx.x / 2
+// (hb = blockIdx.x % 2), so twice as many workgroups of half the work.  Its NW
+// waves take TPW word tiles each, two at a time: lane l = r8 + 8 g + 32 t reads
+// the 16-byte chunk of row 8 hb + r8, lane group g, of tile 2 i + t of the
+// wave's run -- one 16-byte load per lane and pair, as gemv_kernel.  Same
+// dequant and dot products; lanes sum over g and t, the waves through LDS in
+// wave order.
+template <int FMT, int NW, int TPW>
+__global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
+  using F = Fmt<FMT>;
+  static_assert(!F::KQ, "fp16 scale-and-zero formats only");
+  static_assert(TPW % 2 == 0, "tiles go in pairs");
+  constexpr int NP = TPW / 2;                  // tile pairs per wave
+  constexpr int KW = TPW * F::KT;              // k range of one wave
+  constexpr int GWMAX = KW / 32;
+  constexpr int XCH = KW / 8;
+  constexpr int NXC = (XCH + 63) / 64;
+  constexpr int NSZ = (8 * GWMAX + 63) / 64;
+  constexpr int XB = KW * 2, WB = XB + 8 * GWMAX * 4;
+  __shared__ __align__(16) uint8_t half_smem[NW * WB + NW * 8 * sizeof(float)];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f16* xs = reinterpret_cast<f16*>(half_smem + wave * WB);                 // [KW]
+  uint32_t* sz = reinterpret_cast<uint32_t*>(half_smem + wave * WB + XB);  // [8][GWMAX] s | z << 16
+  float* red = reinterpret_cast<float*>(half_smem + NW * WB);              // [NW][8]
+  const int r8 = lane & 7, g = (lane >> 3) & 3, t = lane >> 5;
+  const int rb = blockIdx.x >> 1, hb = blockIdx.x & 1, split = blockIdx.y;
+  const int row0 = rb * 16 + hb * 8;
+  const int T0 = split * a.tps, T1 = min(a.wordtiles, T0 + a.tps);
+  const int wt0 = T0 + wave * TPW;
+  const int nt = max(0, min(T1, wt0 + TPW) - wt0);   // tiles of this wave
+  const int k0 = wt0 * F::KT;
+  const int lg = __builtin_ctz(a.group);
+  const int ng = a.K >> lg;
+  const int gstride = KW >> lg;                   // groups per wave, a power of two
+  const int lgs = __builtin_ctz(gstride);
+  const int gs0 = k0 >> lg;
+
+  // 1. loads: (scale, zero) entries of the 8 rows, x slice, one code chunk
+  //    per tile pair; clamped, never out of range
+  const int64_t szbase = (int64_t)row0 * ng * 2;
+  const char* sp = reinterpret_cast<const char*>(a.scales) + szbase;
+  const char* zp = reinterpret_cast<const char*>(F::HAS_Z ? a.zeros : a.scales) + szbase;
+  uint32_t sraw[NSZ], zraw[NSZ];
+#pragma unroll
+  for (int j = 0; j < NSZ; ++j) {
+    const int e = lane + 64 * j;   // row e >> lgs, group gs0 + e % gstride
+    const int er = e >> lgs, eg = gs0 + (e & (gstride - 1));
+    const bool ok = e < 8 * gstride && row0 + er < a.N && eg < ng;
+    const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
+    sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
+    if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+    else zraw[j] = F::ZBITS;
+  }
+  float res = 0.0f;
+  if (a.resid && a.splits == 1 && tid < 8) res = (float)a.resid[min(row0 + tid, a.N - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+  u4 xr[NXC];
+#pragma unroll
+  for (int j = 0; j < NXC; ++j) {
+    const int k = k0 + (lane + 64 * j) * 8;
+    xr[j] = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(a.x) + (k < a.K ? (uint32_t)k * 2u : 0u));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u4 code[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int64_t tile = (int64_t)rb * a.wordtiles + min(wt0 + 2 * i + t, a.wordtiles - 1);
+    code[i] = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(a.packed) + tile * 1024 +
+                                           (g * 16 + hb * 8 + r8) * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. stage x (zero past K) and the (scale, zero) pairs in the wave's region
+#pragma unroll
+  for (int j = 0; j < NXC; ++j) {
+    const int c = lane + 64 * j;
+    if (c < XCH) *reinterpret_cast<u4*>(xs + c * 8) = k0 + c * 8 < a.K ? xr[j] : u4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int j = 0; j < NSZ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < 8 * gstride) sz[(e >> lgs) * GWMAX + (e & (gstride - 1))] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // 3. dot products of the lane's chunk, one run of SW codes at a time
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    if (2 * i + t >= nt) continue;
+#pragma unroll
+    for (int p = 0; p < F::NSEG; ++p) {
+      const int kl = (2 * i + t) * F::KT + g * F::LS + p * F::SW;
+      const uint32_t szv = sz[r8 * GWMAX + (kl >> lg)];
+      const float sf = (float)__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu));
+      const f16 z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
+      h2 q[F::SW / 2];
+      run_qmz<FMT>(code[i], p, z, q);
+      const h8* xp = reinterpret_cast<const h8*>(xs + kl);
+      float A0 = 0.0f, A1 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < F::SW / 8; ++c) {
+        const h8 xv = xp[c];
+        float t0 = (c & 1) ? A1 : A0;
+        t0 = __builtin_amdgcn_fdot2(q[4 * c + 0], h2{xv[0], xv[1]}, t0, false);
+        t0 = __builtin_amdgcn_fdot2(q[4 * c + 1], h2{xv[2], xv[3]}, t0, false);
+        t0 = __builtin_amdgcn_fdot2(q[4 * c + 2], h2{xv[4], xv[5]}, t0, false);
+        t0 = __builtin_amdgcn_fdot2(q[4 * c + 3], h2{xv[6], xv[7]}, t0, false);
+        if (c & 1) A1 = t0; else A0 = t0;
+      }
+      acc = fmaf(sf, A0 + A1, acc);
+    }
+  }
+
+  // 4. sum over g and t (lanes r8 + 8 i), then over the waves in wave order
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if (lane < 8) red[wave * 8 + lane] = acc;
+  __syncthreads();
+  if (tid >= 8) return;
+  float total = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) total += red[w * 8 + tid];
+  if (a.splits == 1) {
+    if (row0 + tid < a.N) a.y[row0 + tid] = (f16)(total + res);
+    return;
+  }
+  // split-K: the same partial layout as gemv_kernel with one row of x
+  a.ws[((int64_t)rb * a.splits + split) * 16 + hb * 8 + tid] = total;
+}
+
 // LDS bytes of gemv_mfma_kernel: per wave its x rows (padded by 16 bytes so
 // that the A-fragment reads of 16 rows fall in distinct banks) and its
 // (scale, zero) pairs, then one 16 x 16 fp32 block per wave for the final sum
@@ -1258,7 +1395,18 @@ static bool launch_gemv_dot_w(const GemvArgs& a, int tps, hipStream_t s) {
 // 16 waves when a workgroup has at least 16 word tiles (more waves in flight,
 // one tile each at K = 2048), 8 otherwise
 template <int FMT>
-static bool launch_gemv_dot(const GemvArgs& a, int tps, hipStream_t s) {
+static bool launch_gemv_dot(const GemvArgs& a, int tps, int rows, hipStream_t s) {
+  if constexpr (!Fmt<FMT>::KQ) {
+    if (rows == 8) {   // half row blocks: 4 waves of 2 tiles, 8 of 2, or 8 of 4
+      const dim3 grid((unsigned)(2 * a.rowblocks), (unsigned)a.splits);
+      if (tps <= 8) hipLaunchKernelGGL((gemv_half_kernel<FMT, 4, 2>), grid, dim3(256), 0, s, a);
+      else if (tps <= 16) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, 2>), grid, dim3(512), 0, s, a);
+      else if (tps <= 8 * GEMV_HALF_TPW) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, GEMV_HALF_TPW>), grid, dim3(512), 0, s, a);
+      else return false;
+      return true;
+    }
+  }
+  if (rows != 16) return false;
   return tps >= 16 ? launch_gemv_dot_w<FMT, 16>(a, tps, s) : launch_gemv_dot_w<FMT, 8>(a, tps, s);
 }
 
@@ -1276,11 +1424,11 @@ static bool launch_gemv_mfma(const GemvArgs& a, int tps, hipStream_t s) {
   return true;
 }
 
-// mmax 1: v_dot2 GEMV; 4, 8, 16: rows of the MFMA GEMV
+// mmax 1: v_dot2 GEMV (16- or 8-row workgroups); 4, 8, 16: rows of the MFMA GEMV
 template <int FMT>
-static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, hipStream_t s) {
+static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, int rows, hipStream_t s) {
   switch (mmax) {
-    case 1: return launch_gemv_dot<FMT>(a, tps, s);
+    case 1: return launch_gemv_dot<FMT>(a, tps, rows, s);
     case 4: return launch_gemv_mfma<FMT, 4>(a, tps, s);
     case 8: return launch_gemv_mfma<FMT, 8>(a, tps, s);
     default: return launch_gemv_mfma<FMT, 16>(a, tps, s);
@@ -1364,11 +1512,11 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
       return QG_E_UNSUPPORTED;
     bool launched;
     switch (fmt) {
-      case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, p.tps, s); break;
-      case QG_INT2_ASYM: launched = launch_gemv_f<INT2_ASYM>(a, p.mmax, p.tps, s); break;
-      case QG_Q8_0: launched = launch_gemv_f<Q8_0>(a, p.mmax, p.tps, s); break;
-      case QG_Q4K: launched = launch_gemv_f<Q4K>(a, p.mmax, p.tps, s); break;
-      default: launched = launch_gemv_f<Q4_0>(a, p.mmax, p.tps, s); break;
+      case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, p.tps, p.rows, s); break;
+      case QG_INT2_ASYM: launched = launch_gemv_f<INT2_ASYM>(a, p.mmax, p.tps, p.rows, s); break;
+      case QG_Q8_0: launched = launch_gemv_f<Q8_0>(a, p.mmax, p.tps, p.rows, s); break;
+      case QG_Q4K: launched = launch_gemv_f<Q4K>(a, p.mmax, p.tps, p.rows, s); break;
+      default: launched = launch_gemv_f<Q4_0>(a, p.mmax, p.tps, p.rows, s); break;
     }
     if (!launched) return QG_E_UNSUPPORTED;
     if (p.splits > 1) {

@@ -155,6 +155,15 @@ def test_host_repack_is_a_permutation_of_codes():
     assert np.array_equal(a, b)
 
 
+def test_gemv_rows_override(monkeypatch):
+    monkeypatch.setenv("QGEMM_GEMV_ROWS", "16")
+    assert qgm.plan(1, 6144, 2048, 128, 0)["tile_n"] == 16
+    monkeypatch.setenv("QGEMM_GEMV_ROWS", "8")
+    assert qgm.plan(1, 8192, 2048, 128, 0)["tile_n"] == 8
+    assert qgm.plan(1, 8192, 2048, 256, 4)["tile_n"] == 16      # q4k has no 8-row kernel
+    assert qgm.plan(1, 8192, 16384, 128, 0)["tile_n"] == 16     # 128 tiles: past 8 waves x 4 tiles
+
+
 def test_plans_for_the_workloads():
     assert qgm.plan(1, 6144, 2048, 128, 0)["path"] == "gemv"
     assert qgm.plan(8, 6144, 2048, 128, 0)["path"] == "gemv"
@@ -177,3 +186,10 @@ def test_plans_for_the_workloads():
     k = qgm.plan(128, 8192, 2048, 256, 4)
     assert k["path"] == "gemm" and k["splits"] == 1
     assert qgm.plan(1, 8192, 2048, 256, 4)["path"] == "gemv"
+    # M = 1: 8-row workgroups when 16-row ones leave the CUs unevenly loaded
+    # (384 row blocks on 256 CUs), 16-row ones when they already fill them
+    assert (qgm.plan(1, 6144, 2048, 128, 0)["tile_n"], qgm.plan(1, 6144, 2048, 128, 0)["workgroups"]) == (8, 768)
+    assert (qgm.plan(1, 8192, 2048, 128, 0)["tile_n"], qgm.plan(1, 8192, 2048, 128, 0)["workgroups"]) == (16, 512)
+    assert qgm.plan(1, 6144, 2048, 32, 3)["tile_n"] == 8
+    assert qgm.plan(1, 6144, 2048, 256, 4)["tile_n"] == 16   # q4k: 16-row kernel only
+    assert qgm.plan(8, 6144, 2048, 128, 0)["tile_n"] == 16
