@@ -322,10 +322,15 @@ struct GemvArgs {
   int wordtiles, rowblocks, splits, tps;
 };
 
-// sum over lanes l, l^16, l^32, l^48 (result in every lane)
-__device__ __forceinline__ float sum_lane_groups(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+// v plus its value in lane l ^ 8: a DPP rotate of each 16-lane row by 8 (no
+// LDS round trip, no lane-index arithmetic)
+__device__ __forceinline__ float add_lane_xor8(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+}
+
+// v plus its value in lane l ^ 16: ds_swizzle in bit mode (and 0x1f, xor 0x10)
+__device__ __forceinline__ float add_lane_xor16(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401f));
 }
 
 // LDS bytes of gemv_kernel: per wave its x slice, (scale, zero) pairs (q4k:
@@ -335,7 +340,7 @@ template <int FMT> constexpr size_t gemv_lds_bytes_for(int mmax, int tpw, int nw
   const int KW = tpw * Fmt<FMT>::KT;
   const int SZB = Fmt<FMT>::KQ ? 8 : 4;
   const int XSB = Fmt<FMT>::KQ ? mmax * (KW / 32) * 4 : 0;
-  return (size_t)nw * (mmax * KW * 2 + 16 * (KW / 32) * SZB + XSB) + (size_t)nw * mmax * 16 * sizeof(float);
+  return (size_t)nw * (mmax * KW * 2 + 16 * (KW / 32) * SZB + XSB) + (size_t)nw * mmax * 32 * sizeof(float);
 }
 template <int FMT, int MMAX, int TPW, int NW> constexpr size_t gemv_lds_bytes() {
   return gemv_lds_bytes_for<FMT>(MMAX, TPW, NW);
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   uint32_t* sz = reinterpret_cast<uint32_t*>(gemv_smem + wave * WB + XB);  // [16][GWMAX] s | z << 16
   float2* szk = reinterpret_cast<float2*>(gemv_smem + wave * WB + XB);     // q4k: [16][GWMAX] (d*sc, dmin*m)
   float* xsum = reinterpret_cast<float*>(gemv_smem + wave * WB + XB + SB); // q4k: [MMAX][GWMAX]
-  float* red = reinterpret_cast<float*>(gemv_smem + NW * WB);              // [NW][MMAX][16]
+  float* red = reinterpret_cast<float*>(gemv_smem + NW * WB);              // [NW][MMAX][2][16]
 
   const int g = lane >> 4, r = lane & 15;
   const int rb = blockIdx.x, split = blockIdx.y;
@@ -406,11 +411,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
       else zraw[j] = F::ZBITS;  // the implicit zero point
     }
   }
-  const int om = tid >> 4, orow = tid & 15;
-  float res = 0.0f;
+  const int om = tid >> 5, orow = tid & 15;   // output of thread tid < 32 MMAX (final sum)
+  uint32_t res = 0u;                           // residual, fp16 bits
   if (a.resid && a.splits == 1) {
     const int mm = min(om, a.M - 1), nc = min(rb * 16 + orow, a.N - 1);
-    res = (float)a.resid[(int64_t)mm * a.ldr + nc];
+    res = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)mm * a.ldr + nc];
   }
   __builtin_amdgcn_sched_barrier(0);
   u4 xr[NXC];
@@ -521,25 +526,28 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  // 4. Sum the 4 lane groups across lanes, then the NW waves through LDS in
-  //    wave order (deterministic).
+  // 4. Sum lane groups g and g ^ 1 across lanes; the pairs (0, 1) and (2, 3)
+  //    of every wave go through LDS, summed over the waves in wave order
+  //    (deterministic), then the two pairs across lanes.
 #pragma unroll
   for (int m = 0; m < MMAX; ++m) {
-    const float v = sum_lane_groups(acc[m]);
-    if (g == 0) red[(wave * MMAX + m) * 16 + r] = v;
+    const float v = add_lane_xor16(acc[m]);
+    if ((g & 1) == 0) red[((wave * MMAX + m) * 2 + (g >> 1)) * 16 + r] = v;
   }
   __syncthreads();
-  if (tid >= MMAX * 16) return;
+  if (tid >= MMAX * 32) return;
   float total = 0.0f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) total += red[(w * MMAX + om) * 16 + orow];
+  for (int w = 0; w < NW; ++w) total += red[(w * MMAX + om) * 32 + (tid & 31)];
+  total = add_lane_xor16(total);
+  if (tid & 16) return;
   const int on = rb * 16 + orow;
   if (a.splits == 1) {
-    if (om < a.M && on < a.N) a.y[(int64_t)om * a.ldy + on] = (f16)(total + res);
+    if (om < a.M && on < a.N) a.y[(int64_t)om * a.ldy + on] = (f16)(total + (float)__builtin_bit_cast(f16, (uint16_t)res));
     return;
   }
   // split-K: this split's partial; gemv_reduce_kernel sums the splits in order
-  a.ws[((int64_t)rb * a.splits + split) * MMAX * 16 + tid] = total;
+  a.ws[((int64_t)rb * a.splits + split) * MMAX * 16 + om * 16 + orow] = total;
 }
 
 // Decode GEMV on half row blocks (M = 1, used when the row blocks alone would
@@ -563,12 +571,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   constexpr int NXC = (XCH + 63) / 64;
   constexpr int NSZ = (8 * GWMAX + 63) / 64;
   constexpr int XB = KW * 2, WB = XB + 8 * GWMAX * 4;
-  __shared__ __align__(16) uint8_t half_smem[NW * WB + NW * 8 * sizeof(float)];
+  __shared__ __align__(16) uint8_t half_smem[NW * WB + NW * 16 * sizeof(float)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f16* xs = reinterpret_cast<f16*>(half_smem + wave * WB);                 // [KW]
   uint32_t* sz = reinterpret_cast<uint32_t*>(half_smem + wave * WB + XB);  // [8][GWMAX] s | z << 16
-  float* red = reinterpret_cast<float*>(half_smem + NW * WB);              // [NW][8]
+  float* red = reinterpret_cast<float*>(half_smem + NW * WB);              // [NW][2][8]
   const int r8 = lane & 7, g = (lane >> 3) & 3, t = lane >> 5;
   const int rb = blockIdx.x >> 1, hb = blockIdx.x & 1, split = blockIdx.y;
   const int row0 = rb * 16 + hb * 8;
@@ -598,8 +606,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
     if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
     else zraw[j] = F::ZBITS;
   }
-  float res = 0.0f;
-  if (a.resid && a.splits == 1 && tid < 8) res = (float)a.resid[min(row0 + tid, a.N - 1)];
+  uint32_t res = 0u;   // residual of row row0 + (tid & 7), fp16 bits (no branch, no wait here)
+  if (a.resid && a.splits == 1) res = reinterpret_cast<const uint16_t*>(a.resid)[min(row0 + (tid & 7), a.N - 1)];
   __builtin_amdgcn_sched_barrier(0);
   u4 xr[NXC];
 #pragma unroll
@@ -661,18 +669,20 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
     }
   }
 
-  // 4. sum over g and t (lanes r8 + 8 i), then over the waves in wave order
-  acc += __shfl_xor(acc, 8);
-  acc += __shfl_xor(acc, 16);
-  acc += __shfl_xor(acc, 32);
-  if (lane < 8) red[wave * 8 + lane] = acc;
+  // 4. sum over g across lanes (l ^ 8, l ^ 16); the two tiles t of every wave
+  //    through LDS, summed over the waves in wave order, then over t across
+  //    lanes (l ^ 8 of the first row)
+  acc = add_lane_xor16(add_lane_xor8(acc));
+  if (g == 0) red[wave * 16 + t * 8 + r8] = acc;
   __syncthreads();
-  if (tid >= 8) return;
+  if (tid >= 16) return;
   float total = 0.0f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) total += red[w * 8 + tid];
+  for (int w = 0; w < NW; ++w) total += red[w * 16 + tid];
+  total = add_lane_xor8(total);
+  if (tid >= 8) return;
   if (a.splits == 1) {
-    if (row0 + tid < a.N) a.y[row0 + tid] = (f16)(total + res);
+    if (row0 + tid < a.N) a.y[row0 + tid] = (f16)(total + (float)__builtin_bit_cast(f16, (uint16_t)res));
     return;
   }
   // split-K: the same partial layout as gemv_kernel with one row of x
