@@ -71,10 +71,10 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     p.tps = (int)ceil_div(p.wordtiles, s);
     p.splits = (int)ceil_div(p.wordtiles, p.tps);
     p.workgroups = (int64_t)p.rowblocks * p.splits;
-    if (p.splits > 1) p.ws_partial_bytes = (size_t)p.rowblocks * p.splits * p.mmax * 16 * sizeof(float);
-    // M = 1: 8-row workgroups (twice as many) when they spread over the
-    // compute units more evenly, e.g. 384 row blocks -> 768 = 3 per CU
-    if (p.mmax == 1 && fmt != Q4K && p.tps <= 8 * GEMV_HALF_TPW) {
+    // M <= 2: 8-row workgroups (twice as many) when they spread over the
+    // compute units more evenly, e.g. 384 row blocks -> 768 = 3 per CU; M = 2
+    // then takes the v_dot2 kernel with both rows sharing each dequantized pair
+    if (M <= 2 && fmt != Q4K && p.tps <= 8 * GEMV_HALF_TPW) {
       const auto fill = [](int64_t w) {   // busy share of the last round of workgroups
         return (double)w / (double)(ceil_div(w, GEMM_TARGET_WG) * GEMM_TARGET_WG);
       };
@@ -83,9 +83,11 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
       if (rows_env == 8 || rows_env == 16) half = rows_env == 8;
       if (half) {
         p.rows = 8;
+        p.mmax = M;
         p.workgroups *= 2;
       }
     }
+    if (p.splits > 1) p.ws_partial_bytes = (size_t)p.rowblocks * p.splits * p.mmax * 16 * sizeof(float);
     return p;
   }
   p.path = 2;

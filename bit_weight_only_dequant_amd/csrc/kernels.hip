@@ -18,7 +18,10 @@
 //                        that each wave stages for itself in LDS, fp32 scale
 //                        per 32 codes (q8_0: 16; q4k: d*sc and the offset
 //                        dmin*m times the run's x sum), lane groups summed by
-//                        lane shuffles and waves through LDS.
+//                        DPP and ds_swizzle, waves through LDS.
+//   gemv_half<FMT, R>    M <= 2 when 16-row workgroups would load the CUs
+//                        unevenly (N = 6144: 384 blocks on 256 CUs): the same
+//                        work on 8-row workgroups, twice as many.
 //   gemv_mfma<FMT, R>    2 <= M <= 16.  Same loads and staging; every 8 codes,
 //                        dequantized to fp16 weights, are one
 //                        v_mfma_f32_16x16x32_f16 step (the packed layout is
@@ -550,16 +553,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   a.ws[((int64_t)rb * a.splits + split) * MMAX * 16 + om * 16 + orow] = total;
 }
 
-// Decode GEMV on half row blocks (M = 1, used when the row blocks alone would
+// Decode GEMV on half row blocks (M = 1 or 2, used when the row blocks alone would
 // leave the compute units unevenly loaded, e.g. 384 blocks on 256 CUs): a
 // workgroup takes rows 8 hb .. 8 hb + 7 of row block blockIdx.x / 2
 // (hb = blockIdx.x % 2), so twice as many workgroups of half the work.  Its NW
 // waves take TPW word tiles each, two at a time: lane l = r8 + 8 g + 32 t reads
 // the 16-byte chunk of row 8 hb + r8, lane group g, of tile 2 i + t of the
 // wave's run -- one 16-byte load per lane and pair, as gemv_kernel.  Same
-// dequant and dot products; lanes sum over g and t, the waves through LDS in
-// wave order.
-template <int FMT, int NW, int TPW>
+// dequant and dot products (MMAX rows of x share each exact (q - z) pair); lanes
+// sum over g and t, the waves through LDS in wave order.
+template <int FMT, int NW, int TPW, int MMAX>
 __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   using F = Fmt<FMT>;
   static_assert(!F::KQ, "fp16 scale-and-zero formats only");
@@ -567,16 +570,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   constexpr int NP = TPW / 2;                  // tile pairs per wave
   constexpr int KW = TPW * F::KT;              // k range of one wave
   constexpr int GWMAX = KW / 32;
-  constexpr int XCH = KW / 8;
+  constexpr int XCH = MMAX * KW / 8;
   constexpr int NXC = (XCH + 63) / 64;
   constexpr int NSZ = (8 * GWMAX + 63) / 64;
-  constexpr int XB = KW * 2, WB = XB + 8 * GWMAX * 4;
-  __shared__ __align__(16) uint8_t half_smem[NW * WB + NW * 16 * sizeof(float)];
+  constexpr int XB = MMAX * KW * 2, WB = XB + 8 * GWMAX * 4;
+  __shared__ __align__(16) uint8_t half_smem[NW * WB + NW * MMAX * 16 * sizeof(float)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  f16* xs = reinterpret_cast<f16*>(half_smem + wave * WB);                 // [KW]
+  f16* xs = reinterpret_cast<f16*>(half_smem + wave * WB);                 // [MMAX][KW]
   uint32_t* sz = reinterpret_cast<uint32_t*>(half_smem + wave * WB + XB);  // [8][GWMAX] s | z << 16
-  float* red = reinterpret_cast<float*>(half_smem + NW * WB);              // [NW][2][8]
+  float* red = reinterpret_cast<float*>(half_smem + NW * WB);              // [NW][MMAX][2][8]
   const int r8 = lane & 7, g = (lane >> 3) & 3, t = lane >> 5;
   const int rb = blockIdx.x >> 1, hb = blockIdx.x & 1, split = blockIdx.y;
   const int row0 = rb * 16 + hb * 8;
@@ -589,9 +592,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   const int gstride = KW >> lg;                   // groups per wave, a power of two
   const int lgs = __builtin_ctz(gstride);
   const int gs0 = k0 >> lg;
-
-  // 1. loads: (scale, zero) entries of the 8 rows, x slice, one code chunk
-  //    per tile pair; clamped, never out of range
+  // 1. loads: (scale, zero) entries of the 8 rows, the residual, x rows, one
+  //    code chunk per tile pair; clamped, never out of range
   const int64_t szbase = (int64_t)row0 * ng * 2;
   const char* sp = reinterpret_cast<const char*>(a.scales) + szbase;
   const char* zp = reinterpret_cast<const char*>(F::HAS_Z ? a.zeros : a.scales) + szbase;
@@ -606,14 +608,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
     if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
     else zraw[j] = F::ZBITS;
   }
-  uint32_t res = 0u;   // residual of row row0 + (tid & 7), fp16 bits (no branch, no wait here)
-  if (a.resid && a.splits == 1) res = reinterpret_cast<const uint16_t*>(a.resid)[min(row0 + (tid & 7), a.N - 1)];
+  const int om = (tid >> 4) % MMAX;   // output row of thread tid < 16 MMAX (final sum)
+  uint32_t res = 0u;                  // its residual, fp16 bits (no branch, no wait here)
+  if (a.resid && a.splits == 1)
+    res = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)min(om, a.M - 1) * a.ldr + min(row0 + (tid & 7), a.N - 1)];
   __builtin_amdgcn_sched_barrier(0);
   u4 xr[NXC];
 #pragma unroll
   for (int j = 0; j < NXC; ++j) {
-    const int k = k0 + (lane + 64 * j) * 8;
-    xr[j] = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(a.x) + (k < a.K ? (uint32_t)k * 2u : 0u));
+    const int c = lane + 64 * j;   // one row: chunk c at k0 + 8c (lanes past the wave's slice read in range too)
+    const int m = MMAX == 1 ? 0 : c / (KW / 8), k = k0 + (MMAX == 1 ? c : c % (KW / 8)) * 8;
+    const bool ok = (MMAX == 1 || m < a.M) && k < a.K;
+    xr[j] = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(a.x) + (ok ? ((uint32_t)m * a.ldx + k) * 2u : 0u));
   }
   __builtin_amdgcn_sched_barrier(0);
   u4 code[NP];
@@ -625,11 +631,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. stage x (zero past K) and the (scale, zero) pairs in the wave's region
+  // 2. stage x (zero past M and K) and the (scale, zero) pairs in the wave's region
 #pragma unroll
   for (int j = 0; j < NXC; ++j) {
     const int c = lane + 64 * j;
-    if (c < XCH) *reinterpret_cast<u4*>(xs + c * 8) = k0 + c * 8 < a.K ? xr[j] : u4{0u, 0u, 0u, 0u};
+    const int m = c / (KW / 8), kk = (c % (KW / 8)) * 8;
+    if (c < XCH) *reinterpret_cast<u4*>(xs + m * KW + kk) = (MMAX == 1 || m < a.M) && k0 + kk < a.K ? xr[j] : u4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
@@ -639,9 +646,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  // 3. dot products of the lane's chunk, one run of SW codes at a time
-  float acc = 0.0f;
+  // 3. dot products of the lane's chunk, one run of SW codes at a time; the
+  //    exact (q - z) pairs serve every row of x
+  float acc[MMAX];
+#pragma unroll
+  for (int m = 0; m < MMAX; ++m) acc[m] = 0.0f;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     if (2 * i + t >= nt) continue;
@@ -653,40 +662,47 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
       const f16 z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
       h2 q[F::SW / 2];
       run_qmz<FMT>(code[i], p, z, q);
-      const h8* xp = reinterpret_cast<const h8*>(xs + kl);
-      float A0 = 0.0f, A1 = 0.0f;
 #pragma unroll
-      for (int c = 0; c < F::SW / 8; ++c) {
-        const h8 xv = xp[c];
-        float t0 = (c & 1) ? A1 : A0;
-        t0 = __builtin_amdgcn_fdot2(q[4 * c + 0], h2{xv[0], xv[1]}, t0, false);
-        t0 = __builtin_amdgcn_fdot2(q[4 * c + 1], h2{xv[2], xv[3]}, t0, false);
-        t0 = __builtin_amdgcn_fdot2(q[4 * c + 2], h2{xv[4], xv[5]}, t0, false);
-        t0 = __builtin_amdgcn_fdot2(q[4 * c + 3], h2{xv[6], xv[7]}, t0, false);
-        if (c & 1) A1 = t0; else A0 = t0;
+      for (int m = 0; m < MMAX; ++m) {
+        const h8* xp = reinterpret_cast<const h8*>(xs + m * KW + kl);
+        float A0 = 0.0f, A1 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < F::SW / 8; ++c) {
+          const h8 xv = xp[c];
+          float t0 = (c & 1) ? A1 : A0;
+          t0 = __builtin_amdgcn_fdot2(q[4 * c + 0], h2{xv[0], xv[1]}, t0, false);
+          t0 = __builtin_amdgcn_fdot2(q[4 * c + 1], h2{xv[2], xv[3]}, t0, false);
+          t0 = __builtin_amdgcn_fdot2(q[4 * c + 2], h2{xv[4], xv[5]}, t0, false);
+          t0 = __builtin_amdgcn_fdot2(q[4 * c + 3], h2{xv[6], xv[7]}, t0, false);
+          if (c & 1) A1 = t0; else A0 = t0;
+        }
+        acc[m] = fmaf(sf, A0 + A1, acc[m]);
       }
-      acc = fmaf(sf, A0 + A1, acc);
     }
   }
-
   // 4. sum over g across lanes (l ^ 8, l ^ 16); the two tiles t of every wave
   //    through LDS, summed over the waves in wave order, then over t across
-  //    lanes (l ^ 8 of the first row)
-  acc = add_lane_xor16(add_lane_xor8(acc));
-  if (g == 0) red[wave * 16 + t * 8 + r8] = acc;
+  //    lanes (l ^ 8 within a 16-lane row)
+#pragma unroll
+  for (int m = 0; m < MMAX; ++m) {
+    const float v = add_lane_xor16(add_lane_xor8(acc[m]));
+    if (g == 0) red[(wave * MMAX + m) * 16 + t * 8 + r8] = v;
+  }
   __syncthreads();
-  if (tid >= 16) return;
+  if (tid >= MMAX * 16) return;
   float total = 0.0f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) total += red[w * 16 + tid];
+  for (int w = 0; w < NW; ++w) total += red[(w * MMAX + om) * 16 + (tid & 15)];
   total = add_lane_xor8(total);
-  if (tid >= 8) return;
+  if (tid & 8) return;
+  const int on = row0 + (tid & 7);
   if (a.splits == 1) {
-    if (row0 + tid < a.N) a.y[row0 + tid] = (f16)(total + (float)__builtin_bit_cast(f16, (uint16_t)res));
+    if (om < a.M && on < a.N)
+      a.y[(int64_t)om * a.ldy + on] = (f16)(total + (float)__builtin_bit_cast(f16, (uint16_t)res));
     return;
   }
-  // split-K: the same partial layout as gemv_kernel with one row of x
-  a.ws[((int64_t)rb * a.splits + split) * 16 + hb * 8 + tid] = total;
+  // split-K: the same partial layout as gemv_kernel with MMAX rows of x
+  a.ws[((int64_t)rb * a.splits + split) * MMAX * 16 + om * 16 + hb * 8 + (tid & 7)] = total;
 }
 
 // LDS bytes of gemv_mfma_kernel: per wave its x rows (padded by 16 bytes so
@@ -1404,18 +1420,24 @@ static bool launch_gemv_dot_w(const GemvArgs& a, int tps, hipStream_t s) {
 
 // 16 waves when a workgroup has at least 16 word tiles (more waves in flight,
 // one tile each at K = 2048), 8 otherwise
+// half row blocks (8-row workgroups): 4 waves of 2 tiles, 8 of 2, or 8 of 4
+template <int FMT, int MMAX>
+static bool launch_gemv_half(const GemvArgs& a, int tps, hipStream_t s) {
+  if constexpr (Fmt<FMT>::KQ) {
+    return false;
+  } else {
+    const dim3 grid((unsigned)(2 * a.rowblocks), (unsigned)a.splits);
+    if (tps <= 8) hipLaunchKernelGGL((gemv_half_kernel<FMT, 4, 2, MMAX>), grid, dim3(256), 0, s, a);
+    else if (tps <= 16) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, 2, MMAX>), grid, dim3(512), 0, s, a);
+    else if (tps <= 8 * GEMV_HALF_TPW) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, GEMV_HALF_TPW, MMAX>), grid, dim3(512), 0, s, a);
+    else return false;
+    return true;
+  }
+}
+
 template <int FMT>
 static bool launch_gemv_dot(const GemvArgs& a, int tps, int rows, hipStream_t s) {
-  if constexpr (!Fmt<FMT>::KQ) {
-    if (rows == 8) {   // half row blocks: 4 waves of 2 tiles, 8 of 2, or 8 of 4
-      const dim3 grid((unsigned)(2 * a.rowblocks), (unsigned)a.splits);
-      if (tps <= 8) hipLaunchKernelGGL((gemv_half_kernel<FMT, 4, 2>), grid, dim3(256), 0, s, a);
-      else if (tps <= 16) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, 2>), grid, dim3(512), 0, s, a);
-      else if (tps <= 8 * GEMV_HALF_TPW) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, GEMV_HALF_TPW>), grid, dim3(512), 0, s, a);
-      else return false;
-      return true;
-    }
-  }
+  if (rows == 8) return launch_gemv_half<FMT, 1>(a, tps, s);
   if (rows != 16) return false;
   return tps >= 16 ? launch_gemv_dot_w<FMT, 16>(a, tps, s) : launch_gemv_dot_w<FMT, 8>(a, tps, s);
 }
@@ -1434,11 +1456,13 @@ static bool launch_gemv_mfma(const GemvArgs& a, int tps, hipStream_t s) {
   return true;
 }
 
-// mmax 1: v_dot2 GEMV (16- or 8-row workgroups); 4, 8, 16: rows of the MFMA GEMV
+// mmax 1: v_dot2 GEMV (16- or 8-row workgroups); 2: v_dot2 on 8-row workgroups;
+// 4, 8, 16: rows of the MFMA GEMV
 template <int FMT>
 static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, int rows, hipStream_t s) {
   switch (mmax) {
     case 1: return launch_gemv_dot<FMT>(a, tps, rows, s);
+    case 2: return rows == 8 && launch_gemv_half<FMT, 2>(a, tps, s);
     case 4: return launch_gemv_mfma<FMT, 4>(a, tps, s);
     case 8: return launch_gemv_mfma<FMT, 8>(a, tps, s);
     default: return launch_gemv_mfma<FMT, 16>(a, tps, s);

@@ -222,9 +222,9 @@ def test_split_k_variants(monkeypatch, splits, M):
     check_close(run_gemm(lin, c.x), ref_y(c, c.x), f"splitk {splits}")
 
 
-# M = 1 through both v_dot2 kernels: 16-row workgroups and 8-row (half row
-# block) workgroups of 4 x 2, 8 x 2 and 8 x 4 word tiles, with and without
-# split-K, ragged N and K, and a fused residual
+# M = 1 and 2 through 16-row workgroups (v_dot2 kernel, MFMA GEMV for M = 2)
+# and 8-row (half row block) workgroups of 4 x 2, 8 x 2 and 8 x 4 word tiles,
+# with and without split-K, ragged N and K, and a fused residual
 HALF_CASES = [
     # fmt, group, N, K, splits (0: the plan's own)
     (0, 128, 6144, 2048, 0), (0, 32, 100, 96, 0), (0, 64, 1000, 1024, 0), (0, 128, 4100, 4096, 0),
@@ -234,19 +234,20 @@ HALF_CASES = [
 ]
 
 
+@pytest.mark.parametrize("M", [1, 2])
 @pytest.mark.parametrize("rows", [8, 16])
 @pytest.mark.parametrize("fmt,group,N,K,splits", HALF_CASES)
-def test_gemv_row_variants(monkeypatch, rows, fmt, group, N, K, splits):
+def test_gemv_row_variants(monkeypatch, M, rows, fmt, group, N, K, splits):
     monkeypatch.setenv("QGEMM_GEMV_ROWS", str(rows))
     if splits:
         monkeypatch.setenv("QGEMM_SPLITK", str(splits))
-    p = qgm.plan(1, N, K, group, fmt)
-    say(f"gemv rows={rows} fmt={fmt} g={group} N={N} K={K} plan={p}")
+    p = qgm.plan(M, N, K, group, fmt)
+    say(f"gemv M={M} rows={rows} fmt={fmt} g={group} N={N} K={K} plan={p}")
     assert p["path"] == "gemv" and p["tile_n"] == rows
-    c = synth.random_codes_case(N + 3 * K + fmt + rows, fmt, group, N, K, 1)
+    c = synth.random_codes_case(N + 3 * K + fmt + rows + 7 * M, fmt, group, N, K, M)
     lin = qgm.QuantLinear.from_case(c, DEV)
-    res = synth.draw_x(np.random.default_rng(N + K), 1, N) if N % 2 else None
-    check_close(run_gemm(lin, c.x, residual=res), ref_y(c, c.x, residual=res), f"rows {rows}")
+    res = synth.draw_x(np.random.default_rng(N + K), M, N) if N % 2 else None
+    check_close(run_gemm(lin, c.x, residual=res), ref_y(c, c.x, residual=res), f"M {M} rows {rows}")
 
 
 # ----------------------------------------------------------------------------
