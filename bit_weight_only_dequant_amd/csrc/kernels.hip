@@ -776,11 +776,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
       else zraw[j] = F::ZBITS;  // the implicit zero point
     }
   }
-  float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // residual as raw fp16 bits, converted only at the store: a conversion here
+  // would make the wave wait for every load issued so far
+  uint32_t res[4] = {0u, 0u, 0u, 0u};
   if (a.resid && a.splits == 1 && wave == 0) {
     const int nc = min(rb * 16 + r, a.N - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) res[i] = (float)a.resid[(int64_t)min(4 * g + i, a.M - 1) * a.ldr + nc];
+    for (int i = 0; i < 4; ++i)
+      res[i] = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)min(4 * g + i, a.M - 1) * a.ldr + nc];
   }
   __builtin_amdgcn_sched_barrier(0);
   u4 xr[NXC];
@@ -866,7 +869,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * g + i;
-      if (m < a.M && n < a.N) a.y[(int64_t)m * a.ldy + n] = (f16)(tot[i] + res[i]);
+      if (m < a.M && n < a.N)
+        a.y[(int64_t)m * a.ldy + n] = (f16)(tot[i] + (float)__builtin_bit_cast(f16, (uint16_t)res[i]));
     }
     return;
   }
@@ -1182,18 +1186,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
     if (d < nst) issue_stage(d);
-  float res[16];
+  uint32_t res[16];   // residual, fp16 bits, converted only in the epilogue (no wait here)
   const int fb = wave < NBLK ? wave : 0;                 // block this wave finishes: (fb / NB, fb % NB)
   if (a.resid && a.splits == 1 && wave < NBLK) {
     const int colc = min(n0 + (fb % NB) * 32 + (lane & 31), a.N - 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = min(m0 + (fb / NB) * 32 + acc_row(i, lane), a.M - 1);
-      res[i] = (float)a.resid[(int64_t)row * a.ldr + colc];
+      res[i] = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)row * a.ldr + colc];
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) res[i] = 0.0f;
+    for (int i = 0; i < 16; ++i) res[i] = 0u;
   }
   {
     const int ist = min(DEPTH, nst);
@@ -1258,7 +1262,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = m0 + (fb / NB) * 32 + acc_row(i, lane);
-      if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(tot[i >> 2][i & 3] + res[i]);
+      if (row < a.M && col < a.N)
+        a.y[(int64_t)row * a.ldy + col] = (f16)(tot[i >> 2][i & 3] + (float)__builtin_bit_cast(f16, (uint16_t)res[i]));
     }
     return;
   }
