@@ -56,37 +56,49 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   const int split_env = env_int("QGEMM_SPLITK", 0);
   if (gemv) {
     p.path = 1;
-    p.mmax = M <= 1 ? 1 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     const int nw = GEMV_THREADS / 64;
     const int tps_lds = std::max(1, GEMV_LDS_X_BYTES / (kt_width * 2));
-    const int tps_max = p.mmax == 1 ? std::min(tps_lds, nw * GEMV_TPW_MAX) : nw * (GEMV_MFMA_KW / kt_width);
-    const int s_min = (int)ceil_div(p.wordtiles, tps_max);
-    // split only when there are too few row blocks to fill the chip: a split
-    // costs a second (reduce) launch
-    const int s_par = p.rowblocks >= GEMM_TARGET_WG ? 1 : (int)ceil_div(2 * GEMM_TARGET_WG, p.rowblocks);
-    const int s_fill = (int)ceil_div(p.wordtiles, nw);  // keep every wave busy
-    int s = std::max(s_min, std::min(s_par, s_fill));
-    if (split_env > 0) s = std::max(s_min, split_env);
-    s = std::min(std::max(s, 1), p.wordtiles);
-    p.tps = (int)ceil_div(p.wordtiles, s);
-    p.splits = (int)ceil_div(p.wordtiles, p.tps);
-    p.workgroups = (int64_t)p.rowblocks * p.splits;
-    // M <= 2: 8-row workgroups (twice as many) when they spread over the
-    // compute units more evenly, e.g. 384 row blocks -> 768 = 3 per CU; M = 2
-    // then takes the v_dot2 kernel with both rows sharing each dequantized pair
-    if (M <= 2 && fmt != Q4K && p.tps <= 8 * GEMV_HALF_TPW) {
-      const auto fill = [](int64_t w) {   // busy share of the last round of workgroups
-        return (double)w / (double)(ceil_div(w, GEMM_TARGET_WG) * GEMM_TARGET_WG);
-      };
-      bool half = fill(2 * p.workgroups) > fill(p.workgroups);
+    // per-workgroup word-tile caps: v_dot2 kernel (M = 1), MFMA GEMV (M > 1),
+    // 8-row v_dot2 kernel (M <= 2, not q4k)
+    const int cap16 = M <= 1 ? std::min(tps_lds, nw * GEMV_TPW_MAX) : nw * (GEMV_MFMA_KW / kt_width);
+    const int cap8 = nw * GEMV_HALF_TPW;
+    const bool can8 = M <= 2 && fmt != Q4K;
+    // K splits for a cap.  A split costs a second (reduce) launch and the fp32
+    // partials, about 2 us, more than an unsplit launch loses to idle CUs:
+    // split only when the cap forces it, or when fewer than GEMV_SPLIT_RB row
+    // blocks each carry more than GEMV_SPLIT_TILES word tiles (long streams on
+    // few CUs).  Once the reduce is paid, split far enough to fill the chip.
+    const auto splits_for = [&](int cap) {
+      const int s_min = (int)ceil_div(p.wordtiles, cap);
+      const bool split = s_min > 1 || (p.rowblocks < GEMV_SPLIT_RB && p.wordtiles > GEMV_SPLIT_TILES);
+      const int s_par = p.rowblocks >= GEMM_TARGET_WG ? 1 : (int)ceil_div(2 * GEMM_TARGET_WG, p.rowblocks);
+      const int s_fill = (int)ceil_div(p.wordtiles, nw);  // keep every wave busy
+      int s = split ? std::max(s_min, std::min(s_par, s_fill)) : 1;
+      if (split_env > 0) s = std::max(s_min, split_env);
+      s = std::min(std::max(s, 1), p.wordtiles);
+      return (int)ceil_div(p.wordtiles, ceil_div(p.wordtiles, s));   // splits of equal tile counts
+    };
+    const auto fill = [](int64_t w) {   // busy share of the last round of workgroups
+      return (double)w / (double)(ceil_div(w, GEMM_TARGET_WG) * GEMM_TARGET_WG);
+    };
+    const int s16 = splits_for(cap16);
+    const int s8 = can8 ? splits_for(cap8) : 0;
+    // 8-row workgroups (twice as many) when they need fewer launches, or as
+    // few and spread over the compute units more evenly (384 row blocks ->
+    // 768 = 3 per CU); M = 2 there takes the v_dot2 kernel with both rows
+    // sharing each dequantized pair
+    bool half = false;
+    if (can8) {
+      if ((s8 > 1) != (s16 > 1)) half = s8 == 1;
+      else half = fill(2 * (int64_t)p.rowblocks * s8) > fill((int64_t)p.rowblocks * s16);
       const int rows_env = env_int("QGEMM_GEMV_ROWS", 0);
       if (rows_env == 8 || rows_env == 16) half = rows_env == 8;
-      if (half) {
-        p.rows = 8;
-        p.mmax = M;
-        p.workgroups *= 2;
-      }
     }
+    p.rows = half ? 8 : 16;
+    p.mmax = half ? M : M <= 1 ? 1 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    p.splits = half ? s8 : s16;
+    p.tps = (int)ceil_div(p.wordtiles, p.splits);
+    p.workgroups = (int64_t)p.rowblocks * p.splits * (half ? 2 : 1);
     if (p.splits > 1) p.ws_partial_bytes = (size_t)p.rowblocks * p.splits * p.mmax * 16 * sizeof(float);
     return p;
   }

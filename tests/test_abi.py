@@ -163,7 +163,22 @@ def test_gemv_rows_override(monkeypatch):
     assert (qgm.plan(2, 8192, 2048, 128, 0)["tile_m"], qgm.plan(2, 8192, 2048, 128, 0)["tile_n"]) == (2, 8)
     assert qgm.plan(4, 8192, 2048, 128, 0)["tile_n"] == 16      # M > 2: MFMA GEMV only
     assert qgm.plan(1, 8192, 2048, 256, 4)["tile_n"] == 16      # q4k has no 8-row kernel
-    assert qgm.plan(1, 8192, 16384, 128, 0)["tile_n"] == 16     # 128 tiles: past 8 waves x 4 tiles
+    # 128 word tiles: past 8 waves x 4 tiles, so 8-row workgroups need K splits
+    p = qgm.plan(1, 8192, 16384, 128, 0)
+    assert p["tile_n"] == 8 and p["splits"] == 4
+
+
+def test_gemv_split_policy():
+    # no K split unless the per-workgroup tile cap forces one, or few row blocks
+    # carry long K: one launch beats a split plus its reduce launch
+    assert qgm.plan(1, 2048, 2048, 128, 0)["splits"] == 1
+    assert qgm.plan(1, 512, 4096, 128, 0)["splits"] == 1
+    assert qgm.plan(8, 2048, 2048, 128, 0)["splits"] == 1
+    assert qgm.plan(2, 512, 4096, 128, 0)["splits"] == 1       # 8-row kernel: 32 tiles per workgroup
+    assert qgm.plan(1, 256, 8192, 128, 0)["splits"] > 1        # 16 row blocks x 64 tiles
+    assert qgm.plan(8, 1024, 4096, 128, 0)["splits"] > 1       # MFMA GEMV cap: 16 tiles
+    assert qgm.plan(1, 16, 1 << 20, 128, 0)["splits"] == 512
+    assert qgm.workspace_bytes(1, 2048, 2048, 128, 0) == 0
 
 
 def test_plans_for_the_workloads():
