@@ -107,6 +107,11 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   // M = 64, so a single row of tiles still spreads over the CUs without a split
   p.tm = M <= GEMM_SMALL_M ? 32 : GEMM_TM;
   p.tn = M <= 2 * GEMM_SMALL_M ? 32 : GEMM_TN;
+  const int tile_env = env_int("QGEMM_GEMM_TILE", 0);   // 3232, 6432 or 6464 (tuning, tests)
+  if (tile_env == 3232 || tile_env == 6432 || tile_env == 6464) {
+    p.tm = tile_env / 100;
+    p.tn = tile_env % 100;
+  }
   p.tiles_n = (int)ceil_div(N, p.tn);
   p.tiles_m = (int)ceil_div(M, p.tm);
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;

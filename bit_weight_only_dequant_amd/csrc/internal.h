@@ -55,7 +55,8 @@ int check_align(const void* p);
 int check_ld(int ld, int minimum);
 
 // Launch plan for a validated problem.  Environment overrides (for tuning and
-// tests): QGEMM_FORCE=gemv|gemm, QGEMM_SPLITK=<n>, QGEMM_GEMV_ROWS=8|16 (M <= 2).
+// tests): QGEMM_FORCE=gemv|gemm, QGEMM_SPLITK=<n>, QGEMM_GEMV_ROWS=8|16 (M <= 2),
+// QGEMM_GEMM_TILE=3232|6432|6464 (GEMM tile rows x columns).
 Plan make_plan(int M, int N, int K, int group, int fmt);
 
 }  // namespace qg

@@ -1327,6 +1327,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
 struct DeviceWs {
   void* ptr = nullptr;
   size_t bytes = 0;
+  std::vector<void*> retired;   // outgrown buffers, kept until the process ends
 };
 static std::mutex g_ws_mutex;
 static std::vector<DeviceWs> g_ws;
@@ -1354,18 +1355,16 @@ static int current_device(int* dev) {
 static void clear_pending_error() { (void)hipGetLastError(); }
 
 // Library-owned zero-initialised workspace of at least `bytes` on `dev`.
+// Growing never frees the buffer it replaces: a HIP graph captured earlier
+// holds that buffer's address in its kernel arguments and may be replayed
+// later, so the outgrown buffer is retired (kept until the process ends).
+// Sizes at least double, so the retired buffers total less than the live one.
 static int library_ws(int dev, size_t bytes, void** out) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
   DeviceWs& w = g_ws[dev];
   if (w.bytes < bytes) {
-    if (w.ptr) {
-      if (hip_status(hipDeviceSynchronize()) != QG_OK) return QG_E_DEVICE;
-      (void)hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    size_t want = std::max(bytes, (size_t)1 << 20);
+    const size_t want = std::max({bytes, 2 * w.bytes, (size_t)1 << 20});
     void* p = nullptr;
     if (hipMalloc(&p, want) != hipSuccess) {
       clear_pending_error();
@@ -1375,6 +1374,7 @@ static int library_ws(int dev, size_t bytes, void** out) {
       (void)hipFree(p);
       return QG_E_DEVICE;
     }
+    if (w.ptr) w.retired.push_back(w.ptr);
     w.ptr = p;
     w.bytes = want;
   }

@@ -135,7 +135,10 @@ int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt)
  * split-K partials are reduced in a fixed order, so the result is
  * deterministic.  M == 0 or N == 0 is a no-op; K == 0 writes zeros.
  * Uses a library-owned per-device workspace, allocated (hipMalloc) on first
- * need and grown as needed; call once before capturing into a HIP graph.
+ * need and grown as needed; call once before capturing into a HIP graph (an
+ * allocation cannot happen during capture).  Growing never frees a buffer:
+ * an outgrown one is kept until the process ends, so a graph captured before
+ * a later, larger call still replays into valid memory.
  * Errors: QG_E_ARG, QG_E_ALIGN, QG_E_DEVICE, QG_E_NOMEM.
  */
 int qgemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,

@@ -522,6 +522,39 @@ def test_graph_replays_match_eager(name, M):
         assert torch.equal(other.view(torch.int16), eager.view(torch.int16))
 
 
+def test_graph_survives_workspace_growth():
+    # a graph captured with the library-owned split-K workspace must still
+    # replay correctly after a later, larger call has grown that workspace
+    # (the outgrown buffer is kept, never freed)
+    ca = synth.random_codes_case(5150, 0, 128, 512, 2048, 32)     # 32 x 32 tiles, 16-way split
+    assert qgm.workspace_bytes(32, 512, 2048, 128, 0) > 0
+    la = qgm.QuantLinear.from_case(ca, DEV)
+    xa = dev_half(ca.x)
+    eager = la(xa).clone()
+    torch.cuda.synchronize()
+    ya = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        la(xa, out=ya)
+    # 128 tiles x 8 splits of 64 x 64 fp32 partials: 16 MiB, more than any
+    # earlier call in this process asked for, so the workspace grows
+    Mb, Nb, Kb = 256, 2048, 16384
+    assert qgm.workspace_bytes(Mb, Nb, Kb, 128, 0) >= 16 << 20
+    cb = synth.random_codes_case(5151, 0, 128, Nb, Kb, 1)
+    lb = qgm.QuantLinear.from_case(cb, DEV)
+    xb = torch.randn((Mb, Kb), device=DEV).to(torch.float16)
+    yb0 = lb(xb).clone()
+    torch.cuda.synchronize()
+    say(f"workspace growth: graph plan {qgm.plan(32, 512, 2048, 128, 0)}, big plan {qgm.plan(Mb, Nb, Kb, 128, 0)}")
+    for rep in range(3):
+        ya.fill_(float("nan"))
+        g.replay()
+        yb = lb(xb)               # eager call on the grown workspace between replays
+        torch.cuda.synchronize()
+        assert torch.equal(ya.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(yb.view(torch.int16), yb0.view(torch.int16))
+
+
 # ----------------------------------------------------------------------------
 # looped shared block: qloop_block against the oracle's chain
 # ----------------------------------------------------------------------------
