@@ -107,6 +107,23 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   // M = 64, so a single row of tiles still spreads over the CUs without a split
   p.tm = M <= GEMM_SMALL_M ? 32 : GEMM_TM;
   p.tn = M <= 2 * GEMM_SMALL_M ? 32 : GEMM_TN;
+  const int nw = GEMM_THREADS / 64;
+  const int tpw = gemm_tpw(fmt);
+  const int s_tiles = (int)ceil_div(p.wordtiles, nw * tpw);
+  const int mg = meta_group(fmt, group);   // scale entries the kernel stages per 'group'
+  const int s_groups = (int)ceil_div((int64_t)p.wordtiles * kt_width / mg, GEMM_GCAP);
+  const int s_min = std::max(s_tiles, s_groups);
+  const int64_t split_below = (GEMM_TARGET_WG * 5) / 8;   // fewer tiles than this: split K
+  // Where the M-sized tiles would leave the CUs idle and so split K, but
+  // 32 x 32 tiles fill them with no split (s_min = 1), one launch of 32 x 32
+  // tiles beats a split plus its reduce launch, though every code is then
+  // dequantized in twice as many workgroups (128 x 2048 x 2048: 7.4 against
+  // 9.3 us for 64 x 64 tiles split 4 ways); measured up to M = 128
+  if (s_min == 1 && M <= 2 * GEMM_TM && (int64_t)ceil_div(N, p.tn) * ceil_div(M, p.tm) < split_below &&
+      (int64_t)ceil_div(N, 32) * ceil_div(M, 32) >= split_below) {
+    p.tm = 32;
+    p.tn = 32;
+  }
   const int tile_env = env_int("QGEMM_GEMM_TILE", 0);   // 3232, 6432 or 6464 (tuning, tests)
   if (tile_env == 3232 || tile_env == 6432 || tile_env == 6464) {
     p.tm = tile_env / 100;
@@ -118,13 +135,7 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   // at most gemm_tpw(fmt) word tiles per wave and GEMM_GCAP groups per workgroup;
   // split K across workgroups only when the tiles leave most compute units
   // idle, since a split writes fp32 partials and costs a second (reduce) launch
-  const int nw = GEMM_THREADS / 64;
-  const int tpw = gemm_tpw(fmt);
-  const int s_tiles = (int)ceil_div(p.wordtiles, nw * tpw);
-  const int mg = meta_group(fmt, group);   // scale entries the kernel stages per 'group'
-  const int s_groups = (int)ceil_div((int64_t)p.wordtiles * kt_width / mg, GEMM_GCAP);
-  const int s_min = std::max(s_tiles, s_groups);
-  int s = tiles >= (GEMM_TARGET_WG * 5) / 8 ? 1 : (int)ceil_div(GEMM_TARGET_WG, tiles);
+  int s = tiles >= split_below ? 1 : (int)ceil_div(GEMM_TARGET_WG, tiles);
   if (split_env > 0) s = split_env;
   s = std::min(std::max(s, s_min), p.wordtiles);
   p.tps = (int)ceil_div(p.wordtiles, s);

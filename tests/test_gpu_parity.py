@@ -57,6 +57,7 @@ def _clean_env(monkeypatch):
     monkeypatch.delenv("QGEMM_FORCE", raising=False)
     monkeypatch.delenv("QGEMM_SPLITK", raising=False)
     monkeypatch.delenv("QGEMM_GEMV_ROWS", raising=False)
+    monkeypatch.delenv("QGEMM_GEMM_TILE", raising=False)
     yield
 
 
@@ -248,6 +249,31 @@ def test_gemv_row_variants(monkeypatch, M, rows, fmt, group, N, K, splits):
     lin = qgm.QuantLinear.from_case(c, DEV)
     res = synth.draw_x(np.random.default_rng(N + K), M, N) if N % 2 else None
     check_close(run_gemm(lin, c.x, residual=res), ref_y(c, c.x, residual=res), f"M {M} rows {rows}")
+
+
+# GEMM tiles forced to each shape (32 x 32, 64 x 32, 64 x 64) on ragged M, N, K
+@pytest.mark.parametrize("tile", [3232, 6432, 6464])
+@pytest.mark.parametrize("fmt,group,N,K,M", [(0, 128, 300, 2048, 129), (3, 32, 100, 96, 100),
+                                             (1, 64, 272, 320, 127), (4, 256, 130, 1280, 70),
+                                             (2, 32, 520, 1056, 40)])
+def test_gemm_tile_variants(monkeypatch, tile, fmt, group, N, K, M):
+    monkeypatch.setenv("QGEMM_GEMM_TILE", str(tile))
+    p = qgm.plan(M, N, K, group, fmt)
+    say(f"gemm tile {tile} fmt={fmt} g={group} N={N} K={K} M={M} plan={p}")
+    assert (p["tile_m"], p["tile_n"]) == (tile // 100, tile % 100)
+    c = synth.random_codes_case(tile + N + K + M + fmt, fmt, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    check_close(run_gemm(lin, c.x), ref_y(c, c.x), f"tile {tile}")
+
+
+def test_gemm_small_tiles_without_split():
+    # 128 x 2048 x 2048 (the looped block's O projection): 32 x 32 tiles fill
+    # the CUs with no K split where 64 x 64 tiles would split 4 ways
+    p = qgm.plan(128, 2048, 2048, 128, 0)
+    assert (p["tile_m"], p["tile_n"], p["splits"]) == (32, 32, 1)
+    c = synth.random_codes_case(777, 0, 128, 2048, 2048, 128)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    check_close(run_gemm(lin, c.x), ref_y(c, c.x), "32x32 no split")
 
 
 # ----------------------------------------------------------------------------
