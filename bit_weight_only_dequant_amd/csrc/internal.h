@@ -16,7 +16,7 @@ constexpr int GEMV_MFMA_KW = 256;        // K covered by one wave of the MFMA GE
 constexpr int GEMV_THREADS = 512;          // 8 waves per workgroup
 constexpr int GEMV_TPW_MAX = 8;          // word tiles one wave streams per launch
 constexpr int GEMV_LDS_X_BYTES = 32768;  // x slice staged per workgroup
-constexpr int GEMV_HALF_TPW = 4;        // word tiles per wave of the half-row-block GEMV, at most
+constexpr int GEMV_HALF_TPW = 8;        // word tiles per wave of the half-row-block GEMV, at most
 constexpr int GEMV_SPLIT_RB = 32;        // GEMV: split K unforced only below this many row blocks
 constexpr int GEMV_SPLIT_TILES = 32;     // ... and above this many word tiles (32 KiB of codes) per row block
 constexpr int GEMM_THREADS = 512;        // 8 waves; they split the workgroup's K range

@@ -1425,7 +1425,7 @@ static bool launch_gemv_dot_w(const GemvArgs& a, int tps, hipStream_t s) {
 
 // 16 waves when a workgroup has at least 16 word tiles (more waves in flight,
 // one tile each at K = 2048), 8 otherwise
-// half row blocks (8-row workgroups): 4 waves of 2 tiles, 8 of 2, or 8 of 4
+// half row blocks (8-row workgroups): 4 waves of 2 tiles, 8 of 2, 8 of 4 or 8 of 8
 template <int FMT, int MMAX>
 static bool launch_gemv_half(const GemvArgs& a, int tps, hipStream_t s) {
   if constexpr (Fmt<FMT>::KQ) {
@@ -1434,6 +1434,7 @@ static bool launch_gemv_half(const GemvArgs& a, int tps, hipStream_t s) {
     const dim3 grid((unsigned)(2 * a.rowblocks), (unsigned)a.splits);
     if (tps <= 8) hipLaunchKernelGGL((gemv_half_kernel<FMT, 4, 2, MMAX>), grid, dim3(256), 0, s, a);
     else if (tps <= 16) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, 2, MMAX>), grid, dim3(512), 0, s, a);
+    else if (tps <= 32) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, 4, MMAX>), grid, dim3(512), 0, s, a);
     else if (tps <= 8 * GEMV_HALF_TPW) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, GEMV_HALF_TPW, MMAX>), grid, dim3(512), 0, s, a);
     else return false;
     return true;

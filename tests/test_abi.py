@@ -163,9 +163,9 @@ def test_gemv_rows_override(monkeypatch):
     assert (qgm.plan(2, 8192, 2048, 128, 0)["tile_m"], qgm.plan(2, 8192, 2048, 128, 0)["tile_n"]) == (2, 8)
     assert qgm.plan(4, 8192, 2048, 128, 0)["tile_n"] == 16      # M > 2: MFMA GEMV only
     assert qgm.plan(1, 8192, 2048, 256, 4)["tile_n"] == 16      # q4k has no 8-row kernel
-    # 128 word tiles: past 8 waves x 4 tiles, so 8-row workgroups need K splits
+    # 128 word tiles: past 8 waves x 8 tiles, so 8-row workgroups need K splits
     p = qgm.plan(1, 8192, 16384, 128, 0)
-    assert p["tile_n"] == 8 and p["splits"] == 4
+    assert p["tile_n"] == 8 and p["splits"] == 2
 
 
 def test_gemv_split_policy():

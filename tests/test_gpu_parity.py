@@ -224,14 +224,16 @@ def test_split_k_variants(monkeypatch, splits, M):
 
 
 # M = 1 and 2 through 16-row workgroups (v_dot2 kernel, MFMA GEMV for M = 2)
-# and 8-row (half row block) workgroups of 4 x 2, 8 x 2 and 8 x 4 word tiles,
-# with and without split-K, ragged N and K, and a fused residual
+# and 8-row (half row block) workgroups of 4 x 2, 8 x 2, 8 x 4 and 8 x 8 word
+# tiles, with and without split-K, ragged N and K, and a fused residual
 HALF_CASES = [
     # fmt, group, N, K, splits (0: the plan's own)
     (0, 128, 6144, 2048, 0), (0, 32, 100, 96, 0), (0, 64, 1000, 1024, 0), (0, 128, 4100, 4096, 0),
     (0, 128, 384, 2048, 3), (1, 64, 272, 2048, 0), (1, 32, 40, 8192, 0), (1, 64, 272, 4096, 5),
     (2, 32, 33, 224, 0), (2, 32, 6144, 2048, 0), (2, 32, 520, 1056, 2), (3, 32, 6144, 2048, 0),
     (3, 32, 130, 160, 0), (3, 32, 72, 1056, 3), (3, 32, 300, 2080, 0),
+    # 33..64 word tiles per workgroup: 8 waves of 8 tiles on 8-row workgroups
+    (0, 128, 520, 8192, 0), (3, 32, 520, 4096, 0), (0, 64, 48, 6016, 1),
 ]
 
 
