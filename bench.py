@@ -135,9 +135,10 @@ def cpu_baseline(case, M, seconds):
                        f"elementwise steps single-threaded, BLAS with {blas_threads} threads")
 
 
-def loop_leg(qgm, torch, synth, L=8, flush=True):
-    """Looped shared block: per-loop time, cold (on-die cache flushed) vs warm."""
-    lc = synth.loop_workload(M=128, L=L)
+def loop_leg(qgm, torch, synth, L=8, flush=True, M=128):
+    """Looped shared block: per-loop time, cold (on-die cache flushed) vs warm.
+    M = 128 is the prefill-sized block; M = 1 the decode step (GEMV kernels)."""
+    lc = synth.loop_workload(M=M, L=L)
     lins = [qgm.QuantLinear.from_case(c, "cuda") for c in lc.linears()]
     x0 = qgm.to_half_tensor(lc.x0, "cuda")
     M, D = lc.x0.shape
@@ -163,7 +164,8 @@ def loop_leg(qgm, torch, synth, L=8, flush=True):
     wbytes = sum(l.weight_bytes for l in lins)
     flops = 2.0 * M * (D * 3 * D + D * D + D * F + F * D)
     cold, warm = res["cold"], res["warm"]
-    return dict(leg="loop_block_int4_g128", M=M, D=D, F=F, L=L, weight_bytes_per_loop=wbytes,
+    return dict(leg="loop_block_int4_g128" + ("" if M == 128 else f"_M{M}"), M=M, D=D, F=F, L=L,
+                weight_bytes_per_loop=wbytes,
                 cold_loop_ms=[round(v, 4) for v in cold], warm_loop_ms=[round(v, 4) for v in warm],
                 loop1_cold_ms=round(cold[0], 4),
                 loops2_L_ms=round(float(np.mean(cold[1:])), 4),
@@ -324,6 +326,7 @@ def main():
     secondary.append(dict(leg_result("decode_int4_g128_M1_cache_resident", hot, hot.time(400, 40), 1)))
     del hot
     secondary.append(loop_leg(qgm, torch, synth))
+    secondary.append(loop_leg(qgm, torch, synth, M=1))
     secondary.append(fp16_leg(qgm, torch, synth, Ms=(1, 8, 128, 512)))
 
     leg, ms, main_r = out["main"]

@@ -621,10 +621,12 @@ def test_loop_block_exact_chain(M):
     assert np.array_equal(x.cpu().numpy().astype(np.float64), x0.astype(np.float64) * 4.0 ** L)
 
 
-def test_loop_block_full_size():
-    # the benchmark's block: D = 2048, F = 8192, M = 128, INT4 g128, all 8 loops
-    lc = synth.loop_workload(M=128, L=8)
-    say("loop full size M=128 D=2048 F=8192 L=8")
+@pytest.mark.parametrize("M", [1, 128])
+def test_loop_block_full_size(M):
+    # the benchmark's block: D = 2048, F = 8192, INT4 g128, all 8 loops; M = 128
+    # runs the GEMM path, M = 1 (decode) the GEMV kernels with fused residuals
+    lc = synth.loop_workload(M=M, L=8)
+    say(f"loop full size M={M} D=2048 F=8192 L=8")
     lins = [qgm.QuantLinear.from_case(c, DEV) for c in lc.linears()]
     x = dev_half(lc.x0)
     qgm.loop_block(x, lins, lc.L)
