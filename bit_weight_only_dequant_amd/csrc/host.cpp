@@ -59,10 +59,10 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     const int nw = GEMV_THREADS / 64;
     const int tps_lds = std::max(1, GEMV_LDS_X_BYTES / (kt_width * 2));
     // per-workgroup word-tile caps: v_dot2 kernel (M = 1), MFMA GEMV (M > 1),
-    // 8-row v_dot2 kernel (M <= 2, not q4k)
+    // 8-row v_dot2 kernel (M <= 2)
     const int cap16 = M <= 1 ? std::min(tps_lds, nw * GEMV_TPW_MAX) : nw * (GEMV_MFMA_KW / kt_width);
     const int cap8 = nw * GEMV_HALF_TPW;
-    const bool can8 = M <= 2 && fmt != Q4K;
+    const bool can8 = M <= 2;
     // K splits for a cap.  A split costs a second (reduce) launch and the fp32
     // partials, about 2 us, more than an unsplit launch loses to idle CUs:
     // split only when the cap forces it, or when fewer than GEMV_SPLIT_RB row

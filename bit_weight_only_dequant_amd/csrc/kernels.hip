@@ -560,12 +560,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
 // waves take TPW word tiles each, two at a time: lane l = r8 + 8 g + 32 t reads
 // the 16-byte chunk of row 8 hb + r8, lane group g, of tile 2 i + t of the
 // wave's run -- one 16-byte load per lane and pair, as gemv_kernel.  Same
-// dequant and dot products (MMAX rows of x share each exact (q - z) pair); lanes
-// sum over g and t, the waves through LDS in wave order.
+// dequant and dot products (MMAX rows of x share each exact (q - z) pair; q4k
+// as in gemv_kernel); lanes sum over g and t, the waves through LDS in wave order.
 template <int FMT, int NW, int TPW, int MMAX>
 __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   using F = Fmt<FMT>;
-  static_assert(!F::KQ, "fp16 scale-and-zero formats only");
   static_assert(TPW % 2 == 0, "tiles go in pairs");
   constexpr int NP = TPW / 2;                  // tile pairs per wave
   constexpr int KW = TPW * F::KT;              // k range of one wave
@@ -573,12 +572,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   constexpr int XCH = MMAX * KW / 8;
   constexpr int NXC = (XCH + 63) / 64;
   constexpr int NSZ = (8 * GWMAX + 63) / 64;
-  constexpr int XB = MMAX * KW * 2, WB = XB + 8 * GWMAX * 4;
+  constexpr int SZB = F::KQ ? 8 : 4;           // q4k: fp32 (d*sc, dmin*m) per (row, sub-block)
+  constexpr int XB = MMAX * KW * 2, SB = 8 * GWMAX * SZB;
+  constexpr int WB = XB + SB + (F::KQ ? MMAX * GWMAX * 4 : 0);
   __shared__ __align__(16) uint8_t half_smem[NW * WB + NW * MMAX * 16 * sizeof(float)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f16* xs = reinterpret_cast<f16*>(half_smem + wave * WB);                 // [MMAX][KW]
   uint32_t* sz = reinterpret_cast<uint32_t*>(half_smem + wave * WB + XB);  // [8][GWMAX] s | z << 16
+  float2* szk = reinterpret_cast<float2*>(half_smem + wave * WB + XB);     // q4k: [8][GWMAX] (d*sc, dmin*m)
+  float* xsum = reinterpret_cast<float*>(half_smem + wave * WB + XB + SB); // q4k: [MMAX][GWMAX]
   float* red = reinterpret_cast<float*>(half_smem + NW * WB);              // [NW][MMAX][2][8]
   const int r8 = lane & 7, g = (lane >> 3) & 3, t = lane >> 5;
   const int rb = blockIdx.x >> 1, hb = blockIdx.x & 1, split = blockIdx.y;
@@ -595,8 +598,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   // 1. loads: (scale, zero) entries of the 8 rows, the residual, x rows, one
   //    code chunk per tile pair; clamped, never out of range
   const int64_t szbase = (int64_t)row0 * ng * 2;
-  const char* sp = reinterpret_cast<const char*>(a.scales) + szbase;
-  const char* zp = reinterpret_cast<const char*>(F::HAS_Z ? a.zeros : a.scales) + szbase;
+  // q4k: the (d, dmin) pair of each super-block (8 sub-blocks) as 32 bits,
+  // so the 8 rows' pairs start at row0 * (ng / 8) * 4 bytes
+  const char* sp = reinterpret_cast<const char*>(a.scales) + (F::KQ ? szbase / 4 : szbase);
+  const char* zp = reinterpret_cast<const char*>(F::HAS_Z || F::KQ ? a.zeros : a.scales) + szbase;
   uint32_t sraw[NSZ], zraw[NSZ];
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
@@ -604,9 +609,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
     const int er = e >> lgs, eg = gs0 + (e & (gstride - 1));
     const bool ok = e < 8 * gstride && row0 + er < a.N && eg < ng;
     const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
-    sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
-    if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
-    else zraw[j] = F::ZBITS;
+    if constexpr (F::KQ) {
+      sraw[j] = *reinterpret_cast<const uint32_t*>(sp + (ok ? (uint32_t)(er * (ng >> 3) + (eg >> 3)) * 4u : 0u));
+      zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+    } else {
+      sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
+      if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+      else zraw[j] = F::ZBITS;
+    }
   }
   const int om = (tid >> 4) % MMAX;   // output row of thread tid < 16 MMAX (final sum)
   uint32_t res = 0u;                  // its residual, fp16 bits (no branch, no wait here)
@@ -641,11 +651,33 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
     const int e = lane + 64 * j;
-    if (e < 8 * gstride) sz[(e >> lgs) * GWMAX + (e & (gstride - 1))] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+    if (e < 8 * gstride) {
+      const int idx = (e >> lgs) * GWMAX + (e & (gstride - 1));
+      if constexpr (F::KQ) szk[idx] = kq_terms(sraw[j], zraw[j]);
+      else sz[idx] = (sraw[j] & 0xffffu) | (zraw[j] << 16);
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if constexpr (F::KQ) {
+    // x sum of every 32-wide run of the wave's range (zeros past K), one lane
+    // per (row of x, run)
+    for (int e = lane; e < MMAX * GWMAX; e += 64) {
+      const h8* xp = reinterpret_cast<const h8*>(xs + (e / GWMAX) * KW + (e % GWMAX) * 32);
+      float v = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const h8 xv = xp[c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v = __builtin_amdgcn_fdot2(h2{xv[2 * u], xv[2 * u + 1]}, splat((f16)1.0f), v, false);
+      }
+      xsum[e] = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   // 3. dot products of the lane's chunk, one run of SW codes at a time; the
   //    exact (q - z) pairs serve every row of x
   float acc[MMAX];
@@ -657,9 +689,19 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
 #pragma unroll
     for (int p = 0; p < F::NSEG; ++p) {
       const int kl = (2 * i + t) * F::KT + g * F::LS + p * F::SW;
-      const uint32_t szv = sz[r8 * GWMAX + (kl >> lg)];
-      const float sf = (float)__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu));
-      const f16 z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
+      const int run = kl >> lg;
+      float sf, bk = 0.0f;
+      f16 z;
+      if constexpr (F::KQ) {   // q4k: exact q; d*sc * (x . q) - dmin*m * sum(x), in fp32
+        const float2 kt = szk[r8 * GWMAX + run];
+        sf = kt.x;
+        bk = kt.y;
+        z = (f16)0.0f;
+      } else {
+        const uint32_t szv = sz[r8 * GWMAX + run];
+        sf = (float)__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu));
+        z = __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
+      }
       h2 q[F::SW / 2];
       run_qmz<FMT>(code[i], p, z, q);
 #pragma unroll
@@ -677,6 +719,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
           if (c & 1) A1 = t0; else A0 = t0;
         }
         acc[m] = fmaf(sf, A0 + A1, acc[m]);
+        if constexpr (F::KQ) acc[m] = fmaf(-bk, xsum[m * GWMAX + run], acc[m]);
       }
     }
   }
@@ -1428,9 +1471,7 @@ static bool launch_gemv_dot_w(const GemvArgs& a, int tps, hipStream_t s) {
 // half row blocks (8-row workgroups): 4 waves of 2 tiles, 8 of 2, 8 of 4 or 8 of 8
 template <int FMT, int MMAX>
 static bool launch_gemv_half(const GemvArgs& a, int tps, hipStream_t s) {
-  if constexpr (Fmt<FMT>::KQ) {
-    return false;
-  } else {
+  {
     const dim3 grid((unsigned)(2 * a.rowblocks), (unsigned)a.splits);
     if (tps <= 8) hipLaunchKernelGGL((gemv_half_kernel<FMT, 4, 2, MMAX>), grid, dim3(256), 0, s, a);
     else if (tps <= 16) hipLaunchKernelGGL((gemv_half_kernel<FMT, 8, 2, MMAX>), grid, dim3(512), 0, s, a);

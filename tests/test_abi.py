@@ -162,7 +162,7 @@ def test_gemv_rows_override(monkeypatch):
     assert qgm.plan(1, 8192, 2048, 128, 0)["tile_n"] == 8
     assert (qgm.plan(2, 8192, 2048, 128, 0)["tile_m"], qgm.plan(2, 8192, 2048, 128, 0)["tile_n"]) == (2, 8)
     assert qgm.plan(4, 8192, 2048, 128, 0)["tile_n"] == 16      # M > 2: MFMA GEMV only
-    assert qgm.plan(1, 8192, 2048, 256, 4)["tile_n"] == 16      # q4k has no 8-row kernel
+    assert qgm.plan(1, 8192, 2048, 256, 4)["tile_n"] == 8
     # 128 word tiles: past 8 waves x 8 tiles, so 8-row workgroups need K splits
     p = qgm.plan(1, 8192, 16384, 128, 0)
     assert p["tile_n"] == 8 and p["splits"] == 2
@@ -213,7 +213,7 @@ def test_plans_for_the_workloads():
     assert (qgm.plan(1, 6144, 2048, 128, 0)["tile_n"], qgm.plan(1, 6144, 2048, 128, 0)["workgroups"]) == (8, 768)
     assert (qgm.plan(1, 8192, 2048, 128, 0)["tile_n"], qgm.plan(1, 8192, 2048, 128, 0)["workgroups"]) == (16, 512)
     assert qgm.plan(1, 6144, 2048, 32, 3)["tile_n"] == 8
-    assert qgm.plan(1, 6144, 2048, 256, 4)["tile_n"] == 16   # q4k: 16-row kernel only
+    assert qgm.plan(1, 6144, 2048, 256, 4)["tile_n"] == 8    # q4k too
     assert qgm.plan(8, 6144, 2048, 128, 0)["tile_n"] == 16
     # M = 2: the v_dot2 kernel on 8-row workgroups where they balance, else the MFMA GEMV
     assert (qgm.plan(2, 6144, 2048, 128, 0)["tile_m"], qgm.plan(2, 6144, 2048, 128, 0)["tile_n"]) == (2, 8)

@@ -234,6 +234,8 @@ HALF_CASES = [
     (3, 32, 130, 160, 0), (3, 32, 72, 1056, 3), (3, 32, 300, 2080, 0),
     # 33..64 word tiles per workgroup: 8 waves of 8 tiles on 8-row workgroups
     (0, 128, 520, 8192, 0), (3, 32, 520, 4096, 0), (0, 64, 48, 6016, 1),
+    # q4k: (d*sc, dmin*m) per sub-block and per-run x sums on either row count
+    (4, 256, 6144, 2048, 0), (4, 256, 130, 1280, 0), (4, 256, 520, 8192, 0), (4, 256, 300, 2048, 3),
 ]
 
 
