@@ -59,10 +59,10 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     const int nw = GEMV_THREADS / 64;
     const int tps_lds = std::max(1, GEMV_LDS_X_BYTES / (kt_width * 2));
     // per-workgroup word-tile caps: v_dot2 kernel (M = 1), MFMA GEMV (M > 1),
-    // 8-row v_dot2 kernel (M <= 2)
+    // 8-row v_dot2 kernel (M <= 4)
     const int cap16 = M <= 1 ? std::min(tps_lds, nw * GEMV_TPW_MAX) : nw * (GEMV_MFMA_KW / kt_width);
     const int cap8 = nw * GEMV_HALF_TPW;
-    const bool can8 = M <= 2;
+    const bool can8 = M <= 4;
     // K splits for a cap.  A split costs a second (reduce) launch and the fp32
     // partials, about 2 us, more than an unsplit launch loses to idle CUs:
     // split only when the cap forces it, or when fewer than GEMV_SPLIT_RB row
@@ -83,19 +83,22 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     };
     const int s16 = splits_for(cap16);
     const int s8 = can8 ? splits_for(cap8) : 0;
-    // 8-row workgroups (twice as many) when they need fewer launches, or as
-    // few and spread over the compute units more evenly (384 row blocks ->
-    // 768 = 3 per CU); M = 2 there takes the v_dot2 kernel with both rows
-    // sharing each dequantized pair
+    // M <= 2: 8-row workgroups (twice as many) when they need fewer launches,
+    // or as few and spread over the compute units more evenly (384 row blocks
+    // -> 768 = 3 per CU); M = 2 there takes the v_dot2 kernel with both rows
+    // sharing each dequantized pair.  M = 3, 4: the v_dot2 work grows with M,
+    // so the 8-row kernel replaces the MFMA GEMV only where it saves the split
+    // and the reduce launch and its workgroups fit one round of the CUs
     bool half = false;
     if (can8) {
-      if ((s8 > 1) != (s16 > 1)) half = s8 == 1;
+      if (M > 2) half = s16 > 1 && s8 == 1 && 2 * (int64_t)p.rowblocks <= GEMM_TARGET_WG;
+      else if ((s8 > 1) != (s16 > 1)) half = s8 == 1;
       else half = fill(2 * (int64_t)p.rowblocks * s8) > fill((int64_t)p.rowblocks * s16);
       const int rows_env = env_int("QGEMM_GEMV_ROWS", 0);
       if (rows_env == 8 || rows_env == 16) half = rows_env == 8;
     }
     p.rows = half ? 8 : 16;
-    p.mmax = half ? M : M <= 1 ? 1 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    p.mmax = half ? (M <= 2 ? M : 4) : M <= 1 ? 1 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     p.splits = half ? s8 : s16;
     p.tps = (int)ceil_div(p.wordtiles, p.splits);
     p.workgroups = (int64_t)p.rowblocks * p.splits * (half ? 2 : 1);

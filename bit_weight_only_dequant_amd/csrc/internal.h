@@ -34,7 +34,7 @@ inline constexpr int gemm_tpw(int fmt) { return fmt == Q8_0 ? GEMM_TPW_Q8 : GEMM
 
 struct Plan {
   int path = 0;        // 0 none (no-op / zero fill), 1 GEMV, 2 GEMM
-  int mmax = 0;        // GEMV: rows of x per launch (1, 2: v_dot2 kernels; 4, 8, 16: MFMA kernel)
+  int mmax = 0;        // GEMV: rows of x per launch (1, 2, 4 on 8-row workgroups: v_dot2; 4, 8, 16: MFMA)
   int splits = 1;      // K splits
   int tps = 0;         // word tiles per split
   int wordtiles = 0;   // total word tiles along K
@@ -55,7 +55,7 @@ int check_align(const void* p);
 int check_ld(int ld, int minimum);
 
 // Launch plan for a validated problem.  Environment overrides (for tuning and
-// tests): QGEMM_FORCE=gemv|gemm, QGEMM_SPLITK=<n>, QGEMM_GEMV_ROWS=8|16 (M <= 2),
+// tests): QGEMM_FORCE=gemv|gemm, QGEMM_SPLITK=<n>, QGEMM_GEMV_ROWS=8|16 (M <= 4),
 // QGEMM_GEMM_TILE=3232|6432|6464 (GEMM tile rows x columns).
 Plan make_plan(int M, int N, int K, int group, int fmt);
 

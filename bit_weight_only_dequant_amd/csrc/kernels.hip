@@ -19,7 +19,7 @@
 //                        per 32 codes (q8_0: 16; q4k: d*sc and the offset
 //                        dmin*m times the run's x sum), lane groups summed by
 //                        DPP and ds_swizzle, waves through LDS.
-//   gemv_half<FMT, R>    M <= 2 when 16-row workgroups would load the CUs
+//   gemv_half<FMT, R>    M <= 4 when 16-row workgroups would load the CUs
 //                        unevenly (N = 6144: 384 blocks on 256 CUs): the same
 //                        work on 8-row workgroups, twice as many.
 //   gemv_mfma<FMT, R>    2 <= M <= 16.  Same loads and staging; every 8 codes,
@@ -1504,13 +1504,13 @@ static bool launch_gemv_mfma(const GemvArgs& a, int tps, hipStream_t s) {
 }
 
 // mmax 1: v_dot2 GEMV (16- or 8-row workgroups); 2: v_dot2 on 8-row workgroups;
-// 4, 8, 16: rows of the MFMA GEMV
+// 4: MFMA GEMV or v_dot2 on 8-row workgroups; 8, 16: MFMA GEMV
 template <int FMT>
 static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, int rows, hipStream_t s) {
   switch (mmax) {
     case 1: return launch_gemv_dot<FMT>(a, tps, rows, s);
     case 2: return rows == 8 && launch_gemv_half<FMT, 2>(a, tps, s);
-    case 4: return launch_gemv_mfma<FMT, 4>(a, tps, s);
+    case 4: return rows == 8 ? launch_gemv_half<FMT, 4>(a, tps, s) : launch_gemv_mfma<FMT, 4>(a, tps, s);
     case 8: return launch_gemv_mfma<FMT, 8>(a, tps, s);
     default: return launch_gemv_mfma<FMT, 16>(a, tps, s);
   }

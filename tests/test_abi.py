@@ -161,7 +161,8 @@ def test_gemv_rows_override(monkeypatch):
     monkeypatch.setenv("QGEMM_GEMV_ROWS", "8")
     assert qgm.plan(1, 8192, 2048, 128, 0)["tile_n"] == 8
     assert (qgm.plan(2, 8192, 2048, 128, 0)["tile_m"], qgm.plan(2, 8192, 2048, 128, 0)["tile_n"]) == (2, 8)
-    assert qgm.plan(4, 8192, 2048, 128, 0)["tile_n"] == 16      # M > 2: MFMA GEMV only
+    assert (qgm.plan(4, 8192, 2048, 128, 0)["tile_m"], qgm.plan(4, 8192, 2048, 128, 0)["tile_n"]) == (4, 8)
+    assert qgm.plan(5, 8192, 2048, 128, 0)["tile_n"] == 16      # M > 4: MFMA GEMV only
     assert qgm.plan(1, 8192, 2048, 256, 4)["tile_n"] == 8
     # 128 word tiles: past 8 waves x 8 tiles, so 8-row workgroups need K splits
     p = qgm.plan(1, 8192, 16384, 128, 0)
@@ -219,3 +220,8 @@ def test_plans_for_the_workloads():
     assert (qgm.plan(2, 6144, 2048, 128, 0)["tile_m"], qgm.plan(2, 6144, 2048, 128, 0)["tile_n"]) == (2, 8)
     assert (qgm.plan(2, 8192, 2048, 128, 0)["tile_m"], qgm.plan(2, 8192, 2048, 128, 0)["tile_n"]) == (4, 16)
     assert qgm.plan(3, 6144, 2048, 128, 0)["tile_n"] == 16
+    # M = 3, 4: the 8-row v_dot2 kernel only where it saves the MFMA GEMV's split
+    # and fits one round of workgroups
+    p = qgm.plan(4, 2048, 8192, 128, 0)
+    assert (p["tile_m"], p["tile_n"], p["splits"]) == (4, 8, 1)
+    assert qgm.plan(4, 6144, 8192, 128, 0)["tile_n"] == 16

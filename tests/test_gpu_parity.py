@@ -223,9 +223,10 @@ def test_split_k_variants(monkeypatch, splits, M):
     check_close(run_gemm(lin, c.x), ref_y(c, c.x), f"splitk {splits}")
 
 
-# M = 1 and 2 through 16-row workgroups (v_dot2 kernel, MFMA GEMV for M = 2)
-# and 8-row (half row block) workgroups of 4 x 2, 8 x 2, 8 x 4 and 8 x 8 word
-# tiles, with and without split-K, ragged N and K, and a fused residual
+# M = 1, 2, 4 through 16-row workgroups (v_dot2 kernel for M = 1, MFMA GEMV
+# above) and 8-row (half row block) v_dot2 workgroups of 4 x 2, 8 x 2, 8 x 4
+# and 8 x 8 word tiles, with and without split-K, ragged N and K, and a fused
+# residual
 HALF_CASES = [
     # fmt, group, N, K, splits (0: the plan's own)
     (0, 128, 6144, 2048, 0), (0, 32, 100, 96, 0), (0, 64, 1000, 1024, 0), (0, 128, 4100, 4096, 0),
@@ -239,7 +240,7 @@ HALF_CASES = [
 ]
 
 
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 4])
 @pytest.mark.parametrize("rows", [8, 16])
 @pytest.mark.parametrize("fmt,group,N,K,splits", HALF_CASES)
 def test_gemv_row_variants(monkeypatch, M, rows, fmt, group, N, K, splits):
