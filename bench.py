@@ -168,8 +168,8 @@ def loop_leg(qgm, torch, synth, L=8, flush=True, M=128):
                 weight_bytes_per_loop=wbytes,
                 cold_loop_ms=[round(v, 4) for v in cold], warm_loop_ms=[round(v, 4) for v in warm],
                 loop1_cold_ms=round(cold[0], 4),
-                loops2_L_ms=round(float(np.mean(cold[1:])), 4),
-                TFLOPs_loops2_L=round(flops / (float(np.mean(cold[1:])) * 1e-3) / 1e12, 2),
+                loops2_L_ms=round(float(np.median(cold[1:])), 4),   # median: robust to launch jitter
+                TFLOPs_loops2_L=round(flops / (float(np.median(cold[1:])) * 1e-3) / 1e12, 2),
                 weight_GBps_loop1_cold=round(wbytes / (cold[0] * 1e-3) / 1e9, 1))
 
 
