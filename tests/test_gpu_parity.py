@@ -192,6 +192,17 @@ def test_very_long_k(fmt, group, N, K, M):
     check_close(run_gemm(lin, c.x), ref_y(c, c.x), "long K")
 
 
+@pytest.mark.parametrize("fmt,group,N,K,M", [(0, 128, 131080, 256, 1), (3, 32, 65544, 128, 2),
+                                             (0, 32, 65544, 256, 8), (4, 256, 40968, 256, 40),
+                                             (1, 64, 98312, 256, 130)])
+def test_very_wide_n(fmt, group, N, K, M):
+    # tens of thousands of row blocks (large grid x, ragged last block) through every path
+    say(f"wide N fmt={fmt} N={N} K={K} M={M} plan={qgm.plan(M, N, K, group, fmt)}")
+    c = synth.random_codes_case(N + K + M + fmt, fmt, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    check_close(run_gemm(lin, c.x), ref_y(c, c.x), "wide N")
+
+
 def test_offset_guards_reject_oversized_shapes():
     # shapes whose byte offsets would not fit the kernels' 32-bit arithmetic are
     # refused before any launch (the pointers are never dereferenced)
