@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
 
 #include "../../include/qgemm.h"
 #include "internal.h"
@@ -60,7 +61,7 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     const int tps_lds = std::max(1, GEMV_LDS_X_BYTES / (kt_width * 2));
     // per-workgroup word-tile caps: v_dot2 kernel (M = 1), MFMA GEMV (M > 1),
     // 8-row v_dot2 kernel (M <= 4)
-    const int cap16 = M <= 1 ? std::min(tps_lds, nw * GEMV_TPW_MAX) : nw * (GEMV_MFMA_KW / kt_width);
+    const int cap16 = M <= 1 ? std::min(tps_lds, gemv_m1_tile_cap(fmt)) : nw * (GEMV_MFMA_KW / kt_width);
     const int cap8 = nw * GEMV_HALF_TPW;
     const bool can8 = M <= 4;
     // K splits for a cap.  A split costs a second (reduce) launch and the fp32
@@ -81,20 +82,53 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     const auto fill = [](int64_t w) {   // busy share of the last round of workgroups
       return (double)w / (double)(ceil_div(w, GEMM_TARGET_WG) * GEMM_TARGET_WG);
     };
-    const int s16 = splits_for(cap16);
-    const int s8 = can8 ? splits_for(cap8) : 0;
-    // M <= 2: 8-row workgroups (twice as many) when they need fewer launches,
-    // or as few and spread over the compute units more evenly (384 row blocks
-    // -> 768 = 3 per CU); M = 2 there takes the v_dot2 kernel with both rows
-    // sharing each dequantized pair.  M = 3, 4: the v_dot2 work grows with M,
-    // so the 8-row kernel replaces the MFMA GEMV only where it saves the split
-    // and the reduce launch and its workgroups fit one round of the CUs
+    (void)fill;
+    int s16 = splits_for(cap16);
+    int s8 = can8 ? splits_for(cap8) : 0;
+    const int rows_env = env_int("QGEMM_GEMV_ROWS", 0);
     bool half = false;
-    if (can8) {
-      if (M > 2) half = s16 > 1 && s8 == 1 && 2 * (int64_t)p.rowblocks <= GEMM_TARGET_WG;
-      else if ((s8 > 1) != (s16 > 1)) half = s8 == 1;
-      else half = fill(2 * (int64_t)p.rowblocks * s8) > fill((int64_t)p.rowblocks * s16);
-      const int rows_env = env_int("QGEMM_GEMV_ROWS", 0);
+    if (M <= 2) {
+      // Rows per workgroup (16 or 8) and K splits from a cost model in units
+      // of one row of W times one word tile streamed by a workgroup (about
+      // 5 ns measured): rounds of workgroups over the 256 CUs x rows x tiles
+      // per workgroup, plus GEMV_SPLIT_COST for a split's reduce launch and
+      // fp32 partials (about 2 us) and GEMV_SPLIT_COST_PER per split (the
+      // reduce sums each output's partials in order: about 20 ns each).  Ties
+      // go to fewer workgroups.  M = 2 on
+      // 8-row workgroups takes the v_dot2 kernel with both rows sharing each
+      // dequantized pair, on 16-row workgroups the MFMA GEMV.
+      int64_t best_cost = INT64_MAX, best_wg = INT64_MAX;
+      for (int rows = 16; rows >= 8; rows -= 8) {
+        if (rows_env == 8 || rows_env == 16) {
+          if (rows != rows_env) continue;
+        }
+        const int cap = rows == 16 ? cap16 : cap8;
+        const int per = 16 / rows;   // workgroups per row block and split
+        const int s_min = (int)ceil_div(p.wordtiles, cap);
+        const int s_top = std::min(p.wordtiles, std::max(s_min, (int)ceil_div(4 * GEMM_TARGET_WG, (int64_t)p.rowblocks * per)));
+        for (int s = s_min; s <= s_top; ++s) {
+          const int tps = (int)ceil_div(p.wordtiles, s);
+          if (ceil_div(p.wordtiles, tps) != s) continue;   // splits of equal tile counts only
+          if (split_env > 0) {   // the forced split count, as equal tile counts make it
+            const int se = std::max(s_min, std::min(split_env, p.wordtiles));
+            if (s != (int)ceil_div(p.wordtiles, ceil_div(p.wordtiles, se))) continue;
+          }
+          const int64_t wg = (int64_t)p.rowblocks * per * s;
+          const int64_t cost = ceil_div(wg, GEMM_TARGET_WG) * rows * tps +
+                               (s > 1 ? GEMV_SPLIT_COST + GEMV_SPLIT_COST_PER * s : 0);
+          if (cost < best_cost || (cost == best_cost && wg < best_wg)) {
+            best_cost = cost;
+            best_wg = wg;
+            half = rows == 8;
+            (half ? s8 : s16) = s;
+          }
+        }
+      }
+    } else if (can8) {
+      // M = 3, 4: the v_dot2 work grows with M, so the 8-row kernel replaces
+      // the MFMA GEMV only where it saves the split and the reduce launch and
+      // its workgroups fit one round of the CUs
+      half = s16 > 1 && s8 == 1 && 2 * (int64_t)p.rowblocks <= GEMM_TARGET_WG;
       if (rows_env == 8 || rows_env == 16) half = rows_env == 8;
     }
     p.rows = half ? 8 : 16;

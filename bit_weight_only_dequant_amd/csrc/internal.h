@@ -19,6 +19,8 @@ constexpr int GEMV_LDS_X_BYTES = 32768;  // x slice staged per workgroup
 constexpr int GEMV_HALF_TPW = 8;        // word tiles per wave of the half-row-block GEMV, at most
 constexpr int GEMV_SPLIT_RB = 32;        // GEMV: split K unforced only below this many row blocks
 constexpr int GEMV_SPLIT_TILES = 32;     // ... and above this many word tiles (32 KiB of codes) per row block
+constexpr int64_t GEMV_SPLIT_COST = 370;  // M <= 2 plan: a split's reduce launch, in row x word-tile units
+constexpr int64_t GEMV_SPLIT_COST_PER = 4;  // ... and per split (the in-order sum of the partials)
 constexpr int GEMM_THREADS = 512;        // 8 waves; they split the workgroup's K range
 constexpr int GEMM_TM = 64;              // workgroup tile rows (M)
 constexpr int GEMM_TN = 64;              // workgroup tile columns (N)
@@ -28,6 +30,12 @@ constexpr int GEMM_TPW_Q8 = 4;           // q8_0: a tile is 64 wide, so 4 per wa
 constexpr int GEMM_DEPTH = 1;            // x/code stages in flight per wave
 constexpr int GEMM_GCAP = 64;            // quantization groups per workgroup, at most
 constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
+
+// word tiles one M = 1 GEMV workgroup of 16 waves streams, at most: 8 per wave
+// within a 32 KiB x slice (INT2: 4 per wave), q4k 4 per wave (its fp32 terms
+// and x sums keep the workgroup's LDS within 80 KiB); kernels.hip checks
+// these against its own tile caps
+inline constexpr int gemv_m1_tile_cap(int fmt) { return fmt == INT2_ASYM || fmt == Q4K ? 64 : 128; }
 
 // word tiles one GEMM wave covers, at most
 inline constexpr int gemm_tpw(int fmt) { return fmt == Q8_0 ? GEMM_TPW_Q8 : GEMM_TPW; }

@@ -1456,6 +1456,7 @@ template <int FMT, int NW>
 static bool launch_gemv_dot_w(const GemvArgs& a, int tps, hipStream_t s) {
   constexpr int TMAX = gemv_dot_tmax<FMT, NW>();
   static_assert(gemv_lds_bytes<FMT, 1, TMAX, NW>() <= 80 * 1024, "tile cap and LDS size disagree");
+  static_assert(NW != 16 || NW * TMAX >= gemv_m1_tile_cap(FMT), "the plan's M = 1 tile cap exceeds the kernel's");
   constexpr int T2 = TMAX >= 2 ? 2 : 1, T4 = TMAX >= 4 ? 4 : T2, T8 = TMAX >= 8 ? 8 : T4;
   const int tpw = (tps + NW - 1) / NW;
   if (tpw > TMAX) return false;

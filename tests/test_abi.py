@@ -169,6 +169,21 @@ def test_gemv_rows_override(monkeypatch):
     assert p["tile_n"] == 8 and p["splits"] == 2
 
 
+@pytest.mark.parametrize("rows", [8, 16])
+@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 5, 16])
+def test_gemv_rows_override_holds_with_any_split(monkeypatch, rows, M, splits):
+    # the plan honours a forced row count for M <= 4 under every forced K
+    # split, including counts that equal tile shares round to another count
+    monkeypatch.setenv("QGEMM_GEMV_ROWS", str(rows))
+    if splits:
+        monkeypatch.setenv("QGEMM_SPLITK", str(splits))
+    for fmt, group, N, K in [(0, 128, 384, 2048), (1, 64, 272, 4096), (3, 32, 72, 1056), (4, 256, 300, 2048),
+                             (0, 64, 48, 6016), (2, 32, 33, 224)]:
+        p = qgm.plan(M, N, K, group, fmt)
+        assert p["path"] == "gemv" and p["tile_n"] == rows, (fmt, N, K, M, p)
+
+
 def test_gemv_split_policy():
     # no K split unless the per-workgroup tile cap forces one, or few row blocks
     # carry long K: one launch beats a split plus its reduce launch
@@ -178,7 +193,14 @@ def test_gemv_split_policy():
     assert qgm.plan(2, 512, 4096, 128, 0)["splits"] == 1       # 8-row kernel: 32 tiles per workgroup
     assert qgm.plan(1, 256, 8192, 128, 0)["splits"] > 1        # 16 row blocks x 64 tiles
     assert qgm.plan(8, 1024, 4096, 128, 0)["splits"] > 1       # MFMA GEMV cap: 16 tiles
-    assert qgm.plan(1, 16, 1 << 20, 128, 0)["splits"] == 512
+    p = qgm.plan(1, 16, 1 << 20, 128, 0)                         # 8192 tiles on one row block
+    assert p["splits"] * 64 >= 8192 and p["splits"] <= 256
+    # the M <= 2 cost model: 4096 x 14336 stays unsplit on 16-row workgroups (one
+    # round of 256), 6144 x 16384 splits in two rather than run 1.5 rounds
+    p = qgm.plan(1, 4096, 14336, 128, 0)
+    assert (p["tile_n"], p["splits"]) == (16, 1)
+    assert qgm.plan(1, 6144, 16384, 128, 0)["splits"] == 2
+    assert qgm.plan(1, 6144, 8192, 128, 0)["tile_n"] == 8
     assert qgm.workspace_bytes(1, 2048, 2048, 128, 0) == 0
 
 
