@@ -61,7 +61,8 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     const int tps_lds = std::max(1, GEMV_LDS_X_BYTES / (kt_width * 2));
     // per-workgroup word-tile caps: v_dot2 kernel (M = 1), MFMA GEMV (M > 1),
     // 8-row v_dot2 kernel (M <= 4)
-    const int cap16 = M <= 1 ? std::min(tps_lds, gemv_m1_tile_cap(fmt)) : nw * (GEMV_MFMA_KW / kt_width);
+    const int cap16 = M <= 1 ? std::min(tps_lds, gemv_m1_tile_cap(fmt))
+                             : nw * std::max(1, GEMV_MFMA_KW / kt_width) * GEMV_MFMA_CH;
     const int cap8 = nw * GEMV_HALF_TPW;
     const bool can8 = M <= 4;
     // K splits for a cap.  A split costs a second (reduce) launch and the fp32
@@ -79,33 +80,35 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
       s = std::min(std::max(s, 1), p.wordtiles);
       return (int)ceil_div(p.wordtiles, ceil_div(p.wordtiles, s));   // splits of equal tile counts
     };
-    const auto fill = [](int64_t w) {   // busy share of the last round of workgroups
-      return (double)w / (double)(ceil_div(w, GEMM_TARGET_WG) * GEMM_TARGET_WG);
-    };
-    (void)fill;
     int s16 = splits_for(cap16);
     int s8 = can8 ? splits_for(cap8) : 0;
     const int rows_env = env_int("QGEMM_GEMV_ROWS", 0);
     bool half = false;
-    if (M <= 2) {
-      // Rows per workgroup (16 or 8) and K splits from a cost model in units
-      // of one row of W times one word tile streamed by a workgroup (about
-      // 5 ns measured): rounds of workgroups over the 256 CUs x rows x tiles
-      // per workgroup, plus GEMV_SPLIT_COST for a split's reduce launch and
-      // fp32 partials (about 2 us) and GEMV_SPLIT_COST_PER per split (the
-      // reduce sums each output's partials in order: about 20 ns each).  Ties
-      // go to fewer workgroups.  M = 2 on
+    {
+      // Rows per workgroup (16 or 8; M > 2: the MFMA GEMV's 16) and K splits
+      // from a cost model in units of one row of W times one word tile
+      // streamed by a workgroup (about 5 ns measured): rounds of workgroups
+      // over the 256 CUs x rows x tiles per workgroup, plus GEMV_SPLIT_COST
+      // for a split's reduce launch and fp32 partials (about 2 us) and
+      // GEMV_SPLIT_COST_PER per split (the reduce sums each output's partials
+      // in order: about 20 ns each).  Ties go to fewer workgroups.  M = 2 on
       // 8-row workgroups takes the v_dot2 kernel with both rows sharing each
       // dequantized pair, on 16-row workgroups the MFMA GEMV.
       int64_t best_cost = INT64_MAX, best_wg = INT64_MAX;
       for (int rows = 16; rows >= 8; rows -= 8) {
-        if (rows_env == 8 || rows_env == 16) {
+        if (rows == 8 && M > 2) continue;
+        if (M <= 2 && (rows_env == 8 || rows_env == 16)) {
           if (rows != rows_env) continue;
         }
         const int cap = rows == 16 ? cap16 : cap8;
         const int per = 16 / rows;   // workgroups per row block and split
         const int s_min = (int)ceil_div(p.wordtiles, cap);
-        const int s_top = std::min(p.wordtiles, std::max(s_min, (int)ceil_div(4 * GEMM_TARGET_WG, (int64_t)p.rowblocks * per)));
+        int s_top = std::min(p.wordtiles, std::max(s_min, (int)ceil_div(4 * GEMM_TARGET_WG, (int64_t)p.rowblocks * per)));
+        // the MFMA GEMV streams K in chunks with the next chunk's loads in
+        // flight, so a long unsplit stream costs less than the model's linear
+        // tiles (M = 8, 2048 x 8192: unsplit 7.8 against 8.2 us in two splits):
+        // with 64 row blocks or more it runs unsplit whenever its cap allows
+        if (M > 2 && s_min == 1 && p.rowblocks >= 64 && split_env <= 0) s_top = 1;
         for (int s = s_min; s <= s_top; ++s) {
           const int tps = (int)ceil_div(p.wordtiles, s);
           if (ceil_div(p.wordtiles, tps) != s) continue;   // splits of equal tile counts only
@@ -124,13 +127,11 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
           }
         }
       }
-    } else if (can8) {
-      // M = 3, 4: the v_dot2 work grows with M, so the 8-row kernel replaces
-      // the MFMA GEMV only where it saves the split and the reduce launch and
-      // its workgroups fit one round of the CUs
-      half = s16 > 1 && s8 == 1 && 2 * (int64_t)p.rowblocks <= GEMM_TARGET_WG;
-      if (rows_env == 8 || rows_env == 16) half = rows_env == 8;
     }
+    // M = 3, 4 run the 8-row v_dot2 kernel (four x rows per pair) only when a
+    // test forces it: its dot products grow with M, and since the MFMA GEMV
+    // streams K unsplit it is never ahead (M = 4, 2048 x 8192: 6.66 against 6.67 us)
+    if (M > 2 && can8 && rows_env == 8) half = true;
     p.rows = half ? 8 : 16;
     p.mmax = half ? (M <= 2 ? M : 4) : M <= 1 ? 1 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     p.splits = half ? s8 : s16;

@@ -12,7 +12,8 @@ namespace qg {
 // Path choice: decode GEMV for M <= GEMV_MAX_M (v_dot2 for M = 1, 16 x 16 MFMA
 // blocks for 2..16 rows), MFMA GEMM above.
 constexpr int GEMV_MAX_M = 16;
-constexpr int GEMV_MFMA_KW = 256;        // K covered by one wave of the MFMA GEMV, at most
+constexpr int GEMV_MFMA_KW = 256;        // K covered by one chunk of an MFMA GEMV wave, at most
+constexpr int GEMV_MFMA_CH = 8;          // chunks one MFMA GEMV wave streams, at most
 constexpr int GEMV_THREADS = 512;          // 8 waves per workgroup
 constexpr int GEMV_TPW_MAX = 8;          // word tiles one wave streams per launch
 constexpr int GEMV_LDS_X_BYTES = 32768;  // x slice staged per workgroup

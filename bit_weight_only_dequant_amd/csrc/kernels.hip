@@ -765,14 +765,14 @@ template <int FMT, int MROWS, int TPW> constexpr size_t gemv_mfma_lds_bytes() {
 // for 4-bit codes, the GEMM's dequant, whatever M is) they are one MFMA step;
 // A is row r of x (zero for r >= MROWS) at the same k.  The 16 x 16 accumulator holds
 // y[4g + i][16 rb + r] in lane 16g + r, element i.
-template <int FMT, int MROWS, int TPW>
+template <int FMT, int MROWS, int TPW, int CH>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
   using F = Fmt<FMT>;
   constexpr int NW = GEMV_THREADS / 64;
-  constexpr int KW = TPW * F::KT;              // k range of one wave
+  constexpr int KW = TPW * F::KT;              // k range of one chunk
   constexpr int KWP = KW + 8;                  // padded x row (halves)
   constexpr int GWMAX = KW / 32;
-  constexpr int XCH = MROWS * KW / 8;          // 16-byte x chunks per wave
+  constexpr int XCH = MROWS * KW / 8;          // 16-byte x chunks per wave and chunk
   constexpr int NXC = (XCH + 63) / 64;
   constexpr int NSZ = (16 * GWMAX + 63) / 64;
   constexpr int XB = MROWS * KWP * 2, WB = XB + 16 * GWMAX * 4;
@@ -787,40 +787,64 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
   const int g = lane >> 4, r = lane & 15;
   const int rb = blockIdx.x, split = blockIdx.y;
   const int T0 = split * a.tps, T1 = min(a.wordtiles, T0 + a.tps);
-  const int tpw = (T1 - T0 + NW - 1) / NW;
+  const int tpw = (T1 - T0 + NW - 1) / NW;           // <= CH * TPW (the launch picks CH)
   const int wt0 = T0 + wave * tpw;
-  const int nt = max(0, min(T1, wt0 + tpw) - wt0);
-  const int k0 = wt0 * F::KT;
+  const int nt = max(0, min(T1, wt0 + tpw) - wt0);   // word tiles of this wave
   const int lg = __builtin_ctz(a.group);
   const int ng = a.K >> lg;
   const int gstride = KW >> lg;
   const int lgs = __builtin_ctz(gstride);
-  const int gs0 = k0 >> lg;
 
-  // 1. every global load first, branch-free: scales/zeros, residual, x, codes
+  // The wave streams its tiles in CH chunks of TPW tiles (KW of K): the loads
+  // of chunk c + 1 are issued before chunk c is staged and multiplied, so one
+  // chunk's loads are always in flight behind the current one's MFMAs.  Loads
+  // are clamped, never out of range, and issued for every chunk (a chunk past
+  // the wave's tiles only adds no products), so every wait is a fixed count.
   const int64_t szbase = (int64_t)rb * 16 * ng * 2;
   // q4k: the (d, dmin) pair of each super-block (8 sub-blocks) as 32 bits,
   // so a row block's pairs start at rb * 16 * (ng / 8) * 4 bytes
   const char* sp = reinterpret_cast<const char*>(a.scales) + (F::KQ ? szbase / 4 : szbase);
   const char* zp = reinterpret_cast<const char*>(F::HAS_Z || F::KQ ? a.zeros : a.scales) + szbase;
-  uint32_t sraw[NSZ], zraw[NSZ];
+  const char* pkrow = reinterpret_cast<const char*>(a.packed) + (int64_t)rb * a.wordtiles * 1024;
+  uint32_t sraw[2][NSZ], zraw[2][NSZ];
+  u4 xr[2][NXC];
+  u4 code[2][TPW];
+  auto load_chunk = [&](int c, uint32_t (&sr)[NSZ], uint32_t (&zr)[NSZ], u4 (&xv)[NXC], u4 (&cv)[TPW]) {
+    const int kc0 = (wt0 + c * TPW) * F::KT;            // a group boundary (KT % group == 0)
+    const int gs0 = kc0 >> lg;
 #pragma unroll
-  for (int j = 0; j < NSZ; ++j) {
-    const int e = lane + 64 * j;
-    const int er = e >> lgs, eg = gs0 + (e & (gstride - 1));
-    const bool ok = e < 16 * gstride && rb * 16 + er < a.N && eg < ng;
-    const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
-    if constexpr (F::KQ) {
-      sraw[j] = *reinterpret_cast<const uint32_t*>(sp + (ok ? (uint32_t)(er * (ng >> 3) + (eg >> 3)) * 4u : 0u));
-      zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
-    } else {
-      sraw[j] = *reinterpret_cast<const uint16_t*>(sp + off);
-      if constexpr (F::HAS_Z) zraw[j] = *reinterpret_cast<const uint16_t*>(zp + off);
-      else zraw[j] = F::ZBITS;  // the implicit zero point
+    for (int j = 0; j < NSZ; ++j) {
+      const int e = lane + 64 * j;
+      const int er = e >> lgs, eg = gs0 + (e & (gstride - 1));
+      const bool ok = e < 16 * gstride && rb * 16 + er < a.N && eg < ng;
+      const uint32_t off = ok ? (uint32_t)(er * ng + eg) * 2u : 0u;
+      if constexpr (F::KQ) {
+        sr[j] = *reinterpret_cast<const uint32_t*>(sp + (ok ? (uint32_t)(er * (ng >> 3) + (eg >> 3)) * 4u : 0u));
+        zr[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+      } else {
+        sr[j] = *reinterpret_cast<const uint16_t*>(sp + off);
+        if constexpr (F::HAS_Z) zr[j] = *reinterpret_cast<const uint16_t*>(zp + off);
+        else zr[j] = F::ZBITS;  // the implicit zero point
+      }
     }
-  }
-  // residual as raw fp16 bits, converted only at the store: a conversion here
-  // would make the wave wait for every load issued so far
+#pragma unroll
+    for (int j = 0; j < NXC; ++j) {
+      const int q = lane + 64 * j;
+      const int m = q / (KW / 8), k = kc0 + (q % (KW / 8)) * 8;
+      const bool ok = q < XCH && m < a.M && k < a.K;
+      const uint32_t off = ok ? (uint32_t)(m * a.ldx + k) * 2u : 0u;
+      xv[j] = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(a.x) + off);
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int T = min(wt0 + c * TPW + i, a.wordtiles - 1);
+      cv[i] = *reinterpret_cast<const u4*>(pkrow + (uint32_t)(T * 1024 + lane * 16));
+    }
+  };
+
+  // 1. chunk 0's loads, the residual (raw fp16 bits, converted only at the
+  //    store: a conversion here would make the wave wait for every load)
+  load_chunk(0, sraw[0], zraw[0], xr[0], code[0]);
   uint32_t res[4] = {0u, 0u, 0u, 0u};
   if (a.resid && a.splits == 1 && wave == 0) {
     const int nc = min(rb * 16 + r, a.N - 1);
@@ -828,73 +852,64 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
     for (int i = 0; i < 4; ++i)
       res[i] = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)min(4 * g + i, a.M - 1) * a.ldr + nc];
   }
-  __builtin_amdgcn_sched_barrier(0);
-  u4 xr[NXC];
-#pragma unroll
-  for (int j = 0; j < NXC; ++j) {
-    const int c = lane + 64 * j;
-    const int m = c / (KW / 8), k = k0 + (c % (KW / 8)) * 8;
-    const bool ok = c < XCH && m < a.M && k < a.K;
-    const uint32_t off = ok ? (uint32_t)(m * a.ldx + k) * 2u : 0u;
-    xr[j] = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(a.x) + off);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  u4 code[TPW];
-  const char* pkrow = reinterpret_cast<const char*>(a.packed) + (int64_t)rb * a.wordtiles * 1024;
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int T = min(wt0 + i, a.wordtiles - 1);
-    code[i] = *reinterpret_cast<const u4*>(pkrow + (uint32_t)(T * 1024 + lane * 16));
-  }
-  __builtin_amdgcn_sched_barrier(0);
 
-  // 2. stage this wave's x rows (zeros beyond M and K) and (scale, zero) pairs
-#pragma unroll
-  for (int j = 0; j < NXC; ++j) {
-    const int c = lane + 64 * j;
-    const int m = c / (KW / 8), kk = (c % (KW / 8)) * 8;
-    const bool ok = m < a.M && k0 + kk < a.K;
-    if (c < XCH) *reinterpret_cast<u4*>(xs + m * KWP + kk) = ok ? xr[j] : u4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int j = 0; j < NSZ; ++j) {
-    const int e = lane + 64 * j;
-    if (e < 16 * gstride)
-      sz[(e >> lgs) * GWMAX + (e & (gstride - 1))] =
-          F::KQ ? kq_half_pair(sraw[j], zraw[j]) : (sraw[j] & 0xffffu) | (zraw[j] << 16);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  // 3. per run of SW codes: dequantize to fp16 s*(q - z), one MFMA per 8 codes
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
   const bool arow = r < MROWS;
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    if (i < nt) {
+  for (int c = 0; c < CH; ++c) {
+    const int b = c & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < CH) load_chunk(c + 1, sraw[b ^ 1], zraw[b ^ 1], xr[b ^ 1], code[b ^ 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kc0 = (wt0 + c * TPW) * F::KT;
+
+    // 2. stage the chunk's x rows (zeros beyond M and K) and (scale, zero)
+    //    pairs; this wave's earlier LDS reads complete first (in order)
 #pragma unroll
-      for (int p = 0; p < F::NSEG; ++p) {
-        const int kl = i * F::KT + g * F::LS + p * F::SW;  // this lane's run inside the wave's range
-        const uint32_t szv = sz[r * GWMAX + (kl >> lg)];
-        const h2 s2 = splat(__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu)));
-        // q4k: the high half is -fp16(dmin*m), codes are unpacked with zero point 0
-        const f16 z = F::KQ ? (f16)0.0f : __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
-        h8 av[F::SW / 8];
+    for (int j = 0; j < NXC; ++j) {
+      const int q = lane + 64 * j;
+      const int m = q / (KW / 8), kk = (q % (KW / 8)) * 8;
+      const bool ok = m < a.M && kc0 + kk < a.K;
+      if (q < XCH) *reinterpret_cast<u4*>(xs + m * KWP + kk) = ok ? xr[b][j] : u4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-        for (int t = 0; t < F::SW / 8; ++t)
-          av[t] = arow ? *reinterpret_cast<const h8*>(xs + (arow ? r : 0) * KWP + kl + 8 * t) : h8{};
-        h2 q[F::SW / 2];
-        run_qmz<FMT>(code[i], p, z, q);
-        if constexpr (F::KQ) kq_weights(q, szv, q, F::SW / 2);   // fma(q, d*sc, -dmin*m)
+    for (int j = 0; j < NSZ; ++j) {
+      const int e = lane + 64 * j;
+      if (e < 16 * gstride)
+        sz[(e >> lgs) * GWMAX + (e & (gstride - 1))] =
+            F::KQ ? kq_half_pair(sraw[b][j], zraw[b][j]) : (sraw[b][j] & 0xffffu) | (zraw[b][j] << 16);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // 3. per run of SW codes: dequantize to fp16 s*(q - z), one MFMA per 8 codes
 #pragma unroll
-        for (int t = 0; t < F::SW / 8; ++t) {
-          h2 w0 = q[4 * t], w1 = q[4 * t + 1], w2 = q[4 * t + 2], w3 = q[4 * t + 3];
-          if constexpr (!F::KQ) {
-            w0 *= s2; w1 *= s2; w2 *= s2; w3 *= s2;
+    for (int i = 0; i < TPW; ++i) {
+      if (c * TPW + i < nt) {
+#pragma unroll
+        for (int p = 0; p < F::NSEG; ++p) {
+          const int kl = i * F::KT + g * F::LS + p * F::SW;  // this lane's run inside the chunk
+          const uint32_t szv = sz[r * GWMAX + (kl >> lg)];
+          const h2 s2 = splat(__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu)));
+          // q4k: the high half is -fp16(dmin*m), codes are unpacked with zero point 0
+          const f16 z = F::KQ ? (f16)0.0f : __builtin_bit_cast(f16, (uint16_t)(szv >> 16));
+          h8 av[F::SW / 8];
+#pragma unroll
+          for (int t = 0; t < F::SW / 8; ++t)
+            av[t] = arow ? *reinterpret_cast<const h8*>(xs + (arow ? r : 0) * KWP + kl + 8 * t) : h8{};
+          h2 q[F::SW / 2];
+          run_qmz<FMT>(code[b][i], p, z, q);
+          if constexpr (F::KQ) kq_weights(q, szv, q, F::SW / 2);   // fma(q, d*sc, -dmin*m)
+#pragma unroll
+          for (int t = 0; t < F::SW / 8; ++t) {
+            h2 w0 = q[4 * t], w1 = q[4 * t + 1], w2 = q[4 * t + 2], w3 = q[4 * t + 3];
+            if constexpr (!F::KQ) {
+              w0 *= s2; w1 *= s2; w2 *= s2; w3 *= s2;
+            }
+            const h8 bf = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t], bf, acc, 0, 0, 0);
           }
-          const h8 bf = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t], bf, acc, 0, 0, 0);
         }
       }
     }
@@ -1490,17 +1505,22 @@ static bool launch_gemv_dot(const GemvArgs& a, int tps, int rows, hipStream_t s)
   return tps >= 16 ? launch_gemv_dot_w<FMT, 16>(a, tps, s) : launch_gemv_dot_w<FMT, 8>(a, tps, s);
 }
 
-// grid: x = row blocks, y = K splits; a wave covers at most GEMV_MFMA_KW of K
+// grid: x = row blocks, y = K splits; a chunk covers at most GEMV_MFMA_KW of
+// K, a wave up to GEMV_MFMA_CH chunks (1, 2, 4 or 8, the fewest that hold its tiles)
 template <int FMT, int MROWS>
 static bool launch_gemv_mfma(const GemvArgs& a, int tps, hipStream_t s) {
   constexpr int TMAX = GEMV_MFMA_KW / Fmt<FMT>::KT;
   const int tpw = (tps + GEMV_THREADS / 64 - 1) / (GEMV_THREADS / 64);
   static_assert(TMAX >= 1 && gemv_mfma_lds_bytes<FMT, MROWS, TMAX>() <= 80 * 1024,
                 "MFMA GEMV LDS: at least two workgroups per CU");
+  static_assert(GEMV_MFMA_CH == 8, "chunk counts instantiated below");
   const dim3 grid((unsigned)a.rowblocks, (unsigned)a.splits), block(GEMV_THREADS);
-  if (tpw > TMAX) return false;
-  if (tpw <= 1) hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MROWS, 1>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MROWS, TMAX>), grid, block, 0, s, a);
+  if (tpw > TMAX * GEMV_MFMA_CH) return false;
+  if (tpw <= 1) hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MROWS, 1, 1>), grid, block, 0, s, a);
+  else if (tpw <= TMAX) hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MROWS, TMAX, 1>), grid, block, 0, s, a);
+  else if (tpw <= 2 * TMAX) hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MROWS, TMAX, 2>), grid, block, 0, s, a);
+  else if (tpw <= 4 * TMAX) hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MROWS, TMAX, 4>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MROWS, TMAX, 8>), grid, block, 0, s, a);
   return true;
 }
 

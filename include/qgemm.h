@@ -202,8 +202,8 @@ int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* z
  * out[0] = path (1 GEMV, 2 GEMM), out[1] = K splits, out[2] = workgroups,
  * out[3] = tile rows (M), out[4] = tile columns (N) -- for the GEMV, the rows of
  * x per launch (1, 2, 4, 8 or 16) and the rows of W per workgroup (16, or 8 when
- * M <= 4 and 8-row workgroups need fewer launches or spread more evenly over
- * the compute units).
+ * M <= 2 and 8-row workgroups need fewer launches or spread more evenly over
+ * the compute units; M = 3, 4 only when QGEMM_GEMV_ROWS=8 forces it).
  * Errors as qgemm. */
 int qg_plan(int M, int N, int K, int group, int fmt, int out[5]);
 

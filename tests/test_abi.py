@@ -192,7 +192,8 @@ def test_gemv_split_policy():
     assert qgm.plan(8, 2048, 2048, 128, 0)["splits"] == 1
     assert qgm.plan(2, 512, 4096, 128, 0)["splits"] == 1       # 8-row kernel: 32 tiles per workgroup
     assert qgm.plan(1, 256, 8192, 128, 0)["splits"] > 1        # 16 row blocks x 64 tiles
-    assert qgm.plan(8, 1024, 4096, 128, 0)["splits"] > 1       # MFMA GEMV cap: 16 tiles
+    assert qgm.plan(8, 1024, 4096, 128, 0)["splits"] == 1      # the MFMA GEMV streams K in chunks
+    assert qgm.plan(8, 4096, 14336, 128, 0)["splits"] == 1
     p = qgm.plan(1, 16, 1 << 20, 128, 0)                         # 8192 tiles on one row block
     assert p["splits"] * 64 >= 8192 and p["splits"] <= 256
     # the M <= 2 cost model: 4096 x 14336 stays unsplit on 16-row workgroups (one
@@ -242,8 +243,7 @@ def test_plans_for_the_workloads():
     assert (qgm.plan(2, 6144, 2048, 128, 0)["tile_m"], qgm.plan(2, 6144, 2048, 128, 0)["tile_n"]) == (2, 8)
     assert (qgm.plan(2, 8192, 2048, 128, 0)["tile_m"], qgm.plan(2, 8192, 2048, 128, 0)["tile_n"]) == (4, 16)
     assert qgm.plan(3, 6144, 2048, 128, 0)["tile_n"] == 16
-    # M = 3, 4: the 8-row v_dot2 kernel only where it saves the MFMA GEMV's split
-    # and fits one round of workgroups
+    # M = 3, 4: the MFMA GEMV, which streams K unsplit (8-row v_dot2 only when forced)
     p = qgm.plan(4, 2048, 8192, 128, 0)
-    assert (p["tile_m"], p["tile_n"], p["splits"]) == (4, 8, 1)
+    assert (p["tile_m"], p["tile_n"], p["splits"]) == (4, 16, 1)
     assert qgm.plan(4, 6144, 8192, 128, 0)["tile_n"] == 16
