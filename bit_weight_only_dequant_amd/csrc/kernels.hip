@@ -1008,9 +1008,9 @@ template <int FMT, int MB, int NB> struct GemmStage {
   static constexpr int SEG = WIDE ? Fmt<FMT>::LS / 32 : 1;  // 32-code runs per chunk
   static constexpr int CH = WIDE ? 1 : 2;                  // chunks per stage
   static constexpr int STAGES = WIDE ? 2 * SEG : 1;        // stages per word tile
-  static constexpr int XB = 32 * MB * 64 * 2;              // x bytes per stage
-  static constexpr int SB = XB + CH * NB * 1024;           // + code chunks of the column blocks
-  static constexpr int DMA = XB / 1024 + NB * CH;          // direct loads per lane per stage (10, 12 at 2 x 2)
+  static constexpr int XB = 32 * MB * 64 * 2;              // x bytes per stage (LDS)
+  static constexpr int SB = XB;                            // codes go to VGPRs
+  static constexpr int DMA = XB / 1024 + NB * CH;          // vector loads per lane per stage (10, 12 at 2 x 2)
 };
 
 // Prefill GEMM (M > 16).  Workgroup tile 32*MB (M) x 32*NB (N) -- 64 x 64,
@@ -1030,7 +1030,7 @@ template <int FMT, int MB, int NB> struct GemmStage {
 // consecutive rows hit 16 distinct bank groups.  All LDS operands of a stage
 // are read first; group barriers then interleave one MFMA with a few VALU of
 // the dequantization so the two pipes overlap.
-template <int FMT, int NW, int TPW, int DEPTH, int MB, int NB>
+template <int FMT, int NW, int TPW, int DEPTH, int MB, int NB, bool ALL>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   using F = Fmt<FMT>;
   using S = GemmStage<FMT, MB, NB>;
@@ -1066,6 +1066,22 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 
   auto seg_k = [](int gg, int h, int j) { return (gg + 2 * h) * F::LS + j * 32; };
 
+  // 0. the residual of the block this wave finishes, fp16 bits, converted
+  //    only in the epilogue; issued first, so no later wait depends on it
+  uint32_t res[16];
+  const int fb = wave < NBLK ? wave : 0;                 // block this wave finishes: (fb / NB, fb % NB)
+  if (a.resid && a.splits == 1 && wave < NBLK) {
+    const int colc = min(n0 + (fb % NB) * 32 + (lane & 31), a.N - 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = min(m0 + (fb / NB) * 32 + acc_row(i, lane), a.M - 1);
+      res[i] = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)row * a.ldr + colc];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) res[i] = 0u;
+  }
+
   // 1. the workgroup's scales and zeros, loaded cooperatively (clamped) and
   //    staged in LDS as [column][group] (rows padded by one word)
   constexpr int NSZ = (TN * GEMM_GCAP + NW * 64 - 1) / (NW * 64);
@@ -1075,10 +1091,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   uint32_t sraw[NSZ], zraw[NSZ];
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
-    if (j < nsz) {
+    {   // unconditional (clamped): a branch here makes the compiler wait on the loads at once
       const int e = tid + NW * 64 * j;                   // column e >> lgs, group e % gsr
       const int ec = e >> lgs, eg = e & (gsr - 1);
-      const bool ok = ec < TN && eg < gwn && n0 + ec < a.N;
+      const bool ok = j < nsz && ec < TN && eg < gwn && n0 + ec < a.N;
       const int64_t off = ok ? ((int64_t)(n0 + ec) * ng + gw0 + eg) : 0;
       if constexpr (F::KQ) {   // (d, dmin) of the super-block, (sc, m) of the sub-block
         const int64_t soff = ok ? ((int64_t)(n0 + ec) * (ng >> 3) + ((gw0 + eg) >> 3)) : 0;
@@ -1112,9 +1128,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     const int rb = min((n0 >> 4) + 2 * nb + ((lane >> 4) & 1), a.rowblocks - 1);  // columns past N: never stored
     cb[nb] = reinterpret_cast<const char*>(a.packed) + (int64_t)rb * a.wordtiles * 1024 + (g2 * 16 + r) * 16;
   }
+  // ALL: every wave issues all TPW * STAGES stages, those past its share with
+  // the tile clamped in bounds (never computed), so the loads form one
+  // straight-line sequence and every wait is a fixed count (the compiler's
+  // own waits for the code registers then need no merge over branches).
+  // Otherwise (splits that leave waves with few or no tiles) a wave issues
+  // only its own stages.
+  u4 bq[DEPTH][S::CH][NB];   // code chunks of the stages in flight
   auto issue_stage = [&](int st) {
     const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
-    const int kt = wt0 + t;
+    const int kt = min(wt0 + t, a.wordtiles - 1);
     uint8_t* dst = wbuf + (st % DEPTH) * S::SB;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -1136,9 +1159,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     for (int c = 0; c < S::CH; ++c)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(cb[nb] + (int64_t)kt * 1024 + (h + c) * 512),
-            (void __attribute__((address_space(3)))*)(dst + S::XB + (c * NB + nb) * 1024), 16, 0, 0);
+        bq[st % DEPTH][c][nb] = *reinterpret_cast<const u4*>(cb[nb] + (int64_t)kt * 1024 + (h + c) * 512);
+    __builtin_amdgcn_sched_barrier(0);   // stages stay in issue order (the waits count them)
   };
 
   f16v acc[MB][NB];
@@ -1174,7 +1196,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       const int gi = min(max((kseg >> lg) - gw0, 0), gwn - 1);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        bt[c][nb] = *reinterpret_cast<const u4*>(sb + S::XB + (c * NB + nb) * 1024 + lane * 16);
+        bt[c][nb] = bq[st % DEPTH][c][nb];
         szv[c][nb] = szl[(nb * 32 + (lane & 31)) * SZS + gi];
       }
     }
@@ -1239,26 +1261,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     }
   };
 
-  // 4. first stages in flight, residual prefetch, then the scale/zero table
-  //    (waiting for the scale/zero loads only)
+  // 4. first stages in flight, then the scale/zero table (waiting for the
+  //    scale/zero loads only)
+  constexpr int NST = TPW * S::STAGES;
+  const int lim = ALL ? NST : min(nst, NST);   // stages this wave issues
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
-    if (d < nst) issue_stage(d);
-  uint32_t res[16];   // residual, fp16 bits, converted only in the epilogue (no wait here)
-  const int fb = wave < NBLK ? wave : 0;                 // block this wave finishes: (fb / NB, fb % NB)
-  if (a.resid && a.splits == 1 && wave < NBLK) {
-    const int colc = min(n0 + (fb % NB) * 32 + (lane & 31), a.N - 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = min(m0 + (fb / NB) * 32 + acc_row(i, lane), a.M - 1);
-      res[i] = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)row * a.ldr + colc];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) res[i] = 0u;
-  }
+    if (d < lim) issue_stage(d);
+  // the table is written with the stages still in flight: its stores are
+  // plain ds_write_b32 in asm, since the compiler would otherwise wait for
+  // every outstanding global->LDS load before an LDS store it cannot tell
+  // apart from them (the table lies outside every wave's ring)
   {
-    const int ist = min(DEPTH, nst);
+    const int ist = min(DEPTH, lim);
     if (ist >= 3) wait_vm<(DEPTH >= 3 ? 3 : 0) * S::DMA>();
     else if (ist == 2) wait_vm<(DEPTH >= 2 ? 2 : 0) * S::DMA>();
     else if (ist == 1) wait_vm<S::DMA>();
@@ -1268,25 +1283,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
     const int e = tid + NW * 64 * j;
-    if (j < nsz && (e >> lgs) < TN)
-      szl[(e >> lgs) * SZS + (e & (gsr - 1))] =
-          F::KQ ? kq_half_pair(sraw[j], zraw[j]) : (sraw[j] & 0xffffu) | (zraw[j] << 16);
+    if (j < nsz && (e >> lgs) < TN) {
+      const uint32_t v = F::KQ ? kq_half_pair(sraw[j], zraw[j]) : (sraw[j] & 0xffffu) | (zraw[j] << 16);
+      const uint32_t addr = (uint32_t)(uintptr_t)(szl + (e >> lgs) * SZS + (e & (gsr - 1)));
+      asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+    }
   }
-  __syncthreads();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
 
   // 5. the K loop: wait for stage st (newer stages may stay in flight),
   //    compute it, refill its buffer with stage st + DEPTH
 #pragma unroll
-  for (int st = 0; st < TPW * S::STAGES; ++st) {
-    if (st < nst) {
-      const int newer = min(DEPTH - 1, nst - 1 - st);
+  for (int st = 0; st < NST; ++st) {
+    if (st < lim) {
+      const int newer = min(DEPTH - 1, lim - 1 - st);   // stages issued after st
       if (newer >= 2) wait_vm<(DEPTH >= 3 ? 2 : 0) * S::DMA>();
       else if (newer == 1) wait_vm<(DEPTH >= 2 ? 1 : 0) * S::DMA>();
       else wait_vm<0>();
       __builtin_amdgcn_sched_barrier(0);
-      compute_stage(st);
+      if (!ALL || st < nst) compute_stage(st);
       __builtin_amdgcn_sched_barrier(0);
-      if (st + DEPTH < nst) {
+      if (st + DEPTH < lim) {
         wait_lgkm0();  // this buffer's reads are back
         __builtin_amdgcn_sched_barrier(0);
         issue_stage(st + DEPTH);
@@ -1537,17 +1555,42 @@ static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, int rows, hipStr
   }
 }
 
-// grid: x = column tiles, y = row tiles, z = K splits; MB x NB blocks of 32 x 32
-template <int MB, int NB>
-static void launch_gemm_tiles(const GemmArgs& a, const Plan& p, int fmt, hipStream_t s) {
+// grid: x = column tiles, y = row tiles, z = K splits; MB x NB blocks of 32 x 32.
+// Two stages in flight per wave where that measured faster (32 x 32 tiles,
+// q8_0), one elsewhere (the 64-row tiles' rings then leave the L2 path less
+// crowded).  TPW is the fewest word tiles per wave that cover the split, since
+// every wave issues all TPW * STAGES stages.
+template <int FMT, int D, int MB, int NB, int TPW>
+static void launch_gemm_tpw(const GemmArgs& a, const Plan& p, hipStream_t s) {
   const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.splits), block(GEMM_THREADS);
   constexpr int NW = GEMM_THREADS / 64;
+  // issue every stage in every wave when that wastes at most an eighth of them
+  if ((int64_t)8 * (NW * TPW - p.tps) <= NW * TPW)
+    hipLaunchKernelGGL((gemm_kernel<FMT, NW, TPW, D, MB, NB, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<FMT, NW, TPW, D, MB, NB, false>), grid, block, 0, s, a);
+}
+
+template <int FMT, int D, int MB, int NB>
+static void launch_gemm_fmt(const GemmArgs& a, const Plan& p, hipStream_t s) {
+  constexpr int NW = GEMM_THREADS / 64;
+  constexpr int TMAX = FMT == Q8_0 ? GEMM_TPW_Q8 : GEMM_TPW;
+  static_assert(TMAX == 2 || TMAX == 4, "tile counts instantiated below");
+  const int per = (int)ceil_div(p.tps, NW);
+  if (per <= 1) launch_gemm_tpw<FMT, D, MB, NB, 1>(a, p, s);
+  else if (per <= 2) launch_gemm_tpw<FMT, D, MB, NB, 2>(a, p, s);
+  else launch_gemm_tpw<FMT, D, MB, NB, TMAX>(a, p, s);
+}
+
+template <int MB, int NB>
+static void launch_gemm_tiles(const GemmArgs& a, const Plan& p, int fmt, hipStream_t s) {
+  constexpr int D = MB * NB == 1 ? GEMM_DEPTH : 1;
   switch (fmt) {
-    case QG_INT4_ASYM: hipLaunchKernelGGL((gemm_kernel<INT4_ASYM, NW, GEMM_TPW, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
-    case QG_INT2_ASYM: hipLaunchKernelGGL((gemm_kernel<INT2_ASYM, NW, GEMM_TPW, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
-    case QG_Q8_0: hipLaunchKernelGGL((gemm_kernel<Q8_0, NW, GEMM_TPW_Q8, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
-    case QG_Q4K: hipLaunchKernelGGL((gemm_kernel<Q4K, NW, GEMM_TPW, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_kernel<Q4_0, NW, GEMM_TPW, GEMM_DEPTH, MB, NB>), grid, block, 0, s, a); break;
+    case QG_INT4_ASYM: launch_gemm_fmt<INT4_ASYM, D, MB, NB>(a, p, s); break;
+    case QG_INT2_ASYM: launch_gemm_fmt<INT2_ASYM, D, MB, NB>(a, p, s); break;
+    case QG_Q8_0: launch_gemm_fmt<Q8_0, GEMM_DEPTH, MB, NB>(a, p, s); break;
+    case QG_Q4K: launch_gemm_fmt<Q4K, D, MB, NB>(a, p, s); break;
+    default: launch_gemm_fmt<Q4_0, D, MB, NB>(a, p, s); break;
   }
 }
 
