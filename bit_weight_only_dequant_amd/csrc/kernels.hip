@@ -1066,20 +1066,27 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 
   auto seg_k = [](int gg, int h, int j) { return (gg + 2 * h) * F::LS + j * 32; };
 
-  // 0. the residual of the block this wave finishes, fp16 bits, converted
-  //    only in the epilogue; issued first, so no later wait depends on it
-  uint32_t res[16];
-  const int fb = wave < NBLK ? wave : 0;                 // block this wave finishes: (fb / NB, fb % NB)
-  if (a.resid && a.splits == 1 && wave < NBLK) {
-    const int colc = min(n0 + (fb % NB) * 32 + (lane & 31), a.N - 1);
+  // 0. the residual of the quads this wave finishes (UPW quads of 32 x 32
+  //    blocks: all NW waves share the final sums), fp16 bits, converted only
+  //    in the epilogue; issued first, so no later wait depends on it
+  constexpr int UNITS = NBLK * 4, UPW = UNITS >= NW ? UNITS / NW : 1;
+  static_assert(UNITS < NW || UNITS % NW == 0, "quads per wave");
+  const bool fin = wave * UPW < UNITS;                  // this wave finishes quads
+  uint32_t res[4 * UPW];
+  if (a.resid && a.splits == 1 && fin) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = min(m0 + (fb / NB) * 32 + acc_row(i, lane), a.M - 1);
-      res[i] = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)row * a.ldr + colc];
+    for (int k = 0; k < UPW; ++k) {
+      const int u = wave * UPW + k, blk = u >> 2, q = u & 3;
+      const int colc = min(n0 + (blk % NB) * 32 + (lane & 31), a.N - 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = min(m0 + (blk / NB) * 32 + acc_row(4 * q + e, lane), a.M - 1);
+        res[4 * k + e] = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)row * a.ldr + colc];
+      }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) res[i] = 0u;
+    for (int i = 0; i < 4 * UPW; ++i) res[i] = 0u;
   }
 
   // 1. the workgroup's scales and zeros, loaded cooperatively (clamped) and
@@ -1313,7 +1320,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   }
 
   // 6. sum the NW waves' accumulators through LDS in wave order
-  //    (deterministic); wave w < NBLK finishes block w
+  //    (deterministic); wave w finishes quads w * UPW .. + UPW - 1, so the
+  //    reads, sums and stores spread over every wave
   __syncthreads();
   f4* red = reinterpret_cast<f4*>(smem);
 #pragma unroll
@@ -1324,31 +1332,36 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       red[((wave * NBLK + blk) * 4 + q) * 64 + lane] = f4{A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]};
     }
   __syncthreads();
-  if (wave >= NBLK) return;
-  f4 tot[4];
+  if (!fin) return;
+  f4 tot[UPW];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f4 v = red[((0 * NBLK + fb) * 4 + q) * 64 + lane];
+  for (int k = 0; k < UPW; ++k) {
+    const int u = wave * UPW + k;                       // quad u & 3 of block u >> 2
+    f4 v = red[(0 * UNITS + u) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) v += red[((w * NBLK + fb) * 4 + q) * 64 + lane];
-    tot[q] = v;
+    for (int w = 1; w < NW; ++w) v += red[(w * UNITS + u) * 64 + lane];
+    tot[k] = v;
   }
-  const int col = n0 + (fb % NB) * 32 + (lane & 31);
   if (a.splits == 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = m0 + (fb / NB) * 32 + acc_row(i, lane);
-      if (row < a.M && col < a.N)
-        a.y[(int64_t)row * a.ldy + col] = (f16)(tot[i >> 2][i & 3] + (float)__builtin_bit_cast(f16, (uint16_t)res[i]));
+    for (int k = 0; k < UPW; ++k) {
+      const int u = wave * UPW + k, blk = u >> 2, q = u & 3;
+      const int col = n0 + (blk % NB) * 32 + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + (blk / NB) * 32 + acc_row(4 * q + e, lane);
+        if (row < a.M && col < a.N)
+          a.y[(int64_t)row * a.ldy + col] = (f16)(tot[k][e] + (float)__builtin_bit_cast(f16, (uint16_t)res[4 * k + e]));
+      }
     }
     return;
   }
   // split-K: this split's TM x TN partial; gemm_reduce_kernel sums the splits
   f4* wsp = reinterpret_cast<f4*>(a.ws);
   const int64_t tile = (int64_t)tm * a.tiles_n + tn;
-  const int64_t base = ((tile * a.splits + split) * NBLK + fb) * 4;
+  const int64_t base = (tile * a.splits + split) * UNITS;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) wsp[(base + q) * 64 + lane] = tot[q];
+  for (int k = 0; k < UPW; ++k) wsp[(base + wave * UPW + k) * 64 + lane] = tot[k];
 }
 
 // Sums a tile's split partials in split order (deterministic), adds the

@@ -282,6 +282,41 @@ def test_gemm_tile_variants(monkeypatch, tile, fmt, group, N, K, M):
     check_close(run_gemm(lin, c.x), ref_y(c, c.x), f"tile {tile}")
 
 
+# GEMM stage issue: word tiles per wave (TPW) follow the split, and every wave
+# issues all TPW x stages (those past its share clamped, not computed) when at
+# most an eighth would be wasted, else only its own.  Each case names the TPW
+# and mode it reaches; ragged K and short waves on both modes and both depths.
+def gemm_issue_mode(fmt, K, splits):
+    cpw = {0: 8, 1: 16, 2: 8, 3: 4, 4: 8}[fmt]
+    wordtiles = -(-(K // cpw) // 16)
+    tps = -(-wordtiles // splits)
+    per = -(-tps // 8)
+    tpw = 1 if per <= 1 else 2 if per <= 2 else (4 if fmt == 3 else 2)
+    return tpw, 8 * (8 * tpw - tps) <= 8 * tpw
+
+
+@pytest.mark.parametrize("tile", [3232, 6464])
+@pytest.mark.parametrize("fmt,group,K,splits,tpw,all_", [
+    (0, 128, 1024, 1, 1, True), (0, 128, 2048, 1, 2, True), (0, 128, 2048, 4, 1, False),
+    (0, 128, 1920, 1, 2, True), (0, 128, 1664, 1, 2, False),
+    (3, 32, 2048, 1, 4, True), (3, 32, 1344, 1, 4, False), (3, 32, 1984, 1, 4, True),
+    (1, 64, 2048, 1, 1, True), (1, 64, 2048, 2, 1, False),
+    (4, 256, 2048, 1, 2, True), (4, 256, 1792, 1, 2, True), (2, 32, 1056, 1, 2, False)])
+def test_gemm_stage_issue_modes(monkeypatch, tile, fmt, group, K, splits, tpw, all_):
+    monkeypatch.setenv("QGEMM_GEMM_TILE", str(tile))
+    monkeypatch.setenv("QGEMM_SPLITK", str(splits))
+    N, M = 200, 72
+    p = qgm.plan(M, N, K, group, fmt)
+    say(f"gemm issue tile {tile} fmt={fmt} g={group} K={K} splits={splits} plan={p}")
+    assert p["path"] == "gemm" and p["splits"] == splits
+    assert gemm_issue_mode(fmt, K, splits) == (tpw, all_)
+    c = synth.random_codes_case(tile + K + 31 * splits + fmt, fmt, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    res = synth.draw_x(np.random.default_rng(K + fmt), M, N) if splits == 1 else None
+    check_close(run_gemm(lin, c.x, residual=res), ref_y(c, c.x, residual=res),
+                f"issue tile {tile} K {K} splits {splits}")
+
+
 def test_gemm_small_tiles_without_split():
     # 128 x 2048 x 2048 (the looped block's O projection): 32 x 32 tiles fill
     # the CUs with no K split where 64 x 64 tiles would split 4 ways
