@@ -1036,9 +1036,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   using S = GemmStage<FMT, MB, NB>;
   constexpr int SEG = S::SEG;
   constexpr int TM = 32 * MB, TN = 32 * NB, NBLK = MB * NB;
-  constexpr int PIPE = NW * DEPTH * S::SB;
-  constexpr int RED = NW * NBLK * 4 * 64 * 16;          // [wave][block][quad][lane] f4
-  constexpr int BIG = PIPE > RED ? PIPE : RED;
+  // per-wave LDS region: its stage ring, large enough to take the wave's
+  // accumulators ([block][quad][lane] f4) at the end, so a wave writes them
+  // as soon as its own K loop is done, without waiting for the others
+  constexpr int UNITS = NBLK * 4;                        // 32 x 32 block quads
+  constexpr int WS = DEPTH * S::SB > UNITS * 1024 ? DEPTH * S::SB : UNITS * 1024;
+  constexpr int BIG = NW * WS;
   // (s | z << 16) per column and group; a column's row is padded by one
   // word so that the 32 columns one lookup reads fall in 32 distinct banks
   constexpr int SZS = GEMM_GCAP + 1;
@@ -1062,14 +1065,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   const int ng = a.K >> lg;
   const int gw0 = (kt0 * F::KT) >> lg;                   // first group (KT % group == 0)
   const int gwn = min(ng, ((kt1 * F::KT) + a.group - 1) >> lg) - gw0;  // <= GEMM_GCAP (plan)
-  uint8_t* wbuf = smem + wave * DEPTH * S::SB;
+  uint8_t* wbuf = smem + wave * WS;
 
   auto seg_k = [](int gg, int h, int j) { return (gg + 2 * h) * F::LS + j * 32; };
 
   // 0. the residual of the quads this wave finishes (UPW quads of 32 x 32
   //    blocks: all NW waves share the final sums), fp16 bits, converted only
   //    in the epilogue; issued first, so no later wait depends on it
-  constexpr int UNITS = NBLK * 4, UPW = UNITS >= NW ? UNITS / NW : 1;
+  constexpr int UPW = UNITS >= NW ? UNITS / NW : 1;
   static_assert(UNITS < NW || UNITS % NW == 0, "quads per wave");
   const bool fin = wave * UPW < UNITS;                  // this wave finishes quads
   uint32_t res[4 * UPW];
@@ -1320,16 +1323,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   }
 
   // 6. sum the NW waves' accumulators through LDS in wave order
-  //    (deterministic); wave w finishes quads w * UPW .. + UPW - 1, so the
-  //    reads, sums and stores spread over every wave
-  __syncthreads();
+  //    (deterministic); each wave first writes its own into its ring region
+  //    (its loads and LDS reads are done), then wave w finishes quads
+  //    w * UPW .. + UPW - 1, so the reads, sums and stores spread over every wave
   f4* red = reinterpret_cast<f4*>(smem);
+  constexpr int WSF = WS / 16;                           // region stride in f4
 #pragma unroll
   for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f16v& A = acc[blk / NB][blk % NB];
-      red[((wave * NBLK + blk) * 4 + q) * 64 + lane] = f4{A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]};
+      red[wave * WSF + (blk * 4 + q) * 64 + lane] = f4{A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]};
     }
   __syncthreads();
   if (!fin) return;
@@ -1337,9 +1341,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int k = 0; k < UPW; ++k) {
     const int u = wave * UPW + k;                       // quad u & 3 of block u >> 2
-    f4 v = red[(0 * UNITS + u) * 64 + lane];
+    f4 v = red[u * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) v += red[(w * UNITS + u) * 64 + lane];
+    for (int w = 1; w < NW; ++w) v += red[w * WSF + u * 64 + lane];
     tot[k] = v;
   }
   if (a.splits == 1) {
