@@ -146,18 +146,21 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   p.tm = M <= GEMM_SMALL_M ? 32 : GEMM_TM;
   p.tn = M <= 2 * GEMM_SMALL_M ? 32 : GEMM_TN;
   const int nw = GEMM_THREADS / 64;
-  const int tpw = gemm_tpw(fmt);
-  const int s_tiles = (int)ceil_div(p.wordtiles, nw * tpw);
   const int mg = meta_group(fmt, group);   // scale entries the kernel stages per 'group'
-  const int s_groups = (int)ceil_div((int64_t)p.wordtiles * kt_width / mg, GEMM_GCAP);
-  const int s_min = std::max(s_tiles, s_groups);
+  // fewest K splits a tile shape allows: word tiles per wave, groups per workgroup
+  const auto s_min_for = [&](int tm, int tn) {
+    const int s_tiles = (int)ceil_div(p.wordtiles, nw * gemm_tpw(fmt, tm == 32 && tn == 32));
+    const int s_groups = (int)ceil_div((int64_t)p.wordtiles * kt_width / mg, GEMM_GCAP);
+    return std::max(s_tiles, s_groups);
+  };
   const int64_t split_below = (GEMM_TARGET_WG * 5) / 8;   // fewer tiles than this: split K
   // Where the M-sized tiles would leave the CUs idle and so split K, but
-  // 32 x 32 tiles fill them with no split (s_min = 1), one launch of 32 x 32
-  // tiles beats a split plus its reduce launch, though every code is then
-  // dequantized in twice as many workgroups (128 x 2048 x 2048: 7.4 against
-  // 9.3 us for 64 x 64 tiles split 4 ways); measured up to M = 128
-  if (s_min == 1 && M <= 2 * GEMM_TM && (int64_t)ceil_div(N, p.tn) * ceil_div(M, p.tm) < split_below &&
+  // 32 x 32 tiles fill them with no split, one launch of 32 x 32 tiles beats
+  // a split plus its reduce launch, though every code is then dequantized in
+  // more workgroups (128 x 2048 x 2048: 4.8 against 9.3 us for 64 x 64 tiles
+  // split 4 ways); measured up to M = 128
+  if (s_min_for(32, 32) == 1 && M <= 2 * GEMM_TM &&
+      (int64_t)ceil_div(N, p.tn) * ceil_div(M, p.tm) < split_below &&
       (int64_t)ceil_div(N, 32) * ceil_div(M, 32) >= split_below) {
     p.tm = 32;
     p.tn = 32;
@@ -167,10 +170,13 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     p.tm = tile_env / 100;
     p.tn = tile_env % 100;
   }
+  const bool small_tile = p.tm == 32 && p.tn == 32;
+  const int tpw = gemm_tpw(fmt, small_tile);
+  const int s_min = s_min_for(p.tm, p.tn);
   p.tiles_n = (int)ceil_div(N, p.tn);
   p.tiles_m = (int)ceil_div(M, p.tm);
   const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m;
-  // at most gemm_tpw(fmt) word tiles per wave and GEMM_GCAP groups per workgroup;
+  // at most gemm_tpw word tiles per wave and GEMM_GCAP groups per workgroup;
   // split K across workgroups only when the tiles leave most compute units
   // idle, since a split writes fp32 partials and costs a second (reduce) launch
   int s = tiles >= split_below ? 1 : (int)ceil_div(GEMM_TARGET_WG, tiles);

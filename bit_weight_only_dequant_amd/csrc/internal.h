@@ -28,6 +28,7 @@ constexpr int GEMM_TN = 64;              // workgroup tile columns (N)
 constexpr int GEMM_SMALL_M = 32;         // M <= this: 32 x 32 tiles; M <= 2x this: 64 x 32
 constexpr int GEMM_TPW = 2;              // word tiles per wave (K per workgroup <= 16 tiles)
 constexpr int GEMM_TPW_Q8 = 4;           // q8_0: a tile is 64 wide, so 4 per wave (256 of K)
+constexpr int GEMM_TPW_SMALL = 8;        // 32 x 32 tiles (two stages in flight): long K unsplit
 constexpr int GEMM_DEPTH = 2;            // x/code stages in flight per wave
 constexpr int GEMM_GCAP = 64;            // quantization groups per workgroup, at most
 constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
@@ -39,7 +40,9 @@ constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
 inline constexpr int gemv_m1_tile_cap(int fmt) { return fmt == INT2_ASYM || fmt == Q4K ? 64 : 128; }
 
 // word tiles one GEMM wave covers, at most
-inline constexpr int gemm_tpw(int fmt) { return fmt == Q8_0 ? GEMM_TPW_Q8 : GEMM_TPW; }
+inline constexpr int gemm_tpw(int fmt, bool small_tile) {
+  return small_tile ? GEMM_TPW_SMALL : fmt == Q8_0 ? GEMM_TPW_Q8 : GEMM_TPW;
+}
 
 struct Plan {
   int path = 0;        // 0 none (no-op / zero fill), 1 GEMV, 2 GEMM

@@ -1575,8 +1575,8 @@ static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, int rows, hipStr
 // grid: x = column tiles, y = row tiles, z = K splits; MB x NB blocks of 32 x 32.
 // Two stages in flight per wave where that measured faster (32 x 32 tiles,
 // q8_0), one elsewhere (the 64-row tiles' rings then leave the L2 path less
-// crowded).  TPW is the fewest word tiles per wave that cover the split, since
-// every wave issues all TPW * STAGES stages.
+// crowded).  TPW is the fewest word tiles per wave (1, 2, 4, or 8 on 32 x 32
+// tiles) that cover the split, since every wave issues all TPW * STAGES stages.
 template <int FMT, int D, int MB, int NB, int TPW>
 static void launch_gemm_tpw(const GemmArgs& a, const Plan& p, hipStream_t s) {
   const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.splits), block(GEMM_THREADS);
@@ -1591,11 +1591,12 @@ static void launch_gemm_tpw(const GemmArgs& a, const Plan& p, hipStream_t s) {
 template <int FMT, int D, int MB, int NB>
 static void launch_gemm_fmt(const GemmArgs& a, const Plan& p, hipStream_t s) {
   constexpr int NW = GEMM_THREADS / 64;
-  constexpr int TMAX = FMT == Q8_0 ? GEMM_TPW_Q8 : GEMM_TPW;
-  static_assert(TMAX == 2 || TMAX == 4, "tile counts instantiated below");
-  const int per = (int)ceil_div(p.tps, NW);
+  constexpr int TMAX = MB * NB == 1 ? GEMM_TPW_SMALL : FMT == Q8_0 ? GEMM_TPW_Q8 : GEMM_TPW;
+  static_assert(TMAX == 2 || TMAX == 4 || TMAX == 8, "tile counts instantiated below");
+  const int per = (int)ceil_div(p.tps, NW);   // <= TMAX (the plan's cap)
   if (per <= 1) launch_gemm_tpw<FMT, D, MB, NB, 1>(a, p, s);
-  else if (per <= 2) launch_gemm_tpw<FMT, D, MB, NB, 2>(a, p, s);
+  else if (per <= 2 || TMAX == 2) launch_gemm_tpw<FMT, D, MB, NB, 2>(a, p, s);
+  else if (per <= 4 || TMAX == 4) launch_gemm_tpw<FMT, D, MB, NB, (TMAX >= 4 ? 4 : 2)>(a, p, s);
   else launch_gemm_tpw<FMT, D, MB, NB, TMAX>(a, p, s);
 }
 

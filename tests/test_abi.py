@@ -220,10 +220,11 @@ def test_plans_for_the_workloads():
     # 64 x 64 tiles would split K 4 ways at 128 x 2048 x 2048; 32 x 32 tiles fill the CUs unsplit
     p = qgm.plan(128, 2048, 2048, 128, 0)
     assert (p["tile_m"], p["tile_n"], p["splits"]) == (32, 32, 1)
-    p = qgm.plan(128, 2048, 8192, 128, 0)                  # K = 8192 must split: tiles stay 64 x 64
-    assert (p["tile_m"], p["tile_n"], p["splits"]) == (64, 64, 4)
+    # K = 8192: 64 x 64 tiles would split 4 ways; 32 x 32 tiles take 8 word tiles per wave, unsplit
+    p = qgm.plan(128, 2048, 8192, 128, 0)
+    assert (p["tile_m"], p["tile_n"], p["splits"]) == (32, 32, 1)
     assert qgm.workspace_bytes(1, 16, 128, 32, 0) == 0
-    assert qgm.workspace_bytes(128, 2048, 8192, 128, 0) > 0   # split-K for small N
+    assert qgm.workspace_bytes(128, 1024, 8192, 128, 0) > 0   # split-K for small N
     # q8_0: 64-wide word tiles, 4 per GEMM wave, so K = 2048 needs no split
     q = qgm.plan(128, 8192, 2048, 32, 3)
     assert q["path"] == "gemm" and q["splits"] == 1

@@ -286,12 +286,13 @@ def test_gemm_tile_variants(monkeypatch, tile, fmt, group, N, K, M):
 # issues all TPW x stages (those past its share clamped, not computed) when at
 # most an eighth would be wasted, else only its own.  Each case names the TPW
 # and mode it reaches; ragged K and short waves on both modes and both depths.
-def gemm_issue_mode(fmt, K, splits):
+def gemm_issue_mode(fmt, K, splits, small=False):
     cpw = {0: 8, 1: 16, 2: 8, 3: 4, 4: 8}[fmt]
     wordtiles = -(-(K // cpw) // 16)
     tps = -(-wordtiles // splits)
     per = -(-tps // 8)
-    tpw = 1 if per <= 1 else 2 if per <= 2 else (4 if fmt == 3 else 2)
+    tmax = 8 if small else 4 if fmt == 3 else 2
+    tpw = 1 if per <= 1 else 2 if per <= 2 or tmax == 2 else 4 if per <= 4 or tmax == 4 else 8
     return tpw, 8 * (8 * tpw - tps) <= 8 * tpw
 
 
@@ -309,12 +310,31 @@ def test_gemm_stage_issue_modes(monkeypatch, tile, fmt, group, K, splits, tpw, a
     p = qgm.plan(M, N, K, group, fmt)
     say(f"gemm issue tile {tile} fmt={fmt} g={group} K={K} splits={splits} plan={p}")
     assert p["path"] == "gemm" and p["splits"] == splits
-    assert gemm_issue_mode(fmt, K, splits) == (tpw, all_)
+    assert gemm_issue_mode(fmt, K, splits, tile == 3232) == (tpw, all_)
     c = synth.random_codes_case(tile + K + 31 * splits + fmt, fmt, group, N, K, M)
     lin = qgm.QuantLinear.from_case(c, DEV)
     res = synth.draw_x(np.random.default_rng(K + fmt), M, N) if splits == 1 else None
     check_close(run_gemm(lin, c.x, residual=res), ref_y(c, c.x, residual=res),
                 f"issue tile {tile} K {K} splits {splits}")
+
+
+# 32 x 32 tiles take up to 8 word tiles per wave (two stages in flight), so
+# long K runs unsplit; issue-all and own-stage modes, ragged K
+@pytest.mark.parametrize("fmt,group,K,tpw,all_", [(0, 128, 8192, 8, True), (0, 128, 6144, 8, False),
+                                                  (0, 128, 4224, 8, False), (2, 32, 2048, 2, True),
+                                                  (0, 128, 7936, 8, True)])
+def test_gemm_long_k_small_tiles(monkeypatch, fmt, group, K, tpw, all_):
+    monkeypatch.setenv("QGEMM_GEMM_TILE", "3232")
+    monkeypatch.setenv("QGEMM_SPLITK", "1")
+    N, M = 200, 40
+    p = qgm.plan(M, N, K, group, fmt)
+    say(f"long K 32x32 fmt={fmt} g={group} K={K} plan={p}")
+    assert p["path"] == "gemm" and p["splits"] == 1 and (p["tile_m"], p["tile_n"]) == (32, 32)
+    assert gemm_issue_mode(fmt, K, 1, True) == (tpw, all_)
+    c = synth.random_codes_case(K + fmt + group, fmt, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    res = synth.draw_x(np.random.default_rng(K), M, N)
+    check_close(run_gemm(lin, c.x, residual=res), ref_y(c, c.x, residual=res), f"long K {K}")
 
 
 def test_gemm_small_tiles_without_split():
