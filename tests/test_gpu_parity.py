@@ -337,6 +337,35 @@ def test_gemm_long_k_small_tiles(monkeypatch, fmt, group, K, tpw, all_):
     check_close(run_gemm(lin, c.x, residual=res), ref_y(c, c.x, residual=res), f"long K {K}")
 
 
+# Seeded sweep over random shapes, formats and M: every plan branch the
+# shapes reach (GEMV rows, MFMA GEMV chunks, GEMM tiles, word tiles per wave,
+# issue modes, splits) against the oracle, half of the cases with a residual.
+def _random_shape_cases(n=40, seed=20261203):
+    rng = np.random.default_rng(seed)
+    groups = {0: (32, 64, 128), 1: (32, 64, 128), 2: (32,), 3: (32,), 4: (256,)}
+    out = []
+    while len(out) < n:
+        fmt = int(rng.integers(0, 5))
+        g = int(rng.choice(groups[fmt]))
+        M = int(rng.choice([1, 2, 3, 4, 5, 8, 9, 16, 17, 31, 33, 64, 65, 100, 128, 129, 200]))
+        N = int(rng.integers(1, 700))
+        K = g * int(rng.integers(1, max(2, 8192 // g)))
+        if M * N * K > 2e8:
+            continue
+        out.append((fmt, g, M, N, K, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("fmt,group,M,N,K,with_res", _random_shape_cases())
+def test_random_shapes(fmt, group, M, N, K, with_res):
+    p = qgm.plan(M, N, K, group, fmt)
+    say(f"random fmt={fmt} g={group} M={M} N={N} K={K} res={with_res} plan={p}")
+    c = synth.random_codes_case(M * 7919 + N * 31 + K + fmt, fmt, group, N, K, M)
+    lin = qgm.QuantLinear.from_case(c, DEV)
+    res = synth.draw_x(np.random.default_rng(M + N + K), M, N) if with_res else None
+    check_close(run_gemm(lin, c.x, residual=res), ref_y(c, c.x, residual=res), "random shape")
+
+
 def test_gemm_small_tiles_without_split():
     # 128 x 2048 x 2048 (the looped block's O projection): 32 x 32 tiles fill
     # the CUs with no K split where 64 x 64 tiles would split 4 ways
