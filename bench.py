@@ -281,7 +281,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the qGEMM would shard along N across GPUs with no exchange; see DESIGN.md)",
+              "(the qGEMM would shard along N across GPUs with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -6,8 +6,7 @@ fp16 scales (and zero points) and packs the codes into 32-bit words in the
 canonical order.  It holds no dequantization and no matrix product: those live
 in the CPU oracle (``oracle/``) and in the HIP library, which share no code.
 
-Where the sources are silent the readings below are used (each is repeated in
-DESIGN.md under "Readings"):
+Where the sources are silent the readings below are used:
 
 * W is [N, K]; groups run along K inside one output row n.
 * Asymmetric b-bit groups (INT4 with GPTQ-style zero points, and the INT2 body
