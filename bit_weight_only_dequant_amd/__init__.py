@@ -57,6 +57,7 @@ _SIGS = {
     "qg_unpack_codes": ([_P, _P, _I, _I, _I, _P], _I),
     "qg_dequant": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "qg_plan": ([_I, _I, _I, _I, _I, ctypes.POINTER(_I)], _I),
+    "qg_classify_pointer": ([_I, _I, _I, _I], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -268,7 +269,9 @@ def qgemm(x, packed, scales, zeros, N: int, K: int, group: int, fmt: int, out=No
     torch = _torch()
     _dev(x, "x"); _dev(packed, "packed"); _dev(scales, "scales"); _dev(zeros, "zeros")
     _dev(residual, "residual"); _dev(out, "out"); _dev(workspace, "workspace")
-    if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != K or (x.shape[0] > 1 and x.stride(1) != 1):
+    # unit column stride whatever M is: a one-row view with another stride
+    # (x[:, ::2], buf.t()[0:1]) would otherwise be read as K contiguous halves
+    if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != K or (K > 1 and x.stride(1) != 1):
         raise ValueError("x must be an fp16 [M, K] tensor with unit column stride")
     M = x.shape[0]
     _check_weights(packed, scales, zeros, N, K, group, fmt, x.device)

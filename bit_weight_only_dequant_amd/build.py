@@ -31,13 +31,16 @@ def build(verbose: bool = True) -> str:
     out_dir = os.path.join(PKG, "_build")
     os.makedirs(out_dir, exist_ok=True)
     host_o = os.path.join(out_dir, "host.o")
-    dev_o = os.path.join(out_dir, "kernels.o")
     # host-only translation unit (no device code, no device flags)
     _run([hipcc, *COMMON, "-c", os.path.join(CSRC, "host.cpp"), "-o", host_o], verbose)
-    _run([hipcc, *COMMON, f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-c",
-          os.path.join(CSRC, "kernels.hip"), "-o", dev_o], verbose)
+    objs = [host_o]
+    for src in sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")):
+        obj = os.path.join(out_dir, src[:-4] + ".o")
+        _run([hipcc, *COMMON, f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, host_o, dev_o], verbose)
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

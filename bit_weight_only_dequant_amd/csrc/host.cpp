@@ -35,6 +35,19 @@ int check_align(const void* p) {
 
 int check_ld(int ld, int minimum) { return ld >= minimum ? QG_OK : QG_E_ARG; }
 
+// hipMemoryType values (hip_runtime_api.h): 1 host, 2 device, 3 managed,
+// 10 array, 11 unified.  Device memory must belong to the current device;
+// managed and unified memory is reachable from any device.
+int classify_pointer(int hip_rc, int memory_type, int ptr_device, int current_device) {
+  if (hip_rc != 0) return QG_E_NOT_DEVICE;          // unregistered host memory, or not a pointer HIP knows
+  switch (memory_type) {
+    case 2: return ptr_device == current_device ? QG_OK : QG_E_NOT_DEVICE;
+    case 3:
+    case 11: return QG_OK;
+    default: return QG_E_NOT_DEVICE;                // host (pinned or registered), arrays
+  }
+}
+
 static int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
@@ -53,7 +66,7 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   p.wordtiles = (int)n_wordtiles(K, fmt);
   if (K == 0) return p;             // zero fill
   const int kt_width = ktile_width(fmt);
-  const bool gemv = force_is("gemm") ? false : (force_is("gemv") ? M <= GEMV_MAX_M : M <= GEMV_MAX_M);
+  const bool gemv = !force_is("gemm") && M <= GEMV_MAX_M;
   const int split_env = env_int("QGEMM_SPLITK", 0);
   if (gemv) {
     p.path = 1;
@@ -210,6 +223,7 @@ const char* qg_status_str(int status) {
     case QG_E_DEVICE: return "QG_E_DEVICE: no usable HIP device or a HIP call failed";
     case QG_E_NOMEM: return "QG_E_NOMEM: workspace allocation failed";
     case QG_E_WORKSPACE: return "QG_E_WORKSPACE: caller workspace too small";
+    case QG_E_NOT_DEVICE: return "QG_E_NOT_DEVICE: a pointer is not device memory of the current device";
     default: return "unknown qgemm status";
   }
 }
@@ -251,6 +265,10 @@ int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt)
     for (int64_t kw = 0; kw < kw_n; ++kw)
       canon[n * kw_n + kw] = unperm_word(packed[packed_index(n, kw, wt)], bits);
   return QG_OK;
+}
+
+int qg_classify_pointer(int hip_rc, int memory_type, int ptr_device, int current_device) {
+  return classify_pointer(hip_rc, memory_type, ptr_device, current_device);
 }
 
 size_t qgemm_workspace_bytes(int M, int N, int K, int group, int fmt) {

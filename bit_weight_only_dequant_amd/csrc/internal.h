@@ -65,10 +65,32 @@ int check_format_group(int fmt, int group);
 int check_shape(int M, int N, int K, int group, int fmt);
 int check_align(const void* p);
 int check_ld(int ld, int minimum);
+// QGEMM_CHECK=1 pointer test from the result of hipPointerGetAttributes:
+// QG_OK for device memory of the current device (or managed / unified
+// memory), QG_E_NOT_DEVICE otherwise.
+int classify_pointer(int hip_rc, int memory_type, int ptr_device, int current_device);
 
 // Launch plan for a validated problem.  Environment overrides (for tuning and
-// tests): QGEMM_FORCE=gemv|gemm, QGEMM_SPLITK=<n>, QGEMM_GEMV_ROWS=8|16 (M <= 4),
+// tests): QGEMM_FORCE=gemm (the MFMA GEMM for any M), QGEMM_SPLITK=<n>, QGEMM_GEMV_ROWS=8|16 (M <= 4),
 // QGEMM_GEMM_TILE=3232|6432|6464 (GEMM tile rows x columns).
 Plan make_plan(int M, int N, int K, int group, int fmt);
+
+// One qgemm call's arguments (device pointers, fp16 as uint16_t bits).
+struct Call {
+  const uint16_t* x; int ldx; const uint32_t* packed; const uint16_t* scales; const uint16_t* zeros;
+  const uint16_t* resid; int ldr; int M, N, K, group, fmt; uint16_t* y; int ldy;
+};
+
+// Device-side helpers of kernels.hip, shared with the other entry points.
+// validate_call: host-only checks of a call and its plan (no HIP call).
+// launch_call: launches a validated call on `stream`; ws holds the split-K
+// partials (plan.ws_bytes() bytes) when the plan splits K.
+// call_pointers_ok: the QGEMM_CHECK=1 device-pointer test of a call.
+int validate_call(const Call& c, Plan* plan);
+int launch_call(const Call& c, const Plan& p, float* ws, void* stream);
+int call_pointers_ok(const Call& c);
+int current_device(int* dev);          // QG_OK when a HIP device is current
+int hip_status(int hip_error);         // QG_OK, or QG_E_DEVICE (and records the error)
+void clear_pending_error();
 
 }  // namespace qg

@@ -40,8 +40,11 @@
 //                        per workgroup would write back the whole L2 each time.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
+#include <climits>
 #include <mutex>
 #include <vector>
 
@@ -1428,13 +1431,14 @@ static std::vector<DeviceWs> g_ws;
 // Last HIP error seen by this thread inside the library (for qg_last_error).
 static thread_local hipError_t g_last_hip = hipSuccess;
 
-static int hip_status(hipError_t e) {
+int hip_status(int err) {
+  const hipError_t e = static_cast<hipError_t>(err);
   if (e == hipSuccess) return QG_OK;
   g_last_hip = e;
   return QG_E_DEVICE;
 }
 
-static int current_device(int* dev) {
+int current_device(int* dev) {
   int st = hip_status(hipGetDevice(dev));
   if (st != QG_OK) return st;
   int count = 0;
@@ -1445,7 +1449,7 @@ static int current_device(int* dev) {
 
 // Clears any error an earlier, unrelated HIP call left pending, so that the
 // status after a launch reports that launch only.
-static void clear_pending_error() { (void)hipGetLastError(); }
+void clear_pending_error() { (void)hipGetLastError(); }
 
 // Library-owned zero-initialised workspace of at least `bytes` on `dev`.
 // Growing never frees the buffer it replaces: a HIP graph captured earlier
@@ -1612,67 +1616,88 @@ static void launch_gemm_tiles(const GemmArgs& a, const Plan& p, int fmt, hipStre
   }
 }
 
-static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const uint16_t* scales,
-                     const uint16_t* zeros, const uint16_t* resid, int ldr, int M, int N, int K,
-                     int group, int fmt, uint16_t* y, int ldy, void* workspace, size_t ws_bytes,
-                     void* stream) {
-  // ---- validation (host only) ----
-  int st = check_shape(M, N, K, group, fmt);
+// QGEMM_CHECK=1: every device pointer of a call must be device (or managed)
+// memory of the current device; host memory is rejected before any launch.
+// Costs one hipPointerGetAttributes per pointer, so it is off by default.
+static bool pointer_check_on() {
+  const char* v = getenv("QGEMM_CHECK");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
+static int check_device_pointers(const void* const* ptrs, int n) {
+  if (!pointer_check_on()) return QG_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    clear_pending_error();
+    return QG_E_DEVICE;
+  }
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) continue;
+    hipPointerAttribute_t attr;
+    memset(&attr, 0, sizeof(attr));
+    const hipError_t e = hipPointerGetAttributes(&attr, ptrs[i]);
+    if (e != hipSuccess) clear_pending_error();   // unregistered host memory reports an error
+    const int st = classify_pointer((int)e, (int)attr.type, attr.device, dev);
+    if (st != QG_OK) return st;
+  }
+  return QG_OK;
+}
+
+// Host-only validation of a call and its launch plan; no HIP call.
+int validate_call(const Call& c, Plan* plan) {
+  int st = check_shape(c.M, c.N, c.K, c.group, c.fmt);
   if (st != QG_OK) return st;
-  if (M > 0 && N > 0) {
-    if (!y) return QG_E_ARG;
-    if (check_ld(ldy, N) != QG_OK) return QG_E_ARG;
-    if (resid && check_ld(ldr, N) != QG_OK) return QG_E_ARG;
-    if (resid && resid == y && ldr != ldy) return QG_E_ARG;
-    if (check_align(y) != QG_OK || (resid && check_align(resid) != QG_OK)) return QG_E_ALIGN;
-    if (K > 0) {
-      if (!x || !packed || !scales) return QG_E_ARG;
-      if (symmetric_format(fmt) != (zeros == nullptr)) return QG_E_ARG;
-      if (check_ld(ldx, K) != QG_OK) return QG_E_ARG;
-      if (ldx % 8 != 0) return QG_E_ALIGN;
-      if (check_align(x) != QG_OK || check_align(packed) != QG_OK || check_align(scales) != QG_OK ||
-          (zeros && check_align(zeros) != QG_OK))
+  if (c.M > 0 && c.N > 0) {
+    if (!c.y) return QG_E_ARG;
+    if (check_ld(c.ldy, c.N) != QG_OK) return QG_E_ARG;
+    if (c.resid && check_ld(c.ldr, c.N) != QG_OK) return QG_E_ARG;
+    if (c.resid && c.resid == c.y && c.ldr != c.ldy) return QG_E_ARG;
+    if (check_align(c.y) != QG_OK || (c.resid && check_align(c.resid) != QG_OK)) return QG_E_ALIGN;
+    if (c.K > 0) {
+      if (!c.x || !c.packed || !c.scales) return QG_E_ARG;
+      if (symmetric_format(c.fmt) != (c.zeros == nullptr)) return QG_E_ARG;
+      if (check_ld(c.ldx, c.K) != QG_OK) return QG_E_ARG;
+      if (c.ldx % 8 != 0) return QG_E_ALIGN;
+      if (check_align(c.x) != QG_OK || check_align(c.packed) != QG_OK || check_align(c.scales) != QG_OK ||
+          (c.zeros && check_align(c.zeros) != QG_OK))
         return QG_E_ALIGN;
     }
   }
-  const Plan p = make_plan(M, N, K, group, fmt);
-  if (M > 0 && N > 0 && K > 0 && p.path == 0) return QG_E_UNSUPPORTED;
-  if (workspace && ws_bytes < p.ws_bytes()) return QG_E_WORKSPACE;
-  if (workspace && check_align(workspace) != QG_OK) return QG_E_ALIGN;
-  if (M == 0 || N == 0) return QG_OK;  // no-op, no HIP call
-  // ---- device work ----
-  int dev = 0;
-  st = current_device(&dev);
-  if (st != QG_OK) return st;
-  clear_pending_error();
+  const Plan p = make_plan(c.M, c.N, c.K, c.group, c.fmt);
+  if (c.M > 0 && c.N > 0 && c.K > 0) {
+    if (p.path == 0) return QG_E_UNSUPPORTED;
+    // the kernels form byte offsets of x rows and of one row block's codes in 32 bits
+    if ((int64_t)c.M * c.ldx * 2 >= (int64_t)1 << 32 || p.splits > 65535) return QG_E_UNSUPPORTED;
+    if (p.path == 1 && (int64_t)p.wordtiles * 1024 >= (int64_t)1 << 32) return QG_E_UNSUPPORTED;
+    if (p.path == 2 && p.tiles_m > 65535) return QG_E_UNSUPPORTED;
+  }
+  *plan = p;
+  return QG_OK;
+}
+
+// Launches a validated call on the current device.  ws: the split-K partials
+// (at least p.ws_bytes() bytes) when the plan splits K.
+int launch_call(const Call& c, const Plan& p, float* wsf, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  clear_pending_error();
+  const int M = c.M, N = c.N, K = c.K, fmt = c.fmt;
   if (K == 0) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, s,
-                       reinterpret_cast<f16*>(y), M, N, ldy, reinterpret_cast<const f16*>(resid), ldr);
+                       reinterpret_cast<f16*>(c.y), M, N, c.ldy, reinterpret_cast<const f16*>(c.resid), c.ldr);
     return launch_status();
   }
-  void* ws = workspace;
-  if (p.ws_bytes() > 0 && !ws) {
-    st = library_ws(dev, p.ws_bytes(), &ws);
-    if (st != QG_OK) return st;
-  }
-  float* wsf = reinterpret_cast<float*>(ws);
   if (p.path == 1) {
     GemvArgs a;
-    a.x = reinterpret_cast<const f16*>(x);
-    a.packed = packed;
-    a.scales = reinterpret_cast<const f16*>(scales);
-    a.zeros = reinterpret_cast<const f16*>(zeros);
-    a.resid = reinterpret_cast<const f16*>(resid);
-    a.y = reinterpret_cast<f16*>(y);
+    a.x = reinterpret_cast<const f16*>(c.x);
+    a.packed = c.packed;
+    a.scales = reinterpret_cast<const f16*>(c.scales);
+    a.zeros = reinterpret_cast<const f16*>(c.zeros);
+    a.resid = reinterpret_cast<const f16*>(c.resid);
+    a.y = reinterpret_cast<f16*>(c.y);
     a.ws = wsf;
-    a.ldx = ldx; a.ldr = ldr; a.ldy = ldy;
-    a.M = M; a.N = N; a.K = K; a.group = meta_group(fmt, group);   // q4k: the 32-weight sub-block
+    a.ldx = c.ldx; a.ldr = c.ldr; a.ldy = c.ldy;
+    a.M = M; a.N = N; a.K = K; a.group = meta_group(fmt, c.group);   // q4k: the 32-weight sub-block
     a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.splits = p.splits; a.tps = p.tps;
-    // the kernel forms byte offsets of x and of one row block's codes in 32 bits
-    if ((int64_t)M * ldx * 2 >= (int64_t)1 << 32 || (int64_t)p.wordtiles * 1024 >= (int64_t)1 << 32 ||
-        p.splits > 65535)
-      return QG_E_UNSUPPORTED;
     bool launched;
     switch (fmt) {
       case QG_INT4_ASYM: launched = launch_gemv_f<INT4_ASYM>(a, p.mmax, p.tps, p.rows, s); break;
@@ -1683,32 +1708,30 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
     }
     if (!launched) return QG_E_UNSUPPORTED;
     if (p.splits > 1) {
-      st = launch_status();
+      const int st = launch_status();
       if (st != QG_OK) return st;
       hipLaunchKernelGGL(gemv_reduce_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, s, wsf,
-                         a.resid, a.y, M, N, ldr, ldy, p.splits, p.mmax);
+                         a.resid, a.y, M, N, c.ldr, c.ldy, p.splits, p.mmax);
     }
     return launch_status();
   }
   GemmArgs a;
-  a.x = reinterpret_cast<const f16*>(x);
-  a.packed = packed;
-  a.scales = reinterpret_cast<const f16*>(scales);
-  a.zeros = reinterpret_cast<const f16*>(zeros);
-  a.resid = reinterpret_cast<const f16*>(resid);
-  a.y = reinterpret_cast<f16*>(y);
+  a.x = reinterpret_cast<const f16*>(c.x);
+  a.packed = c.packed;
+  a.scales = reinterpret_cast<const f16*>(c.scales);
+  a.zeros = reinterpret_cast<const f16*>(c.zeros);
+  a.resid = reinterpret_cast<const f16*>(c.resid);
+  a.y = reinterpret_cast<f16*>(c.y);
   a.ws = wsf;
-  a.ldx = ldx; a.ldr = ldr; a.ldy = ldy;
-  a.M = M; a.N = N; a.K = K; a.group = meta_group(fmt, group);   // q4k: the 32-weight sub-block
+  a.ldx = c.ldx; a.ldr = c.ldr; a.ldy = c.ldy;
+  a.M = M; a.N = N; a.K = K; a.group = meta_group(fmt, c.group);   // q4k: the 32-weight sub-block
   a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.tiles_n = p.tiles_n;
   a.splits = p.splits; a.tps = p.tps;
-  // the kernel forms byte offsets of x rows in 32 bits
-  if ((int64_t)M * ldx * 2 >= (int64_t)1 << 32 || p.tiles_m > 65535 || p.splits > 65535) return QG_E_UNSUPPORTED;
   if (p.tm == 32) launch_gemm_tiles<1, 1>(a, p, fmt, s);
   else if (p.tn == 32) launch_gemm_tiles<2, 1>(a, p, fmt, s);
   else launch_gemm_tiles<2, 2>(a, p, fmt, s);
   if (p.splits > 1) {
-    st = launch_status();
+    const int st = launch_status();
     if (st != QG_OK) return st;
     if (p.tm == 32)
       hipLaunchKernelGGL((gemm_reduce_kernel<1, 1>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1), dim3(256), 0, s, a);
@@ -1718,6 +1741,36 @@ static int run_qgemm(const uint16_t* x, int ldx, const uint32_t* packed, const u
       hipLaunchKernelGGL((gemm_reduce_kernel<2, 2>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 4), dim3(256), 0, s, a);
   }
   return launch_status();
+}
+
+int call_pointers_ok(const Call& c) {
+  const void* ptrs[6] = {c.x, c.packed, c.scales, c.zeros, c.resid, c.y};
+  return check_device_pointers(ptrs, 6);
+}
+
+static int run_qgemm(const Call& c, void* workspace, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = validate_call(c, &p);
+  if (st != QG_OK) return st;
+  if (workspace && ws_bytes < p.ws_bytes()) return QG_E_WORKSPACE;
+  if (workspace && check_align(workspace) != QG_OK) return QG_E_ALIGN;
+  if (c.M == 0 || c.N == 0) return QG_OK;  // no-op, no HIP call
+  int dev = 0;
+  st = current_device(&dev);
+  if (st != QG_OK) return st;
+  st = call_pointers_ok(c);
+  if (st != QG_OK) return st;
+  if (workspace) {
+    const void* w[1] = {workspace};
+    st = check_device_pointers(w, 1);
+    if (st != QG_OK) return st;
+  }
+  void* ws = workspace;
+  if (p.ws_bytes() > 0 && !ws) {
+    st = library_ws(dev, p.ws_bytes(), &ws);
+    if (st != QG_OK) return st;
+  }
+  return launch_call(c, p, reinterpret_cast<float*>(ws), stream);
 }
 
 static int check_pack(const void* a, const void* b, int N, int K, int fmt) {
@@ -1744,6 +1797,11 @@ int qpack(const uint32_t* canon, uint32_t* packed, int N, int K, int fmt, void* 
   int dev = 0;
   st = current_device(&dev);
   if (st != QG_OK) return st;
+  {
+    const void* ptrs[2] = {canon, packed};
+    st = check_device_pointers(ptrs, (int64_t)N * K > 0 ? 2 : 0);
+    if (st != QG_OK) return st;
+  }
   clear_pending_error();
   const int64_t total = (int64_t)(qg_packed_bytes(N, K, fmt) / sizeof(uint32_t));
   if (total == 0) return QG_OK;
@@ -1759,6 +1817,11 @@ int qunpack(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt, void
   int dev = 0;
   st = current_device(&dev);
   if (st != QG_OK) return st;
+  {
+    const void* ptrs[2] = {packed, canon};
+    st = check_device_pointers(ptrs, (int64_t)N * K > 0 ? 2 : 0);
+    if (st != QG_OK) return st;
+  }
   clear_pending_error();
   const int64_t total = (int64_t)N * (K / cpw_of(fmt));
   if (total == 0) return QG_OK;
@@ -1774,6 +1837,11 @@ int qg_unpack_codes(const uint32_t* packed, uint8_t* codes, int N, int K, int fm
   int dev = 0;
   st = current_device(&dev);
   if (st != QG_OK) return st;
+  {
+    const void* ptrs[2] = {packed, codes};
+    st = check_device_pointers(ptrs, (int64_t)N * K > 0 ? 2 : 0);
+    if (st != QG_OK) return st;
+  }
   clear_pending_error();
   const int64_t total = (int64_t)N * K;
   if (total == 0) return QG_OK;
@@ -1791,13 +1859,20 @@ int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* z
   if (total > 0) {
     if (!packed || !scales || !w) return QG_E_ARG;
     if (symmetric_format(fmt) != (zeros == nullptr)) return QG_E_ARG;
-    if (check_align(packed) != QG_OK || check_align(w) != QG_OK) return QG_E_ALIGN;
+    if (check_align(packed) != QG_OK || check_align(w) != QG_OK || check_align(scales) != QG_OK ||
+        (zeros && check_align(zeros) != QG_OK))
+      return QG_E_ALIGN;
   }
+  if (total == 0) return QG_OK;
   int dev = 0;
   st = current_device(&dev);
   if (st != QG_OK) return st;
+  {
+    const void* ptrs[4] = {packed, scales, zeros, w};
+    st = check_device_pointers(ptrs, 4);
+    if (st != QG_OK) return st;
+  }
   clear_pending_error();
-  if (total == 0) return QG_OK;
   const int wt = (int)n_wordtiles(K, fmt);
   const int64_t units = n_rowblocks(N) * wt;
   const int mg = meta_group(fmt, group);
@@ -1818,15 +1893,15 @@ int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* z
 
 int qgemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros,
           int M, int N, int K, int group, int fmt, uint16_t* y, void* stream) {
-  return run_qgemm(x, K, packed, scales, zeros, nullptr, N, M, N, K, group, fmt, y, N, nullptr, 0,
-                   stream);
+  const Call c{x, K, packed, scales, zeros, nullptr, N, M, N, K, group, fmt, y, N};
+  return run_qgemm(c, nullptr, 0, stream);
 }
 
 int qgemm_ex(const uint16_t* x, int ldx, const uint32_t* packed, const uint16_t* scales,
              const uint16_t* zeros, const uint16_t* residual, int ldr, int M, int N, int K, int group,
              int fmt, uint16_t* y, int ldy, void* workspace, size_t ws_bytes, void* stream) {
-  return run_qgemm(x, ldx, packed, scales, zeros, residual, ldr, M, N, K, group, fmt, y, ldy,
-                   workspace, ws_bytes, stream);
+  const Call c{x, ldx, packed, scales, zeros, residual, ldr, M, N, K, group, fmt, y, ldy};
+  return run_qgemm(c, workspace, ws_bytes, stream);
 }
 
 int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
@@ -1836,25 +1911,53 @@ int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* con
   if (M > 0 && (!x || !scratch)) return QG_E_ARG;
   if (check_align(scratch) != QG_OK || check_align(x) != QG_OK) return QG_E_ALIGN;
   const int64_t D3 = 3 * (int64_t)D;
+  if (D3 > INT_MAX) return QG_E_ARG;
   uint16_t* qkv = scratch;
   uint16_t* h = qkv + (int64_t)M * D3;
   uint16_t* u = h + (int64_t)M * D;
+  // the four calls of a loop, validated (and their workspace obtained) before
+  // anything is recorded or launched
+  const Call calls[4] = {
+      {x, D, packed4[0], scales4[0], zeros4[0], nullptr, 0, M, (int)D3, D, group, fmt, qkv, (int)D3},
+      {qkv + 2 * (int64_t)D, (int)D3, packed4[1], scales4[1], zeros4[1], x, D, M, D, D, group, fmt, h, D},
+      {h, D, packed4[2], scales4[2], zeros4[2], nullptr, 0, M, F, D, group, fmt, u, F},
+      {u, F, packed4[3], scales4[3], zeros4[3], h, D, M, D, F, group, fmt, x, D}};
+  Plan plans[4];
+  size_t ws_need = 0;
+  for (int i = 0; i < 4; ++i) {
+    const int st = validate_call(calls[i], &plans[i]);
+    if (st != QG_OK) return st;
+    ws_need = std::max(ws_need, plans[i].ws_bytes());
+  }
+  if (M == 0 || L == 0) {
+    if (events) {   // still time-stamp the (empty) loops
+      hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+      for (int l = 0; l <= L; ++l)
+        if (events[l] && hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[l]), s)) != QG_OK)
+          return QG_E_DEVICE;
+    }
+    return QG_OK;
+  }
+  int dev = 0;
+  int st = current_device(&dev);
+  if (st != QG_OK) return st;
+  for (int i = 0; i < 4; ++i) {
+    st = call_pointers_ok(calls[i]);
+    if (st != QG_OK) return st;
+  }
+  void* ws = nullptr;
+  if (ws_need > 0) {
+    st = library_ws(dev, ws_need, &ws);
+    if (st != QG_OK) return st;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (events && events[0] && hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[0]), s)) != QG_OK)
     return QG_E_DEVICE;
   for (int l = 0; l < L; ++l) {
-    int st = run_qgemm(x, D, packed4[0], scales4[0], zeros4[0], nullptr, 0, M, (int)D3, D, group, fmt,
-                       qkv, (int)D3, nullptr, 0, stream);
-    if (st == QG_OK)
-      st = run_qgemm(qkv + 2 * (int64_t)D, (int)D3, packed4[1], scales4[1], zeros4[1], x, D, M, D, D,
-                     group, fmt, h, D, nullptr, 0, stream);
-    if (st == QG_OK)
-      st = run_qgemm(h, D, packed4[2], scales4[2], zeros4[2], nullptr, 0, M, F, D, group, fmt, u, F,
-                     nullptr, 0, stream);
-    if (st == QG_OK)
-      st = run_qgemm(u, F, packed4[3], scales4[3], zeros4[3], h, D, M, D, F, group, fmt, x, D, nullptr,
-                     0, stream);
-    if (st != QG_OK) return st;
+    for (int i = 0; i < 4; ++i) {
+      st = launch_call(calls[i], plans[i], reinterpret_cast<float*>(ws), s);
+      if (st != QG_OK) return st;
+    }
     if (events && events[l + 1] &&
         hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[l + 1]), s)) != QG_OK)
       return QG_E_DEVICE;

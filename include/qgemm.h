@@ -37,20 +37,32 @@
  *     QG_Q4K (group = 256) instead takes scales = fp16 [N, K/256, 2], the
  *     pair (d, dmin) of each super-block, and zeros = uint16 [N, K/32], sc in
  *     the low byte and m in the high byte of each sub-block (both < 64).
+ *   - Ownership follows the Mobilint qbruntime.model.Model reference
+ *     ("infer_pinned_memory", "infer_npu_data"): the caller allocates the
+ *     outputs and the library fills them in place; it allocates nothing the
+ *     caller must free.
  *   - "stream" is a hipStream_t (NULL = the default stream).  Every device
  *     call is stream-ordered and asynchronous: QG_OK means "validated and
  *     launched"; a kernel fault is reported by the caller's next sync.
  *   - Arguments are validated on the host before any HIP call.  On error the
- *     function returns a status and launches nothing; nothing aborts or prints.
+ *     function returns a named status (the convention of the named errors of
+ *     the same Mobilint reference, e.g. "Model_InvalidVariantIdx") and
+ *     launches nothing; nothing aborts or prints.
+ *   - QGEMM_CHECK=1 in the environment also asks HIP about every pointer
+ *     before any launch and rejects host memory with QG_E_NOT_DEVICE (the
+ *     residency rule of "infer_npu_data" in the same reference: a mixed set of
+ *     host and device buffers is an error).  Off by default: it costs one
+ *     hipPointerGetAttributes per pointer.
  *   - Shapes: group in {32, 64, 128} for INT4/INT2, group == 32 for q4_0 and
  *     q8_0, group == 256 for q4k;
  *     K % group == 0; M, N, K >= 0.  Any N and any M are accepted.
  *   - Device pointers to x, packed, scales, zeros, y and residual must be
  *     16-byte aligned; leading dimensions must be multiples of 8 elements.
- *   - Thread safety: calls are re-entrant.  Calls that use the library-owned
- *     split-K workspace (qgemm, or qgemm_ex with workspace == NULL) must not
- *     overlap on different streams of one device; give each concurrent stream
- *     its own workspace through qgemm_ex.
+ *   - Thread safety: calls are re-entrant, unlike the serialised model of the
+ *     TinyLoop "Async API" page ("Concurrency model").  Calls that use the
+ *     library-owned split-K workspace (qgemm, or qgemm_ex with workspace ==
+ *     NULL) must not overlap on different streams of one device; give each
+ *     concurrent stream its own workspace through qgemm_ex.
  */
 #ifndef QGEMM_H
 #define QGEMM_H
@@ -77,20 +89,32 @@ typedef enum {
   QG_E_ALIGN = 3,        /* pointer or leading dimension misaligned              */
   QG_E_DEVICE = 4,       /* no usable HIP device, or a HIP call failed            */
   QG_E_NOMEM = 5,        /* the library could not allocate its workspace          */
-  QG_E_WORKSPACE = 6     /* caller workspace too small                            */
+  QG_E_WORKSPACE = 6,    /* caller workspace too small                            */
+  QG_E_NOT_DEVICE = 7    /* QGEMM_CHECK=1: a pointer is not device memory of the current device */
 } qg_status_t;
 
 /* Library version as 10000*major + 100*minor + patch. */
 int qg_version(void);
 
-/* Human-readable name of a status code (static string, never NULL). */
+/* Human-readable name of a status code (static string, never NULL); the
+ * named-error convention of the Mobilint qbruntime.model.Model reference. */
 const char* qg_status_str(int status);
 
 /* Text of the last HIP error the library met on this thread (after a
  * QG_E_DEVICE status); "no error" when there was none.  Static string. */
 const char* qg_last_error(void);
 
-/* Bytes of the packed (qpack) code buffer for an [N, K] weight in format fmt:
+/* The QGEMM_CHECK=1 pointer rule as a pure function (no HIP call), for tests
+ * and callers that query pointer attributes themselves: given the return code
+ * of hipPointerGetAttributes, the reported hipMemoryType, the pointer's
+ * device and the current device, QG_OK for device memory of the current
+ * device or managed / unified memory, QG_E_NOT_DEVICE otherwise (an error
+ * code, host memory, arrays).  The residency rule of the Mobilint
+ * qbruntime.model.Model reference, "infer_npu_data". */
+int qg_classify_pointer(int hip_rc, int memory_type, int ptr_device, int current_device);
+
+/* Bytes of the packed (qpack) code buffer for an [N, K] weight in format fmt
+ * (the repacked form of the TinyLoop README, section "Status"):
  * N and K/cpw are rounded up to multiples of 16 (the tile of 16 rows by 16
  * words); padding holds zero codes.  Returns 0 for an invalid request. */
 size_t qg_packed_bytes(int64_t N, int64_t K, int fmt);
@@ -111,17 +135,22 @@ size_t qg_packed_bytes(int64_t N, int64_t K, int fmt);
  */
 int qpack(const uint32_t* canon, uint32_t* packed, int N, int K, int fmt, void* stream);
 
-/* Inverse of qpack: packed -> canonical words [N, K/cpw] (device).  Same errors. */
+/* Inverse of qpack (TinyLoop README, "Status": the repack is one-time and
+ * lossless): packed -> canonical words [N, K/cpw] (device).  Same errors. */
 int qunpack(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt, void* stream);
 
 /* Host versions of qpack / qunpack on host memory (no HIP call): the same
- * permutation, for offline packing.  Same errors except QG_E_DEVICE. */
+ * permutation, for offline packing (the one-time repack of the TinyLoop
+ * README, "Status").  Same errors except QG_E_DEVICE and QG_E_NOT_DEVICE. */
 int qpack_host(const uint32_t* canon, uint32_t* packed, int N, int K, int fmt);
 int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt);
 
 /*
  * qgemm: y[M,N] = x[M,K] . dequant(W)^T with fp32 accumulation and one
- * round-to-nearest-even to fp16 at the end.
+ * round-to-nearest-even to fp16 at the end -- the dequantizing matmul of the
+ * skyzh/tiny-llm feature list ("Dequantizing Runtimes", "Quantized Matrix
+ * Multiplication": low-bit weights turned back to full precision inside the
+ * compute pass).
  *   x      [device, in]  fp16 [M, K], row-major, leading dimension K.
  *   packed [device, in]  qpack output for W [N, K].
  *   scales [device, in]  fp16 [N, K/group].
@@ -139,7 +168,8 @@ int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt)
  * allocation cannot happen during capture).  Growing never frees a buffer:
  * an outgrown one is kept until the process ends, so a graph captured before
  * a later, larger call still replays into valid memory.
- * Errors: QG_E_ARG, QG_E_ALIGN, QG_E_DEVICE, QG_E_NOMEM.
+ * Errors: QG_E_ARG, QG_E_ALIGN, QG_E_UNSUPPORTED, QG_E_DEVICE, QG_E_NOMEM,
+ * QG_E_NOT_DEVICE.
  */
 int qgemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
           const uint16_t* zeros, int M, int N, int K, int group, int fmt,
@@ -147,7 +177,10 @@ int qgemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
 
 /*
  * qgemm_ex: qgemm with leading dimensions, an optional fused residual and an
- * optional caller workspace:  y = x . dequant(W)^T + residual.
+ * optional caller workspace:  y = x . dequant(W)^T + residual.  The residual
+ * is the add around each pair of linears of the looped block (TinyLoop
+ * README, "Why TinyLoop Exists"); the leading dimension lets the O
+ * projection read the V third of the QKV output in place.
  *   ldx, ldy, ldr  leading dimensions in elements (>= K, >= N, >= N; multiples of 8).
  *   residual       [device, in] fp16 [M, N] with leading dimension ldr, or NULL.
  *                  It may alias y only when ldr == ldy (in-place update).
@@ -161,7 +194,9 @@ int qgemm_ex(const uint16_t* x, int ldx, const uint32_t* packed, const uint16_t*
              int M, int N, int K, int group, int fmt, uint16_t* y, int ldy,
              void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes qgemm_ex needs for this problem (0 when none). */
+/* Workspace bytes qgemm_ex needs for this problem (0 when none): the fp32
+ * split-K partials of the caller-owned workspace convention above (Mobilint
+ * qbruntime.model.Model, "infer_pinned_memory": pre-allocated buffers). */
 size_t qgemm_workspace_bytes(int M, int N, int K, int group, int fmt);
 
 /*
@@ -180,25 +215,34 @@ size_t qgemm_workspace_bytes(int M, int N, int K, int group, int fmt);
  *   scratch  [device] fp16 buffer of at least M*(3D + D + F) elements.
  *   events   NULL, or a host array of L+1 hipEvent_t recorded on the stream
  *            before loop 1 and after each loop (per-loop timing).
- * Errors: as qgemm_ex (the first failing call's status; nothing later runs).
+ * All four calls are validated before any event is recorded or kernel
+ * launched, and the split-K workspace is obtained up front, so on error
+ * nothing is launched and x is untouched.
+ * Errors: as qgemm_ex.
  */
 int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
                 const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt,
                 int L, uint16_t* scratch, void* const* events, void* stream);
 
 /* Debug: packed -> integer codes uint8 [N, K] (device), for the bit-exact
- * check of the kernels' unpack.  Errors as qunpack. */
+ * check of the kernels' unpack (the nibble / crumb unpack of the TinyLoop
+ * README, "Status").  Errors as qunpack. */
 int qg_unpack_codes(const uint32_t* packed, uint8_t* codes, int N, int K, int fmt,
                     void* stream);
 
-/* Debug: packed + scales + zeros -> fp16 w [N, K] (device) through the same
- * device dequant the GEMM uses: fp16_rne(s * (q - z)); for QG_Q4K
+/* Debug and the dequantize-at-load comparison (TinyLoop README, "Current
+ * Runtime Snapshot": an FP16 body whose weights are dequantized once):
+ * packed + scales + zeros -> fp16 w [N, K] (device) through the same device
+ * dequant the GEMM uses: fp16_rne(s * (q - z)); for QG_Q4K
  * fp16_rne(fp16_rne(d*sc) * q - fp16_rne(dmin*m)) (one fused multiply-add).
+ * scales and zeros must be 16-byte aligned like the other buffers.
  * Errors as qgemm. */
 int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros,
                uint16_t* w, int N, int K, int group, int fmt, void* stream);
 
-/* Launch plan the library would use (for tracing and tests; no HIP call):
+/* Launch plan the library would use (for tracing and tests; no HIP call; the
+ * phase timings of the TinyLoop README, "Quick CLI Tour", need the kernel
+ * behind each call):
  * out[0] = path (1 GEMV, 2 GEMM), out[1] = K splits, out[2] = workgroups,
  * out[3] = tile rows (M), out[4] = tile columns (N) -- for the GEMV, the rows of
  * x per launch (1, 2, 4, 8 or 16) and the rows of W per workgroup (16, or 8 when

@@ -16,7 +16,7 @@ qgm = pytest.importorskip("bit_weight_only_dequant_amd")
 lib = qgm._lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, E_ARG, E_UNSUP, E_ALIGN, E_DEVICE, E_NOMEM, E_WS = range(7)
+OK, E_ARG, E_UNSUP, E_ALIGN, E_DEVICE, E_NOMEM, E_WS, E_NOT_DEVICE = range(8)
 A = 0x10000  # a 16-byte aligned fake address: validation never dereferences it
 
 
@@ -100,7 +100,7 @@ def test_no_device_status():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert qgm.status_str(s).startswith("QG_")
     assert "unknown" in qgm.status_str(99)
 
@@ -248,3 +248,59 @@ def test_plans_for_the_workloads():
     p = qgm.plan(4, 2048, 8192, 128, 0)
     assert (p["tile_m"], p["tile_n"], p["splits"]) == (4, 16, 1)
     assert qgm.plan(4, 6144, 8192, 128, 0)["tile_n"] == 16
+
+
+# hipMemoryType: 0 unregistered, 1 host, 2 device, 3 managed, 10 array, 11 unified
+@pytest.mark.parametrize("rc,mtype,pdev,cdev,expect", [
+    (0, 2, 0, 0, OK),            # device memory of the current device
+    (0, 2, 1, 0, E_NOT_DEVICE),  # another GPU's memory
+    (0, 3, 1, 0, OK),            # managed memory is reachable from any device
+    (0, 11, 0, 0, OK),           # unified address space
+    (0, 1, 0, 0, E_NOT_DEVICE),  # pinned / registered host memory
+    (0, 0, 0, 0, E_NOT_DEVICE),  # unregistered
+    (0, 10, 0, 0, E_NOT_DEVICE), # arrays
+    (1, 2, 0, 0, E_NOT_DEVICE),  # hipPointerGetAttributes failed (plain malloc memory)
+])
+def test_pointer_classification(rc, mtype, pdev, cdev, expect):
+    assert lib.qg_classify_pointer(rc, mtype, pdev, cdev) == expect
+
+
+def test_dequant_checks_metadata_alignment():
+    # q4k reads its (d, dmin) pairs as 32-bit words: scales and zeros must be
+    # 16-byte aligned like every other buffer, checked before any HIP call
+    assert lib.qg_dequant(A, A + 2, A, A, 16, 256, 256, 4, None) == E_ALIGN
+    assert lib.qg_dequant(A, A, A + 8, A, 16, 256, 128, 0, None) == E_ALIGN
+    assert lib.qg_dequant(A, A + 4, None, A, 16, 256, 32, 2, None) == E_ALIGN
+
+
+def test_dequant_empty_is_a_noop():
+    assert lib.qg_dequant(None, None, None, None, 0, 256, 128, 0, None) == OK
+
+
+def _loop_status(D=64, F=128, group=32, fmt=0, M=4, L=2, scales=(A, A, A, A), events=None):
+    arr = lambda vals: (ctypes.c_void_p * 4)(*vals)
+    zeros = (None,) * 4 if fmt in (2, 3) else (A,) * 4
+    ev = None if events is None else (ctypes.c_void_p * (L + 1))(*events)
+    return lib.qloop_block(A, arr((A,) * 4), arr(scales), arr(zeros), M, D, F, group, fmt, L, A, ev, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(F=100), E_ARG),                       # F % group: the down projection's K
+    (dict(F=96, group=64), E_ARG),
+    (dict(D=64, group=32, F=128), OK if gpu_present() else E_DEVICE),   # valid
+    (dict(scales=(A, A, A, A + 2)), E_ALIGN),   # the down projection's scales
+    (dict(fmt=7), E_ARG),
+    (dict(L=-1), E_ARG),
+])
+def test_loop_block_validates_every_linear_first(kw, expect):
+    # on error nothing is launched: the four calls are checked before the first
+    # event record or launch, so a bad down projection fails without a GPU
+    if expect == OK:
+        pytest.skip("valid arguments launch work; covered by the GPU tests")
+    assert _loop_status(**kw) == expect
+
+
+def test_loop_block_records_no_event_on_error():
+    # a bad last linear with events given: the status comes back before any
+    # HIP call (the events are fake handles that a record would reject)
+    assert _loop_status(F=100, events=[A] * 3) == E_ARG

@@ -171,7 +171,7 @@ def test_ragged_parity(fmt, group, N, K, M):
     check_close(run_gemm(lin, c.x), ref_y(c, c.x), "ragged")
 
 
-@pytest.mark.parametrize("force,M", [("gemm", 1), ("gemm", 4), ("gemm", 8), ("gemm", 16), ("gemv", 3)])
+@pytest.mark.parametrize("force,M", [("gemm", 1), ("gemm", 3), ("gemm", 4), ("gemm", 8), ("gemm", 16)])
 @pytest.mark.parametrize("fmt,group", [(0, 128), (1, 64), (2, 32), (3, 32), (4, 256)])
 def test_forced_path(monkeypatch, force, M, fmt, group):
     monkeypatch.setenv("QGEMM_FORCE", force)
@@ -600,6 +600,13 @@ def test_binding_rejects_mismatched_tensors():
         qgm.qgemm(x, lin.packed, lin.scales, lin.zeros.view(torch.int16), N, K, c.group, c.fmt)
     with pytest.raises(ValueError):
         qgm.dequant(lin.packed[:10], lin.scales, lin.zeros, N, K, c.group, c.fmt)
+    # x with a column stride other than 1 is refused for every M, M = 1 included
+    wide = dev_half(np.zeros((4, 2 * K), np.float16))
+    for xs in (wide[:1, ::2], wide[:, ::2], torch.zeros((K, 1), dtype=torch.float16, device=DEV).t()[:, :]):
+        if xs.stride(1) == 1:
+            continue
+        with pytest.raises(ValueError):
+            lin(xs)
     # the looped block checks its four shapes and the scratch size
     D, F = 64, 128
     cases = [synth.random_codes_case(70 + i, 0, 32, n, k, 1)
@@ -612,6 +619,29 @@ def test_binding_rejects_mismatched_tensors():
         qgm.loop_block(xl, lins, 1, scratch=torch.empty(10, dtype=torch.float16, device=DEV))
     qgm.loop_block(xl, lins, 1)   # the right shapes run
     torch.cuda.synchronize()
+
+
+def test_loop_block_bad_down_projection_launches_nothing():
+    # F % group != 0 makes only the down projection invalid; the C ABI checks
+    # all four linears before launching, so x and the scratch stay untouched
+    import ctypes
+    D, F, g = 64, 96, 64
+    lins = []
+    for i, (n, k) in enumerate(((3 * D, D), (D, D), (F, D), (D, F))):
+        cc = synth.random_codes_case(90 + i, 0, 32, n, k, 1)
+        lins.append(qgm.QuantLinear.from_case(cc, DEV))
+    x = dev_half(np.random.default_rng(5).standard_normal((4, D)).astype(np.float16))
+    x0 = x.clone()
+    scratch = torch.full((4 * (3 * D + D + F),), 7.0, dtype=torch.float16, device=DEV)
+    arr = lambda vals: (ctypes.c_void_p * 4)(*vals)
+    st = qgm._lib.qloop_block(x.data_ptr(), arr([l.packed.data_ptr() for l in lins]),
+                              arr([l.scales.data_ptr() for l in lins]),
+                              arr([l.zeros.data_ptr() for l in lins]), 4, D, F, g, 0, 2,
+                              scratch.data_ptr(), None, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 1   # QG_E_ARG
+    assert torch.equal(x, x0)
+    assert bool((scratch == 7.0).all())
 
 
 def test_k_zero_writes_zeros():
