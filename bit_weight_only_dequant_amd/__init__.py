@@ -58,6 +58,7 @@ _SIGS = {
     "qg_dequant": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "qg_plan": ([_I, _I, _I, _I, _I, ctypes.POINTER(_I)], _I),
     "qg_classify_pointer": ([_I, _I, _I, _I], _I),
+    "qgemm_noalloc": ([_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -289,6 +290,33 @@ def qgemm(x, packed, scales, zeros, N: int, K: int, group: int, fmt: int, out=No
     st = _lib.qgemm_ex(_ptr(x), ldx, _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(residual), ldr,
                        M, N, K, group, fmt, _ptr(out), ldy, ws_ptr, ws_bytes, _stream(x.device, stream))
     _check(st, "qgemm")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # QGEMM_NOALLOC_SCRATCH_BYTES of include/qgemm.h
+
+
+def qgemm_noalloc(x, packed, scales, zeros, N: int, K: int, group: int, fmt: int, out,
+                  residual=None, stream=None):
+    """The `qgemm_noalloc` entry point: as `qgemm` into a caller-owned `out`,
+    with split-K partials in the library's fixed per-GPU array (no device
+    allocation anywhere in the call)."""
+    torch = _torch()
+    _dev(x, "x"); _dev(packed, "packed"); _dev(scales, "scales"); _dev(zeros, "zeros")
+    _dev(residual, "residual"); _dev(out, "out")
+    if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != K or (K > 1 and x.stride(1) != 1):
+        raise ValueError("x must be an fp16 [M, K] tensor with unit column stride")
+    M = x.shape[0]
+    _check_weights(packed, scales, zeros, N, K, group, fmt, x.device)
+    _check_out(out, M, N, "out", x.device)
+    if residual is not None:
+        _check_out(residual, M, N, "residual", x.device)
+    ldx = x.stride(0) if M > 1 else K
+    ldy = out.stride(0) if M > 1 else N
+    ldr = (residual.stride(0) if M > 1 else N) if residual is not None else N
+    st = _lib.qgemm_noalloc(_ptr(x), ldx, _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(residual), ldr,
+                            M, N, K, group, fmt, _ptr(out), ldy, _stream(x.device, stream))
+    _check(st, "qgemm_noalloc")
     return out
 
 

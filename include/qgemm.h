@@ -194,6 +194,25 @@ int qgemm_ex(const uint16_t* x, int ldx, const uint32_t* packed, const uint16_t*
              int M, int N, int K, int group, int fmt, uint16_t* y, int ldy,
              void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * qgemm_noalloc: qgemm_ex for callers that cannot allocate device memory --
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as qgemm_ex with
+ * workspace == NULL, but it never allocates (no hipMalloc, no library
+ * routine that allocates): the split-K partials go to a fixed array of
+ * QGEMM_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, held from the
+ * library's load until the process ends.  Problems whose plan needs more
+ * partials than that return QG_E_WORKSPACE (qgemm_workspace_bytes() gives
+ * the need).  Every call on one GPU shares that GPU's array and leaves its
+ * partials there: calls that overlap on one GPU (different streams, or
+ * several host threads) race and must be serialised by the caller.
+ * Errors: as qgemm_ex.
+ */
+#define QGEMM_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int qgemm_noalloc(const uint16_t* x, int ldx, const uint32_t* packed, const uint16_t* scales,
+                  const uint16_t* zeros, const uint16_t* residual, int ldr, int M, int N, int K,
+                  int group, int fmt, uint16_t* y, int ldy, void* stream);
+
 /* Workspace bytes qgemm_ex needs for this problem (0 when none): the fp32
  * split-K partials of the caller-owned workspace convention above (Mobilint
  * qbruntime.model.Model, "infer_pinned_memory": pre-allocated buffers). */

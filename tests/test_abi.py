@@ -304,3 +304,12 @@ def test_loop_block_records_no_event_on_error():
     # a bad last linear with events given: the status comes back before any
     # HIP call (the events are fake handles that a record would reject)
     assert _loop_status(F=100, events=[A] * 3) == E_ARG
+
+
+def test_noalloc_refuses_oversized_plans_before_any_hip_call():
+    # 56 MiB of split-K partials is beyond the fixed per-GPU array (8 MiB):
+    # refused during validation, so this holds without a GPU too
+    assert qgm.workspace_bytes(512, 4096, 14336, 32, 2) > qgm.NOALLOC_SCRATCH_BYTES
+    assert lib.qgemm_noalloc(A, 14336, A, A, None, None, 4096, 512, 4096, 14336, 32, 2, A, 4096, None) == E_WS
+    assert lib.qgemm_noalloc(A, 128, A, A, A, None, 16, 0, 16, 128, 32, 0, A, 16, None) == OK   # M = 0: no-op
+    assert lib.qgemm_noalloc(A + 2, 128, A, A, A, None, 16, 1, 16, 128, 32, 0, A, 16, None) == E_ALIGN
