@@ -115,20 +115,24 @@ def test_packed_bytes(N, K, fmt, expect):
 
 
 def decode_packed_by_formula(packed, N, K, fmt):
-    """The packed order as the header documents it, written out in Python."""
+    """The packed order as the header documents it, written out in Python:
+    inside a word tile of 16 * cpw codes, code kt sits in lane group
+    (kt % 32) // 8 at position 8 * (kt // 32) + kt % 8 of the lane's codes."""
     b = oracle.BITS[fmt]
     cpw = 32 // b
-    kw_n = K // cpw
-    wt = -(-kw_n // 16)
+    kt_w = 16 * cpw
+    wt = -(-(K // cpw) // 16)
     codes = np.zeros((N, K), dtype=np.uint8)
     for n in range(N):
-        for kw in range(kw_n):
-            rb, r, T, wi = n // 16, n % 16, kw // 16, kw % 16
-            g, t = wi // 4, wi % 4
+        rb, r = n // 16, n % 16
+        for k in range(K):
+            T, kt = k // kt_w, k % kt_w
+            g = (kt % 32) // 8
+            pos = 8 * (kt // 32) + kt % 8
+            t, j = pos // cpw, pos % cpw
             word = int(packed[((rb * wt + T) * 64 + g * 16 + r) * 4 + t])
-            for j in range(cpw):
-                slot = (j & 1) * (cpw // 2) + (j >> 1)
-                codes[n, kw * cpw + j] = (word >> (b * slot)) & ((1 << b) - 1)
+            slot = (j & 1) * (cpw // 2) + (j >> 1)
+            codes[n, k] = (word >> (b * slot)) & ((1 << b) - 1)
     return codes
 
 
@@ -142,9 +146,11 @@ def test_host_qpack_layout_and_roundtrip(fmt, N, K):
     assert np.array_equal(decode_packed_by_formula(packed, N, K, fmt),
                           oracle.unpack_codes(c.words, N, K, fmt))
     assert np.array_equal(qgm.qunpack_host(packed, N, K, fmt), c.words)
-    # padding is zero
-    nz = np.count_nonzero(packed)
-    assert nz <= np.count_nonzero(c.words)
+    # padding is zero: the codes of every slot of every packed word (padding
+    # included) add up to the canonical codes' sum
+    b = oracle.BITS[fmt]
+    allcodes = sum(int(((packed >> (b * i)) & ((1 << b) - 1)).sum()) for i in range(32 // b))
+    assert allcodes == int(oracle.unpack_codes(c.words, N, K, fmt).astype(np.int64).sum())
 
 
 def test_host_repack_is_a_permutation_of_codes():

@@ -678,7 +678,7 @@ def test_graph_replays_match_eager(name, M):
         assert torch.equal(other.view(torch.int16), eager.view(torch.int16))
 
 
-def test_graph_survives_workspace_growth():
+def test_graph_survives_workspace_growth(monkeypatch):
     # a graph captured with the library-owned split-K workspace must still
     # replay correctly after a later, larger call has grown that workspace
     # (the outgrown buffer is kept, never freed)
@@ -692,9 +692,10 @@ def test_graph_survives_workspace_growth():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         la(xa, out=ya)
-    # 128 tiles x 8 splits of 64 x 64 fp32 partials: 16 MiB, more than any
-    # earlier call in this process asked for, so the workspace grows
+    # 128 tiles x 8 forced splits of 64 x 64 fp32 partials: 16 MiB, more than
+    # any earlier call in this process asked for, so the workspace grows
     Mb, Nb, Kb = 256, 2048, 16384
+    monkeypatch.setenv("QGEMM_SPLITK", "8")
     assert qgm.workspace_bytes(Mb, Nb, Kb, 128, 0) >= 16 << 20
     cb = synth.random_codes_case(5151, 0, 128, Nb, Kb, 1)
     lb = qgm.QuantLinear.from_case(cb, DEV)
