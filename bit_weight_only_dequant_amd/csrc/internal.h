@@ -28,6 +28,7 @@ constexpr int GEMM_TN = 64;              // workgroup tile columns (N)
 constexpr int GEMM_SMALL_M = 32;         // M <= this: 32 x 32 tiles; M <= 2x this: 64 x 32
 constexpr int GEMM_TPW = 8;              // word tiles per wave, at most (4 for 2-bit codes)
 constexpr int GEMM_GCAP = 64;            // quantization groups per workgroup, at most
+constexpr int GEMM_XD = 4;               // steps of x and codes a GEMM wave keeps in flight, plus one
 constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
 
 // word tiles one M = 1 GEMV workgroup of 16 waves streams, at most: 8 per wave

@@ -1049,10 +1049,15 @@ template <int FMT> __device__ __forceinline__ h8 gtab_weights(const u4& c, int p
 // are not adjacent lanes, and the vector memory path merges only adjacent
 // lanes: x is loaded with one 64-byte sector per lane quad instead and moved
 // into the operand layout with ds_bpermute (the LDS crossbar, no LDS storage).
-// XD steps of x are in flight per wave, and the code chunks of the word tiles
-// they belong to (CD tiles live).  Every wave issues all TPW * NR steps (those
-// past its share clamped in bounds and not computed), so the loads form one
-// straight-line sequence and every wait the compiler places is exact.  The
+// XD - 1 steps of x are in flight per wave while it computes, and the code
+// chunks of the word tiles they belong to (CD tiles live).  Every wave issues
+// all TPW * NR steps (those past its share clamped in bounds and not
+// computed), so the loads form one straight-line sequence and every wait the
+// compiler places is exact.  Each step runs the MFMAs of step s with the LDS
+// phase of step s + 1 (operand permute, table reads) after the first few of
+// them, and its dequantization after the LDS round trip: the VALU overlaps
+// the matrix core only partly, so the dequantization is kept to one B operand
+// per MB MFMAs.  The
 // (scale, zero) entries of the workgroup's columns and groups are staged in
 // LDS once; each step reads one per column block (its run lies in one group,
 // the same for all four lane groups).
@@ -1185,24 +1190,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 
   h8 xa[XD][MB];                  // A fragments of the steps in flight
   u4 cq[CD][NB];                  // code chunks of the word tiles in flight
-  // steps are issued in pairs: the x of runs p and p + 1 of a row block are
-  // the two halves of the same 128-byte lines, so their loads go out back to
-  // back and the second finds the lines the first is fetching
-  auto issue = [&](int s) {       // wave-local steps s, s + 1 (s even)
+  auto issue = [&](int s) {       // the loads of wave-local step s
     const int tau = s / NR, p = s % NR;
     const int T = min(wt0 + tau, tlast);                 // clamped; dead steps are not computed
     if (p == 0) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) cq[tau % CD][nb] = buf_load16(cr, coff[nb], (uint32_t)T * 1024u);
     }
-    const int k = T * F::KT + 32 * p;                    // the runs' first k (all lane groups)
-    const uint32_t ks0 = (uint32_t)(k < a.K ? k : 0) * 2u;           // past K: finite data, zero scale
-    const uint32_t ks1 = (uint32_t)(k + 32 < a.K ? k + 32 : 0) * 2u;
+    const int k = T * F::KT + 32 * p;                    // the run's first k (all lane groups)
+    const uint32_t ks = (uint32_t)(k < a.K ? k : 0) * 2u;            // past K: finite data, zero scale
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      xa[s % XD][mb] = __builtin_bit_cast(h8, buf_load16(xr, xoff[mb], ks0));
-      xa[(s + 1) % XD][mb] = __builtin_bit_cast(h8, buf_load16(xr, xoff[mb], ks1));
-    }
+    for (int mb = 0; mb < MB; ++mb) xa[s % XD][mb] = __builtin_bit_cast(h8, buf_load16(xr, xoff[mb], ks));
     __builtin_amdgcn_sched_barrier(0);   // steps stay in issue order
   };
 
@@ -1223,8 +1221,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     const int gv = min(max((k >> lg) - gw0, 0), gwn - 1);
     return ((k < a.K) & (s < nlive)) ? gv : GEMM_GCAP;
   };
-  auto prep = [&](int s, h8 (&bf)[NB]) {
-    const int tau = s / NR, p = s % NR;
+  // the LDS phase of a step's operands: A permuted in place, the table
+  // entries of its column blocks read
+  auto fetch = [&](int s, uint32_t (&ent)[NB][TW]) {
     const int gi = gidx(s);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -1236,21 +1235,25 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      uint32_t ent[TW];
       const uint32_t* tp = szl + ((16 * nb + r) * SZS + gi) * TW;
       if constexpr (TW == 2) {
         const uint2 v = *reinterpret_cast<const uint2*>(tp);
-        ent[0] = v.x; ent[1] = v.y;
+        ent[nb][0] = v.x; ent[nb][1] = v.y;
       } else {
 #pragma unroll
         for (int q = 0; q < TW / 4; ++q) {
           const u4 v = *reinterpret_cast<const u4*>(tp + 4 * q);
 #pragma unroll
-          for (int d = 0; d < 4; ++d) ent[4 * q + d] = v[d];
+          for (int d = 0; d < 4; ++d) ent[nb][4 * q + d] = v[d];
         }
       }
-      bf[nb] = gtab_weights<FMT>(cq[tau % CD][nb], p, ent);
     }
+  };
+  // the VALU phase: B dequantized from the run's codes and the entries
+  auto dequant = [&](int s, const uint32_t (&ent)[NB][TW], h8 (&bf)[NB]) {
+    const int tau = s / NR, p = s % NR;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) bf[nb] = gtab_weights<FMT>(cq[tau % CD][nb], p, ent[nb]);
   };
   auto mma = [&](int s, const h8 (&bf)[NB]) {
 #pragma unroll
@@ -1260,11 +1263,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s % XD][mb], bf[nb], acc[mb][nb], 0, 0, 0);
   };
 
-  // 3. the first XD steps in flight, then the table (the compiler waits for
-  //    the scale/zero loads only: they were issued first)
-  static_assert(NR % 2 == 0 && XD % 2 == 0, "steps go in pairs");
+  // 3. the first XD - 1 steps in flight, then the table (the compiler waits
+  //    for the scale/zero loads only: they were issued first)
 #pragma unroll
-  for (int s = 0; s < XD && s < STEPS; s += 2) issue(s);
+  for (int s = 0; s < XD - 1 && s < STEPS; ++s) issue(s);
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
     const int e = tid + NW * 64 * j;
@@ -1282,35 +1284,43 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   }
   __syncthreads();
 
-  // 4. the K loop, software-pipelined: the MFMAs of step s interleaved with
-  //    the operands of step s + 1 (the compiler waits for that step's loads
-  //    only), then the loads of steps s + XD - 1, s + XD into the registers of
-  //    the two steps just finished
+  // 4. the K loop, software-pipelined: the loads of step s + XD - 1 (so XD - 1
+  //    steps stay in flight while the wave waits), then the MFMAs of step s
+  //    interleaved with the operands of step s + 1 (the compiler waits for
+  //    that step's loads only)
   h8 bf0[NB], bf1[NB];
-  prep(0, bf0);
+  uint32_t ent[NB][TW];
+  fetch(0, ent);
+  dequant(0, ent, bf0);
   constexpr int VW = FMT == Q8_0 ? 14 : 13;               // VALU per B operand
-  constexpr int VPER = (VW * NB + NBLK - 1) / NBLK;
+  constexpr int MLEAD = NBLK >= 16 ? 4 : NBLK / 4;        // MFMAs ahead of each LDS phase
+  constexpr int VPER = (VW * NB + NBLK - 2 * MLEAD - 1) / (NBLK - 2 * MLEAD);
+  static_assert(NBLK > 2 * MLEAD, "MFMAs per step");
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
+    // the loads of step s + XD - 1 first, into the slot step s - 1 has left
+    if (s + XD - 1 < STEPS) issue(s + XD - 1);
     __builtin_amdgcn_sched_barrier(0);
     if (s % 2 == 0) {
       mma(s, bf0);
-      if (s + 1 < STEPS) prep(s + 1, bf1);
+      if (s + 1 < STEPS) { fetch(s + 1, ent); dequant(s + 1, ent, bf1); }
     } else {
       mma(s, bf1);
-      if (s + 1 < STEPS) prep(s + 1, bf0);
+      if (s + 1 < STEPS) { fetch(s + 1, ent); dequant(s + 1, ent, bf0); }
     }
     if (s + 1 < STEPS) {
-      // each MFMA with a share of the next step's dequantization and LDS reads
+      // MFMAs of step s cover the wait for step s + 1's loads and the LDS
+      // round trip of its operands; the rest carry its dequantization
+      __builtin_amdgcn_sched_group_barrier(0x008, MLEAD, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x080, 4 * MB + NB * (TW + 3) / 4, 0);   // DS
+      __builtin_amdgcn_sched_group_barrier(0x008, MLEAD, 0);
 #pragma unroll
-      for (int t = 0; t < NBLK; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0); // VALU
+      for (int t = 0; t < NBLK - 2 * MLEAD; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (s % 2 == 1 && s + XD - 1 < STEPS) issue(s + XD - 1);
   }
 
   // 5. sum the waves' accumulators through LDS in wave order; wave w finishes
@@ -1559,10 +1569,10 @@ static void launch_gemm_fmt(const GemmArgs& a, const Plan& p, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)p.tiles_n * p.tiles_m * p.splits)), block(GEMM_THREADS);
   constexpr int TMAX = gemm_tpw_cap(FMT, MB * NB == 16);   // the plan's cap
   const int per = (int)ceil_div(p.tps, NW);
-  if (per <= 1) hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, 1, 4>), grid, block, 0, s, a);
-  else if (per <= 2) hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, 2, 4>), grid, block, 0, s, a);
-  else if (per <= 4 || TMAX <= 4) hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, (TMAX < 4 ? TMAX : 4), 4>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, TMAX, 4>), grid, block, 0, s, a);
+  if (per <= 1) hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, 1, GEMM_XD>), grid, block, 0, s, a);
+  else if (per <= 2) hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, 2, GEMM_XD>), grid, block, 0, s, a);
+  else if (per <= 4 || TMAX <= 4) hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, (TMAX < 4 ? TMAX : 4), GEMM_XD>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, TMAX, GEMM_XD>), grid, block, 0, s, a);
 }
 
 template <int MB, int NB>
