@@ -5,13 +5,19 @@
 A step is one qgemm call of the decode workload: INT4 asymmetric, group 128,
 M=1, N=6144, K=2048 (the fused QKV of a D=2048 block).  Each step reads a
 different copy of the packed weight, scales and zero points; the copies add
-up to more than twice the 256 MB on-die cache, so every step streams its
-weight bytes from HBM.  The K timed steps are captured once in a HIP graph and
-replayed, bracketed by events on the stream the kernels run on.
+up to more than twice the 256 MB on-die cache, and a 512 MiB write evicts that
+cache before every timed replay, so every timed step streams its weight bytes
+from HBM whatever K is.  The K timed steps are captured once in a HIP graph
+and replayed (median of several replays), bracketed by events on the stream
+the kernels run on.
 
 One JSON line is printed: value = weight GB/s at M=1, plus the roofline of the
-GEMV kernel, the CPU oracle timed on the host, and secondary legs (M=8, the
-M=128 MFMA GEMM in TFLOP/s, INT2 and q4_0, the looped shared block).
+GEMV kernel against the published HBM peak and against the ceilings measured
+in the same run (a plain streaming read of the same bytes, the empty-kernel
+launch floor, the sustained MFMA rate), per-dispatch percentiles (from the
+committed kernel-trace summary), the CPU
+oracle timed on the host for every workload, and secondary legs (M=8, the
+M=128 MFMA GEMM in TFLOP/s, INT2, q4_0, q8_0, q4k, the looped shared block).
 """
 from __future__ import annotations
 
@@ -31,7 +37,20 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, published
 MALL_BYTES = 256 << 20         # on-die cache that rotating copies must exceed
 SECONDARY_REPLAYS = 5          # secondary legs report the median of this many timed replays
+MAIN_REPLAYS = 5               # the headline: median of this many timed replays
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+LOOP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "loop_traffic.json")
+DISPATCH_FILE = os.path.join(ROOT, "profiles", "dispatch.json")
+_EVICT = {}
+
+
+def evict(torch):
+    """Write 512 MiB (twice the on-die cache) so that no weight bytes stay
+    cached from earlier work; issued on the current stream, outside any graph."""
+    buf = _EVICT.get("buf")
+    if buf is None:
+        buf = _EVICT["buf"] = torch.empty(2 * MALL_BYTES // 2, dtype=torch.float16, device="cuda")
+    buf.fill_(1.0)
 KERNEL_SRC = os.path.join(ROOT, "bit_weight_only_dequant_amd", "csrc", "kernels.hip")
 
 
@@ -44,10 +63,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=810)
     ap.add_argument("--warmup", type=int, default=81)
-    ap.add_argument("--only", choices=["all", "main", "gemm", "loop", "fp16", "copy"], default="all",
-                    help="main/gemm/loop/fp16: run one leg (for profiler runs); copy: the calibration copy")
+    ap.add_argument("--only", choices=["all", "main", "gemm", "loop", "loop_prof", "fp16", "copy", "stream"],
+                    default="all",
+                    help="main/gemm/loop/fp16/stream: run one leg (for profiler runs); copy: the calibration "
+                         "copy; loop_prof: the looped block resident and with the cache evicted between loops")
+    ap.add_argument("--loop-m", type=int, default=128, help="M of --only loop / loop_prof")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-reps", type=int, default=5, help="oracle timings per workload and thread count")
     return ap.parse_args()
 
 
@@ -75,9 +97,10 @@ class Leg:
         self.lins[i % self.copies](self.x, out=self.y)
 
     def time(self, steps, warmup, replays=1):
-        """ms per step: one timed replay of a graph of `steps` calls, or the
-        median over `replays` timed replays of it (secondary legs: a single
-        replay of a ~2 ms graph varies by up to 10 % at M = 128)."""
+        """ms per step: the median over `replays` timed replays of a graph of
+        `steps` calls, each replay preceded by an eviction of the on-die cache
+        (outside the timed region), so no step finds its weights cached
+        whatever `steps` is."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
@@ -88,17 +111,25 @@ class Leg:
                 self.step(i)
         g.replay()  # first replay uploads the graph; not timed
         torch.cuda.synchronize()
+        self.replay_ms = replay_times(torch, g, steps, replays)
+        return float(np.median(self.replay_ms))
+
+
+def replay_times(torch, g, steps, replays):
+    """ms per step of each of `replays` timed replays of graph g, the on-die
+    cache evicted before each."""
+    stream = torch.cuda.current_stream()
+    out = []
+    for _ in range(replays):
+        evict(torch)
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
-        stream = torch.cuda.current_stream()
-        times = []
-        for _ in range(replays):
-            start.record(stream)
-            g.replay()
-            stop.record(stream)
-            stop.synchronize()
-            times.append(start.elapsed_time(stop) / steps)
-        return sorted(times)[len(times) // 2]
+        start.record(stream)
+        g.replay()
+        stop.record(stream)
+        stop.synchronize()
+        out.append(start.elapsed_time(stop) / steps)
+    return out
 
 
 FORMAT_NAMES = ("int4_asym", "int2_asym", "q4_0", "q8_0", "q4k")
@@ -118,34 +149,73 @@ def leg_result(name, leg, ms, M, replays=1):
     return r
 
 
-def cpu_baseline(case, M, seconds):
-    """The oracle as it stands, on a bounded sample of the decode workload."""
+CPU_WORKLOADS = (("tiny_int4_g32", 1), ("tiny_int4_g32", 4), ("decode_int4_g128", 1), ("decode_int4_g128", 8),
+                 ("prefill_int4_g128", 128), ("int2_g64", 1), ("int2_g64", 128), ("q4_0_b32", 1),
+                 ("q4_0_b32", 128))
+
+
+def cpu_baseline(synth, reps):
+    """The oracle as it stands, timed on the host for every workload: one
+    oracle call per sample (one loop of the block for the looped workload),
+    `reps` samples with every BLAS thread and `reps` with one, the median of
+    each.  The headline is the decode workload at M = 1 on every thread."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
-    x = case.x[:M]
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.qgemm_ref(x, case.words, case.scales, case.zeros, M, case.N, case.K, case.group, case.fmt)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    wbytes = case.weight_bytes
-    return dict(value=round(wbytes * calls / el / 1e9, 4), unit="GB/s", cores=int(blas_threads),
-                kind="oracle",
-                sample=f"{calls} oracle calls (unpack, fp32 dequant, fp64 product) on the decode "
-                       f"workload M={M} N={case.N} K={case.K} INT4 g{case.group}, {el:.1f} s; "
-                       f"elementwise steps single-threaded, BLAS with {blas_threads} threads")
+    from threadpoolctl import threadpool_info, threadpool_limits
+    blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+
+    def timed(fn, min_s=0.2):
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= min_s or calls >= 1 and el >= 0.05 and calls * 50 > 1e4:
+                return el / calls
+
+    rows = []
+    for name, M in CPU_WORKLOADS:
+        c = synth.workload(name)
+        x = c.x[:M]
+        fn = lambda c=c, x=x, M=M: oracle.qgemm_ref(x, c.words, c.scales, c.zeros, M, c.N, c.K, c.group, c.fmt)
+        r = dict(workload=name, M=M, N=c.N, K=c.K, weight_bytes=c.weight_bytes)
+        for tag, lim in (("all", None), ("1", 1)):
+            with threadpool_limits(limits=lim):
+                sec = float(np.median([timed(fn) for _ in range(reps)]))
+            r[f"s_per_call_{tag}"] = round(sec, 5)
+            r[f"GBps_{tag}"] = round(c.weight_bytes / sec / 1e9, 4)
+            r[f"TFLOPs_{tag}"] = round(2.0 * M * c.N * c.K / sec / 1e12, 6)
+        rows.append(r)
+    # the looped block: one loop (four linears and two residual adds) per sample
+    lc = synth.loop_workload(M=128, L=1)
+    lin = [dict(words=q.words, scales=q.scales, zeros=q.zeros, N=q.N, K=q.K, group=q.group, fmt=q.fmt)
+           for q in lc.linears()]
+    D = lc.x0.shape[1]
+    wb = sum(q.weight_bytes for q in lc.linears())
+    r = dict(workload="loop_block_int4_g128", M=128, D=D, L_sampled=1, weight_bytes_per_loop=wb)
+    for tag, lim in (("all", None), ("1", 1)):
+        with threadpool_limits(limits=lim):
+            sec = float(np.median([timed(lambda: oracle.loop_block_ref(lc.x0, lin, 1, D=D), 0.0)
+                                   for _ in range(reps)]))
+        r[f"s_per_loop_{tag}"] = round(sec, 4)
+        r[f"GBps_{tag}"] = round(wb / sec / 1e9, 4)
+    rows.append(r)
+    head = next(r for r in rows if r["workload"] == "decode_int4_g128" and r["M"] == 1)
+    return dict(value=head["GBps_all"], unit="GB/s", cores=int(blas_threads), host_cpus=os.cpu_count(),
+                kind="oracle", value_1thread=head["GBps_1"],
+                sample=f"median of {reps} timings per workload and thread count; each timing is one oracle call "
+                       f"(repeated to >= 0.2 s for the tiny workload; unpack, fp32 dequant, fp64 product) on the "
+                       f"full workload, one loop of L for the looped block; 'all' = BLAS pool of {blas_threads} "
+                       f"threads (the unpack and dequant are single-threaded numpy), '1' = one BLAS thread; "
+                       f"headline: decode M=1 N=6144 K=2048 INT4 g128 on all threads",
+                workloads=rows)
 
 
-def loop_leg(qgm, torch, synth, L=8, flush=True, M=128):
-    """Looped shared block: per-loop time, cold (on-die cache flushed) vs warm.
-    M = 128 is the prefill-sized block; M = 1 the decode step (GEMV kernels)."""
+def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
+    """Looped shared block: per-loop time with the on-die cache evicted once
+    before loop 1 ("cold": loops 2..L find the shared weights where loop 1 left
+    them), with it warm, and -- the control -- with the cache evicted before
+    every loop (outside the timed loops), so every loop streams its weights
+    from HBM.  M = 128 is the prefill-sized block; M = 1 the decode step."""
     lc = synth.loop_workload(M=M, L=L)
     lins = [qgm.QuantLinear.from_case(c, "cuda") for c in lc.linears()]
     x0 = qgm.to_half_tensor(lc.x0, "cuda")
@@ -155,34 +225,150 @@ def loop_leg(qgm, torch, synth, L=8, flush=True, M=128):
     x = x0.clone()
     qgm.loop_block(x, lins, L, scratch=scratch)  # warm-up, allocates the workspace
     torch.cuda.synchronize()
-    flush_buf = torch.empty(2 * MALL_BYTES // 2, dtype=torch.float16, device="cuda")
     res = {}
     for mode in ("cold", "warm"):
         x.copy_(x0)
         if mode == "cold":
-            flush_buf.fill_(1.0)  # evicts the weights from the on-die cache
+            evict(torch)
         else:
             qgm.loop_block(x, lins, 1, scratch=scratch)
             x.copy_(x0)
         events = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
         qgm.loop_block(x, lins, L, scratch=scratch, events=events)
         events[-1].synchronize()
-        per = [events[i].elapsed_time(events[i + 1]) for i in range(L)]
-        res[mode] = per
+        res[mode] = [events[i].elapsed_time(events[i + 1]) for i in range(L)]
+    if control:
+        x.copy_(x0)
+        per = []
+        for _ in range(L):
+            evict(torch)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            qgm.loop_block(x, lins, 1, scratch=scratch, events=ev)
+            ev[-1].synchronize()
+            per.append(ev[0].elapsed_time(ev[1]))
+        res["evict"] = per
     wbytes = sum(l.weight_bytes for l in lins)
     flops = 2.0 * M * (D * 3 * D + D * D + D * F + F * D)
     cold, warm = res["cold"], res["warm"]
-    return dict(leg="loop_block_int4_g128" + ("" if M == 128 else f"_M{M}"), M=M, D=D, F=F, L=L,
-                weight_bytes_per_loop=wbytes,
-                cold_loop_ms=[round(v, 4) for v in cold], warm_loop_ms=[round(v, 4) for v in warm],
-                loop1_cold_ms=round(cold[0], 4),
-                loops2_L_ms=round(float(np.median(cold[1:])), 4),   # median: robust to launch jitter
-                TFLOPs_loops2_L=round(flops / (float(np.median(cold[1:])) * 1e-3) / 1e12, 2),
-                weight_GBps_loop1_cold=round(wbytes / (cold[0] * 1e-3) / 1e9, 1))
+    name = "loop_block_int4_g128" + ("" if M == 128 else f"_M{M}")
+    out = dict(leg=name, M=M, D=D, F=F, L=L,
+               weight_bytes_per_loop=wbytes,
+               cold_loop_ms=[round(v, 4) for v in cold], warm_loop_ms=[round(v, 4) for v in warm],
+               loop1_cold_ms=round(cold[0], 4),
+               loops2_L_ms=round(float(np.median(cold[1:])), 4),   # median: robust to launch jitter
+               TFLOPs_loops2_L=round(flops / (float(np.median(cold[1:])) * 1e-3) / 1e12, 2),
+               weight_GBps_loop1_cold=round(wbytes / (cold[0] * 1e-3) / 1e9, 1))
+    if control:
+        ev_ms = float(np.median(res["evict"]))
+        out.update(evict_each_loop_ms=[round(v, 4) for v in res["evict"]],
+                   evict_each_loop_median_ms=round(ev_ms, 4),
+                   weight_GBps_evict_each_loop=round(wbytes / (ev_ms * 1e-3) / 1e9, 1))
+    hb = load_loop_traffic(name)
+    if hb is not None:
+        out["hbm_bytes_per_loop"] = hb   # counters (profiles/loop_traffic.json)
+    return out
+
+
+def loop_prof(qgm, torch, synth, L=8, M=128):
+    """For the HBM byte counters: the looped block once resident (cache
+    evicted before loop 1 only), then L single loops each after an eviction.
+    The evictions are fill kernels between the qGEMM dispatches."""
+    lc = synth.loop_workload(M=M, L=L)
+    lins = [qgm.QuantLinear.from_case(c, "cuda") for c in lc.linears()]
+    x0 = qgm.to_half_tensor(lc.x0, "cuda")
+    D, F = lc.x0.shape[1], lc.up.N
+    scratch = torch.empty(M * (3 * D + D + F), dtype=torch.float16, device="cuda")
+    x = x0.clone()
+    qgm.loop_block(x, lins, 1, scratch=scratch)  # allocates the workspace
+    x.copy_(x0)
+    evict(torch)
+    qgm.loop_block(x, lins, L, scratch=scratch)
+    x.copy_(x0)
+    for _ in range(L):
+        evict(torch)
+        qgm.loop_block(x, lins, 1, scratch=scratch)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(loop_prof=True, M=M, L=L)), flush=True)
+
+
+def stream_leg(qgm, torch, nbytes, steps, replays, grids=(256, 512, 1024, 2048)):
+    """The streaming-read ceiling of one launch over `nbytes` (the headline's
+    weight bytes): rotating slices of a buffer larger than twice the on-die
+    cache, the same graph and eviction protocol as the qGEMM legs; the best
+    grid of `grids` is the ceiling."""
+    stride = -(-nbytes // 256) * 256
+    copies = max(1, -(-2 * MALL_BYTES // stride))
+    buf = torch.empty(copies * stride, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.zeros(max(grids), dtype=torch.int32, device="cuda")
+    best = None
+    rows = []
+    for wg in grids:
+        def step(i, wg=wg):
+            qgm.stream_read(buf[(i % copies) * stride:], nbytes, sink, wg)
+        for i in range(4):
+            step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        ms = float(np.median(replay_times(torch, g, steps, replays)))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rows.append(dict(workgroups=wg, us_per_launch=round(ms * 1e3, 3), GBps=round(gbs, 1)))
+        if best is None or gbs > best["GBps"]:
+            best = rows[-1]
+        del g
+    return dict(bytes_per_launch=nbytes, copies=copies, best=best, grids=rows)
+
+
+def empty_floor(qgm, torch, workgroups, threads, steps, replays):
+    """us per launch of an empty kernel of the given grid, in a graph."""
+    for _ in range(4):
+        qgm.empty_launch(workgroups, threads)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            qgm.empty_launch(workgroups, threads)
+    g.replay()
+    torch.cuda.synchronize()
+    ms = float(np.median(replay_times(torch, g, steps, replays)))
+    return dict(workgroups=workgroups, threads=threads, us_per_launch=round(ms * 1e3, 3))
+
+
+def mfma_peaks(qgm, torch):
+    """The dense fp16 MFMA peak from the device's compute units and clock (4
+    SIMDs per CU, 16*16*32*2 flops per 16-cycle v_mfma_f32_16x16x32_f16 per
+    SIMD = 4096 flops per CU per cycle), and the rate the probe sustains."""
+    info = qgm.device_info(0)
+    derived = info["compute_units"] * 4096 * info["clock_khz"] * 1e3 / 1e12
+    wg = info["compute_units"] * 2          # 8 waves per CU: 2 per SIMD
+    iters = 4000
+    out = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    qgm.mfma_probe(out, wg, 10)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        qgm.mfma_probe(out, wg, iters)
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    flops = wg * 4 * iters * qgm.MFMA_PROBE_FLOPS
+    return dict(device=info, derived_TFLOPs=round(derived, 1),
+                sustained_TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1), published_TFLOPs=MFMA_F16_PEAK_TFLOPS,
+                probe=f"{wg} workgroups x 4 waves x {iters} rounds of 16 independent v_mfma_f32_16x16x32_f16")
 
 
 def graph_time(torch, step, steps, warmup):
-    """ms per step of `step(i)`, captured once in a HIP graph and replayed."""
+    """ms per step of `step(i)`, captured once in a HIP graph and replayed
+    once after an eviction of the on-die cache."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -192,14 +378,7 @@ def graph_time(torch, step, steps, warmup):
             step(i)
     g.replay()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    stream = torch.cuda.current_stream()
-    start.record(stream)
-    g.replay()
-    stop.record(stream)
-    stop.synchronize()
-    return start.elapsed_time(stop) / steps
+    return replay_times(torch, g, steps, 1)[0]
 
 
 def fp16_leg(qgm, torch, synth, Ms=(1, 8, 32, 128, 512, 2048)):
@@ -271,6 +450,31 @@ def load_traffic(kernel):
     return None if entry is None else entry.get("bytes")
 
 
+def load_dispatch(kernel):
+    """Per-dispatch duration percentiles (us) of `kernel` from the committed
+    kernel-trace summary, or None when the kernel sources changed since."""
+    try:
+        t = json.load(open(DISPATCH_FILE))
+    except Exception:
+        return None
+    if t.get("kernel_src_sha") != kernel_hash():
+        return None
+    return t.get(kernel)
+
+
+def load_loop_traffic(leg):
+    """Per-loop HBM bytes of the looped block from the committed counter
+    summary (resident loops and the evict-every-loop control), or None when
+    the kernel sources changed since the counters were taken."""
+    try:
+        t = json.load(open(LOOP_TRAFFIC_FILE))
+    except Exception:
+        return None
+    if t.get("kernel_src_sha") != kernel_hash():
+        return None
+    return t.get(leg)
+
+
 def gemv_kernel_name(qgm, c):
     """The M = 1 kernel the library's plan picks: 16-row or 8-row workgroups."""
     rows = qgm.plan(1, c.N, c.K, c.group, c.fmt)["tile_n"]
@@ -294,15 +498,6 @@ def main():
         return
 
     main_case = synth.workload("decode_int4_g128")
-    out = {}
-    if args.only in ("all", "main"):
-        leg = Leg(qgm, torch, main_case, 1)
-        ms = leg.time(args.steps, args.warmup)
-        main_r = leg_result("decode_int4_g128_M1", leg, ms, 1)
-        out["main"] = (leg, ms, main_r)
-        if args.only == "main":
-            print(json.dumps(main_r), flush=True)
-            return
     if args.only == "gemm":
         c = synth.workload("prefill_int4_g128")
         leg = Leg(qgm, torch, c, 128)
@@ -310,11 +505,35 @@ def main():
         print(json.dumps(leg_result("prefill_int4_g128_M128", leg, ms, 128, SECONDARY_REPLAYS)), flush=True)
         return
     if args.only == "loop":
-        print(json.dumps(loop_leg(qgm, torch, synth)), flush=True)
+        print(json.dumps(loop_leg(qgm, torch, synth, M=args.loop_m)), flush=True)
+        return
+    if args.only == "loop_prof":
+        loop_prof(qgm, torch, synth, M=args.loop_m)
         return
     if args.only == "fp16":
         print(json.dumps(fp16_leg(qgm, torch, synth)), flush=True)
         return
+    if args.only == "stream":
+        print(json.dumps(stream_leg(qgm, torch, main_case.weight_bytes, args.steps, MAIN_REPLAYS)), flush=True)
+        return
+
+    leg = Leg(qgm, torch, main_case, 1)
+    ms = leg.time(args.steps, args.warmup, replays=MAIN_REPLAYS)
+    main_r = leg_result("decode_int4_g128_M1", leg, ms, 1)
+    if args.only == "main":
+        print(json.dumps(main_r), flush=True)
+        return
+    replay_ms = list(leg.replay_ms)
+    wbytes, copies = leg.wbytes, leg.copies
+    del leg
+    torch.cuda.empty_cache()
+
+    # ceilings measured in the same run
+    stream = stream_leg(qgm, torch, wbytes, args.steps, MAIN_REPLAYS)
+    pl = qgm.plan(1, main_case.N, main_case.K, main_case.group, main_case.fmt)
+    floor = empty_floor(qgm, torch, pl["workgroups"], 512, args.steps, MAIN_REPLAYS)
+    peaks = mfma_peaks(qgm, torch)
+    torch.cuda.empty_cache()
 
     secondary = []
     leg8 = Leg(qgm, torch, main_case, 8)
@@ -324,10 +543,21 @@ def main():
                     ("q4_0_b32", 1), ("q4_0_b32", 128), ("q8_0_b32", 1), ("q8_0_b32", 128),
                     ("q4k_s256", 1), ("q4k_s256", 128)):
         c = synth.workload(name)
-        leg = Leg(qgm, torch, c, M)
+        leg2 = Leg(qgm, torch, c, M)
         steps = 400 if M == 1 else 200
-        secondary.append(leg_result(f"{name}_M{M}", leg, leg.time(steps, steps // 10, SECONDARY_REPLAYS), M, SECONDARY_REPLAYS))
-        del leg
+        r = leg_result(f"{name}_M{M}", leg2, leg2.time(steps, steps // 10, SECONDARY_REPLAYS), M, SECONDARY_REPLAYS)
+        if M == 1:   # the streaming read of this leg's own bytes per launch
+            sc = stream_leg(qgm, torch, leg2.wbytes, 200, 3, grids=(1024, 2048))["best"]
+            r["stream_ceiling_GBps"] = sc["GBps"]
+            r["frac_of_stream_ceiling"] = round(r["weight_GBps"] / sc["GBps"], 4)
+        else:
+            r["mfma_frac_derived_peak"] = round(r["TFLOPs"] / peaks["derived_TFLOPs"], 4)
+            r["mfma_frac_sustained"] = round(r["TFLOPs"] / peaks["sustained_TFLOPs"], 4)
+        if name == "prefill_int4_g128":
+            r["traffic"] = load_traffic("gemm_int4_m128")
+            r["dispatch_us"] = load_dispatch("gemm_int4_m128")
+        secondary.append(r)
+        del leg2
         torch.cuda.empty_cache()
     # same-buffer (cache-resident) rate of the headline case
     hot = Leg(qgm, torch, main_case, 1, min_bytes=0)
@@ -337,10 +567,9 @@ def main():
     secondary.append(loop_leg(qgm, torch, synth, M=1))
     secondary.append(fp16_leg(qgm, torch, synth, Ms=(1, 8, 128, 512)))
 
-    leg, ms, main_r = out["main"]
-    wbytes = leg.wbytes
     achieved = wbytes / (ms * 1e-3) / 1e9
     traffic = load_traffic("gemv_int4_m1")
+    ceiling = stream["best"]["GBps"]
     result = {
         "metric": "qGEMM weight GB/s at M=1, TFLOP/s at M=128, % of HBM/MFMA roofline",
         "value": round(achieved, 1),
@@ -356,17 +585,26 @@ def main():
         "data": "synthetic (seeded; W ~ N(0, 0.02) quantized, x ~ N(0, 1))",
         "config": {"workload": "decode GEMV, INT4 asymmetric g128, M=1, N=6144, K=2048",
                    "M": 1, "N": 6144, "K": 2048, "group": 128, "format": "int4_asym",
-                   "weight_bytes_per_step": wbytes, "weight_copies": leg.copies,
-                   "timing": "K steps captured in one HIP graph, replayed once between events"},
+                   "weight_bytes_per_step": wbytes, "weight_copies": copies,
+                   "weight_bytes_per_replay": wbytes * args.steps, "on_die_cache_bytes": MALL_BYTES,
+                   "timing": f"K steps captured in one HIP graph; median of {MAIN_REPLAYS} timed replays, "
+                             "each after a 512 MiB write that evicts the on-die cache",
+                   "replay_ms_per_step": [round(v, 6) for v in replay_ms]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": gemv_kernel_name(qgm, main_case),
-                     "algorithmic_bytes_per_launch": wbytes},
+                     "algorithmic_bytes_per_launch": wbytes,
+                     "achievable": ceiling,
+                     "frac_of_achievable": round(achieved / ceiling, 4),
+                     "achievable_kind": "plain streaming read of the same bytes per launch, same protocol",
+                     "launch_floor_us": floor["us_per_launch"],
+                     "dispatch_us": load_dispatch("gemv_int4_m1")},
+        "ceilings": {"stream_read": stream, "empty_kernel": floor, "mfma": peaks},
         "secondary": secondary,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(main_case, 1, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(synth, args.cpu_reps)
     print(json.dumps(result), flush=True)
 
 

@@ -59,6 +59,10 @@ _SIGS = {
     "qg_plan": ([_I, _I, _I, _I, _I, ctypes.POINTER(_I)], _I),
     "qg_classify_pointer": ([_I, _I, _I, _I], _I),
     "qgemm_noalloc": ([_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P], _I),
+    "qg_stream_read": ([_P, _SZ, _P, _I, _P], _I),
+    "qg_empty_launch": ([_I, _I, _P], _I),
+    "qg_mfma_probe": ([_P, _I, _I, _P], _I),
+    "qg_device_info": ([_I] + [ctypes.POINTER(_I)] * 4, _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -402,3 +406,47 @@ def loop_block(x, linears: Sequence[QuantLinear], L: int, scratch=None, events=N
                           ev, _stream(x.device, stream))
     _check(st, "qloop_block")
     return x
+
+
+# ----------------------------------------------------------------------------
+# Measurement helpers (not on the qGEMM path): the ceilings a kernel is read
+# against, taken on the device it runs on.
+
+MFMA_PROBE_FLOPS = 16 * 16 * 32 * 2 * 16   # per wave per qg_mfma_probe round
+
+
+def stream_read(src, nbytes: int, sink, workgroups: int, stream=None):
+    """Plain streaming read of the first `nbytes` bytes of device tensor `src`."""
+    _dev(src, "src")
+    _dev(sink, "sink")
+    if nbytes > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds src")
+    if sink.numel() * sink.element_size() < 4 * workgroups:
+        raise ValueError("sink must hold one uint32 per workgroup")
+    _check(_lib.qg_stream_read(_ptr(src), nbytes, _ptr(sink), workgroups, _stream(src.device, stream)),
+           "qg_stream_read")
+
+
+def empty_launch(workgroups: int, threads: int, stream=None):
+    """An empty kernel of workgroups x threads on the current device."""
+    torch = _torch()
+    _check(_lib.qg_empty_launch(workgroups, threads, _stream(torch.cuda.current_device(), stream)),
+           "qg_empty_launch")
+
+
+def mfma_probe(out, workgroups: int, iters: int, stream=None):
+    """Back-to-back independent fp16 MFMAs: iters * MFMA_PROBE_FLOPS per wave,
+    4 waves per workgroup; out: float32 device tensor of workgroups * 256."""
+    _dev(out, "out")
+    torch = _torch()
+    if out.dtype != torch.float32 or out.numel() < workgroups * 256:
+        raise ValueError("out must be float32 with workgroups * 256 elements")
+    _check(_lib.qg_mfma_probe(_ptr(out), workgroups, iters, _stream(out.device, stream)), "qg_mfma_probe")
+
+
+def device_info(device: int = 0) -> dict:
+    """Compute units and clocks of `device` as the HIP runtime reports them."""
+    v = [_I() for _ in range(4)]
+    _check(_lib.qg_device_info(device, *[ctypes.byref(x) for x in v]), "qg_device_info")
+    return dict(compute_units=v[0].value, clock_khz=v[1].value, memory_clock_khz=v[2].value,
+                memory_bus_bits=v[3].value)

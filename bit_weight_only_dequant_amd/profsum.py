@@ -1,0 +1,254 @@
+"""Summaries of the rocprofv3 runs of profile.sh: per-dispatch durations of
+the benchmarked kernels and their HBM bytes (FETCH_SIZE / WRITE_SIZE scaled
+by what the same counters read for a plain copy of known size), written as
+the JSON files bench.py reads and as Markdown tables.
+
+    python3 -m bit_weight_only_dequant_amd.profsum OUTDIR [--write DEST]
+
+OUTDIR is the folder profile.sh filled; with --write the files go to DEST
+(normally profiles/), else they are printed.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SRC = os.path.join(ROOT, "bit_weight_only_dequant_amd", "csrc", "kernels.hip")
+COPY_BYTES = 512 << 20     # bench.py --only copy
+GEMV_BYTES = 6684672       # INT4 g128 N=6144 K=2048: codes + scales + zeros
+GEMM_BYTES = 8912896       # INT4 g128 N=8192 K=2048
+PROFILE_CMD = "bash bit_weight_only_dequant_amd/profile.sh OUTDIR"
+SUMMARY_CMD = "python3 -m bit_weight_only_dequant_amd.profsum OUTDIR --write profiles"
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def _csv(outdir, run, suffix):
+    files = sorted(glob.glob(os.path.join(outdir, run, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {os.path.join(outdir, run)}")
+    out = []
+    for f in files:
+        with open(f, newline="") as fh:
+            out += list(csv.DictReader(fh))
+    return out
+
+
+def trace(outdir, run):
+    """(kernel name, duration ns) per dispatch, in dispatch order."""
+    rows = _csv(outdir, run, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in rows]
+
+
+def counter(outdir, run, name):
+    """(kernel name, counter value) per dispatch, in dispatch order."""
+    rows = [r for r in _csv(outdir, run, "counter_collection.csv") if r["Counter_Name"] == name]
+    per = {}
+    for r in rows:   # one row per dispatch for these derived counters; sum if split
+        d = int(r["Dispatch_Id"])
+        k, v = per.get(d, (r["Kernel_Name"], 0.0))
+        per[d] = (k, v + float(r["Counter_Value"]))
+    return [per[d] for d in sorted(per)]
+
+
+def stats_us(durs_ns):
+    v = np.asarray(durs_ns, dtype=np.float64) / 1e3
+    return dict(n=int(v.size), avg=round(float(v.mean()), 3), p10=round(float(np.percentile(v, 10)), 3),
+                p50=round(float(np.percentile(v, 50)), 3), p90=round(float(np.percentile(v, 90)), 3),
+                min=round(float(v.min()), 3), max=round(float(v.max()), 3))
+
+
+def select(items, key):
+    return [v for k, v in items if key in k]
+
+
+def calibration(outdir):
+    f = select(counter(outdir, "pmc_copy_FETCH_SIZE", "FETCH_SIZE"), "copy")
+    w = select(counter(outdir, "pmc_copy_WRITE_SIZE", "WRITE_SIZE"), "copy")
+    fk, wk = float(np.median(f)), float(np.median(w))
+    return dict(copy_bytes=COPY_BYTES, fetch_kib_per_copy=fk, write_kib_per_copy=wk,
+                fetch_factor=round(COPY_BYTES / (fk * 1024), 4), write_factor=round(COPY_BYTES / (wk * 1024), 4),
+                copies=len(f))
+
+
+def kernel_bytes(outdir, leg, key, cal, algo):
+    f = select(counter(outdir, f"pmc_{leg}_FETCH_SIZE", "FETCH_SIZE"), key)
+    w = select(counter(outdir, f"pmc_{leg}_WRITE_SIZE", "WRITE_SIZE"), key)
+    fb = float(np.median(f)) * 1024 * cal["fetch_factor"]
+    wb = float(np.median(w)) * 1024 * cal["write_factor"]
+    return dict(fetch_kib_median=round(float(np.median(f)), 1), write_kib_median=round(float(np.median(w)), 1),
+                fetch_bytes=int(round(fb)), write_bytes=int(round(wb)), bytes=int(round(fb + wb)),
+                algorithmic_weight_bytes=algo, ratio=round((fb + wb) / algo, 3), dispatches=len(f))
+
+
+def loop_bytes(outdir, leg, cal, L=8):
+    """Per-loop calibrated bytes of the loop_prof run: qGEMM dispatches split
+    at the eviction fills into the warm-up loop, the resident loops 1..L and
+    the L loops that each follow an eviction."""
+    segs = []
+    for name, fac in (("FETCH_SIZE", cal["fetch_factor"]), ("WRITE_SIZE", cal["write_factor"])):
+        seq = counter(outdir, f"pmc_{leg}_{name}", name)
+        cur, out = [], []
+        for k, v in seq:
+            if "Fill" in k:          # an eviction (torch fill of 512 MiB)
+                out.append(cur)
+                cur = []
+            elif "qg::" in k and "pack" not in k:   # the qGEMM kernels, not the weight repack
+                cur.append(v * 1024 * fac)
+        out.append(cur)
+        segs.append(out)
+    (fs, ws) = segs
+    k = len(fs[0])                   # dispatches per loop (the warm-up loop)
+    if len(fs) != L + 2 or len(fs[1]) != L * k or any(len(s) != k for s in fs[2:]):
+        raise ValueError(f"unexpected dispatch layout in {leg}: {[len(s) for s in fs]}")
+    tot = [f + w for f, w in zip(np.concatenate(fs), np.concatenate(ws))]
+    tot = np.asarray(tot)
+    res = tot[k:k + L * k].reshape(L, k).sum(axis=1)
+    ctl = tot[k + L * k:].reshape(L, k).sum(axis=1)
+    return dict(dispatches_per_loop=k, resident_loop_bytes=[int(v) for v in res],
+                loop1_bytes=int(res[0]), loops2_L_median_bytes=int(np.median(res[1:])),
+                evict_each_loop_bytes=[int(v) for v in ctl], evict_each_loop_median_bytes=int(np.median(ctl)))
+
+
+def md_trace(title, cmd_note, rows):
+    out = [f"# {title}", "", "Commands (GPU host, repository root):", "", "```", PROFILE_CMD, SUMMARY_CMD, "```", "",
+           cmd_note, "", "| kernel | dispatches | avg us | p10 | p50 | p90 | min | max |", "|---|---|---|---|---|---|---|---|"]
+    for name, s in rows:
+        out.append(f"| {name} | {s['n']} | {s['avg']} | {s['p10']} | {s['p50']} | {s['p90']} | {s['min']} | {s['max']} |")
+    return "\n".join(out) + "\n"
+
+
+def short(name):
+    return name.replace("(qg::GemvArgs)", "").replace("(qg::GemmArgs)", "").replace("void ", "")[:90]
+
+
+def per_kernel(items):
+    names = []
+    for k, _ in items:
+        if "qg::" in k and k not in names:
+            names.append(k)
+    return [(short(n), stats_us([d for k, d in items if k == n])) for n in names]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("outdir")
+    ap.add_argument("--write", default=None)
+    a = ap.parse_args()
+    sha = kernel_hash()
+    files = {}
+
+    tm = trace(a.outdir, "trace_main")
+    tg = trace(a.outdir, "trace_gemm")
+    ts = trace(a.outdir, "trace_stream")
+    gemv = stats_us(select(tm, "gemv"))
+    gemm = stats_us(select(tg, "gemm_kernel"))
+    stream = stats_us(select(ts, "stream_read"))
+    files["dispatch.json"] = json.dumps(dict(kernel_src_sha=sha, gemv_int4_m1=gemv, gemm_int4_m128=gemm,
+                                             stream_read_decode_bytes=stream), indent=1) + "\n"
+    files["gemv_int4_g128_m1_n6144_k2048_kernel_trace.md"] = md_trace(
+        "Kernel trace: decode GEMV, INT4 g128, M=1, N=6144, K=2048",
+        f"Run `trace_main` (`rocprofv3 --kernel-trace --stats -- python3 bench.py --only main`): every dispatch "
+        f"of the headline leg (warm-up, graph upload and the timed replays; the cache is evicted before each "
+        f"timed replay).  Kernel sources sha256[:16] = `{sha}`.  Algorithmic bytes per launch {GEMV_BYTES}: "
+        f"{GEMV_BYTES / (gemv['avg'] * 1e3):.1f} GB/s at the average duration.", per_kernel(tm))
+    files["gemm_int4_g128_m128_n8192_k2048_kernel_trace.md"] = md_trace(
+        "Kernel trace: prefill GEMM, INT4 g128, M=128, N=8192, K=2048",
+        f"Run `trace_gemm` (`... -- python3 bench.py --only gemm`).  Kernel sources sha256[:16] = `{sha}`.  "
+        f"2*M*N*K = {2 * 128 * 8192 * 2048} flops per launch: "
+        f"{2 * 128 * 8192 * 2048 / (gemm['avg'] * 1e3) / 1e3:.1f} TFLOP/s at the average duration.", per_kernel(tg))
+    files["stream_read_6684672B_kernel_trace.md"] = md_trace(
+        "Kernel trace: streaming read of 6684672 bytes per launch (the decode weight bytes)",
+        f"Run `trace_stream` (`... -- python3 bench.py --only stream`): four grids (256, 512, 1024, 2048 "
+        f"workgroups) in turn, so the rows mix them; bench.py reports the best grid.  Best p10 "
+        f"{GEMV_BYTES / (stream['p10'] * 1e3):.1f} GB/s.", [("stream_read_kernel (all grids)", stream)])
+    for m, run in ((128, "trace_loop128"), (1, "trace_loop1")):
+        tl = trace(a.outdir, run)
+        files[f"loop_block_int4_g128_m{m}_d2048_f8192_kernel_trace.md"] = md_trace(
+            f"Kernel trace: looped shared block, INT4 g128, M={m}, D=2048, F=8192, L=8",
+            f"Run `{run}` (`... -- python3 bench.py --only loop --loop-m {m}`): the block resident (cache "
+            f"evicted before loop 1), warm, and with the cache evicted before every loop.  Kernel sources "
+            f"sha256[:16] = `{sha}`.", per_kernel(tl))
+
+    cal = calibration(a.outdir)
+    t_gemv = kernel_bytes(a.outdir, "main", "gemv", cal, GEMV_BYTES)
+    t_gemm = kernel_bytes(a.outdir, "gemm", "gemm_kernel", cal, GEMM_BYTES)
+    files["traffic.json"] = json.dumps(dict(kernel_src_sha=sha, calibration=cal, gemv_int4_m1=t_gemv,
+                                            gemm_int4_m128=t_gemm), indent=1) + "\n"
+    lm = {}
+    for m, leg, name in ((128, "loop128", "loop_block_int4_g128"), (1, "loop1", "loop_block_int4_g128_M1")):
+        lm[name] = loop_bytes(a.outdir, leg, cal)
+        lm[name]["weight_bytes_per_loop"] = 26738688
+    files["loop_traffic.json"] = json.dumps(dict(kernel_src_sha=sha, calibration=cal, **lm), indent=1) + "\n"
+
+    hdr = ["Commands (GPU host, repository root):", "", "```", PROFILE_CMD, SUMMARY_CMD, "```", "",
+           f"Kernel sources sha256[:16] = `{sha}` (bench.py reports these bytes only while kernels.hip has "
+           f"this hash).", "",
+           f"Calibration: a plain device copy of 512 MiB (`bench.py --only copy`, torch `copy_`) reads "
+           f"FETCH_SIZE = {cal['fetch_kib_per_copy']:.1f} KiB and WRITE_SIZE = {cal['write_kib_per_copy']:.1f} "
+           f"KiB per dispatch, so bytes = FETCH_SIZE x {cal['fetch_factor']} x 1024 and WRITE_SIZE x "
+           f"{cal['write_factor']} x 1024.", ""]
+    t = ["# HBM traffic counters (rocprofv3 --pmc), per dispatch", ""] + hdr + [
+        "| kernel | dispatches | FETCH_SIZE KiB (median) | WRITE_SIZE KiB (median) | calibrated bytes | "
+        "algorithmic weight bytes | ratio |", "|---|---|---|---|---|---|---|",
+        f"| GEMV (M=1, N=6144, K=2048, INT4 g128) | {t_gemv['dispatches']} | {t_gemv['fetch_kib_median']} | "
+        f"{t_gemv['write_kib_median']} | {t_gemv['bytes']} | {GEMV_BYTES} | {t_gemv['ratio']} |",
+        f"| GEMM (M=128, N=8192, K=2048, INT4 g128) | {t_gemm['dispatches']} | {t_gemm['fetch_kib_median']} | "
+        f"{t_gemm['write_kib_median']} | {t_gemm['bytes']} | {GEMM_BYTES} | {t_gemm['ratio']} |", ""]
+    files["hbm_traffic_counters.md"] = "\n".join(t) + "\n"
+    lt = ["# Looped shared block: HBM bytes per loop (rocprofv3 --pmc)", ""] + hdr + [
+        "Run `pmc_loop128_*` / `pmc_loop1_*` (`bench.py --only loop_prof`): the warm-up loop, an eviction, L=8 "
+        "loops back to back (loop 1 cold, loops 2..8 find the shared weights where loop 1 left them), then 8 "
+        "single loops each after an eviction (the control).  Bytes per loop = the calibrated FETCH_SIZE + "
+        "WRITE_SIZE of the loop's qGEMM dispatches; the shared weights are 26738688 bytes per loop.", "",
+        "| block | dispatches per loop | loop 1 (cold) | loops 2..8 (median) | evicted before every loop (median) "
+        "| loops 2..8 each |", "|---|---|---|---|---|---|"]
+    for name, v in lm.items():
+        lt.append(f"| {name} | {v['dispatches_per_loop']} | {v['loop1_bytes']} | {v['loops2_L_median_bytes']} | "
+                  f"{v['evict_each_loop_median_bytes']} | {', '.join(str(x) for x in v['resident_loop_bytes'][1:])} |")
+    files["loop_block_int4_g128_traffic.md"] = "\n".join(lt) + "\n"
+
+    mc = {}
+    for name in ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"):
+        mc[name] = float(np.median(select(counter(a.outdir, "pmc_gemm_mfma", name), "gemm_kernel")))
+    flops = 2 * 128 * 8192 * 2048
+    cycles = gemm["avg"] * 1e-6 * 2.4e9
+    busy = mc["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cycles)
+    files["gemm_int4_g128_m128_n8192_k2048_mfma_counters.md"] = "\n".join([
+        "# MFMA counters: prefill GEMM, INT4 g128, M=128, N=8192, K=2048 (rocprofv3 --pmc, per dispatch)", "",
+        "Commands (GPU host, repository root):", "", "```", PROFILE_CMD, SUMMARY_CMD, "```", "",
+        f"Run `pmc_gemm_mfma` (`rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+        f"GRBM_GUI_ACTIVE -- python3 bench.py --only gemm --steps 64 --warmup 8`).  Kernel sources sha256[:16] = "
+        f"`{sha}`; medians over the GEMM dispatches:", "",
+        "| counter | value | reading |", "|---|---|---|",
+        f"| SQ_INSTS_VALU_MFMA_MOPS_F16 | {mc['SQ_INSTS_VALU_MFMA_MOPS_F16']:.0f} | x 512 = "
+        f"{mc['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512:.4g} FLOP; 2*M*N*K = {flops:.4g} |",
+        f"| SQ_VALU_MFMA_BUSY_CYCLES | {mc['SQ_VALU_MFMA_BUSY_CYCLES']:.0f} | busy SIMD-cycles |",
+        f"| SQ_BUSY_CYCLES | {mc['SQ_BUSY_CYCLES']:.0f} | |",
+        f"| GRBM_GUI_ACTIVE | {mc['GRBM_GUI_ACTIVE']:.0f} | summed over the 8 XCDs |", "",
+        f"MFMA busy share = busy SIMD-cycles / (1024 SIMDs x the kernel's average duration in cycles at 2.4 GHz, "
+        f"{gemm['avg']} us from `trace_gemm`) = {100 * busy:.1f} %.", ""]) + "\n"
+
+    if a.write:
+        os.makedirs(a.write, exist_ok=True)
+        for n, txt in files.items():
+            open(os.path.join(a.write, n), "w").write(txt)
+            print("wrote", os.path.join(a.write, n))
+    else:
+        for n, txt in files.items():
+            print(f"---- {n}\n{txt}")
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -274,6 +274,38 @@ int qg_dequant(const uint32_t* packed, const uint16_t* scales, const uint16_t* z
  * Errors as qgemm. */
 int qg_plan(int M, int N, int K, int group, int fmt, int out[5]);
 
+/*
+ * Measurement helpers: the ceilings a qGEMM kernel is read against, taken on
+ * the device it runs on (the hot-op microbenchmarks of the TinyLoop README,
+ * "Validation", and the phase timings of its "Quick CLI Tour", "Benchmark").
+ * They are not on the qGEMM path.  Launches are asynchronous on `stream`
+ * (NULL: the default stream); the return code reports the launch only.
+ */
+
+/* Plain streaming read of `bytes` bytes at src (device, 16-byte aligned) by
+ * `workgroups` workgroups of 256 lanes, 16-byte non-temporal loads at a grid
+ * stride: the bandwidth one launch reaches over that many bytes.
+ *   sink [device, out] uint32 [workgroups]; written only in the (practically
+ *        impossible) case that the folded data equals a fixed constant.
+ * Errors: QG_E_ARG (NULL pointer, workgroups <= 0), QG_E_ALIGN, QG_E_DEVICE. */
+int qg_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, void* stream);
+
+/* An empty kernel of `workgroups` x `threads` (1..1024): the launch floor of
+ * that grid.  Errors: QG_E_ARG, QG_E_DEVICE. */
+int qg_empty_launch(int workgroups, int threads, void* stream);
+
+/* `iters` rounds of 16 independent v_mfma_f32_16x16x32_f16 (16*16*32*2 flops
+ * each) in every wave of `workgroups` workgroups of 4 waves: the sustained
+ * dense fp16 matrix rate.  out [device, out] float [workgroups * 256].
+ * Errors: QG_E_ARG, QG_E_DEVICE. */
+int qg_mfma_probe(float* out, int workgroups, int iters, void* stream);
+
+/* Compute units, shader clock (kHz), memory clock (kHz) and memory bus width
+ * (bits) of `device`, as the HIP runtime reports them.
+ * Errors: QG_E_ARG (NULL pointer), QG_E_DEVICE. */
+int qg_device_info(int device, int* compute_units, int* clock_khz, int* memory_clock_khz,
+                   int* memory_bus_bits);
+
 #ifdef __cplusplus
 }
 #endif

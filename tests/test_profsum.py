@@ -1,0 +1,98 @@
+"""The rocprofv3 summarizer on fabricated CSV files (no GPU): calibration
+against the plain copy, per-kernel medians, and the split of the looped
+block's dispatches into resident and evict-every-loop loops."""
+import csv
+import json
+import os
+
+import numpy as np
+import pytest
+
+from bit_weight_only_dequant_amd import profsum
+
+TRACE_COLS = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+PMC_COLS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+FILL = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<c10::Half> >"
+COPY = "void at::native::direct_copy_kernel_cuda(at::TensorIteratorBase&)"
+GEMM = "void qg::gemm_kernel<0, 4, 4, 8, 2, 4>(qg::GemmArgs)"
+GEMV = "void qg::gemv_half_kernel<0, 8, 2, 1>(qg::GemvArgs)"
+PACK = "qg::qpack_kernel(unsigned int const*, unsigned int*, int, int, int, int, long)"
+
+
+def write(path, cols, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def pmc(outdir, run, counter, seq):
+    rows = [dict(Dispatch_Id=i + 1, Kernel_Name=k, Counter_Name=counter, Counter_Value=v)
+            for i, (k, v) in enumerate(seq)]
+    write(os.path.join(outdir, run, "host", "1", f"{run}_counter_collection.csv"), PMC_COLS, rows)
+
+
+def trace(outdir, run, seq):
+    rows, t = [], 1000
+    for i, (k, d) in enumerate(seq):
+        rows.append(dict(Kind="KERNEL_DISPATCH", Dispatch_Id=i + 1, Kernel_Name=k, Start_Timestamp=t,
+                         End_Timestamp=t + d))
+        t += d + 500
+    write(os.path.join(outdir, run, "host", "1", f"{run}_kernel_trace.csv"), TRACE_COLS, rows)
+
+
+def test_calibration_and_kernel_bytes(tmp_path):
+    out = str(tmp_path)
+    kib = profsum.COPY_BYTES / 1024
+    pmc(out, "pmc_copy_FETCH_SIZE", "FETCH_SIZE", [(FILL, 0.0)] + [(COPY, kib / 2)] * 3)
+    pmc(out, "pmc_copy_WRITE_SIZE", "WRITE_SIZE", [(FILL, kib)] + [(COPY, kib)] * 3)
+    cal = profsum.calibration(out)
+    assert cal["fetch_factor"] == 2.0 and cal["write_factor"] == 1.0 and cal["copies"] == 3
+    pmc(out, "pmc_gemm_FETCH_SIZE", "FETCH_SIZE", [(PACK, 99.0), (GEMM, 4000.0), (GEMM, 5000.0), (GEMM, 6000.0)])
+    pmc(out, "pmc_gemm_WRITE_SIZE", "WRITE_SIZE", [(PACK, 99.0), (GEMM, 2048.0), (GEMM, 2048.0), (GEMM, 2048.0)])
+    t = profsum.kernel_bytes(out, "gemm", "gemm_kernel", cal, profsum.GEMM_BYTES)
+    assert t["dispatches"] == 3
+    assert t["bytes"] == 5000 * 1024 * 2 + 2048 * 1024
+
+
+def test_loop_split(tmp_path):
+    out = str(tmp_path)
+    cal = dict(fetch_factor=2.0, write_factor=1.0)
+    L, k = 8, 4
+    # repack kernels, the warm-up loop, eviction, L resident loops, then L x (eviction, one loop)
+    fetch = [(PACK, 1.0)] * 4 + [(GEMM, 10.0)] * k + [(COPY, 50.0), (FILL, 0.0)]
+    for i in range(L):
+        fetch += [(GEMM, 100.0 if i == 0 else 3.0)] * k
+    fetch.append((COPY, 50.0))
+    for i in range(L):
+        fetch += [(FILL, 0.0)] + [(GEMM, 100.0)] * k
+    write_seq = [(kname, 0.5 if "qg::gemm" in kname else 7.0) for kname, _ in fetch]
+    pmc(out, "pmc_loop128_FETCH_SIZE", "FETCH_SIZE", fetch)
+    pmc(out, "pmc_loop128_WRITE_SIZE", "WRITE_SIZE", write_seq)
+    r = profsum.loop_bytes(out, "loop128", cal, L=L)
+    per = lambda f: k * (f * 1024 * 2 + 0.5 * 1024)
+    assert r["dispatches_per_loop"] == k
+    assert r["loop1_bytes"] == int(per(100.0))
+    assert r["loops2_L_median_bytes"] == int(per(3.0))
+    assert r["evict_each_loop_bytes"] == [int(per(100.0))] * L
+
+
+def test_loop_split_rejects_a_bad_layout(tmp_path):
+    out = str(tmp_path)
+    seq = [(GEMM, 1.0)] * 4 + [(FILL, 0.0)] + [(GEMM, 1.0)] * 5
+    pmc(out, "pmc_x_FETCH_SIZE", "FETCH_SIZE", seq)
+    pmc(out, "pmc_x_WRITE_SIZE", "WRITE_SIZE", seq)
+    with pytest.raises(ValueError):
+        profsum.loop_bytes(out, "x", dict(fetch_factor=1.0, write_factor=1.0), L=8)
+
+
+def test_trace_stats(tmp_path):
+    out = str(tmp_path)
+    durs = list(range(1000, 11000, 1000))   # 1..10 us
+    trace(out, "trace_main", [(PACK, 5)] + [(GEMV, d) for d in durs])
+    items = profsum.trace(out, "trace_main")
+    s = profsum.stats_us(profsum.select(items, "gemv"))
+    assert s["n"] == 10 and s["avg"] == 5.5 and s["min"] == 1.0 and s["max"] == 10.0
+    assert s["p50"] == pytest.approx(float(np.percentile(np.arange(1, 11), 50)))
