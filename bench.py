@@ -63,9 +63,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=810)
     ap.add_argument("--warmup", type=int, default=81)
-    ap.add_argument("--only", choices=["all", "main", "gemm", "loop", "loop_prof", "fp16", "copy", "stream"],
+    ap.add_argument("--only", choices=["all", "main", "gemm", "loop", "loop_prof", "fp16", "copy", "stream", "floor"],
                     default="all",
-                    help="main/gemm/loop/fp16/stream: run one leg (for profiler runs); copy: the calibration "
+                    help="main/gemm/loop/fp16/stream/floor: run one leg (for profiler runs); copy: the calibration "
                          "copy; loop_prof: the looped block resident and with the cache evicted between loops")
     ap.add_argument("--loop-m", type=int, default=128, help="M of --only loop / loop_prof")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -265,7 +265,7 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
                    weight_GBps_evict_each_loop=round(wbytes / (ev_ms * 1e-3) / 1e9, 1))
     hb = load_loop_traffic(name)
     if hb is not None:
-        out["hbm_bytes_per_loop"] = hb   # counters (profiles/loop_traffic.json)
+        out["residency_counters"] = hb   # L2 fetch bytes and latency per loop (profiles/loop_traffic.json)
     return out
 
 
@@ -515,6 +515,10 @@ def main():
         return
     if args.only == "stream":
         print(json.dumps(stream_leg(qgm, torch, main_case.weight_bytes, args.steps, MAIN_REPLAYS)), flush=True)
+        return
+    if args.only == "floor":
+        pl = qgm.plan(1, main_case.N, main_case.K, main_case.group, main_case.fmt)
+        print(json.dumps(empty_floor(qgm, torch, pl["workgroups"], 512, args.steps, MAIN_REPLAYS)), flush=True)
         return
 
     leg = Leg(qgm, torch, main_case, 1)

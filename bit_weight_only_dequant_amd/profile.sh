@@ -33,6 +33,7 @@ timeout -k 10 300 python3 -c "import torch; print(torch.__version__)"
 step trace_main 300 --kernel-trace --stats -- --only main
 step trace_gemm 300 --kernel-trace --stats -- --only gemm
 step trace_stream 300 --kernel-trace --stats -- --only stream
+step trace_floor 300 --kernel-trace --stats -- --only floor
 step trace_loop128 300 --kernel-trace --stats -- --only loop --loop-m 128
 step trace_loop1 300 --kernel-trace --stats -- --only loop --loop-m 1
 step pmc_gemm_mfma 180 --pmc SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE \
@@ -43,5 +44,8 @@ for c in FETCH_SIZE WRITE_SIZE; do
   step "pmc_gemm_$c" 180 --pmc "$c" -- --only gemm --steps 64 --warmup 8
   step "pmc_loop128_$c" 180 --pmc "$c" -- --only loop_prof --loop-m 128
   step "pmc_loop1_$c" 180 --pmc "$c" -- --only loop_prof --loop-m 1
+done
+for m in 128 1; do   # L2-miss latency: in-flight reads accumulated per cycle, and their count
+  step "pmc_loop${m}_lat" 180 --pmc TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum -- --only loop_prof --loop-m "$m"
 done
 echo "profile runs complete: $OUT"

@@ -45,10 +45,18 @@ def _csv(outdir, run, suffix):
 
 
 def trace(outdir, run):
-    """(kernel name, duration ns) per dispatch, in dispatch order."""
+    """(kernel name, duration ns) per dispatch, in dispatch order; the name
+    carries the workgroup count when the trace has the grid columns."""
     rows = _csv(outdir, run, "kernel_trace.csv")
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-    return [(r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in rows]
+    out = []
+    for r in rows:
+        name = r["Kernel_Name"]
+        if r.get("Grid_Size_X") and r.get("Workgroup_Size_X"):
+            wg = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))) * int(r.get("Grid_Size_Y") or 1)
+            name = f"{name} [{wg} wg]"
+        out.append((name, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
 
 
 def counter(outdir, run, name):
@@ -92,33 +100,53 @@ def kernel_bytes(outdir, leg, key, cal, algo):
                 algorithmic_weight_bytes=algo, ratio=round((fb + wb) / algo, 3), dispatches=len(f))
 
 
+def loop_segments(outdir, run, name, L=8):
+    """Per-dispatch values of counter `name` in the loop_prof run `run`, split
+    at the eviction fills: (dispatches per loop k, the resident loops 1..L as
+    an L x k array, the L loops that each follow an eviction as L x k).  Only
+    the qGEMM kernels count, not the weight repack or torch's copies."""
+    seq = counter(outdir, run, name)
+    cur, segs = [], []
+    for k, v in seq:
+        if "Fill" in k:          # an eviction (torch fill of 512 MiB)
+            segs.append(cur)
+            cur = []
+        elif "qg::" in k and "pack" not in k:
+            cur.append(v)
+    segs.append(cur)
+    k = len(segs[0])                 # dispatches per loop (the warm-up loop)
+    if k == 0 or len(segs) != L + 2 or len(segs[1]) != L * k or any(len(x) != k for x in segs[2:]):
+        raise ValueError(f"unexpected dispatch layout in {run}: {[len(x) for x in segs]}")
+    return k, np.asarray(segs[1]).reshape(L, k), np.asarray(sum(segs[2:], [])).reshape(L, k)
+
+
 def loop_bytes(outdir, leg, cal, L=8):
-    """Per-loop calibrated bytes of the loop_prof run: qGEMM dispatches split
-    at the eviction fills into the warm-up loop, the resident loops 1..L and
-    the L loops that each follow an eviction."""
-    segs = []
-    for name, fac in (("FETCH_SIZE", cal["fetch_factor"]), ("WRITE_SIZE", cal["write_factor"])):
-        seq = counter(outdir, f"pmc_{leg}_{name}", name)
-        cur, out = [], []
-        for k, v in seq:
-            if "Fill" in k:          # an eviction (torch fill of 512 MiB)
-                out.append(cur)
-                cur = []
-            elif "qg::" in k and "pack" not in k:   # the qGEMM kernels, not the weight repack
-                cur.append(v * 1024 * fac)
-        out.append(cur)
-        segs.append(out)
-    (fs, ws) = segs
-    k = len(fs[0])                   # dispatches per loop (the warm-up loop)
-    if len(fs) != L + 2 or len(fs[1]) != L * k or any(len(s) != k for s in fs[2:]):
-        raise ValueError(f"unexpected dispatch layout in {leg}: {[len(s) for s in fs]}")
-    tot = [f + w for f, w in zip(np.concatenate(fs), np.concatenate(ws))]
-    tot = np.asarray(tot)
-    res = tot[k:k + L * k].reshape(L, k).sum(axis=1)
-    ctl = tot[k + L * k:].reshape(L, k).sum(axis=1)
+    """Per-loop calibrated FETCH_SIZE + WRITE_SIZE bytes of the loop_prof run:
+    what the L2 reads from and writes to the fabric (Infinity Cache or HBM)."""
+    k, fr, fc = loop_segments(outdir, f"pmc_{leg}_FETCH_SIZE", "FETCH_SIZE", L)
+    _, wr, wc = loop_segments(outdir, f"pmc_{leg}_WRITE_SIZE", "WRITE_SIZE", L)
+    res = ((fr * cal["fetch_factor"] + wr * cal["write_factor"]) * 1024).sum(axis=1)
+    ctl = ((fc * cal["fetch_factor"] + wc * cal["write_factor"]) * 1024).sum(axis=1)
     return dict(dispatches_per_loop=k, resident_loop_bytes=[int(v) for v in res],
                 loop1_bytes=int(res[0]), loops2_L_median_bytes=int(np.median(res[1:])),
                 evict_each_loop_bytes=[int(v) for v in ctl], evict_each_loop_median_bytes=int(np.median(ctl)))
+
+
+def loop_latency(outdir, leg, L=8):
+    """Average latency (L2 cycles) of the L2's read requests to the fabric per
+    loop, by Little's law: in-flight requests summed over cycles over the
+    number of requests.  Reads the Infinity Cache serves return sooner than
+    reads from HBM, so this tells the resident loops from the evicted ones."""
+    _, lr, lc = loop_segments(outdir, f"pmc_{leg}_lat", "TCC_EA0_RDREQ_LEVEL_sum", L)
+    _, qr, qc = loop_segments(outdir, f"pmc_{leg}_lat", "TCC_EA0_RDREQ_sum", L)
+    res = lr.sum(axis=1) / qr.sum(axis=1)
+    ctl = lc.sum(axis=1) / qc.sum(axis=1)
+    return dict(resident_loop_latency_cycles=[round(float(v), 1) for v in res],
+                loop1_latency_cycles=round(float(res[0]), 1),
+                loops2_L_median_latency_cycles=round(float(np.median(res[1:])), 1),
+                evict_each_loop_latency_cycles=[round(float(v), 1) for v in ctl],
+                evict_each_loop_median_latency_cycles=round(float(np.median(ctl)), 1),
+                read_requests_per_loop=int(np.median(qr.sum(axis=1))))
 
 
 def md_trace(title, cmd_note, rows):
@@ -130,7 +158,12 @@ def md_trace(title, cmd_note, rows):
 
 
 def short(name):
-    return name.replace("(qg::GemvArgs)", "").replace("(qg::GemmArgs)", "").replace("void ", "")[:90]
+    """Kernel name without its parameter list, keeping the workgroup count."""
+    base, _, grid = name.partition(" [")
+    base = base.replace("void ", "").replace("(anonymous namespace)::", "")
+    if "(" in base:
+        base = base[:base.index("(")]
+    return base + (f" [{grid}" if grid else "")
 
 
 def per_kernel(items):
@@ -152,11 +185,19 @@ def main():
     tm = trace(a.outdir, "trace_main")
     tg = trace(a.outdir, "trace_gemm")
     ts = trace(a.outdir, "trace_stream")
+    tf = trace(a.outdir, "trace_floor")
     gemv = stats_us(select(tm, "gemv"))
     gemm = stats_us(select(tg, "gemm_kernel"))
-    stream = stats_us(select(ts, "stream_read"))
+    empty = stats_us(select(tf, "empty_kernel"))
     files["dispatch.json"] = json.dumps(dict(kernel_src_sha=sha, gemv_int4_m1=gemv, gemm_int4_m128=gemm,
-                                             stream_read_decode_bytes=stream), indent=1) + "\n"
+                                             empty_kernel=empty), indent=1) + "\n"
+    files["empty_kernel_launch_floor_kernel_trace.md"] = md_trace(
+        "Kernel trace: the empty kernel of the decode GEMV's grid (768 x 512), graph-replayed",
+        "Run `trace_floor` (`... -- python3 bench.py --only floor`): bench.py times the same graph at its "
+        "launch floor per step; the traced duration of each dispatch also carries what the profiler adds "
+        "to every dispatch, the same for every kernel of the other traces.",
+        [(short(n), stats_us([d for k, d in tf if k == n])) for n in dict.fromkeys(k for k, _ in tf)
+         if "empty_kernel" in n])
     files["gemv_int4_g128_m1_n6144_k2048_kernel_trace.md"] = md_trace(
         "Kernel trace: decode GEMV, INT4 g128, M=1, N=6144, K=2048",
         f"Run `trace_main` (`rocprofv3 --kernel-trace --stats -- python3 bench.py --only main`): every dispatch "
@@ -171,8 +212,9 @@ def main():
     files["stream_read_6684672B_kernel_trace.md"] = md_trace(
         "Kernel trace: streaming read of 6684672 bytes per launch (the decode weight bytes)",
         f"Run `trace_stream` (`... -- python3 bench.py --only stream`): four grids (256, 512, 1024, 2048 "
-        f"workgroups) in turn, so the rows mix them; bench.py reports the best grid.  Best p10 "
-        f"{GEMV_BYTES / (stream['p10'] * 1e3):.1f} GB/s.", [("stream_read_kernel (all grids)", stream)])
+        f"workgroups) in turn; one row per grid.",
+        [(short(n), stats_us([d for k, d in ts if k == n])) for n in dict.fromkeys(k for k, _ in ts)
+         if "stream_read" in n])
     for m, run in ((128, "trace_loop128"), (1, "trace_loop1")):
         tl = trace(a.outdir, run)
         files[f"loop_block_int4_g128_m{m}_d2048_f8192_kernel_trace.md"] = md_trace(
@@ -189,6 +231,7 @@ def main():
     lm = {}
     for m, leg, name in ((128, "loop128", "loop_block_int4_g128"), (1, "loop1", "loop_block_int4_g128_M1")):
         lm[name] = loop_bytes(a.outdir, leg, cal)
+        lm[name].update(loop_latency(a.outdir, leg))
         lm[name]["weight_bytes_per_loop"] = 26738688
     files["loop_traffic.json"] = json.dumps(dict(kernel_src_sha=sha, calibration=cal, **lm), indent=1) + "\n"
 
@@ -207,16 +250,28 @@ def main():
         f"| GEMM (M=128, N=8192, K=2048, INT4 g128) | {t_gemm['dispatches']} | {t_gemm['fetch_kib_median']} | "
         f"{t_gemm['write_kib_median']} | {t_gemm['bytes']} | {GEMM_BYTES} | {t_gemm['ratio']} |", ""]
     files["hbm_traffic_counters.md"] = "\n".join(t) + "\n"
-    lt = ["# Looped shared block: HBM bytes per loop (rocprofv3 --pmc)", ""] + hdr + [
-        "Run `pmc_loop128_*` / `pmc_loop1_*` (`bench.py --only loop_prof`): the warm-up loop, an eviction, L=8 "
+    lt = ["# Looped shared block: L2 fabric bytes and L2-miss latency per loop (rocprofv3 --pmc)", ""] + hdr + [
+        "Runs `pmc_loop128_*` / `pmc_loop1_*` (`bench.py --only loop_prof`): the warm-up loop, an eviction, L=8 "
         "loops back to back (loop 1 cold, loops 2..8 find the shared weights where loop 1 left them), then 8 "
-        "single loops each after an eviction (the control).  Bytes per loop = the calibrated FETCH_SIZE + "
-        "WRITE_SIZE of the loop's qGEMM dispatches; the shared weights are 26738688 bytes per loop.", "",
-        "| block | dispatches per loop | loop 1 (cold) | loops 2..8 (median) | evicted before every loop (median) "
-        "| loops 2..8 each |", "|---|---|---|---|---|---|"]
+        "single loops each after an eviction (the control).  Per loop, over its qGEMM dispatches:", "",
+        "- bytes = calibrated FETCH_SIZE + WRITE_SIZE: what the L2s read from and write to the fabric.  The "
+        "L2s keep nothing from one kernel to the next, so this is the same in every loop; whether the "
+        "Infinity Cache (256 MB, behind the L2s) or HBM serves those reads the counter cannot tell;",
+        "- latency = TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum (run `pmc_loop*_lat`): the average time, in "
+        "L2 cycles, that the L2's read requests to the fabric are in flight.  Reads the Infinity Cache "
+        "serves return sooner than reads from HBM, so the resident loops against the control show where "
+        "the shared weights are read from.", "",
+        "The shared weights are 26738688 bytes per loop.", "",
+        "| block | dispatches per loop | bytes loop 1 | bytes loops 2..8 (median) | bytes, evicted before every "
+        "loop (median) | latency loop 1 | latency loops 2..8 (median) | latency, evicted before every loop "
+        "(median) |", "|---|---|---|---|---|---|---|---|"]
     for name, v in lm.items():
         lt.append(f"| {name} | {v['dispatches_per_loop']} | {v['loop1_bytes']} | {v['loops2_L_median_bytes']} | "
-                  f"{v['evict_each_loop_median_bytes']} | {', '.join(str(x) for x in v['resident_loop_bytes'][1:])} |")
+                  f"{v['evict_each_loop_median_bytes']} | {v['loop1_latency_cycles']} | "
+                  f"{v['loops2_L_median_latency_cycles']} | {v['evict_each_loop_median_latency_cycles']} |")
+    lt += ["", "Latency of each loop (resident run, loops 1..8; then the control):", ""]
+    for name, v in lm.items():
+        lt.append(f"- {name}: {v['resident_loop_latency_cycles']}; control {v['evict_each_loop_latency_cycles']}")
     files["loop_block_int4_g128_traffic.md"] = "\n".join(lt) + "\n"
 
     mc = {}

@@ -79,6 +79,26 @@ def test_loop_split(tmp_path):
     assert r["evict_each_loop_bytes"] == [int(per(100.0))] * L
 
 
+def test_loop_latency(tmp_path):
+    out = str(tmp_path)
+    L, k = 8, 4
+    lev, req = [(GEMM, 1.0)] * k + [(FILL, 0.0)], [(GEMM, 1.0)] * k + [(FILL, 0.0)]
+    for i in range(L):   # resident: 200 cycles in loops 2..8, 900 in loop 1
+        lev += [(GEMM, (900.0 if i == 0 else 200.0) * 10)] * k
+        req += [(GEMM, 10.0)] * k
+    for i in range(L):   # control: 800 cycles
+        lev += [(FILL, 0.0)] + [(GEMM, 8000.0)] * k
+        req += [(FILL, 0.0)] + [(GEMM, 10.0)] * k
+    rows = [dict(Dispatch_Id=i + 1, Kernel_Name=kn, Counter_Name=c, Counter_Value=v)
+            for c, seq in (("TCC_EA0_RDREQ_LEVEL_sum", lev), ("TCC_EA0_RDREQ_sum", req))
+            for i, (kn, v) in enumerate(seq)]
+    write(os.path.join(out, "pmc_loop1_lat", "h", "1", "x_counter_collection.csv"), PMC_COLS, rows)
+    r = profsum.loop_latency(out, "loop1", L=L)
+    assert r["loop1_latency_cycles"] == 900.0
+    assert r["loops2_L_median_latency_cycles"] == 200.0
+    assert r["evict_each_loop_median_latency_cycles"] == 800.0
+
+
 def test_loop_split_rejects_a_bad_layout(tmp_path):
     out = str(tmp_path)
     seq = [(GEMM, 1.0)] * 4 + [(FILL, 0.0)] + [(GEMM, 1.0)] * 5
