@@ -247,6 +247,28 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
             ev[-1].synchronize()
             per.append(ev[0].elapsed_time(ev[1]))
         res["evict"] = per
+    if M == 1:   # the same loops as one launch each, grid barriers between the four GEMVs
+        status = torch.zeros(4, dtype=torch.int32, device="cuda")
+        qgm.loop_block_persistent(x, lins, 1, scratch=scratch, status=status)   # warm-up
+        for mode in ("cold", "evict"):
+            x.copy_(x0)
+            per = []
+            if mode == "cold":
+                evict(torch)
+                events = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+                qgm.loop_block_persistent(x, lins, L, scratch=scratch, status=status, events=events)
+                events[-1].synchronize()
+                per = [events[i].elapsed_time(events[i + 1]) for i in range(L)]
+            else:
+                for _ in range(L):
+                    evict(torch)
+                    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                    qgm.loop_block_persistent(x, lins, 1, scratch=scratch, status=status, events=ev)
+                    ev[-1].synchronize()
+                    per.append(ev[0].elapsed_time(ev[1]))
+            if int(status[0]) != 0:
+                raise RuntimeError("qloop_block_persistent: a grid barrier gave up")
+            res["persistent_" + mode] = per
     wbytes = sum(l.weight_bytes for l in lins)
     flops = 2.0 * M * (D * 3 * D + D * D + D * F + F * D)
     cold, warm = res["cold"], res["warm"]
@@ -263,6 +285,12 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
         out.update(evict_each_loop_ms=[round(v, 4) for v in res["evict"]],
                    evict_each_loop_median_ms=round(ev_ms, 4),
                    weight_GBps_evict_each_loop=round(wbytes / (ev_ms * 1e-3) / 1e9, 1))
+    if "persistent_cold" in res:
+        pc, pe = res["persistent_cold"], res["persistent_evict"]
+        out.update(persistent_cold_loop_ms=[round(v, 4) for v in pc],
+                   persistent_loop1_cold_ms=round(pc[0], 4),
+                   persistent_loops2_L_ms=round(float(np.median(pc[1:])), 4),
+                   persistent_evict_each_loop_median_ms=round(float(np.median(pe)), 4))
     hb = load_loop_traffic(name)
     if hb is not None:
         out["residency_counters"] = hb   # L2 fetch bytes and latency per loop (profiles/loop_traffic.json)

@@ -59,6 +59,7 @@ _SIGS = {
     "qg_plan": ([_I, _I, _I, _I, _I, ctypes.POINTER(_I)], _I),
     "qg_classify_pointer": ([_I, _I, _I, _I], _I),
     "qgemm_noalloc": ([_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P], _I),
+    "qloop_block_persistent": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "qg_stream_read": ([_P, _SZ, _P, _I, _P], _I),
     "qg_empty_launch": ([_I, _I, _P], _I),
     "qg_mfma_probe": ([_P, _I, _I, _P], _I),
@@ -363,8 +364,8 @@ class QuantLinear:
                      out=out, residual=residual, workspace=workspace, stream=stream)
 
 
-def loop_block(x, linears: Sequence[QuantLinear], L: int, scratch=None, events=None, stream=None):
-    """Run the looped shared block in place on x (fp16 [M, D]); see qloop_block."""
+def _loop_args(x, linears, L, scratch, events, stream):
+    """Checked arguments of qloop_block / qloop_block_persistent."""
     torch = _torch()
     _dev(x, "x")
     qkv, o, up, down = linears
@@ -402,10 +403,35 @@ def loop_block(x, linears: Sequence[QuantLinear], L: int, scratch=None, events=N
             else:
                 handles.append(e)
         ev = (ctypes.c_void_p * (L + 1))(*handles)
-    st = _lib.qloop_block(_ptr(x), packed4, scales4, zeros4, M, D, F, group, fmt, L, _ptr(scratch),
-                          ev, _stream(x.device, stream))
+    return (packed4, scales4, zeros4, M, D, F, group, fmt, scratch, ev, _stream(x.device, stream))
+
+
+def loop_block(x, linears: Sequence[QuantLinear], L: int, scratch=None, events=None, stream=None):
+    """Run the looped shared block in place on x (fp16 [M, D]); see qloop_block."""
+    packed4, scales4, zeros4, M, D, F, group, fmt, scratch, ev, st_ = _loop_args(x, linears, L, scratch, events,
+                                                                                  stream)
+    st = _lib.qloop_block(_ptr(x), packed4, scales4, zeros4, M, D, F, group, fmt, L, _ptr(scratch), ev, st_)
     _check(st, "qloop_block")
     return x
+
+
+def loop_block_persistent(x, linears: Sequence[QuantLinear], L: int, scratch=None, status=None, events=None,
+                          stream=None):
+    """The looped shared block at M = 1 with one launch per loop (grid
+    barriers between the four GEMVs); see qloop_block_persistent.  Returns
+    (x, status): status is an int32 device tensor, 0 once the loops completed
+    and 1 if a barrier stopped waiting (read it after synchronizing)."""
+    torch = _torch()
+    packed4, scales4, zeros4, M, D, F, group, fmt, scratch, ev, st_ = _loop_args(x, linears, L, scratch, events,
+                                                                                  stream)
+    if status is None:
+        status = torch.zeros(4, dtype=torch.int32, device=x.device)
+    elif status.dtype != torch.int32 or status.device != x.device:
+        raise ValueError("status must be an int32 tensor on x's device")
+    st = _lib.qloop_block_persistent(_ptr(x), packed4, scales4, zeros4, M, D, F, group, fmt, L, _ptr(scratch),
+                                     _ptr(status), ev, st_)
+    _check(st, "qloop_block_persistent")
+    return x, status
 
 
 # ----------------------------------------------------------------------------

@@ -48,7 +48,7 @@ int classify_pointer(int hip_rc, int memory_type, int ptr_device, int current_de
   }
 }
 
-static int env_int(const char* name, int dflt) {
+int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
   return atoi(v);

@@ -91,6 +91,7 @@ int launch_call(const Call& c, const Plan& p, float* ws, void* stream);
 int call_pointers_ok(const Call& c);
 int current_device(int* dev);          // QG_OK when a HIP device is current
 int hip_status(int hip_error);         // QG_OK, or QG_E_DEVICE (and records the error)
+int env_int(const char* name, int dflt);   // integer environment setting (tuning, tests)
 void clear_pending_error();
 
 }  // namespace qg

@@ -555,8 +555,22 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
 // wave's run -- one 16-byte load per lane and pair, as gemv_kernel.  Same
 // dequant and dot products (MMAX rows of x share each exact (q - z) pair; q4k
 // as in gemv_kernel); lanes sum over g and t, the waves through LDS in wave order.
-template <int FMT, int NW, int TPW, int MMAX>
-__global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
+// LDS bytes of gemv_half_body: per wave its x rows, (scale, zero) pairs and
+// (q4k) run sums of x, then NW x MMAX x 16 fp32 for the sum over the waves
+template <int FMT, int NW, int TPW, int MMAX> constexpr size_t gemv_half_lds_bytes() {
+  using F = Fmt<FMT>;
+  constexpr int KW = TPW * F::KT;
+  constexpr int WB = MMAX * KW * 2 + 8 * (KW / 32) * (F::KQ ? 8 : 4) + (F::KQ ? MMAX * (KW / 8) * 4 : 0);
+  return (size_t)NW * WB + (size_t)NW * MMAX * 16 * sizeof(float);
+}
+
+// One half row block (bx: row block bx / 2, half bx % 2) and K split `by` of
+// the decode GEMV, by a workgroup of NW waves, in half_smem
+// (gemv_half_lds_bytes); the kernel below and the persistent looped block
+// both run it.  COHERENT: the outputs are stored with agent scope (written
+// through to the level every XCD reads), for readers in the same launch.
+template <int FMT, int NW, int TPW, int MMAX, bool COHERENT = false>
+__device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by, uint8_t* half_smem) {
   using F = Fmt<FMT>;
   static_assert(TPW % 2 == 0, "tiles go in pairs");
   constexpr int NP = TPW / 2;                  // tile pairs per wave
@@ -569,7 +583,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   constexpr int XB = MMAX * KW * 2, SB = 8 * GWMAX * SZB;
   constexpr int XR = KW / 8;                   // q4k: 8-wide runs per row of the wave's range
   constexpr int WB = XB + SB + (F::KQ ? MMAX * XR * 4 : 0);
-  __shared__ __align__(16) uint8_t half_smem[NW * WB + NW * MMAX * 16 * sizeof(float)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f16* xs = reinterpret_cast<f16*>(half_smem + wave * WB);                 // [MMAX][KW]
@@ -578,7 +591,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   float* xsum = reinterpret_cast<float*>(half_smem + wave * WB + XB + SB); // q4k: [MMAX][XR]
   float* red = reinterpret_cast<float*>(half_smem + NW * WB);              // [NW][MMAX][2][8]
   const int r8 = lane & 7, g = (lane >> 3) & 3, t = lane >> 5;
-  const int rb = blockIdx.x >> 1, hb = blockIdx.x & 1, split = blockIdx.y;
+  const int rb = bx >> 1, hb = bx & 1, split = by;
   const int row0 = rb * 16 + hb * 8;
   const int T0 = split * a.tps, T1 = min(a.wordtiles, T0 + a.tps);
   const int wt0 = T0 + wave * TPW;
@@ -730,12 +743,101 @@ __global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
   if (tid & 8) return;
   const int on = row0 + (tid & 7);
   if (a.splits == 1) {
-    if (om < a.M && on < a.N)
-      a.y[(int64_t)om * a.ldy + on] = (f16)(total + (float)__builtin_bit_cast(f16, (uint16_t)res));
+    if (om < a.M && on < a.N) {
+      const f16 v = (f16)(total + (float)__builtin_bit_cast(f16, (uint16_t)res));
+      if constexpr (COHERENT)
+        __hip_atomic_store(reinterpret_cast<unsigned short*>(a.y) + (int64_t)om * a.ldy + on,
+                           __builtin_bit_cast(unsigned short, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        a.y[(int64_t)om * a.ldy + on] = v;
+    }
     return;
   }
   // split-K: the same partial layout as gemv_kernel with MMAX rows of x
   a.ws[((int64_t)rb * a.splits + split) * MMAX * 16 + om * 16 + hb * 8 + (tid & 7)] = total;
+}
+
+template <int FMT, int NW, int TPW, int MMAX>
+__global__ __launch_bounds__(NW * 64) void gemv_half_kernel(GemvArgs a) {
+  __shared__ __align__(16) uint8_t half_smem[gemv_half_lds_bytes<FMT, NW, TPW, MMAX>()];
+  gemv_half_body<FMT, NW, TPW, MMAX>(a, blockIdx.x, blockIdx.y, half_smem);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent looped block at M = 1: one launch per loop runs the loop's four
+// GEMVs (QKV, O + x, up, down + h) as phases over half row blocks, the
+// workgroups of a co-resident grid taking blocks round robin, with a grid
+// barrier between phases -- the shared-block loop of the TinyLoop README
+// ("Why TinyLoop Exists"; "Status", on the weights staying cache-resident
+// across the L iterations), without the three kernel boundaries per loop.
+
+struct LoopArgs {
+  GemvArgs lin[4];
+  unsigned* counter;   // arrivals, zeroed before the call's first loop
+  int* status;         // set to 1 when a barrier gives up waiting
+  int barrier0;        // barriers passed before this loop (3 per loop)
+  int cap;             // polls before a barrier gives up
+};
+
+// Barrier of all workgroups of the grid through arrival counters that only
+// grow: the b-th barrier of the call waits until they sum to
+// (b + 1) * gridDim.x.  Workgroup w arrives at counter w % 8 -- eight 128-byte
+// lines, so arrivals do not all queue on one address.  The phases store their
+// outputs with agent scope, visible to every XCD once complete: every wave
+// waits for its own memory operations, then thread 0 arrives and polls
+// (relaxed, agent scope) with sleeps.  A phase's inputs were produced earlier
+// in the same launch and never read before them in it (the launch begins with
+// clean caches), so no cache holds a stale copy and no cache maintenance is
+// needed.  After `cap` polls, or once another workgroup has given up, thread
+// 0 records the failure in *status and stops waiting, so the kernel always
+// ends.
+constexpr int LOOP_COUNTERS = 8, LOOP_COUNTER_STRIDE = 32;   // uint32 apart
+
+__device__ __forceinline__ void grid_barrier(unsigned* counter, unsigned target, int* status, int cap) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(counter + LOOP_COUNTER_STRIDE * (blockIdx.x % LOOP_COUNTERS), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    int polls = 0;
+    while (true) {
+      unsigned arrived = 0;
+#pragma unroll
+      for (int i = 0; i < LOOP_COUNTERS; ++i)
+        arrived += __hip_atomic_load(counter + LOOP_COUNTER_STRIDE * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (arrived >= target) break;
+      if (polls++ >= cap || __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+constexpr int LOOP_THREADS = 512;   // 8 waves, as the 8-row GEMV
+
+// TA word tiles per wave for the K = D linears (QKV, O, up), TB for down (K = F)
+template <int FMT, int TA, int TB>
+__global__ __launch_bounds__(LOOP_THREADS) void loop_block_kernel(LoopArgs p) {
+  constexpr size_t LA = gemv_half_lds_bytes<FMT, 8, TA, 1>(), LB = gemv_half_lds_bytes<FMT, 8, TB, 1>();
+  __shared__ __align__(16) uint8_t smem[LA > LB ? LA : LB];
+#pragma unroll
+  for (int ph = 0; ph < 4; ++ph) {
+    const int nb = 2 * p.lin[ph].rowblocks;
+    for (int vb = blockIdx.x; vb < nb; vb += gridDim.x) {
+      if (ph < 3) gemv_half_body<FMT, 8, TA, 1, true>(p.lin[ph], vb, 0, smem);
+      else gemv_half_body<FMT, 8, TB, 1, true>(p.lin[ph], vb, 0, smem);
+      __syncthreads();   // smem is reused by the next block
+    }
+    if (ph < 3) grid_barrier(p.counter, (unsigned)(p.barrier0 + ph + 1) * gridDim.x, p.status, p.cap);
+  }
+}
+
+__global__ void loop_reset_kernel(unsigned* counter, int* status) {
+  for (int i = 0; i < LOOP_COUNTERS; ++i) counter[LOOP_COUNTER_STRIDE * i] = 0u;
+  *status = 0;
 }
 
 // LDS bytes of gemv_mfma_kernel: per wave its x rows (padded by 16 bytes so
@@ -1876,9 +1978,17 @@ int qgemm_ex(const uint16_t* x, int ldx, const uint32_t* packed, const uint16_t*
   return run_qgemm(c, workspace, ws_bytes, stream);
 }
 
-int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
-                const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt, int L,
-                uint16_t* scratch, void* const* events, void* stream) {
+// The four calls of a loop of the shared block (QKV, O + x, up, down + h),
+// validated with their plans and workspace size; nothing is launched.
+struct LoopSetup {
+  Call calls[4];
+  Plan plans[4];
+  size_t ws_need = 0;
+};
+
+static int loop_setup(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
+                      const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt, int L,
+                      uint16_t* scratch, LoopSetup* ls) {
   if (!packed4 || !scales4 || !zeros4 || L < 0 || D <= 0 || F <= 0 || M < 0) return QG_E_ARG;
   if (M > 0 && (!x || !scratch)) return QG_E_ARG;
   if (check_align(scratch) != QG_OK || check_align(x) != QG_OK) return QG_E_ALIGN;
@@ -1887,52 +1997,193 @@ int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* con
   uint16_t* qkv = scratch;
   uint16_t* h = qkv + (int64_t)M * D3;
   uint16_t* u = h + (int64_t)M * D;
-  // the four calls of a loop, validated (and their workspace obtained) before
-  // anything is recorded or launched
   const Call calls[4] = {
       {x, D, packed4[0], scales4[0], zeros4[0], nullptr, 0, M, (int)D3, D, group, fmt, qkv, (int)D3},
       {qkv + 2 * (int64_t)D, (int)D3, packed4[1], scales4[1], zeros4[1], x, D, M, D, D, group, fmt, h, D},
       {h, D, packed4[2], scales4[2], zeros4[2], nullptr, 0, M, F, D, group, fmt, u, F},
       {u, F, packed4[3], scales4[3], zeros4[3], h, D, M, D, F, group, fmt, x, D}};
-  Plan plans[4];
-  size_t ws_need = 0;
   for (int i = 0; i < 4; ++i) {
-    const int st = validate_call(calls[i], &plans[i]);
+    ls->calls[i] = calls[i];
+    const int st = validate_call(calls[i], &ls->plans[i]);
     if (st != QG_OK) return st;
-    ws_need = std::max(ws_need, plans[i].ws_bytes());
+    ls->ws_need = std::max(ls->ws_need, ls->plans[i].ws_bytes());
   }
-  if (M == 0 || L == 0) {
-    if (events) {   // still time-stamp the (empty) loops
-      hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-      for (int l = 0; l <= L; ++l)
-        if (events[l] && hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[l]), s)) != QG_OK)
-          return QG_E_DEVICE;
-    }
+  return QG_OK;
+}
+
+static int record_event(void* const* events, int i, hipStream_t s) {
+  if (events && events[i] && hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s)) != QG_OK)
+    return QG_E_DEVICE;
+  return QG_OK;
+}
+
+int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
+                const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt, int L,
+                uint16_t* scratch, void* const* events, void* stream) {
+  // the four calls of a loop, validated (and their workspace obtained) before
+  // anything is recorded or launched
+  LoopSetup ls;
+  int st = loop_setup(x, packed4, scales4, zeros4, M, D, F, group, fmt, L, scratch, &ls);
+  if (st != QG_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (M == 0 || L == 0) {   // still time-stamp the (empty) loops
+    for (int l = 0; l <= L; ++l)
+      if (record_event(events, l, s) != QG_OK) return QG_E_DEVICE;
     return QG_OK;
   }
   int dev = 0;
-  int st = current_device(&dev);
+  st = current_device(&dev);
   if (st != QG_OK) return st;
   for (int i = 0; i < 4; ++i) {
-    st = call_pointers_ok(calls[i]);
+    st = call_pointers_ok(ls.calls[i]);
     if (st != QG_OK) return st;
   }
   void* ws = nullptr;
-  if (ws_need > 0) {
-    st = library_ws(dev, ws_need, &ws);
+  if (ls.ws_need > 0) {
+    st = library_ws(dev, ls.ws_need, &ws);
     if (st != QG_OK) return st;
   }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (events && events[0] && hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[0]), s)) != QG_OK)
-    return QG_E_DEVICE;
+  if (record_event(events, 0, s) != QG_OK) return QG_E_DEVICE;
   for (int l = 0; l < L; ++l) {
     for (int i = 0; i < 4; ++i) {
-      st = launch_call(calls[i], plans[i], reinterpret_cast<float*>(ws), s);
+      st = launch_call(ls.calls[i], ls.plans[i], reinterpret_cast<float*>(ws), s);
       if (st != QG_OK) return st;
     }
-    if (events && events[l + 1] &&
-        hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[l + 1]), s)) != QG_OK)
-      return QG_E_DEVICE;
+    if (record_event(events, l + 1, s) != QG_OK) return QG_E_DEVICE;
+  }
+  return QG_OK;
+}
+
+// --- the persistent looped block ------------------------------------------
+
+static std::vector<unsigned*> g_loop_counter;   // per device, kept until the process ends
+
+static int loop_counter(int dev, unsigned** out) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if ((int)g_loop_counter.size() <= dev) g_loop_counter.resize(dev + 1, nullptr);
+  if (!g_loop_counter[dev]) {
+    void* p = nullptr;
+    if (hipMalloc(&p, LOOP_COUNTERS * LOOP_COUNTER_STRIDE * sizeof(unsigned)) != hipSuccess) {
+      clear_pending_error();
+      return QG_E_NOMEM;
+    }
+    g_loop_counter[dev] = reinterpret_cast<unsigned*>(p);
+  }
+  *out = g_loop_counter[dev];
+  return QG_OK;
+}
+
+// word tiles per wave (2, 4 or 8) for 8 waves over `wordtiles`, 0 if more
+static int loop_tpw(int64_t wordtiles) {
+  for (int t = 2; t <= 8; t *= 2)
+    if (8 * t >= wordtiles) return t;
+  return 0;
+}
+
+extern "C++" {
+template <int FMT>
+static const void* loop_kernel_for(int ta, int tb) {
+  if (ta == 2 && tb == 2) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 2, 2>);
+  if (ta == 2 && tb == 4) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 2, 4>);
+  if (ta == 2 && tb == 8) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 2, 8>);
+  if (ta == 4 && tb == 4) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 4, 4>);
+  if (ta == 4 && tb == 8) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 4, 8>);
+  if (ta == 8 && tb == 8) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 8, 8>);
+  return nullptr;
+}
+}  // extern "C++"
+
+static const void* loop_kernel(int fmt, int ta, int tb) {
+  switch (fmt) {
+    case QG_INT4_ASYM: return loop_kernel_for<INT4_ASYM>(ta, tb);
+    case QG_INT2_ASYM: return loop_kernel_for<INT2_ASYM>(ta, tb);
+    case QG_Q4_0: return loop_kernel_for<Q4_0>(ta, tb);
+    case QG_Q4K: return loop_kernel_for<Q4K>(ta, tb);
+    default: return nullptr;
+  }
+}
+
+int qloop_block_persistent(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
+                           const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt, int L,
+                           uint16_t* scratch, int* status, void* const* events, void* stream) {
+  LoopSetup ls;
+  int st = loop_setup(x, packed4, scales4, zeros4, M, D, F, group, fmt, L, scratch, &ls);
+  if (st != QG_OK) return st;
+  if (!status) return QG_E_ARG;
+  if (check_align(status) != QG_OK) return QG_E_ALIGN;
+  if (M != 1) return QG_E_UNSUPPORTED;
+  const int ta = loop_tpw(ls.plans[0].wordtiles), tb = loop_tpw(ls.plans[3].wordtiles);
+  for (int i = 0; i < 3; ++i)
+    if (ls.plans[i].wordtiles != ls.plans[0].wordtiles) return QG_E_UNSUPPORTED;
+  const void* fn = ta && tb ? loop_kernel(fmt, ta, tb) : nullptr;
+  if (!fn) return QG_E_UNSUPPORTED;
+  int dev = 0;
+  st = current_device(&dev);
+  if (st != QG_OK) return st;
+  for (int i = 0; i < 4; ++i) {
+    st = call_pointers_ok(ls.calls[i]);
+    if (st != QG_OK) return st;
+  }
+  const void* sp[1] = {status};
+  st = check_device_pointers(sp, 1);
+  if (st != QG_OK) return st;
+  // the grid: one workgroup per compute unit (measured fastest: the barrier's
+  // cost grows with the workgroup count faster than the phases shrink), never
+  // more than are resident together, nor more than the widest phase's half
+  // row blocks.  A plain launch: a cooperative one measured about 16 us more
+  // per loop; if other work keeps some workgroups from starting, the bounded
+  // waits end the kernel and *status reports it.
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, LOOP_THREADS, 0) != hipSuccess || per_cu < 1) {
+    clear_pending_error();
+    return QG_E_DEVICE;
+  }
+  int64_t widest = 0;
+  for (int i = 0; i < 4; ++i) widest = std::max<int64_t>(widest, 2 * (int64_t)ls.plans[i].rowblocks);
+  int64_t grid = std::min<int64_t>(std::min<int64_t>((int64_t)per_cu * cus, cus), widest);
+  const int grid_env = env_int("QGEMM_LOOP_GRID", 0);
+  if (grid_env > 0) grid = std::min<int64_t>(grid, grid_env);
+  if ((int64_t)3 * L * grid >= (int64_t)UINT_MAX) return QG_E_UNSUPPORTED;   // the counter's range
+  unsigned* counter = nullptr;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (L > 0) {
+    st = loop_counter(dev, &counter);
+    if (st != QG_OK) return st;
+  }
+  if (record_event(events, 0, s) != QG_OK) return QG_E_DEVICE;
+  if (L == 0) return QG_OK;
+  hipLaunchKernelGGL(loop_reset_kernel, dim3(1), dim3(1), 0, s, counter, status);
+  st = launch_status();
+  if (st != QG_OK) return st;
+  LoopArgs la;
+  for (int i = 0; i < 4; ++i) {
+    const Call& c = ls.calls[i];
+    const Plan& p = ls.plans[i];
+    GemvArgs& a = la.lin[i];
+    a.x = reinterpret_cast<const f16*>(c.x);
+    a.packed = c.packed;
+    a.scales = reinterpret_cast<const f16*>(c.scales);
+    a.zeros = reinterpret_cast<const f16*>(c.zeros);
+    a.resid = reinterpret_cast<const f16*>(c.resid);
+    a.y = reinterpret_cast<f16*>(c.y);
+    a.ws = nullptr;
+    a.ldx = c.ldx; a.ldr = c.ldr; a.ldy = c.ldy;
+    a.M = c.M; a.N = c.N; a.K = c.K; a.group = meta_group(fmt, c.group);
+    a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.splits = 1; a.tps = p.wordtiles;
+  }
+  la.counter = counter;
+  la.status = status;
+  la.cap = env_int("QGEMM_LOOP_SPIN_CAP", 1 << 18);
+  for (int l = 0; l < L; ++l) {
+    la.barrier0 = 3 * l;
+    void* args[1] = {&la};
+    st = hip_status(hipLaunchKernel(fn, dim3((unsigned)grid), dim3(LOOP_THREADS), args, 0, s));
+    if (st != QG_OK) {
+      clear_pending_error();
+      return st;
+    }
+    if (record_event(events, l + 1, s) != QG_OK) return QG_E_DEVICE;
   }
   return QG_OK;
 }

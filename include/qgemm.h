@@ -247,6 +247,30 @@ int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* con
                 const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt,
                 int L, uint16_t* scratch, void* const* events, void* stream);
 
+/*
+ * qloop_block_persistent: qloop_block at M = 1 with one launch per loop (the
+ * shared block of the TinyLoop README, "Why TinyLoop Exists", run L times;
+ * "Status": the shared weights stay cache-resident across the iterations).
+ * Each launch is a grid of one workgroup per compute unit (never more than
+ * the occupancy calculator says are resident together); they run the loop's
+ * four GEMVs as phases over blocks of 8 rows of W, separated by grid
+ * barriers on counters in device memory the library keeps for the process.
+ * Same arguments, layouts and results as qloop_block, plus
+ *   status [device, out] int32, 16-byte aligned: 0 after the call's loops
+ *          complete, 1 if a barrier stopped waiting (its wait is bounded:
+ *          QGEMM_LOOP_SPIN_CAP polls, 2^18 by default; then x holds no
+ *          meaningful result).
+ *          Written in stream order; read it after the stream is synchronized.
+ * Supported: M == 1; formats QG_INT4_ASYM, QG_INT2_ASYM, QG_Q4_0, QG_Q4K;
+ * K of every linear at most 64 word tiles (8192 for 4-bit codes).  Calls that
+ * overlap on one device (the counter is shared) race.
+ * Errors: as qloop_block, QG_E_ARG (status NULL), QG_E_UNSUPPORTED (M != 1,
+ * format or K outside the above).
+ */
+int qloop_block_persistent(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
+                           const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt, int L,
+                           uint16_t* scratch, int* status, void* const* events, void* stream);
+
 /* Debug: packed -> integer codes uint8 [N, K] (device), for the bit-exact
  * check of the kernels' unpack (the nibble / crumb unpack of the TinyLoop
  * README, "Status").  Errors as qunpack. */
