@@ -162,7 +162,7 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
   const int mg = meta_group(fmt, group);   // scale entries the kernel stages per 'group'
   // fewest K splits a tile shape allows: word tiles per wave, groups per workgroup
   const auto s_min_for = [&](int tm, int tn) {
-    const int s_tiles = (int)ceil_div(p.wordtiles, nw * gemm_tpw_cap(fmt, tm == 64 && tn == 64));
+    const int s_tiles = (int)ceil_div(p.wordtiles, nw * gemm_tpw(fmt, tm == 32 && tn == 32));
     const int s_groups = (int)ceil_div((int64_t)p.wordtiles * kt_width / mg, GEMM_GCAP);
     return std::max(s_tiles, s_groups);
   };
@@ -183,7 +183,8 @@ Plan make_plan(int M, int N, int K, int group, int fmt) {
     p.tm = tile_env / 100;
     p.tn = tile_env % 100;
   }
-  const int tpw = gemm_tpw_cap(fmt, p.tm == 64 && p.tn == 64);
+  const bool small_tile = p.tm == 32 && p.tn == 32;
+  const int tpw = gemm_tpw(fmt, small_tile);
   const int s_min = s_min_for(p.tm, p.tn);
   p.tiles_n = (int)ceil_div(N, p.tn);
   p.tiles_m = (int)ceil_div(M, p.tm);
@@ -244,13 +245,13 @@ int qpack_host(const uint32_t* canon, uint32_t* packed, int N, int K, int fmt) {
   int st = check_pack_args(canon, packed, N, K, fmt);
   if (st != QG_OK) return st;
   const int bits = bits_of(fmt);
-  const int64_t wt = n_wordtiles(K, fmt), rbs = n_rowblocks(N);
-  for (int64_t rb = 0; rb < rbs; ++rb)
-    for (int64_t T = 0; T < wt; ++T)
-      for (int lane = 0; lane < 64; ++lane)
-        for (int t = 0; t < 4; ++t)
-          packed[((rb * wt + T) * 64 + lane) * 4 + t] =
-              gather_packed_word(canon, rb * 16 + (lane & 15), N, K, T, lane >> 4, t, bits);
+  const int64_t kw_n = K / cpw_of(fmt);
+  const int64_t wt = n_wordtiles(K, fmt);
+  const size_t total = qg_packed_bytes(N, K, fmt) / sizeof(uint32_t);
+  if (total) memset(packed, 0, total * sizeof(uint32_t));
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t kw = 0; kw < kw_n; ++kw)
+      packed[packed_index(n, kw, wt)] = perm_word(canon[n * kw_n + kw], bits);
   return QG_OK;
 }
 
@@ -261,7 +262,8 @@ int qunpack_host(const uint32_t* packed, uint32_t* canon, int N, int K, int fmt)
   const int64_t kw_n = K / cpw_of(fmt);
   const int64_t wt = n_wordtiles(K, fmt);
   for (int64_t n = 0; n < N; ++n)
-    for (int64_t kw = 0; kw < kw_n; ++kw) canon[n * kw_n + kw] = gather_canon_word(packed, n, kw, wt, bits);
+    for (int64_t kw = 0; kw < kw_n; ++kw)
+      canon[n * kw_n + kw] = unperm_word(packed[packed_index(n, kw, wt)], bits);
   return QG_OK;
 }
 

@@ -26,9 +26,11 @@ constexpr int GEMM_THREADS = 512;        // 8 waves; they split the workgroup's 
 constexpr int GEMM_TM = 64;              // workgroup tile rows (M)
 constexpr int GEMM_TN = 64;              // workgroup tile columns (N)
 constexpr int GEMM_SMALL_M = 32;         // M <= this: 32 x 32 tiles; M <= 2x this: 64 x 32
-constexpr int GEMM_TPW = 8;              // word tiles per wave, at most (4 for 2-bit codes)
+constexpr int GEMM_TPW = 2;              // word tiles per wave (K per workgroup <= 16 tiles)
+constexpr int GEMM_TPW_Q8 = 4;           // q8_0: a tile is 64 wide, so 4 per wave (256 of K)
+constexpr int GEMM_TPW_SMALL = 8;        // 32 x 32 tiles (two stages in flight): long K unsplit
+constexpr int GEMM_DEPTH = 2;            // x/code stages in flight per wave
 constexpr int GEMM_GCAP = 64;            // quantization groups per workgroup, at most
-constexpr int GEMM_XD = 4;               // steps of x and codes a GEMM wave keeps in flight, plus one
 constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
 
 // word tiles one M = 1 GEMV workgroup of 16 waves streams, at most: 8 per wave
@@ -37,11 +39,9 @@ constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
 // these against its own tile caps
 inline constexpr int gemv_m1_tile_cap(int fmt) { return fmt == INT2_ASYM || fmt == Q4K ? 64 : 128; }
 
-// word tiles one GEMM wave covers, at most: 8 (2-bit tiles are 256 of K wide:
-// 4), halved on 64 x 64 tiles, whose operand registers leave room for fewer
-// unrolled steps
-inline constexpr int gemm_tpw_cap(int fmt, bool big_tile) {
-  return (fmt == INT2_ASYM ? GEMM_TPW / 2 : GEMM_TPW) / (big_tile ? 2 : 1);
+// word tiles one GEMM wave covers, at most
+inline constexpr int gemm_tpw(int fmt, bool small_tile) {
+  return small_tile ? GEMM_TPW_SMALL : fmt == Q8_0 ? GEMM_TPW_Q8 : GEMM_TPW;
 }
 
 struct Plan {

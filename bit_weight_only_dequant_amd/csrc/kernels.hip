@@ -141,22 +141,17 @@ __device__ __forceinline__ void qmz_int8(uint32_t w, const ZC8& zc, h2 out[2]) {
 }
 
 // Per format: bits, codes per word, codes per 16-byte lane chunk (LS), K per
-// word tile (KT), the runs of a lane's chunk (NSEG runs of SW = 8 codes each:
-// run p holds k = 32p + 8g .. +7 of the tile for lane group g, see layout.h),
-// the implicit zero point of the block formats as fp16 bits (8.0 and 128.0),
-// and KQ for the k-quant q4k (codes unpacked with zero point 0; per 32-code
-// sub-block a scale d*sc and an offset dmin*m instead of (s, z)).  A run lies
-// inside one group (groups are multiples of 32 wide and start at multiples of
-// 32), and its group is the same for the four lane groups.
+// word tile (KT), codes per scale lookup (SW: a lane's chunk in runs of at
+// most 32, the smallest group), runs per chunk (NSEG), the implicit zero
+// point of the block formats as fp16 bits (8.0 and 128.0), and KQ for the
+// k-quant q4k (codes unpacked with zero point 0; per 32-code sub-block a
+// scale d*sc and an offset dmin*m instead of (s, z)).
 template <int FMT> struct Fmt;
-template <> struct Fmt<INT4_ASYM> { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 8, NSEG = 4; static constexpr bool HAS_Z = true,  KQ = false; static constexpr uint32_t ZBITS = 0; };
-template <> struct Fmt<INT2_ASYM> { static constexpr int BITS = 2, CPW = 16, LS = 64, KT = 256, SW = 8, NSEG = 8; static constexpr bool HAS_Z = true,  KQ = false; static constexpr uint32_t ZBITS = 0; };
-template <> struct Fmt<Q4_0>      { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 8, NSEG = 4; static constexpr bool HAS_Z = false, KQ = false; static constexpr uint32_t ZBITS = 0x4800; };
-template <> struct Fmt<Q8_0>      { static constexpr int BITS = 8, CPW = 4,  LS = 16, KT = 64,  SW = 8, NSEG = 2; static constexpr bool HAS_Z = false, KQ = false; static constexpr uint32_t ZBITS = 0x5800; };
-template <> struct Fmt<Q4K>       { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 8, NSEG = 4; static constexpr bool HAS_Z = false, KQ = true;  static constexpr uint32_t ZBITS = 0; };
-
-// k inside the word tile of run p of lane group g
-__device__ __forceinline__ int run_k(int g, int p) { return 32 * p + 8 * g; }
+template <> struct Fmt<INT4_ASYM> { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = true,  KQ = false; static constexpr uint32_t ZBITS = 0; };
+template <> struct Fmt<INT2_ASYM> { static constexpr int BITS = 2, CPW = 16, LS = 64, KT = 256, SW = 32, NSEG = 2; static constexpr bool HAS_Z = true,  KQ = false; static constexpr uint32_t ZBITS = 0; };
+template <> struct Fmt<Q4_0>      { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = false, KQ = false; static constexpr uint32_t ZBITS = 0x4800; };
+template <> struct Fmt<Q8_0>      { static constexpr int BITS = 8, CPW = 4,  LS = 16, KT = 64,  SW = 16, NSEG = 1; static constexpr bool HAS_Z = false, KQ = false; static constexpr uint32_t ZBITS = 0x5800; };
+template <> struct Fmt<Q4K>       { static constexpr int BITS = 4, CPW = 8,  LS = 32, KT = 128, SW = 32, NSEG = 1; static constexpr bool HAS_Z = false, KQ = true;  static constexpr uint32_t ZBITS = 0; };
 
 // q4k sub-block terms from the super-block pair ddm = d | dmin << 16 (fp16
 // bits) and the sub-block bytes scm = sc | m << 8.  In fp32 they are exact
@@ -182,17 +177,23 @@ __device__ __forceinline__ void kq_weights(const h2* q, uint32_t dsnb, h2* w, in
   for (int i = 0; i < n; ++i) w[i] = __builtin_elementwise_fma(q[i], ds, nb);
 }
 
-// Exact (q - z) pairs, in k order, of run p (8 codes) of a lane's chunk c
+// Exact (q - z) pairs, in k order, of run p (SW codes) of a lane's chunk c
 template <int FMT>
 __device__ __forceinline__ void run_qmz(const u4& c, int p, f16 z, h2* q) {
   if constexpr (FMT == INT2_ASYM) {
-    qmz_int2_half(c[p >> 1], p & 1, make_zc2(z), q);
+    const ZC2 zc = make_zc2(z);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) qmz_int2_half(c[2 * p + t], h, zc, q + 8 * t + 4 * h);
   } else if constexpr (FMT == Q8_0) {
     const ZC8 zc = make_zc8(z);
-    qmz_int8(c[2 * p], zc, q);
-    qmz_int8(c[2 * p + 1], zc, q + 2);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qmz_int8(c[t], zc, q + 2 * t);
   } else {
-    qmz_int4(c[p], make_zc4(z), q);
+    const ZC4 zc = make_zc4(z);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qmz_int4(c[t], zc, q + 4 * t);
   }
 }
 
@@ -200,14 +201,18 @@ __device__ __forceinline__ void run_qmz(const u4& c, int p, f16 z, h2* q) {
 // repack kernels
 // ---------------------------------------------------------------------------
 __global__ void qpack_kernel(const uint32_t* __restrict__ canon, uint32_t* __restrict__ packed,
-                             int N, int K, int wordtiles, int bits, int64_t total) {
+                             int N, int Kw, int wordtiles, int bits, int64_t total) {
   for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
        p += (int64_t)gridDim.x * blockDim.x) {
     const int t = (int)(p & 3);
     const int lane = (int)((p >> 2) & 63);
     const int64_t rest = p >> 8;
     const int64_t T = rest % wordtiles, rb = rest / wordtiles;
-    packed[p] = gather_packed_word(canon, rb * 16 + (lane & 15), N, K, T, lane >> 4, t, bits);
+    const int64_t n = rb * 16 + (lane & 15);
+    const int64_t kw = T * 16 + (lane >> 4) * 4 + t;
+    uint32_t v = 0;
+    if (n < N && kw < Kw) v = perm_word(canon[n * Kw + kw], bits);
+    packed[p] = v;
   }
 }
 
@@ -215,8 +220,10 @@ __global__ void qunpack_kernel(const uint32_t* __restrict__ packed, uint32_t* __
                                int N, int Kw, int wordtiles, int bits) {
   const int64_t total = (int64_t)N * Kw;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x)
-    canon[i] = gather_canon_word(packed, i / Kw, i % Kw, wordtiles, bits);
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = i / Kw, kw = i % Kw;
+    canon[i] = unperm_word(packed[packed_index(n, kw, wordtiles)], bits);
+  }
 }
 
 __global__ void unpack_codes_kernel(const uint32_t* __restrict__ packed, uint8_t* __restrict__ codes,
@@ -225,8 +232,9 @@ __global__ void unpack_codes_kernel(const uint32_t* __restrict__ packed, uint8_t
   const int64_t total = (int64_t)N * K;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    int slot = 0;
-    const uint32_t w = packed[packed_code_word(i / K, i % K, cpw, wordtiles, &slot)];
+    const int64_t n = i / K, k = i % K;
+    const uint32_t w = packed[packed_index(n, k / cpw, wordtiles)];
+    const int slot = code_slot((int)(k % cpw), cpw);
     codes[i] = (uint8_t)((w >> (bits * slot)) & ((1u << bits) - 1u));
   }
 }
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   const int ng = K / group;   // q4k: group = 32, the sub-block
 #pragma unroll
   for (int p = 0; p < F::NSEG; ++p) {
-    const int kl = run_k(g, p);                     // this lane's run inside the tile
+    const int kl = g * F::LS + p * F::SW;          // this lane's first code inside the tile
     const int k = T * F::KT + kl;
     if (n >= N || k >= K) continue;
     const int grp = k / group;
@@ -337,7 +345,7 @@ __device__ __forceinline__ float add_lane_xor16(float v) {
 template <int FMT> constexpr size_t gemv_lds_bytes_for(int mmax, int tpw, int nw) {
   const int KW = tpw * Fmt<FMT>::KT;
   const int SZB = Fmt<FMT>::KQ ? 8 : 4;
-  const int XSB = Fmt<FMT>::KQ ? mmax * (KW / 8) * 4 : 0;   // q4k: x sum of every 8-wide run
+  const int XSB = Fmt<FMT>::KQ ? mmax * (KW / 32) * 4 : 0;
   return (size_t)nw * (mmax * KW * 2 + 16 * (KW / 32) * SZB + XSB) + (size_t)nw * mmax * 32 * sizeof(float);
 }
 template <int FMT, int MMAX, int TPW, int NW> constexpr size_t gemv_lds_bytes() {
@@ -362,15 +370,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   constexpr int NSZ = (16 * GWMAX + 63) / 64;  // (scale, zero) loads per lane, at most
   constexpr int SZB = F::KQ ? 8 : 4;
   constexpr int XB = MMAX * KW * 2, SB = 16 * GWMAX * SZB;
-  constexpr int XR = KW / 8;                   // q4k: 8-wide runs per row of the wave's range
-  constexpr int WB = XB + SB + (F::KQ ? MMAX * XR * 4 : 0);
+  constexpr int WB = XB + SB + (F::KQ ? MMAX * GWMAX * 4 : 0);
   __shared__ __align__(16) uint8_t gemv_smem[gemv_lds_bytes<FMT, MMAX, TPW, NW>()];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f16* xs = reinterpret_cast<f16*>(gemv_smem + wave * WB);                 // [MMAX][KW]
   uint32_t* sz = reinterpret_cast<uint32_t*>(gemv_smem + wave * WB + XB);  // [16][GWMAX] s | z << 16
   float2* szk = reinterpret_cast<float2*>(gemv_smem + wave * WB + XB);     // q4k: [16][GWMAX] (d*sc, dmin*m)
-  float* xsum = reinterpret_cast<float*>(gemv_smem + wave * WB + XB + SB); // q4k: [MMAX][XR]
+  float* xsum = reinterpret_cast<float*>(gemv_smem + wave * WB + XB + SB); // q4k: [MMAX][GWMAX]
   float* red = reinterpret_cast<float*>(gemv_smem + NW * WB);              // [NW][MMAX][2][16]
 
   const int g = lane >> 4, r = lane & 15;
@@ -459,13 +466,17 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if constexpr (F::KQ) {
-    // x sum of every 8-wide run of the wave's range (zeros past K): a lane's
-    // run meets dmin*m of its sub-block; one lane per (row, run)
-    for (int e = lane; e < MMAX * XR; e += 64) {
-      const h8 xv = *reinterpret_cast<const h8*>(xs + (e / XR) * KW + (e % XR) * 8);
+    // x sum of every 32-wide run of the wave's range (zeros past K), one
+    // lane per (row, run)
+    for (int e = lane; e < MMAX * GWMAX; e += 64) {
+      const h8* xp = reinterpret_cast<const h8*>(xs + (e / GWMAX) * KW + (e % GWMAX) * 32);
       float v = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) v = __builtin_amdgcn_fdot2(h2{xv[2 * t], xv[2 * t + 1]}, splat((f16)1.0f), v, false);
+      for (int c = 0; c < 4; ++c) {
+        const h8 xv = xp[c];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v = __builtin_amdgcn_fdot2(h2{xv[2 * t], xv[2 * t + 1]}, splat((f16)1.0f), v, false);
+      }
       xsum[e] = v;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -485,8 +496,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
     if (i < nt) {
 #pragma unroll
       for (int p = 0; p < F::NSEG; ++p) {
-        const int kl = i * F::KT + run_k(g, p);   // this lane's run inside the wave's range
-        const int run = kl >> lg;
+        const int run = (i * F::KT + g * F::LS + p * F::SW) >> lg;
         float sf, bk = 0.0f;
         f16 z;
         if constexpr (F::KQ) {
@@ -503,7 +513,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
         run_qmz<FMT>(code[i], p, z, q);
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) {
-          const h8* xp = reinterpret_cast<const h8*>(xs + m * KW + kl);
+          const h8* xp = reinterpret_cast<const h8*>(xs + m * KW + i * F::KT + g * F::LS + p * F::SW);
           float A0 = 0.0f, A1 = 0.0f;  // two chains for issue overlap
 #pragma unroll
           for (int c = 0; c < F::SW / 8; ++c) {
@@ -516,7 +526,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
             if (c & 1) A1 = t0; else A0 = t0;
           }
           acc[m] = fmaf(sf, A0 + A1, acc[m]);
-          if constexpr (F::KQ) acc[m] = fmaf(-bk, xsum[m * XR + (kl >> 3)], acc[m]);
+          if constexpr (F::KQ) acc[m] = fmaf(-bk, xsum[m * GWMAX + run], acc[m]);
         }
       }
     }
@@ -556,11 +566,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
 // dequant and dot products (MMAX rows of x share each exact (q - z) pair; q4k
 // as in gemv_kernel); lanes sum over g and t, the waves through LDS in wave order.
 // LDS bytes of gemv_half_body: per wave its x rows, (scale, zero) pairs and
-// (q4k) run sums of x, then NW x MMAX x 16 fp32 for the sum over the waves
+// (q4k) group sums of x, then NW x MMAX x 16 fp32 for the sum over the waves
 template <int FMT, int NW, int TPW, int MMAX> constexpr size_t gemv_half_lds_bytes() {
   using F = Fmt<FMT>;
-  constexpr int KW = TPW * F::KT;
-  constexpr int WB = MMAX * KW * 2 + 8 * (KW / 32) * (F::KQ ? 8 : 4) + (F::KQ ? MMAX * (KW / 8) * 4 : 0);
+  constexpr int KW = TPW * F::KT, GW = KW / 32;
+  constexpr int WB = MMAX * KW * 2 + 8 * GW * (F::KQ ? 8 : 4) + (F::KQ ? MMAX * GW * 4 : 0);
   return (size_t)NW * WB + (size_t)NW * MMAX * 16 * sizeof(float);
 }
 
@@ -581,14 +591,13 @@ __device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by
   constexpr int NSZ = (8 * GWMAX + 63) / 64;
   constexpr int SZB = F::KQ ? 8 : 4;           // q4k: fp32 (d*sc, dmin*m) per (row, sub-block)
   constexpr int XB = MMAX * KW * 2, SB = 8 * GWMAX * SZB;
-  constexpr int XR = KW / 8;                   // q4k: 8-wide runs per row of the wave's range
-  constexpr int WB = XB + SB + (F::KQ ? MMAX * XR * 4 : 0);
+  constexpr int WB = XB + SB + (F::KQ ? MMAX * GWMAX * 4 : 0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   f16* xs = reinterpret_cast<f16*>(half_smem + wave * WB);                 // [MMAX][KW]
   uint32_t* sz = reinterpret_cast<uint32_t*>(half_smem + wave * WB + XB);  // [8][GWMAX] s | z << 16
   float2* szk = reinterpret_cast<float2*>(half_smem + wave * WB + XB);     // q4k: [8][GWMAX] (d*sc, dmin*m)
-  float* xsum = reinterpret_cast<float*>(half_smem + wave * WB + XB + SB); // q4k: [MMAX][XR]
+  float* xsum = reinterpret_cast<float*>(half_smem + wave * WB + XB + SB); // q4k: [MMAX][GWMAX]
   float* red = reinterpret_cast<float*>(half_smem + NW * WB);              // [NW][MMAX][2][8]
   const int r8 = lane & 7, g = (lane >> 3) & 3, t = lane >> 5;
   const int rb = bx >> 1, hb = bx & 1, split = by;
@@ -668,13 +677,17 @@ __device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if constexpr (F::KQ) {
-    // x sum of every 8-wide run of the wave's range (zeros past K), one lane
+    // x sum of every 32-wide run of the wave's range (zeros past K), one lane
     // per (row of x, run)
-    for (int e = lane; e < MMAX * XR; e += 64) {
-      const h8 xv = *reinterpret_cast<const h8*>(xs + (e / XR) * KW + (e % XR) * 8);
+    for (int e = lane; e < MMAX * GWMAX; e += 64) {
+      const h8* xp = reinterpret_cast<const h8*>(xs + (e / GWMAX) * KW + (e % GWMAX) * 32);
       float v = 0.0f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v = __builtin_amdgcn_fdot2(h2{xv[2 * u], xv[2 * u + 1]}, splat((f16)1.0f), v, false);
+      for (int c = 0; c < 4; ++c) {
+        const h8 xv = xp[c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v = __builtin_amdgcn_fdot2(h2{xv[2 * u], xv[2 * u + 1]}, splat((f16)1.0f), v, false);
+      }
       xsum[e] = v;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -691,7 +704,7 @@ __device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by
     if (2 * i + t >= nt) continue;
 #pragma unroll
     for (int p = 0; p < F::NSEG; ++p) {
-      const int kl = (2 * i + t) * F::KT + run_k(g, p);
+      const int kl = (2 * i + t) * F::KT + g * F::LS + p * F::SW;
       const int run = kl >> lg;
       float sf, bk = 0.0f;
       f16 z;
@@ -722,7 +735,7 @@ __device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by
           if (c & 1) A1 = t0; else A0 = t0;
         }
         acc[m] = fmaf(sf, A0 + A1, acc[m]);
-        if constexpr (F::KQ) acc[m] = fmaf(-bk, xsum[m * XR + (kl >> 3)], acc[m]);
+        if constexpr (F::KQ) acc[m] = fmaf(-bk, xsum[m * GWMAX + run], acc[m]);
       }
     }
   }
@@ -981,7 +994,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_mfma_kernel(GemvArgs a) {
       if (c * TPW + i < nt) {
 #pragma unroll
         for (int p = 0; p < F::NSEG; ++p) {
-          const int kl = i * F::KT + run_k(g, p);   // this lane's run inside the chunk
+          const int kl = i * F::KT + g * F::LS + p * F::SW;  // this lane's run inside the chunk
           const uint32_t szv = sz[r * GWMAX + (kl >> lg)];
           const h2 s2 = splat(__builtin_bit_cast(f16, (uint16_t)(szv & 0xffffu)));
           // q4k: the high half is -fp16(dmin*m), codes are unpacked with zero point 0
@@ -1063,430 +1076,431 @@ __global__ void gemv_reduce_kernel(const float* __restrict__ ws, const f16* __re
 }
 
 // ---------------------------------------------------------------------------
-// prefill GEMM (M > 16): v_mfma_f32_16x16x32_f16 on register-dequantized
-// weights, x fragments loaded straight from memory
+// prefill GEMM (M > 16): fp16 MFMA on register-dequantized weights
 // ---------------------------------------------------------------------------
 struct GemmArgs {
   const f16* x; const uint32_t* packed; const f16* scales; const f16* zeros;
   const f16* resid; f16* y; float* ws;
   int ldx, ldr, ldy, M, N, K, group;
-  int wordtiles, rowblocks, tiles_n, tiles_m, splits, tps;
+  int wordtiles, rowblocks, tiles_n, splits, tps;
 };
 
-// Buffer resource over `bytes` bytes at p (raw, stride 0; the third
-// descriptor word of the gfx9 family): loads take a 32-bit per-lane offset
-// and a uniform SGPR offset, so no 64-bit address arithmetic per load, and a
-// per-lane offset at or past `bytes` reads zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+template <int N> __device__ __forceinline__ void wait_vm() {
+  // s_waitcnt vmcnt(N) (GFX9 encoding), expcnt and lgkmcnt left at their maximum
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-__device__ __forceinline__ u4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+__device__ __forceinline__ void wait_lgkm0() {
+  // s_waitcnt lgkmcnt(0), vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
-// Per-group constants of the GEMM, staged in LDS once per workgroup so that
-// each MFMA step's dequantization is the and-or unpack plus one packed add or
-// fma and one packed multiply per code pair: the scale in both halves (s2)
-// and the bias constants zc[i] = -(1024 * 2^-(b*i) + z) of qmz_int4 / int2 /
-// int8, both halves; q4k: fp16(d*sc) and -fp16(dmin*m), both halves.  An
-// all-zero entry (index GEMM_GCAP) serves runs past K.
-template <int FMT> struct GTab {
-  static constexpr int W = FMT == INT2_ASYM ? 8 : FMT == Q8_0 || FMT == Q4K ? 2 : 4;   // u32 per entry
+// Accumulator row of element i (0..15) of a 32 x 32 block for lane l: the
+// output layout of v_mfma_f32_32x32x16_f16 is D[8*(i/4) + 4*(l/32) + i%4][l%32].
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// Stage geometry.  A stage feeds four MFMA steps of 8 k per lane half g2
+// (32 k per half).  4- and 2-bit codes (WIDE: a lane's chunk holds 32 or more
+// codes): a stage is (word tile t, chunk h, 32-code run j) and lane half g2
+// takes its 32 k from lane group g2 + 2h, run j, at seg_k(g2, h, j).  8-bit
+// codes: a stage is a whole word tile and lane half g2 takes 16 k from each of
+// lane groups g2 (steps 0, 1) and g2 + 2 (steps 2, 3), i.e. chunk h = step / 2.
+// x part: 32*MB rows x 2 pieces (one per lane half) x 4 sub-chunks of 8 k
+// (4 KiB per 32 rows); code part: CH chunks of the NB 32-column blocks
+// (1 KiB per block and chunk).
+template <int FMT, int MB, int NB> struct GemmStage {
+  static constexpr int KT = Fmt<FMT>::KT;
+  static constexpr bool WIDE = Fmt<FMT>::LS >= 32;
+  static constexpr int SEG = WIDE ? Fmt<FMT>::LS / 32 : 1;  // 32-code runs per chunk
+  static constexpr int CH = WIDE ? 1 : 2;                  // chunks per stage
+  static constexpr int STAGES = WIDE ? 2 * SEG : 1;        // stages per word tile
+  static constexpr int XB = 32 * MB * 64 * 2;              // x bytes per stage (LDS)
+  static constexpr int SB = XB;                            // codes go to VGPRs
+  static constexpr int DMA = XB / 1024 + NB * CH;          // vector loads per lane per stage (10, 12 at 2 x 2)
 };
-template <int FMT> __device__ __forceinline__ void gtab_entry(uint32_t sraw, uint32_t zraw, uint32_t* e) {
-  if constexpr (Fmt<FMT>::KQ) {
-    const uint32_t dsnb = kq_half_pair(sraw, zraw);
-    e[0] = (dsnb & 0xffffu) * 0x10001u;
-    e[1] = (dsnb >> 16) * 0x10001u;
-  } else {
-    const f16 sv = __builtin_bit_cast(f16, (uint16_t)(sraw & 0xffffu));
-    const f16 z = __builtin_bit_cast(f16, (uint16_t)(zraw & 0xffffu));
-    e[0] = as_u32(splat(sv));
-    if constexpr (FMT == INT2_ASYM) {
-      const ZC2 zc = make_zc2(z);
-      e[1] = as_u32(zc.c0); e[2] = as_u32(zc.c1); e[3] = as_u32(zc.c2); e[4] = as_u32(zc.c3);
-      e[5] = e[6] = e[7] = 0u;
-    } else if constexpr (FMT == Q8_0) {
-      e[1] = as_u32(make_zc8(z).c0);
-    } else {
-      const ZC4 zc = make_zc4(z);
-      e[1] = as_u32(zc.c0); e[2] = as_u32(zc.c1); e[3] = 0u;
-    }
-  }
-}
-// 8 fp16 weights of run p of a lane's chunk c from its table entry e
-template <int FMT> __device__ __forceinline__ h8 gtab_weights(const u4& c, int p, const uint32_t* e) {
-  h2 q[4];
-  if constexpr (Fmt<FMT>::KQ) {
-    qmz_int4(c[p], ZC4{as_h2(0xe400e400u), as_h2(0xd400d400u)}, q);   // zero point 0: -1024, -64
-    const h2 ds = as_h2(e[0]), nb = as_h2(e[1]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = __builtin_elementwise_fma(q[i], ds, nb);
-  } else {
-    if constexpr (FMT == INT2_ASYM) {
-      qmz_int2_half(c[p >> 1], p & 1, ZC2{as_h2(e[1]), as_h2(e[2]), as_h2(e[3]), as_h2(e[4])}, q);
-    } else if constexpr (FMT == Q8_0) {
-      const ZC8 zc{as_h2(e[1])};
-      qmz_int8(c[2 * p], zc, q);
-      qmz_int8(c[2 * p + 1], zc, q + 2);
-    } else {
-      qmz_int4(c[p], ZC4{as_h2(e[1]), as_h2(e[2])}, q);
-    }
-    const h2 s2 = as_h2(e[0]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = q[i] * s2;
-  }
-  return h8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
-}
 
-// Prefill GEMM.  Workgroup tile 16*MB (M) x 16*NB (N) -- 64 x 64 for M > 64,
-// 64 x 32 up to 64, 32 x 32 up to 32 -- over the workgroup's share of K; its NW
-// waves take TPW word tiles each and are summed through LDS in wave order at
-// the end (deterministic), so every code is dequantized once per workgroup.
-// Each wave owns all MB x NB blocks of v_mfma_f32_16x16x32_f16.  One MFMA step
-// is one run of the packed layout (layout.h): lane l = 16g + r supplies B
-// column r (row n0 + 16nb + r of W) with the run's 8 codes, dequantized in
-// registers to fp16 s*(q - z), and A row r (row m0 + 16mb + r of x) at the
-// same 8 k.  The four lanes of a row read 64 contiguous bytes of x, but they
-// are not adjacent lanes, and the vector memory path merges only adjacent
-// lanes: x is loaded with one 64-byte sector per lane quad instead and moved
-// into the operand layout with ds_bpermute (the LDS crossbar, no LDS storage).
-// XD - 1 steps of x are in flight per wave while it computes, and the code
-// chunks of the word tiles they belong to (CD tiles live).  Every wave issues
-// all TPW * NR steps (those past its share clamped in bounds and not
-// computed), so the loads form one straight-line sequence and every wait the
-// compiler places is exact.  Each step runs the MFMAs of step s with the LDS
-// phase of step s + 1 (operand permute, table reads) after the first few of
-// them, and its dequantization after the LDS round trip: the VALU overlaps
-// the matrix core only partly, so the dequantization is kept to one B operand
-// per MB MFMAs.  The
-// (scale, zero) entries of the workgroup's columns and groups are staged in
-// LDS once; each step reads one per column block (its run lies in one group,
-// the same for all four lane groups).
-// Workgroups are numbered so that the row tiles of one column tile differ by
-// multiples of 8: with workgroups dispatched round robin over the 8 XCDs they
-// run on one XCD and share its L2, so each code is fetched from memory once.
-template <int FMT, int MB, int NB, int NW, int TPW, int XD>
+// Prefill GEMM (M > 16).  Workgroup tile 32*MB (M) x 32*NB (N) -- 64 x 64,
+// 64 x 32 when M <= 64, 32 x 32 when M <= 32 -- over the workgroup's share of K; its NW waves
+// split that share and are summed through LDS at the end, so every code is
+// dequantized once per workgroup.  Each wave owns MB x NB blocks of
+// v_mfma_f32_32x32x16_f16 (B operand lane l = column l % 32,
+// k-slots 8*(l/32)..+7): lane l takes its codes from the 16-byte chunk of row
+// block n0/16 + 2*nb + (l%32)/16, row l%16, lane group l/32 + 2h, one packed
+// word (8 codes) per MFMA step, and the A fragment of the step reads the
+// matching 8 k of x, so A and B agree on the k order.
+//
+// Each wave streams its stages through a private DEPTH-deep LDS ring with
+// direct global->LDS loads (x and codes alike, so every wait is an explicit
+// vmcnt).  Inside a stage x sits as [piece][row][4 x 16 B]; sub-chunk u of
+// row m is stored at u ^ ((m >> 2) & 3), so the fragment reads of 16
+// consecutive rows hit 16 distinct bank groups.  All LDS operands of a stage
+// are read first; group barriers then interleave one MFMA with a few VALU of
+// the dequantization so the two pipes overlap.
+template <int FMT, int NW, int TPW, int DEPTH, int MB, int NB, bool ALL>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   using F = Fmt<FMT>;
-  constexpr int NR = F::NSEG;                            // MFMA steps per word tile
-  constexpr int STEPS = TPW * NR;
-  constexpr int CD = 1 + (XD + NR - 1) / NR;             // code tiles live at once
-  constexpr int NBLK = MB * NB;
-  constexpr int TN = 16 * NB;
-  constexpr int RED = NW * NBLK * 64 * 16;               // per wave: NBLK f4 per lane
-  constexpr int TW = GTab<FMT>::W;                       // u32 per table entry
-  constexpr int SZS = GEMM_GCAP + 1;                     // entries per column (the last: zeros, for runs past K)
-  constexpr int TAB = TN * SZS * TW * 4;
-  constexpr int LDS = RED > TAB ? RED : TAB;
-  static_assert(LDS <= 160 * 1024, "LDS");
-  __shared__ __align__(16) uint8_t smem[LDS];
-  uint32_t* szl = reinterpret_cast<uint32_t*>(smem);
-  f4* red = reinterpret_cast<f4*>(smem);
+  using S = GemmStage<FMT, MB, NB>;
+  constexpr int SEG = S::SEG;
+  constexpr int TM = 32 * MB, TN = 32 * NB, NBLK = MB * NB;
+  // per-wave LDS region: its stage ring, large enough to take the wave's
+  // accumulators ([block][quad][lane] f4) at the end, so a wave writes them
+  // as soon as its own K loop is done, without waiting for the others
+  constexpr int UNITS = NBLK * 4;                        // 32 x 32 block quads
+  constexpr int WS = DEPTH * S::SB > UNITS * 1024 ? DEPTH * S::SB : UNITS * 1024;
+  constexpr int BIG = NW * WS;
+  // (s | z << 16) per column and group; a column's row is padded by one
+  // word so that the 32 columns one lookup reads fall in 32 distinct banks
+  constexpr int SZS = GEMM_GCAP + 1;
+  constexpr int SZB = TN * SZS * 4;
+  static_assert(DEPTH >= 1 && DEPTH <= 3 && (DEPTH - 1) * S::DMA <= 63, "vmcnt range");
+  __shared__ __align__(16) uint8_t smem[BIG + SZB];
+  uint32_t* szl = reinterpret_cast<uint32_t*>(smem + BIG);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, r = lane & 15;
-  int tn, tm, split;
-  {
-    const int id = blockIdx.x;
-    const int per_split = a.tiles_n * a.tiles_m;
-    split = id / per_split;
-    const int t = id - split * per_split;
-    const int full = (a.tiles_n / 8) * 8 * a.tiles_m;   // ids in whole groups of 8 column tiles
-    if (t < full) {
-      const int grp = t / (8 * a.tiles_m), in = t - grp * 8 * a.tiles_m;
-      tm = in / 8;
-      tn = grp * 8 + (in & 7);
-    } else {
-      const int rem = a.tiles_n - (a.tiles_n / 8) * 8, in = t - full;
-      tm = in / rem;
-      tn = (a.tiles_n / 8) * 8 + in % rem;
-    }
-  }
-  const int m0 = tm * 16 * MB, n0 = tn * TN;
-  const int kt0 = split * a.tps;                         // the workgroup's word tiles
+  const int g2 = lane >> 5, r = lane & 15;
+  const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
+  const int m0 = tm * TM, n0 = tn * TN;
+  const int kt0 = split * a.tps;
   const int kt1 = min(a.wordtiles, kt0 + a.tps);
-  // the waves' K ranges, rotated by the column-tile group so that workgroups
-  // running side by side on one XCD read different parts of x
-  const int wslot = (wave + (tn >> 3)) & (NW - 1);
-  const int wt0 = kt0 + wslot * TPW;                     // this wave's
-  const int nlive = max(0, min(kt1 - wt0, TPW)) * NR;    // steps this wave computes
-  const int tlast = max(kt1 - 1, kt0);
+  const int per = (kt1 - kt0 + NW - 1) / NW;
+  const int wt0 = kt0 + wave * per;
+  const int nt = max(0, min(kt1, wt0 + per) - wt0);     // <= TPW (plan guarantees)
+  const int nst = nt * S::STAGES;
   const int lg = __builtin_ctz(a.group);
   const int ng = a.K >> lg;
   const int gw0 = (kt0 * F::KT) >> lg;                   // first group (KT % group == 0)
-  const int gwn = min(ng, ((kt1 * F::KT) + a.group - 1) >> lg) - gw0;   // <= GEMM_GCAP (plan)
+  const int gwn = min(ng, ((kt1 * F::KT) + a.group - 1) >> lg) - gw0;  // <= GEMM_GCAP (plan)
+  uint8_t* wbuf = smem + wave * WS;
 
-  // 0. residual of the blocks this wave finishes (fp16 bits, converted at the
-  //    end), through a resource of size 0 when there is none (the loads then
-  //    read zeros): no branch, so nothing waits on these loads early
-  constexpr int UPW = NBLK >= NW ? NBLK / NW : 1;
-  static_assert(NBLK < NW || NBLK % NW == 0, "blocks per wave");
-  const bool fin = wave * UPW < NBLK;
-  const bool has_res = a.resid && a.splits == 1;
-  const __amdgpu_buffer_rsrc_t rres =
-      make_rsrc(has_res ? a.resid : a.y, has_res ? (uint32_t)((int64_t)(a.M - 1) * a.ldr * 2 + (int64_t)a.N * 2) : 0u);
-  uint32_t res[UPW][4];
+  auto seg_k = [](int gg, int h, int j) { return (gg + 2 * h) * F::LS + j * 32; };
+
+  // 0. the residual of the quads this wave finishes (UPW quads of 32 x 32
+  //    blocks: all NW waves share the final sums), fp16 bits, converted only
+  //    in the epilogue; issued first, so no later wait depends on it
+  constexpr int UPW = UNITS >= NW ? UNITS / NW : 1;
+  static_assert(UNITS < NW || UNITS % NW == 0, "quads per wave");
+  const bool fin = wave * UPW < UNITS;                  // this wave finishes quads
+  uint32_t res[4 * UPW];
+  if (a.resid && a.splits == 1 && fin) {
 #pragma unroll
-  for (int u = 0; u < UPW; ++u) {
-    const int blk = min(wave * UPW + u, NBLK - 1);
-    const int colc = min(n0 + 16 * (blk % NB) + r, a.N - 1);
+    for (int k = 0; k < UPW; ++k) {
+      const int u = wave * UPW + k, blk = u >> 2, q = u & 3;
+      const int colc = min(n0 + (blk % NB) * 32 + (lane & 31), a.N - 1);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = min(m0 + 16 * (blk / NB) + 4 * g + e, a.M - 1);
-      res[u][e] = __builtin_amdgcn_raw_buffer_load_b16(rres, (uint32_t)(row * a.ldr + colc) * 2u, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const int row = min(m0 + (blk / NB) * 32 + acc_row(4 * q + e, lane), a.M - 1);
+        res[4 * k + e] = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)row * a.ldr + colc];
+      }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4 * UPW; ++i) res[i] = 0u;
   }
 
-  // 1. the (scale, zero) entries of the workgroup's columns and groups, issued
-  //    first (unconditional; entries outside the tile or past N read zeros) so
-  //    that waiting for them leaves every later load in flight
+  // 1. the workgroup's scales and zeros, loaded cooperatively (clamped) and
+  //    staged in LDS as [column][group] (rows padded by one word)
   constexpr int NSZ = (TN * GEMM_GCAP + NW * 64 - 1) / (NW * 64);
   const int gsr = gwn <= 1 ? 1 : 1 << (32 - __builtin_clz(gwn - 1));   // groups, rounded to a power of two
   const int lgs = __builtin_ctz(gsr);
   const int nsz = (TN * gsr + NW * 64 - 1) / (NW * 64);
-  const uint32_t mbytes = (uint32_t)((int64_t)a.N * ng * 2);            // one fp16 per (row, group)
-  const __amdgpu_buffer_rsrc_t sres = make_rsrc(a.scales, F::KQ ? mbytes / 4 : mbytes);   // q4k: 4 bytes per 8 sub-blocks
-  const __amdgpu_buffer_rsrc_t zres = make_rsrc(F::HAS_Z || F::KQ ? a.zeros : a.scales, mbytes);
   uint32_t sraw[NSZ], zraw[NSZ];
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
-    if (j >= nsz) break;                                 // uniform: only the loads the table needs
-    const int e = tid + NW * 64 * j;                     // column e >> lgs, group e % gsr
-    const int ec = e >> lgs, eg = e & (gsr - 1);
-    const bool ok = ec < TN && eg < gwn && n0 + ec < a.N;
-    const uint32_t off = ok ? (uint32_t)((n0 + ec) * ng + gw0 + eg) : 0x40000000u;
-    if constexpr (F::KQ) {   // (d, dmin) of the super-block as 32 bits, (sc, m) of the sub-block
-      sraw[j] = __builtin_amdgcn_raw_buffer_load_b32(sres, ok ? (off >> 3) * 4u : 0x80000000u, 0, 0);
-      zraw[j] = __builtin_amdgcn_raw_buffer_load_b16(zres, off * 2u, 0, 0);
-    } else {
-      sraw[j] = __builtin_amdgcn_raw_buffer_load_b16(sres, off * 2u, 0, 0);
-      if constexpr (F::HAS_Z) zraw[j] = __builtin_amdgcn_raw_buffer_load_b16(zres, off * 2u, 0, 0);
-      else zraw[j] = F::ZBITS;  // the implicit zero point
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 2. per-lane offsets: x rows (rows past M lie past the resource: zeros),
-  //    the code chunks of the NB column blocks (row blocks past N: zeros)
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)((int64_t)(a.M - 1) * a.ldx * 2 + (int64_t)a.K * 2));
-  // x is loaded coalesced -- lane 4i + c reads piece c (8 k) of row i, so each
-  // lane quad reads one 64-byte sector -- and moved to the MFMA operand
-  // layout (lane 16g + r: row r, piece g) by ds_bpermute from lane 4r + g
-  uint32_t xoff[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int row = m0 + 16 * mb + (lane >> 2);
-    xoff[mb] = row < a.M ? (uint32_t)(row * a.ldx + 8 * (lane & 3)) * 2u : 0x80000000u;
-  }
-  const int xsrc = (4 * r + g) * 4;                     // ds_bpermute byte address of the source lane
-  const int rb0 = n0 >> 4;
-  const int nrb = min(NB, a.rowblocks - rb0);            // row blocks of W in this tile
-  const uint32_t rbbytes = (uint32_t)a.wordtiles * 1024u;
-  const __amdgpu_buffer_rsrc_t cr = make_rsrc(reinterpret_cast<const char*>(a.packed) + (int64_t)rb0 * rbbytes,
-                                              (uint32_t)nrb * rbbytes);
-  uint32_t coff[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) coff[nb] = nb < nrb ? (uint32_t)nb * rbbytes + lane * 16 : 0x80000000u;
-
-  h8 xa[XD][MB];                  // A fragments of the steps in flight
-  u4 cq[CD][NB];                  // code chunks of the word tiles in flight
-  auto issue = [&](int s) {       // the loads of wave-local step s
-    const int tau = s / NR, p = s % NR;
-    const int T = min(wt0 + tau, tlast);                 // clamped; dead steps are not computed
-    if (p == 0) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) cq[tau % CD][nb] = buf_load16(cr, coff[nb], (uint32_t)T * 1024u);
-    }
-    const int k = T * F::KT + 32 * p;                    // the run's first k (all lane groups)
-    const uint32_t ks = (uint32_t)(k < a.K ? k : 0) * 2u;            // past K: finite data, zero scale
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) xa[s % XD][mb] = __builtin_bit_cast(h8, buf_load16(xr, xoff[mb], ks));
-    __builtin_amdgcn_sched_barrier(0);   // steps stay in issue order
-  };
-
-  f4 acc[MB][NB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f4{0.f, 0.f, 0.f, 0.f};
-
-  // Operands of one step: A moved into the MFMA layout in place (ds_bpermute
-  // of its ring slot), B dequantized from the run's codes with its table
-  // entry (13 VALU per 8 4-bit codes).  Steps past this wave's share and runs
-  // past K take the all-zero entry, so their products add nothing; the entry
-  // index is a branch-free scalar select (a branch would split the block the
-  // MFMAs are scheduled in).
-  auto gidx = [&](int s) {
-    const int k = (wt0 + s / NR) * F::KT + 32 * (s % NR);
-    const int gv = min(max((k >> lg) - gw0, 0), gwn - 1);
-    return ((k < a.K) & (s < nlive)) ? gv : GEMM_GCAP;
-  };
-  // the LDS phase of a step's operands: A permuted in place, the table
-  // entries of its column blocks read
-  auto fetch = [&](int s, uint32_t (&ent)[NB][TW]) {
-    const int gi = gidx(s);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const u4 v = __builtin_bit_cast(u4, xa[s % XD][mb]);
-      u4 w;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) w[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(xsrc, (int)v[d]);
-      xa[s % XD][mb] = __builtin_bit_cast(h8, w);
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t* tp = szl + ((16 * nb + r) * SZS + gi) * TW;
-      if constexpr (TW == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(tp);
-        ent[nb][0] = v.x; ent[nb][1] = v.y;
+    {   // unconditional (clamped): a branch here makes the compiler wait on the loads at once
+      const int e = tid + NW * 64 * j;                   // column e >> lgs, group e % gsr
+      const int ec = e >> lgs, eg = e & (gsr - 1);
+      const bool ok = j < nsz && ec < TN && eg < gwn && n0 + ec < a.N;
+      const int64_t off = ok ? ((int64_t)(n0 + ec) * ng + gw0 + eg) : 0;
+      if constexpr (F::KQ) {   // (d, dmin) of the super-block, (sc, m) of the sub-block
+        const int64_t soff = ok ? ((int64_t)(n0 + ec) * (ng >> 3) + ((gw0 + eg) >> 3)) : 0;
+        sraw[j] = reinterpret_cast<const uint32_t*>(a.scales)[soff];
+        zraw[j] = reinterpret_cast<const uint16_t*>(a.zeros)[off];
       } else {
-#pragma unroll
-        for (int q = 0; q < TW / 4; ++q) {
-          const u4 v = *reinterpret_cast<const u4*>(tp + 4 * q);
-#pragma unroll
-          for (int d = 0; d < 4; ++d) ent[nb][4 * q + d] = v[d];
-        }
+        sraw[j] = reinterpret_cast<const uint16_t*>(a.scales)[off];
+        if constexpr (F::HAS_Z) zraw[j] = reinterpret_cast<const uint16_t*>(a.zeros)[off];
+        else zraw[j] = F::ZBITS;  // the implicit zero point
       }
     }
-  };
-  // the VALU phase: B dequantized from the run's codes and the entries
-  auto dequant = [&](int s, const uint32_t (&ent)[NB][TW], h8 (&bf)[NB]) {
-    const int tau = s / NR, p = s % NR;
+  }
+
+  // 2. per-lane byte offsets (fixed for all stages): x row quarters, code rows
+  uint32_t voff[2 * MB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) bf[nb] = gtab_weights<FMT>(cq[tau % CD][nb], p, ent[nb]);
-  };
-  auto mma = [&](int s, const h8 (&bf)[NB]) {
+  for (int q = 0; q < 2 * MB; ++q) {
+    const int m = q * 16 + (lane >> 2);
+    const int u = (lane & 3) ^ ((m >> 2) & 3);
+    const int ucol = S::WIDE ? u * 8 : 0;              // 8-bit codes: added per stage below
+    voff[q] = (uint32_t)((min(m0 + m, a.M - 1) * a.ldx + ucol) * 2);   // rows past M: any finite data
+  }
+  // 8-bit codes: sub-chunk u of a piece sits 8 (u & 1) + 32 (u >> 1) past the
+  // piece's first k (the second half from lane group g2 + 2); u is the same
+  // for every q above, since q moves m by multiples of 16
+  const int usub = (lane & 3) ^ ((lane >> 4) & 3);
+  const int subk = 8 * (usub & 1) + 32 * (usub >> 1);
+  const char* cb[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NB; ++nb) {
+    const int rb = min((n0 >> 4) + 2 * nb + ((lane >> 4) & 1), a.rowblocks - 1);  // columns past N: never stored
+    cb[nb] = reinterpret_cast<const char*>(a.packed) + (int64_t)rb * a.wordtiles * 1024 + (g2 * 16 + r) * 16;
+  }
+  // ALL: every wave issues all TPW * STAGES stages, those past its share with
+  // the tile clamped in bounds (never computed), so the loads form one
+  // straight-line sequence and every wait is a fixed count (the compiler's
+  // own waits for the code registers then need no merge over branches).
+  // Otherwise (splits that leave waves with few or no tiles) a wave issues
+  // only its own stages.
+  u4 bq[DEPTH][S::CH][NB];   // code chunks of the stages in flight
+  auto issue_stage = [&](int st) {
+    const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
+    const int kt = min(wt0 + t, a.wordtiles - 1);
+    uint8_t* dst = wbuf + (st % DEPTH) * S::SB;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s % XD][mb], bf[nb], acc[mb][nb], 0, 0, 0);
+    for (int p = 0; p < 2; ++p) {
+      const char* src;
+      if constexpr (S::WIDE) {
+        const int kp = kt * F::KT + seg_k(p, h, j);
+        src = reinterpret_cast<const char*>(a.x) + (kp < a.K ? kp : 0) * 2;  // past K: scale 0
+      } else {
+        const int kk = kt * F::KT + 16 * p + subk;                          // this lane's sub-chunk
+        src = reinterpret_cast<const char*>(a.x) + (kk < a.K ? kk : 0) * 2;
+      }
+#pragma unroll
+      for (int q = 0; q < 2 * MB; ++q)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(src + voff[q]),
+            (void __attribute__((address_space(3)))*)(dst + (p * 2 * MB + q) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < S::CH; ++c)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        bq[st % DEPTH][c][nb] = *reinterpret_cast<const u4*>(cb[nb] + (int64_t)kt * 1024 + (h + c) * 512);
+    __builtin_amdgcn_sched_barrier(0);   // stages stay in issue order (the waits count them)
   };
 
-  // 3. the first XD - 1 steps in flight, then the table (the compiler waits
-  //    for the scale/zero loads only: they were issued first)
+  f16v acc[MB][NB];
 #pragma unroll
-  for (int s = 0; s < XD - 1 && s < STEPS; ++s) issue(s);
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int jn = 0; jn < NB; ++jn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.0f;
+
+  // byte offset of the A fragment (m-block mb, step) inside a stage: piece
+  // g2 holds TM rows of 64 bytes
+  auto a_off = [&](int mb, int step) {
+    const int m = mb * 32 + (lane & 31);
+    return g2 * (TM * 64) + m * 64 + ((step ^ ((m >> 2) & 3)) << 4);
+  };
+
+  // 3. one stage: every LDS operand first, then B operands (13 VALU per
+  //    4-bit word, 14 per two 8-bit words) interleaved with the 4*MB*NB MFMAs
+  auto compute_stage = [&](int st) {
+    const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
+    const int kt = wt0 + t;
+    const uint8_t* sb = wbuf + (st % DEPTH) * S::SB;
+    uint32_t szv[S::CH][NB];
+    u4 bt[S::CH][NB];
+    bool live[S::CH];
+    h8 af[4][MB];
+#pragma unroll
+    for (int c = 0; c < S::CH; ++c) {
+      // first k of this lane's codes in chunk c
+      const int kseg = kt * F::KT + (S::WIDE ? seg_k(g2, h, j) : 16 * (g2 + 2 * c));
+      live[c] = kseg < a.K;                             // codes past K: scale 0
+      const int gi = min(max((kseg >> lg) - gw0, 0), gwn - 1);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        bt[c][nb] = bq[st % DEPTH][c][nb];
+        szv[c][nb] = szl[(nb * 32 + (lane & 31)) * SZS + gi];
+      }
+    }
+#pragma unroll
+    for (int step = 0; step < 4; ++step)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) af[step][mb] = *reinterpret_cast<const h8*>(sb + a_off(mb, step));
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the math
+    h2 s2[S::CH][NB];
+    f16 z[S::CH][NB];
+    uint32_t kqc[S::CH][NB];   // q4k: fp16 (d*sc) | -fp16(dmin*m) << 16, 0 past K
+#pragma unroll
+    for (int c = 0; c < S::CH; ++c)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        s2[c][nb] = splat(live[c] ? __builtin_bit_cast(f16, (uint16_t)(szv[c][nb] & 0xffffu)) : (f16)0.0f);
+        z[c][nb] = F::KQ ? (f16)0.0f : __builtin_bit_cast(f16, (uint16_t)(szv[c][nb] >> 16));
+        kqc[c][nb] = live[c] ? szv[c][nb] : 0u;
+      }
+    h8 bf[4][NB];
+#pragma unroll
+    for (int step = 0; step < 4; ++step)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int c = S::WIDE ? 0 : step >> 1;
+        h2 q[4];
+        if constexpr (FMT == INT2_ASYM) {
+          qmz_int2_half(bt[0][nb][2 * j + (step >> 1)], step & 1, make_zc2(z[0][nb]), q);
+        } else if constexpr (FMT == Q8_0) {
+          const ZC8 zc = make_zc8(z[c][nb]);
+          qmz_int8(bt[c][nb][2 * (step & 1)], zc, q);
+          qmz_int8(bt[c][nb][2 * (step & 1) + 1], zc, q + 2);
+        } else {
+          qmz_int4(bt[0][nb][step], make_zc4(z[0][nb]), q);
+        }
+        h2 w0, w1, w2, w3;
+        if constexpr (F::KQ) {
+          h2 wq[4];
+          kq_weights(q, kqc[0][nb], wq, 4);
+          w0 = wq[0]; w1 = wq[1]; w2 = wq[2]; w3 = wq[3];
+        } else {
+          const h2 sc = s2[c][nb];
+          w0 = q[0] * sc; w1 = q[1] * sc; w2 = q[2] * sc; w3 = q[3] * sc;
+        }
+        bf[step][nb] = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+      }
+#pragma unroll
+    for (int step = 0; step < 4; ++step)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[step][mb], bf[step][nb], acc[mb][nb], 0, 0, 0);
+    // schedule: the first step's operands, then per MFMA a share of the VALU
+    // (2 x 2 blocks: 26, then 16 x (one MFMA, six VALU))
+    constexpr int VFIRST = 13 * NB, VPER = NBLK == 4 ? 6 : 13 * NB / MB;
+    __builtin_amdgcn_sched_group_barrier(0x002, VFIRST, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * NBLK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
+    }
+  };
+
+  // 4. first stages in flight, then the scale/zero table (waiting for the
+  //    scale/zero loads only)
+  constexpr int NST = TPW * S::STAGES;
+  const int lim = ALL ? NST : min(nst, NST);   // stages this wave issues
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < lim) issue_stage(d);
+  // the table is written with the stages still in flight: its stores are
+  // plain ds_write_b32 in asm, since the compiler would otherwise wait for
+  // every outstanding global->LDS load before an LDS store it cannot tell
+  // apart from them (the table lies outside every wave's ring)
+  {
+    const int ist = min(DEPTH, lim);
+    if (ist >= 3) wait_vm<(DEPTH >= 3 ? 3 : 0) * S::DMA>();
+    else if (ist == 2) wait_vm<(DEPTH >= 2 ? 2 : 0) * S::DMA>();
+    else if (ist == 1) wait_vm<S::DMA>();
+    else wait_vm<0>();
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NSZ; ++j) {
     const int e = tid + NW * 64 * j;
     if (j < nsz && (e >> lgs) < TN) {
-      uint32_t ent[TW];
-      gtab_entry<FMT>(sraw[j], zraw[j], ent);
-      uint32_t* tp = szl + ((e >> lgs) * SZS + (e & (gsr - 1))) * TW;
-#pragma unroll
-      for (int d = 0; d < TW; ++d) tp[d] = ent[d];
+      const uint32_t v = F::KQ ? kq_half_pair(sraw[j], zraw[j]) : (sraw[j] & 0xffffu) | (zraw[j] << 16);
+      const uint32_t addr = (uint32_t)(uintptr_t)(szl + (e >> lgs) * SZS + (e & (gsr - 1)));
+      asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
     }
   }
-  if (tid < TN) {   // the all-zero entry of each column
-#pragma unroll
-    for (int d = 0; d < TW; ++d) szl[(tid * SZS + GEMM_GCAP) * TW + d] = 0u;
-  }
-  __syncthreads();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
 
-  // 4. the K loop, software-pipelined: the loads of step s + XD - 1 (so XD - 1
-  //    steps stay in flight while the wave waits), then the MFMAs of step s
-  //    interleaved with the operands of step s + 1 (the compiler waits for
-  //    that step's loads only)
-  h8 bf0[NB], bf1[NB];
-  uint32_t ent[NB][TW];
-  fetch(0, ent);
-  dequant(0, ent, bf0);
-  constexpr int VW = FMT == Q8_0 ? 14 : 13;               // VALU per B operand
-  constexpr int MLEAD = NBLK >= 16 ? 4 : NBLK / 4;        // MFMAs ahead of each LDS phase
-  constexpr int VPER = (VW * NB + NBLK - 2 * MLEAD - 1) / (NBLK - 2 * MLEAD);
-  static_assert(NBLK > 2 * MLEAD, "MFMAs per step");
+  // 5. the K loop: wait for stage st (newer stages may stay in flight),
+  //    compute it, refill its buffer with stage st + DEPTH
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    // the loads of step s + XD - 1 first, into the slot step s - 1 has left
-    if (s + XD - 1 < STEPS) issue(s + XD - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (s % 2 == 0) {
-      mma(s, bf0);
-      if (s + 1 < STEPS) { fetch(s + 1, ent); dequant(s + 1, ent, bf1); }
-    } else {
-      mma(s, bf1);
-      if (s + 1 < STEPS) { fetch(s + 1, ent); dequant(s + 1, ent, bf0); }
-    }
-    if (s + 1 < STEPS) {
-      // MFMAs of step s cover the wait for step s + 1's loads and the LDS
-      // round trip of its operands; the rest carry its dequantization
-      __builtin_amdgcn_sched_group_barrier(0x008, MLEAD, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x080, 4 * MB + NB * (TW + 3) / 4, 0);   // DS
-      __builtin_amdgcn_sched_group_barrier(0x008, MLEAD, 0);
-#pragma unroll
-      for (int t = 0; t < NBLK - 2 * MLEAD; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
+  for (int st = 0; st < NST; ++st) {
+    if (st < lim) {
+      const int newer = min(DEPTH - 1, lim - 1 - st);   // stages issued after st
+      if (newer >= 2) wait_vm<(DEPTH >= 3 ? 2 : 0) * S::DMA>();
+      else if (newer == 1) wait_vm<(DEPTH >= 2 ? 1 : 0) * S::DMA>();
+      else wait_vm<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (!ALL || st < nst) compute_stage(st);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + DEPTH < lim) {
+        wait_lgkm0();  // this buffer's reads are back
+        __builtin_amdgcn_sched_barrier(0);
+        issue_stage(st + DEPTH);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // 5. sum the waves' accumulators through LDS in wave order; wave w finishes
-  //    blocks w * UPW .. + UPW - 1
-  __syncthreads();                                       // every wave is done with the table
+  // 6. sum the NW waves' accumulators through LDS in wave order
+  //    (deterministic); each wave first writes its own into its ring region
+  //    (its loads and LDS reads are done), then wave w finishes quads
+  //    w * UPW .. + UPW - 1, so the reads, sums and stores spread over every wave
+  f4* red = reinterpret_cast<f4*>(smem);
+  constexpr int WSF = WS / 16;                           // region stride in f4
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) red[(wave * NBLK + mb * NB + nb) * 64 + lane] = acc[mb][nb];
+    for (int q = 0; q < 4; ++q) {
+      const f16v& A = acc[blk / NB][blk % NB];
+      red[wave * WSF + (blk * 4 + q) * 64 + lane] = f4{A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]};
+    }
   __syncthreads();
   if (!fin) return;
   f4 tot[UPW];
 #pragma unroll
-  for (int u = 0; u < UPW; ++u) {
-    const int blk = wave * UPW + u;
-    f4 v = red[blk * 64 + lane];
+  for (int k = 0; k < UPW; ++k) {
+    const int u = wave * UPW + k;                       // quad u & 3 of block u >> 2
+    f4 v = red[u * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) v += red[(w * NBLK + blk) * 64 + lane];
-    tot[u] = v;
+    for (int w = 1; w < NW; ++w) v += red[w * WSF + u * 64 + lane];
+    tot[k] = v;
   }
   if (a.splits == 1) {
 #pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-      const int blk = wave * UPW + u;
-      const int col = n0 + 16 * (blk % NB) + r;
+    for (int k = 0; k < UPW; ++k) {
+      const int u = wave * UPW + k, blk = u >> 2, q = u & 3;
+      const int col = n0 + (blk % NB) * 32 + (lane & 31);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + 16 * (blk / NB) + 4 * g + e;
+        const int row = m0 + (blk / NB) * 32 + acc_row(4 * q + e, lane);
         if (row < a.M && col < a.N)
-          a.y[(int64_t)row * a.ldy + col] = (f16)(tot[u][e] + (float)__builtin_bit_cast(f16, (uint16_t)res[u][e]));
+          a.y[(int64_t)row * a.ldy + col] = (f16)(tot[k][e] + (float)__builtin_bit_cast(f16, (uint16_t)res[4 * k + e]));
       }
     }
     return;
   }
-  // split-K: this split's partial tile, [tile][split][block][lane] f4
+  // split-K: this split's TM x TN partial; gemm_reduce_kernel sums the splits
   f4* wsp = reinterpret_cast<f4*>(a.ws);
   const int64_t tile = (int64_t)tm * a.tiles_n + tn;
-  const int64_t base = (tile * a.splits + split) * NBLK;
+  const int64_t base = (tile * a.splits + split) * UNITS;
 #pragma unroll
-  for (int u = 0; u < UPW; ++u) wsp[(base + wave * UPW + u) * 64 + lane] = tot[u];
+  for (int k = 0; k < UPW; ++k) wsp[(base + wave * UPW + k) * 64 + lane] = tot[k];
 }
 
 // Sums a tile's split partials in split order (deterministic), adds the
-// residual and rounds once to fp16.  One wave per 16 x 16 block (grid:
-// tiles, NBLK / 4 workgroups of 4 waves), 4 outputs per lane in the GEMM's
-// accumulator layout: rows 4g + e, column r.
+// residual and rounds once to fp16.  One workgroup of 4 waves per 32 x 32
+// block fb of the tile (grid: column tile, row tile, block), so the partials
+// are read by MB * NB workgroups per tile; wave q owns quad q of the block in
+// the GEMM's accumulator layout, 4 outputs per lane.
 template <int MB, int NB>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
   constexpr int NBLK = MB * NB;
-  const int64_t tile = blockIdx.x;
-  const int blk = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (blk >= NBLK) return;
-  const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-  const int tm = (int)(tile / a.tiles_n), tn = (int)(tile % a.tiles_n);
-  const int col = tn * 16 * NB + 16 * (blk % NB) + r;
-  const int row0 = tm * 16 * MB + 16 * (blk / NB) + 4 * g;
+  const int tn = blockIdx.x, tm = blockIdx.y, fb = blockIdx.z;
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m0 = tm * 32 * MB, n0 = tn * 32 * NB;
+  const int64_t tile = (int64_t)tm * a.tiles_n + tn;
+  const f4* wsp = reinterpret_cast<const f4*>(a.ws);
+  const int col = n0 + (fb % NB) * 32 + (lane & 31);
   const int colc = min(col, a.N - 1);
+  // every load is issued before the first use: residual, then the partials
+  // four splits at a time, added in split order (deterministic)
   uint32_t rr[4] = {0u, 0u, 0u, 0u};   // fp16 bits, one per register (no packing wait)
-  if (a.resid) {
+  if (a.resid) {   // uniform branch: the four loads go out together
+    const uint16_t* rb16 = reinterpret_cast<const uint16_t*>(a.resid);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rr[e] = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)min(row0 + e, a.M - 1) * a.ldr + colc];
+    for (int e = 0; e < 4; ++e) {
+      const int row = min(m0 + (fb / NB) * 32 + acc_row(4 * q + e, lane), a.M - 1);
+      rr[e] = rb16[(int64_t)row * a.ldr + colc];
+    }
   }
-  const f4* pp = reinterpret_cast<const f4*>(a.ws) + (tile * a.splits * NBLK + blk) * 64 + lane;
-  const int64_t pstride = (int64_t)NBLK * 64;            // one split, in f4
+  const f4* pp = wsp + ((tile * a.splits * NBLK + fb) * 4 + q) * 64 + lane;
+  const int64_t pstride = NBLK * 4 * 64;        // one split, in f4
   f4 sum = f4{0.f, 0.f, 0.f, 0.f};
   int s = 0;
   for (; s + 4 <= a.splits; s += 4) {
@@ -1495,11 +1509,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
     sum += p0; sum += p1; sum += p2; sum += p3;
   }
   for (; s < a.splits; ++s) sum += pp[s * pstride];
+  float res[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) res[e] = (float)__builtin_bit_cast(f16, (uint16_t)rr[e]);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int row = row0 + e;
-    if (row < a.M && col < a.N)
-      a.y[(int64_t)row * a.ldy + col] = (f16)(sum[e] + (float)__builtin_bit_cast(f16, (uint16_t)rr[e]));
+    const int row = m0 + (fb / NB) * 32 + acc_row(4 * q + e, lane);
+    if (row < a.M && col < a.N) a.y[(int64_t)row * a.ldy + col] = (f16)(sum[e] + res[e]);
   }
 }
 
@@ -1662,29 +1678,43 @@ static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, int rows, hipStr
   }
 }
 
-// GEMM: one workgroup per (column tile, row tile, split) on a 1-D grid (the
-// kernel maps ids to tiles); TPW = word tiles per wave, the fewest
-// instantiated (1, 2, 4, 8) that cover the split; XD = 4 steps of x in flight.
-template <int FMT, int MB, int NB>
+// grid: x = column tiles, y = row tiles, z = K splits; MB x NB blocks of 32 x 32.
+// Two stages in flight per wave where that measured faster (32 x 32 tiles,
+// q8_0), one elsewhere (the 64-row tiles' rings then leave the L2 path less
+// crowded).  TPW is the fewest word tiles per wave (1, 2, 4, or 8 on 32 x 32
+// tiles) that cover the split, since every wave issues all TPW * STAGES stages.
+template <int FMT, int D, int MB, int NB, int TPW>
+static void launch_gemm_tpw(const GemmArgs& a, const Plan& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.splits), block(GEMM_THREADS);
+  constexpr int NW = GEMM_THREADS / 64;
+  // issue every stage in every wave when that wastes at most an eighth of them
+  if ((int64_t)8 * (NW * TPW - p.tps) <= NW * TPW)
+    hipLaunchKernelGGL((gemm_kernel<FMT, NW, TPW, D, MB, NB, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<FMT, NW, TPW, D, MB, NB, false>), grid, block, 0, s, a);
+}
+
+template <int FMT, int D, int MB, int NB>
 static void launch_gemm_fmt(const GemmArgs& a, const Plan& p, hipStream_t s) {
   constexpr int NW = GEMM_THREADS / 64;
-  const dim3 grid((unsigned)((int64_t)p.tiles_n * p.tiles_m * p.splits)), block(GEMM_THREADS);
-  constexpr int TMAX = gemm_tpw_cap(FMT, MB * NB == 16);   // the plan's cap
-  const int per = (int)ceil_div(p.tps, NW);
-  if (per <= 1) hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, 1, GEMM_XD>), grid, block, 0, s, a);
-  else if (per <= 2) hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, 2, GEMM_XD>), grid, block, 0, s, a);
-  else if (per <= 4 || TMAX <= 4) hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, (TMAX < 4 ? TMAX : 4), GEMM_XD>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, NW, TMAX, GEMM_XD>), grid, block, 0, s, a);
+  constexpr int TMAX = MB * NB == 1 ? GEMM_TPW_SMALL : FMT == Q8_0 ? GEMM_TPW_Q8 : GEMM_TPW;
+  static_assert(TMAX == 2 || TMAX == 4 || TMAX == 8, "tile counts instantiated below");
+  const int per = (int)ceil_div(p.tps, NW);   // <= TMAX (the plan's cap)
+  if (per <= 1) launch_gemm_tpw<FMT, D, MB, NB, 1>(a, p, s);
+  else if (per <= 2 || TMAX == 2) launch_gemm_tpw<FMT, D, MB, NB, 2>(a, p, s);
+  else if (per <= 4 || TMAX == 4) launch_gemm_tpw<FMT, D, MB, NB, (TMAX >= 4 ? 4 : 2)>(a, p, s);
+  else launch_gemm_tpw<FMT, D, MB, NB, TMAX>(a, p, s);
 }
 
 template <int MB, int NB>
 static void launch_gemm_tiles(const GemmArgs& a, const Plan& p, int fmt, hipStream_t s) {
+  constexpr int D = MB * NB == 1 ? GEMM_DEPTH : 1;
   switch (fmt) {
-    case QG_INT4_ASYM: launch_gemm_fmt<INT4_ASYM, MB, NB>(a, p, s); break;
-    case QG_INT2_ASYM: launch_gemm_fmt<INT2_ASYM, MB, NB>(a, p, s); break;
-    case QG_Q8_0: launch_gemm_fmt<Q8_0, MB, NB>(a, p, s); break;
-    case QG_Q4K: launch_gemm_fmt<Q4K, MB, NB>(a, p, s); break;
-    default: launch_gemm_fmt<Q4_0, MB, NB>(a, p, s); break;
+    case QG_INT4_ASYM: launch_gemm_fmt<INT4_ASYM, D, MB, NB>(a, p, s); break;
+    case QG_INT2_ASYM: launch_gemm_fmt<INT2_ASYM, D, MB, NB>(a, p, s); break;
+    case QG_Q8_0: launch_gemm_fmt<Q8_0, GEMM_DEPTH, MB, NB>(a, p, s); break;
+    case QG_Q4K: launch_gemm_fmt<Q4K, D, MB, NB>(a, p, s); break;
+    default: launch_gemm_fmt<Q4_0, D, MB, NB>(a, p, s); break;
   }
 }
 
@@ -1741,8 +1771,7 @@ int validate_call(const Call& c, Plan* plan) {
     // the kernels form byte offsets of x rows and of one row block's codes in 32 bits
     if ((int64_t)c.M * c.ldx * 2 >= (int64_t)1 << 32 || p.splits > 65535) return QG_E_UNSUPPORTED;
     if (p.path == 1 && (int64_t)p.wordtiles * 1024 >= (int64_t)1 << 32) return QG_E_UNSUPPORTED;
-    // the GEMM addresses the metadata as one 32-bit buffer range
-    if (p.path == 2 && (int64_t)c.N * (c.K / meta_group(c.fmt, c.group)) * 2 >= (int64_t)1 << 32) return QG_E_UNSUPPORTED;
+    if (p.path == 2 && p.tiles_m > 65535) return QG_E_UNSUPPORTED;
   }
   *plan = p;
   return QG_OK;
@@ -1798,21 +1827,20 @@ int launch_call(const Call& c, const Plan& p, float* wsf, void* stream) {
   a.ws = wsf;
   a.ldx = c.ldx; a.ldr = c.ldr; a.ldy = c.ldy;
   a.M = M; a.N = N; a.K = K; a.group = meta_group(fmt, c.group);   // q4k: the 32-weight sub-block
-  a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.tiles_n = p.tiles_n; a.tiles_m = p.tiles_m;
+  a.wordtiles = p.wordtiles; a.rowblocks = p.rowblocks; a.tiles_n = p.tiles_n;
   a.splits = p.splits; a.tps = p.tps;
-  if (p.tm == 32) launch_gemm_tiles<2, 2>(a, p, fmt, s);
-  else if (p.tn == 32) launch_gemm_tiles<4, 2>(a, p, fmt, s);
-  else launch_gemm_tiles<4, 4>(a, p, fmt, s);
+  if (p.tm == 32) launch_gemm_tiles<1, 1>(a, p, fmt, s);
+  else if (p.tn == 32) launch_gemm_tiles<2, 1>(a, p, fmt, s);
+  else launch_gemm_tiles<2, 2>(a, p, fmt, s);
   if (p.splits > 1) {
     const int st = launch_status();
     if (st != QG_OK) return st;
-    const unsigned tiles = (unsigned)((int64_t)p.tiles_n * p.tiles_m);
     if (p.tm == 32)
-      hipLaunchKernelGGL((gemm_reduce_kernel<2, 2>), dim3(tiles, 1), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_reduce_kernel<1, 1>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1), dim3(256), 0, s, a);
     else if (p.tn == 32)
-      hipLaunchKernelGGL((gemm_reduce_kernel<4, 2>), dim3(tiles, 2), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_reduce_kernel<2, 1>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 2), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_reduce_kernel<4, 4>), dim3(tiles, 4), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_reduce_kernel<2, 2>), dim3((unsigned)p.tiles_n, (unsigned)p.tiles_m, 4), dim3(256), 0, s, a);
   }
   return launch_status();
 }
@@ -1880,7 +1908,7 @@ int qpack(const uint32_t* canon, uint32_t* packed, int N, int K, int fmt, void* 
   const int64_t total = (int64_t)(qg_packed_bytes(N, K, fmt) / sizeof(uint32_t));
   if (total == 0) return QG_OK;
   hipLaunchKernelGGL(qpack_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), canon, packed, N, K,
+                     reinterpret_cast<hipStream_t>(stream), canon, packed, N, K / cpw_of(fmt),
                      (int)n_wordtiles(K, fmt), bits_of(fmt), total);
   return launch_status();
 }

@@ -126,14 +126,10 @@ size_t qg_packed_bytes(int64_t N, int64_t K, int fmt);
  * qunpack(qpack(c)) == c bit for bit.
  *   canon  [device, in]  uint32 [N, K/cpw] canonical words.
  *   packed [device, out] qg_packed_bytes(N, K, fmt) bytes.
- * Packed order: uint32 [ceil(N/16)][ceil(K/cpw/16)][64 lanes][4 words].  A
- * word tile spans KT = 16*cpw consecutive k of 16 rows; lane l = 16*g + r
- * holds codes of row 16*rb + r only.  Code kt of the tile (0 <= kt < KT) goes
- * to lane group g = (kt % 32) / 8, position p = 8*(kt / 32) + kt % 8 of the
- * lane's 4*cpw codes: word p / cpw, code j = p % cpw of that word, stored in
- * slot (j&1)*cpw/2 + j/2 (even codes in the low half of the word, odd codes
- * in the high half).  Each lane thus holds runs of 8 consecutive k, and the
- * four lane groups of a row block cover 32 consecutive k per run.
+ * Packed order: uint32 [ceil(N/16)][ceil(K/cpw/16)][64 lanes][4 words]; lane
+ * l = 16*g + r holds words 4g..4g+3 of the 16-word slice of row 16*rb + r,
+ * each word with its codes reordered so that even codes fill the low half and
+ * odd codes the high half (code j -> slot (j&1)*cpw/2 + j/2).
  * Errors: QG_E_ARG (bad format, N or K < 0, K % cpw != 0, NULL with N*K > 0),
  *         QG_E_ALIGN, QG_E_DEVICE.
  */

@@ -115,24 +115,20 @@ def test_packed_bytes(N, K, fmt, expect):
 
 
 def decode_packed_by_formula(packed, N, K, fmt):
-    """The packed order as the header documents it, written out in Python:
-    inside a word tile of 16 * cpw codes, code kt sits in lane group
-    (kt % 32) // 8 at position 8 * (kt // 32) + kt % 8 of the lane's codes."""
+    """The packed order as the header documents it, written out in Python."""
     b = oracle.BITS[fmt]
     cpw = 32 // b
-    kt_w = 16 * cpw
-    wt = -(-(K // cpw) // 16)
+    kw_n = K // cpw
+    wt = -(-kw_n // 16)
     codes = np.zeros((N, K), dtype=np.uint8)
     for n in range(N):
-        rb, r = n // 16, n % 16
-        for k in range(K):
-            T, kt = k // kt_w, k % kt_w
-            g = (kt % 32) // 8
-            pos = 8 * (kt // 32) + kt % 8
-            t, j = pos // cpw, pos % cpw
+        for kw in range(kw_n):
+            rb, r, T, wi = n // 16, n % 16, kw // 16, kw % 16
+            g, t = wi // 4, wi % 4
             word = int(packed[((rb * wt + T) * 64 + g * 16 + r) * 4 + t])
-            slot = (j & 1) * (cpw // 2) + (j >> 1)
-            codes[n, k] = (word >> (b * slot)) & ((1 << b) - 1)
+            for j in range(cpw):
+                slot = (j & 1) * (cpw // 2) + (j >> 1)
+                codes[n, kw * cpw + j] = (word >> (b * slot)) & ((1 << b) - 1)
     return codes
 
 

@@ -42,7 +42,7 @@ def _run_both(c, M, residual):
 # (fmt, group, N, K, M): every pair's first case needs more split-K partials
 # than its second, and each plan splits K, so the array is really used
 PAIRS = [
-    ((2, 32, 2048, 16384, 128), (0, 32, 64, 16384, 40)),   # GEMM split 4 (4 MiB), then GEMM split
+    ((2, 32, 2048, 8192, 128), (0, 32, 64, 16384, 40)),    # GEMM split 4 (4 MiB), then GEMM split
     ((0, 128, 256, 8192, 1), (3, 32, 32, 4096, 1)),        # GEMV split 8, then a smaller GEMV split
     ((3, 32, 1024, 16384, 128), (4, 256, 16, 8192, 8)),    # GEMM split 8, then the MFMA GEMV split
 ]
