@@ -248,7 +248,12 @@ def main():
         f"| GEMV (M=1, N=6144, K=2048, INT4 g128) | {t_gemv['dispatches']} | {t_gemv['fetch_kib_median']} | "
         f"{t_gemv['write_kib_median']} | {t_gemv['bytes']} | {GEMV_BYTES} | {t_gemv['ratio']} |",
         f"| GEMM (M=128, N=8192, K=2048, INT4 g128) | {t_gemm['dispatches']} | {t_gemm['fetch_kib_median']} | "
-        f"{t_gemm['write_kib_median']} | {t_gemm['bytes']} | {GEMM_BYTES} | {t_gemm['ratio']} |", ""]
+        f"{t_gemm['write_kib_median']} | {t_gemm['bytes']} | {GEMM_BYTES} | {t_gemm['ratio']} |", "",
+        "FETCH_SIZE counts what the L2s request from the fabric (Infinity Cache or HBM).  Expected with each "
+        "byte of W fetched once: GEMV W 6684672 + x 4096 per XCD x 8 = 6717440 B read, y 12288 B written; GEMM W "
+        f"{GEMM_BYTES} + x 524288 per XCD x 8 (every column tile reads all of x, and each XCD's L2 fetches its "
+        f"own copy) = {GEMM_BYTES + 8 * 524288} B read, y 2097152 B written.  Measured reads: GEMV "
+        f"{t_gemv['fetch_bytes']} B, GEMM {t_gemm['fetch_bytes']} B.", ""]
     files["hbm_traffic_counters.md"] = "\n".join(t) + "\n"
     lt = ["# Looped shared block: L2 fabric bytes and L2-miss latency per loop (rocprofv3 --pmc)", ""] + hdr + [
         "Runs `pmc_loop128_*` / `pmc_loop1_*` (`bench.py --only loop_prof`): the warm-up loop, an eviction, L=8 "
