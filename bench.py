@@ -63,7 +63,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=810)
     ap.add_argument("--warmup", type=int, default=81)
-    ap.add_argument("--only", choices=["all", "main", "gemm", "loop", "loop_prof", "fp16", "copy", "stream", "floor"],
+    ap.add_argument("--only", choices=["all", "main", "gemm", "loop", "loop_prof", "loop_prof_persistent", "fp16", "copy",
+                                       "stream", "floor"],
                     default="all",
                     help="main/gemm/loop/fp16/stream/floor: run one leg (for profiler runs); copy: the calibration "
                          "copy; loop_prof: the looped block resident and with the cache evicted between loops")
@@ -269,6 +270,16 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
             if int(status[0]) != 0:
                 raise RuntimeError("qloop_block_persistent: a grid barrier gave up")
             res["persistent_" + mode] = per
+        # all L loops in one launch (each XCD keeps its rows' weights in its L2)
+        x.copy_(x0)
+        evict(torch)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        qgm.loop_block_persistent(x, lins, L, scratch=scratch, status=status, events=ev[:1] + [None] * (L - 1) + ev[1:],
+                                  one_launch=True)
+        ev[-1].synchronize()
+        if int(status[0]) != 0:
+            raise RuntimeError("qloop_block_persistent (one launch): a grid barrier gave up")
+        res["persistent_one_launch_total"] = ev[0].elapsed_time(ev[1])
     wbytes = sum(l.weight_bytes for l in lins)
     flops = 2.0 * M * (D * 3 * D + D * D + D * F + F * D)
     cold, warm = res["cold"], res["warm"]
@@ -291,6 +302,7 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
                    persistent_loop1_cold_ms=round(pc[0], 4),
                    persistent_loops2_L_ms=round(float(np.median(pc[1:])), 4),
                    persistent_evict_each_loop_median_ms=round(float(np.median(pe)), 4))
+        out["persistent_one_launch_ms_per_loop"] = round(res["persistent_one_launch_total"] / L, 4)
     hb = load_loop_traffic(name)
     if hb is not None:
         out["residency_counters"] = hb   # L2 fetch bytes and latency per loop (profiles/loop_traffic.json)
@@ -317,6 +329,25 @@ def loop_prof(qgm, torch, synth, L=8, M=128):
         qgm.loop_block(x, lins, 1, scratch=scratch)
     torch.cuda.synchronize()
     print(json.dumps(dict(loop_prof=True, M=M, L=L)), flush=True)
+
+
+def loop_prof_persistent(qgm, torch, synth, L=8, reps=3):
+    """For the counters: the M = 1 block in one persistent launch, `reps`
+    times for one loop and `reps` times for L loops, each after an eviction."""
+    lc = synth.loop_workload(M=1, L=L)
+    lins = [qgm.QuantLinear.from_case(c, "cuda") for c in lc.linears()]
+    x0 = qgm.to_half_tensor(lc.x0, "cuda")
+    D, F = lc.x0.shape[1], lc.up.N
+    scratch = torch.empty(3 * D + D + F, dtype=torch.float16, device="cuda")
+    status = torch.zeros(4, dtype=torch.int32, device="cuda")
+    x = x0.clone()
+    for loops in [1] * reps + [L] * reps:
+        x.copy_(x0)
+        evict(torch)
+        qgm.loop_block_persistent(x, lins, loops, scratch=scratch, status=status, one_launch=True)
+    torch.cuda.synchronize()
+    assert int(status[0]) == 0
+    print(json.dumps(dict(loop_prof_persistent=True, L=L, reps=reps)), flush=True)
 
 
 def stream_leg(qgm, torch, nbytes, steps, replays, grids=(256, 512, 1024, 2048)):
@@ -537,6 +568,9 @@ def main():
         return
     if args.only == "loop_prof":
         loop_prof(qgm, torch, synth, M=args.loop_m)
+        return
+    if args.only == "loop_prof_persistent":
+        loop_prof_persistent(qgm, torch, synth)
         return
     if args.only == "fp16":
         print(json.dumps(fp16_leg(qgm, torch, synth)), flush=True)

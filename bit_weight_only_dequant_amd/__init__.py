@@ -59,7 +59,7 @@ _SIGS = {
     "qg_plan": ([_I, _I, _I, _I, _I, ctypes.POINTER(_I)], _I),
     "qg_classify_pointer": ([_I, _I, _I, _I], _I),
     "qgemm_noalloc": ([_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P], _I),
-    "qloop_block_persistent": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+    "qloop_block_persistent": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P], _I),
     "qg_stream_read": ([_P, _SZ, _P, _I, _P], _I),
     "qg_empty_launch": ([_I, _I, _P], _I),
     "qg_mfma_probe": ([_P, _I, _I, _P], _I),
@@ -416,11 +416,12 @@ def loop_block(x, linears: Sequence[QuantLinear], L: int, scratch=None, events=N
 
 
 def loop_block_persistent(x, linears: Sequence[QuantLinear], L: int, scratch=None, status=None, events=None,
-                          stream=None):
-    """The looped shared block at M = 1 with one launch per loop (grid
-    barriers between the four GEMVs); see qloop_block_persistent.  Returns
-    (x, status): status is an int32 device tensor, 0 once the loops completed
-    and 1 if a barrier stopped waiting (read it after synchronizing)."""
+                          stream=None, one_launch: bool = False):
+    """The looped shared block at M = 1 with one launch per loop, or with one
+    launch for all L loops (one_launch), grid barriers between the GEMVs; see
+    qloop_block_persistent.  Returns (x, status): status is an int32 device
+    tensor, 0 once the loops completed and 1 if a barrier stopped waiting
+    (read it after synchronizing)."""
     torch = _torch()
     packed4, scales4, zeros4, M, D, F, group, fmt, scratch, ev, st_ = _loop_args(x, linears, L, scratch, events,
                                                                                   stream)
@@ -429,7 +430,7 @@ def loop_block_persistent(x, linears: Sequence[QuantLinear], L: int, scratch=Non
     elif status.dtype != torch.int32 or status.device != x.device:
         raise ValueError("status must be an int32 tensor on x's device")
     st = _lib.qloop_block_persistent(_ptr(x), packed4, scales4, zeros4, M, D, F, group, fmt, L, _ptr(scratch),
-                                     _ptr(status), ev, st_)
+                                     1 if one_launch else 0, _ptr(status), ev, st_)
     _check(st, "qloop_block_persistent")
     return x, status
 

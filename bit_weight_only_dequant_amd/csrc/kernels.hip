@@ -579,7 +579,10 @@ template <int FMT, int NW, int TPW, int MMAX> constexpr size_t gemv_half_lds_byt
 // (gemv_half_lds_bytes); the kernel below and the persistent looped block
 // both run it.  COHERENT: the outputs are stored with agent scope (written
 // through to the level every XCD reads), for readers in the same launch.
-template <int FMT, int NW, int TPW, int MMAX, bool COHERENT = false>
+// COHERENT_IN: x and the residual are read with agent scope too (they were
+// written in the same launch after this workgroup may have cached an older
+// copy); the weights keep plain loads, so they can stay in the caches.
+template <int FMT, int NW, int TPW, int MMAX, bool COHERENT = false, bool COHERENT_IN = false>
 __device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by, uint8_t* half_smem) {
   using F = Fmt<FMT>;
   static_assert(TPW % 2 == 0, "tiles go in pairs");
@@ -636,8 +639,14 @@ __device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by
   }
   const int om = (tid >> 4) % MMAX;   // output row of thread tid < 16 MMAX (final sum)
   uint32_t res = 0u;                  // its residual, fp16 bits (no branch, no wait here)
-  if (a.resid && a.splits == 1)
-    res = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)min(om, a.M - 1) * a.ldr + min(row0 + (tid & 7), a.N - 1)];
+  if (a.resid && a.splits == 1) {
+    const uint16_t* rp = reinterpret_cast<const uint16_t*>(a.resid) + (int64_t)min(om, a.M - 1) * a.ldr +
+                         min(row0 + (tid & 7), a.N - 1);
+    if constexpr (COHERENT_IN)
+      res = __hip_atomic_load(reinterpret_cast<const unsigned short*>(rp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      res = *rp;
+  }
   __builtin_amdgcn_sched_barrier(0);
   u4 xr[NXC];
 #pragma unroll
@@ -645,7 +654,14 @@ __device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by
     const int c = lane + 64 * j;   // one row: chunk c at k0 + 8c (lanes past the wave's slice read in range too)
     const int m = MMAX == 1 ? 0 : c / (KW / 8), k = k0 + (MMAX == 1 ? c : c % (KW / 8)) * 8;
     const bool ok = (MMAX == 1 || m < a.M) && k < a.K;
-    xr[j] = *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(a.x) + (ok ? ((uint32_t)m * a.ldx + k) * 2u : 0u));
+    const char* xp = reinterpret_cast<const char*>(a.x) + (ok ? ((uint32_t)m * a.ldx + k) * 2u : 0u);
+    if constexpr (COHERENT_IN) {
+      const unsigned* q = reinterpret_cast<const unsigned*>(xp);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) xr[j][d] = __hip_atomic_load(q + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      xr[j] = *reinterpret_cast<const u4*>(xp);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   u4 code[NP];
@@ -788,7 +804,8 @@ struct LoopArgs {
   GemvArgs lin[4];
   unsigned* counter;   // arrivals, zeroed before the call's first loop
   int* status;         // set to 1 when a barrier gives up waiting
-  int barrier0;        // barriers passed before this loop (3 per loop)
+  int barrier0;        // barriers passed before this launch
+  int loops;           // loops this launch runs (1, or all L of the call)
   int cap;             // polls before a barrier gives up
 };
 
@@ -831,20 +848,29 @@ __device__ __forceinline__ void grid_barrier(unsigned* counter, unsigned target,
 
 constexpr int LOOP_THREADS = 512;   // 8 waves, as the 8-row GEMV
 
-// TA word tiles per wave for the K = D linears (QKV, O, up), TB for down (K = F)
-template <int FMT, int TA, int TB>
+// TA word tiles per wave for the K = D linears (QKV, O, up), TB for down (K = F).
+// ALL: the launch runs all p.loops loops of the call, with a barrier between
+// loops too, and reads its activations with agent scope (they are rewritten
+// every loop); the workgroup that runs a block of rows runs it in every loop,
+// so its XCD's L2 can keep those rows' weights from one loop to the next.
+template <int FMT, int TA, int TB, bool ALL>
 __global__ __launch_bounds__(LOOP_THREADS) void loop_block_kernel(LoopArgs p) {
   constexpr size_t LA = gemv_half_lds_bytes<FMT, 8, TA, 1>(), LB = gemv_half_lds_bytes<FMT, 8, TB, 1>();
+  constexpr int BPL = ALL ? 4 : 3;   // barriers per loop
   __shared__ __align__(16) uint8_t smem[LA > LB ? LA : LB];
+  const int loops = ALL ? p.loops : 1;
+  for (int l = 0; l < loops; ++l) {
 #pragma unroll
-  for (int ph = 0; ph < 4; ++ph) {
-    const int nb = 2 * p.lin[ph].rowblocks;
-    for (int vb = blockIdx.x; vb < nb; vb += gridDim.x) {
-      if (ph < 3) gemv_half_body<FMT, 8, TA, 1, true>(p.lin[ph], vb, 0, smem);
-      else gemv_half_body<FMT, 8, TB, 1, true>(p.lin[ph], vb, 0, smem);
-      __syncthreads();   // smem is reused by the next block
+    for (int ph = 0; ph < 4; ++ph) {
+      const int nb = 2 * p.lin[ph].rowblocks;
+      for (int vb = blockIdx.x; vb < nb; vb += gridDim.x) {
+        if (ph < 3) gemv_half_body<FMT, 8, TA, 1, true, ALL>(p.lin[ph], vb, 0, smem);
+        else gemv_half_body<FMT, 8, TB, 1, true, ALL>(p.lin[ph], vb, 0, smem);
+        __syncthreads();   // smem is reused by the next block
+      }
+      if (ph < 3 || l + 1 < loops)
+        grid_barrier(p.counter, (unsigned)(p.barrier0 + BPL * l + ph + 1) * gridDim.x, p.status, p.cap);
     }
-    if (ph < 3) grid_barrier(p.counter, (unsigned)(p.barrier0 + ph + 1) * gridDim.x, p.status, p.cap);
   }
 }
 
@@ -2109,41 +2135,45 @@ static int loop_tpw(int64_t wordtiles) {
 }
 
 extern "C++" {
-template <int FMT>
+template <int FMT, bool ALL>
 static const void* loop_kernel_for(int ta, int tb) {
-  if (ta == 2 && tb == 2) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 2, 2>);
-  if (ta == 2 && tb == 4) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 2, 4>);
-  if (ta == 2 && tb == 8) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 2, 8>);
-  if (ta == 4 && tb == 4) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 4, 4>);
-  if (ta == 4 && tb == 8) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 4, 8>);
-  if (ta == 8 && tb == 8) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 8, 8>);
+  if (ta == 2 && tb == 2) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 2, 2, ALL>);
+  if (ta == 2 && tb == 4) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 2, 4, ALL>);
+  if (ta == 2 && tb == 8) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 2, 8, ALL>);
+  if (ta == 4 && tb == 4) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 4, 4, ALL>);
+  if (ta == 4 && tb == 8) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 4, 8, ALL>);
+  if (ta == 8 && tb == 8) return reinterpret_cast<const void*>(&loop_block_kernel<FMT, 8, 8, ALL>);
   return nullptr;
+}
+template <bool ALL>
+static const void* loop_kernel_all(int fmt, int ta, int tb) {
+  switch (fmt) {
+    case QG_INT4_ASYM: return loop_kernel_for<INT4_ASYM, ALL>(ta, tb);
+    case QG_INT2_ASYM: return loop_kernel_for<INT2_ASYM, ALL>(ta, tb);
+    case QG_Q4_0: return loop_kernel_for<Q4_0, ALL>(ta, tb);
+    case QG_Q4K: return loop_kernel_for<Q4K, ALL>(ta, tb);
+    default: return nullptr;
+  }
 }
 }  // extern "C++"
 
-static const void* loop_kernel(int fmt, int ta, int tb) {
-  switch (fmt) {
-    case QG_INT4_ASYM: return loop_kernel_for<INT4_ASYM>(ta, tb);
-    case QG_INT2_ASYM: return loop_kernel_for<INT2_ASYM>(ta, tb);
-    case QG_Q4_0: return loop_kernel_for<Q4_0>(ta, tb);
-    case QG_Q4K: return loop_kernel_for<Q4K>(ta, tb);
-    default: return nullptr;
-  }
+static const void* loop_kernel(int fmt, int ta, int tb, bool all) {
+  return all ? loop_kernel_all<true>(fmt, ta, tb) : loop_kernel_all<false>(fmt, ta, tb);
 }
 
 int qloop_block_persistent(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
                            const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt, int L,
-                           uint16_t* scratch, int* status, void* const* events, void* stream) {
+                           uint16_t* scratch, int mode, int* status, void* const* events, void* stream) {
   LoopSetup ls;
   int st = loop_setup(x, packed4, scales4, zeros4, M, D, F, group, fmt, L, scratch, &ls);
   if (st != QG_OK) return st;
-  if (!status) return QG_E_ARG;
+  if (!status || (mode != 0 && mode != 1)) return QG_E_ARG;
   if (check_align(status) != QG_OK) return QG_E_ALIGN;
   if (M != 1) return QG_E_UNSUPPORTED;
   const int ta = loop_tpw(ls.plans[0].wordtiles), tb = loop_tpw(ls.plans[3].wordtiles);
   for (int i = 0; i < 3; ++i)
     if (ls.plans[i].wordtiles != ls.plans[0].wordtiles) return QG_E_UNSUPPORTED;
-  const void* fn = ta && tb ? loop_kernel(fmt, ta, tb) : nullptr;
+  const void* fn = ta && tb ? loop_kernel(fmt, ta, tb, mode == 1) : nullptr;
   if (!fn) return QG_E_UNSUPPORTED;
   int dev = 0;
   st = current_device(&dev);
@@ -2172,7 +2202,7 @@ int qloop_block_persistent(uint16_t* x, const uint32_t* const* packed4, const ui
   int64_t grid = std::min<int64_t>(std::min<int64_t>((int64_t)per_cu * cus, cus), widest);
   const int grid_env = env_int("QGEMM_LOOP_GRID", 0);
   if (grid_env > 0) grid = std::min<int64_t>(grid, grid_env);
-  if ((int64_t)3 * L * grid >= (int64_t)UINT_MAX) return QG_E_UNSUPPORTED;   // the counter's range
+  if ((int64_t)4 * L * grid >= (int64_t)UINT_MAX) return QG_E_UNSUPPORTED;   // the counters' range
   unsigned* counter = nullptr;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (L > 0) {
@@ -2203,15 +2233,21 @@ int qloop_block_persistent(uint16_t* x, const uint32_t* const* packed4, const ui
   la.counter = counter;
   la.status = status;
   la.cap = env_int("QGEMM_LOOP_SPIN_CAP", 1 << 18);
-  for (int l = 0; l < L; ++l) {
+  // mode 0: one launch per loop (3 barriers each); mode 1: one launch for all
+  // L loops (4 barriers per loop but the last), after which every per-loop
+  // event is recorded
+  const int launches = mode == 1 ? 1 : L;
+  for (int l = 0; l < launches; ++l) {
     la.barrier0 = 3 * l;
+    la.loops = mode == 1 ? L : 1;
     void* args[1] = {&la};
     st = hip_status(hipLaunchKernel(fn, dim3((unsigned)grid), dim3(LOOP_THREADS), args, 0, s));
     if (st != QG_OK) {
       clear_pending_error();
       return st;
     }
-    if (record_event(events, l + 1, s) != QG_OK) return QG_E_DEVICE;
+    for (int e = mode == 1 ? 1 : l + 1; e <= (mode == 1 ? L : l + 1); ++e)
+      if (record_event(events, e, s) != QG_OK) return QG_E_DEVICE;
   }
   return QG_OK;
 }

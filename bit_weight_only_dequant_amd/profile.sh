@@ -48,4 +48,9 @@ done
 for m in 128 1; do   # L2-miss latency: in-flight reads accumulated per cycle, and their count
   step "pmc_loop${m}_lat" 180 --pmc TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum -- --only loop_prof --loop-m "$m"
 done
+# the M = 1 block in one persistent launch: L = 1 against L = 8
+for c in FETCH_SIZE WRITE_SIZE; do
+  step "pmc_persist_$c" 180 --pmc "$c" -- --only loop_prof_persistent
+done
+step pmc_persist_lat 180 --pmc TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum -- --only loop_prof_persistent
 echo "profile runs complete: $OUT"

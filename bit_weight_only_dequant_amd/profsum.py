@@ -149,6 +149,27 @@ def loop_latency(outdir, leg, L=8):
                 read_requests_per_loop=int(np.median(qr.sum(axis=1))))
 
 
+def persistent_residency(outdir, cal, L=8, reps=3):
+    """The one-launch persistent block (loop_prof_persistent): `reps` launches
+    of one loop, then `reps` of L loops, each after an eviction.  Per launch:
+    calibrated fabric bytes and the L2-miss latency; per loop of the L-loop
+    launch, bytes / L."""
+    def per_launch(run, name):
+        v = select(counter(outdir, run, name), "loop_block_kernel")
+        if len(v) != 2 * reps:
+            raise ValueError(f"{run}: {len(v)} launches of the persistent kernel, expected {2 * reps}")
+        return np.asarray(v, dtype=np.float64)
+    f = per_launch("pmc_persist_FETCH_SIZE", "FETCH_SIZE") * 1024 * cal["fetch_factor"]
+    w = per_launch("pmc_persist_WRITE_SIZE", "WRITE_SIZE") * 1024 * cal["write_factor"]
+    lev = per_launch("pmc_persist_lat", "TCC_EA0_RDREQ_LEVEL_sum")
+    req = per_launch("pmc_persist_lat", "TCC_EA0_RDREQ_sum")
+    b1, bL = float(np.median((f + w)[:reps])), float(np.median((f + w)[reps:]))
+    l1, lL = float(np.median((lev / req)[:reps])), float(np.median((lev / req)[reps:]))
+    return dict(launch_1_loop_bytes=int(b1), launch_L_loops_bytes=int(bL), L=L,
+                bytes_per_loop_L_launch=int(bL / L), latency_1_loop_cycles=round(l1, 1),
+                latency_L_loops_cycles=round(lL, 1))
+
+
 def md_trace(title, cmd_note, rows):
     out = [f"# {title}", "", "Commands (GPU host, repository root):", "", "```", PROFILE_CMD, SUMMARY_CMD, "```", "",
            cmd_note, "", "| kernel | dispatches | avg us | p10 | p50 | p90 | min | max |", "|---|---|---|---|---|---|---|---|"]
@@ -233,6 +254,8 @@ def main():
         lm[name] = loop_bytes(a.outdir, leg, cal)
         lm[name].update(loop_latency(a.outdir, leg))
         lm[name]["weight_bytes_per_loop"] = 26738688
+    pr = persistent_residency(a.outdir, cal)
+    lm["loop_block_int4_g128_M1"]["one_launch"] = pr
     files["loop_traffic.json"] = json.dumps(dict(kernel_src_sha=sha, calibration=cal, **lm), indent=1) + "\n"
 
     hdr = ["Commands (GPU host, repository root):", "", "```", PROFILE_CMD, SUMMARY_CMD, "```", "",
@@ -274,6 +297,14 @@ def main():
         lt.append(f"| {name} | {v['dispatches_per_loop']} | {v['loop1_bytes']} | {v['loops2_L_median_bytes']} | "
                   f"{v['evict_each_loop_median_bytes']} | {v['loop1_latency_cycles']} | "
                   f"{v['loops2_L_median_latency_cycles']} | {v['evict_each_loop_median_latency_cycles']} |")
+    lt += ["", "The M = 1 block as one persistent launch for all L = 8 loops (`qloop_block_persistent` mode 1; runs "
+           "`pmc_persist_*`, `bench.py --only loop_prof_persistent`: three launches of one loop, then three of eight, "
+           "each after an eviction).  The workgroup that runs a block of rows runs it in every loop, and nothing "
+           "invalidates the L2s between loops inside one launch, so each XCD's L2 can keep its rows' weights:", "",
+           "| launch | fabric bytes per launch | per loop | L2-miss latency (cycles) |", "|---|---|---|---|",
+           f"| 1 loop | {pr['launch_1_loop_bytes']} | {pr['launch_1_loop_bytes']} | {pr['latency_1_loop_cycles']} |",
+           f"| 8 loops | {pr['launch_L_loops_bytes']} | {pr['bytes_per_loop_L_launch']} | "
+           f"{pr['latency_L_loops_cycles']} |"]
     lt += ["", "Latency of each loop (resident run, loops 1..8; then the control):", ""]
     for name, v in lm.items():
         lt.append(f"- {name}: {v['resident_loop_latency_cycles']}; control {v['evict_each_loop_latency_cycles']}")

@@ -252,6 +252,12 @@ int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* con
  * four GEMVs as phases over blocks of 8 rows of W, separated by grid
  * barriers on counters in device memory the library keeps for the process.
  * Same arguments, layouts and results as qloop_block, plus
+ *   mode   0: one launch per loop (three barriers in each); 1: one launch for
+ *          all L loops (a fourth barrier between loops; x and the residuals
+ *          are then read with agent scope, and the workgroup that runs a block
+ *          of rows in one loop runs it in every loop, so its XCD's L2 can keep
+ *          those rows' weights across loops).  With mode 1 every per-loop
+ *          event is recorded after the one launch.
  *   status [device, out] int32, 16-byte aligned: 0 after the call's loops
  *          complete, 1 if a barrier stopped waiting (its wait is bounded:
  *          QGEMM_LOOP_SPIN_CAP polls, 2^18 by default; then x holds no
@@ -260,12 +266,12 @@ int qloop_block(uint16_t* x, const uint32_t* const* packed4, const uint16_t* con
  * Supported: M == 1; formats QG_INT4_ASYM, QG_INT2_ASYM, QG_Q4_0, QG_Q4K;
  * K of every linear at most 64 word tiles (8192 for 4-bit codes).  Calls that
  * overlap on one device (the counter is shared) race.
- * Errors: as qloop_block, QG_E_ARG (status NULL), QG_E_UNSUPPORTED (M != 1,
- * format or K outside the above).
+ * Errors: as qloop_block, QG_E_ARG (status NULL, mode not 0 or 1),
+ * QG_E_UNSUPPORTED (M != 1, format or K outside the above).
  */
 int qloop_block_persistent(uint16_t* x, const uint32_t* const* packed4, const uint16_t* const* scales4,
                            const uint16_t* const* zeros4, int M, int D, int F, int group, int fmt, int L,
-                           uint16_t* scratch, int* status, void* const* events, void* stream);
+                           uint16_t* scratch, int mode, int* status, void* const* events, void* stream);
 
 /* Debug: packed -> integer codes uint8 [N, K] (device), for the bit-exact
  * check of the kernels' unpack (the nibble / crumb unpack of the TinyLoop

@@ -308,11 +308,11 @@ def test_loop_block_records_no_event_on_error():
     assert _loop_status(F=100, events=[A] * 3) == E_ARG
 
 
-def _persistent_status(M=1, D=64, F=128, group=32, fmt=0, L=2, status=A):
+def _persistent_status(M=1, D=64, F=128, group=32, fmt=0, L=2, status=A, mode=0):
     arr = lambda vals: (ctypes.c_void_p * 4)(*vals)
     zeros = (None,) * 4 if fmt in (2, 3) else (A,) * 4
     return lib.qloop_block_persistent(A, arr((A,) * 4), arr((A,) * 4), arr(zeros), M, D, F, group, fmt, L, A,
-                                      status, None, None)
+                                      mode, status, None, None)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -320,6 +320,8 @@ def _persistent_status(M=1, D=64, F=128, group=32, fmt=0, L=2, status=A):
     (dict(M=1, fmt=3), E_UNSUP),           # q8_0 is not among its formats
     (dict(D=64, F=128 * 128), E_UNSUP),    # K of down: 2048 word tiles, beyond 8 waves x 8
     (dict(status=None), E_ARG),
+    (dict(mode=2), E_ARG),
+    (dict(mode=-1), E_ARG),
     (dict(status=A + 4), E_ALIGN),
     (dict(F=100), E_ARG),                        # the same validation as qloop_block
 ])
