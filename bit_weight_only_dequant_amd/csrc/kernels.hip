@@ -1161,7 +1161,7 @@ template <int FMT, int MB, int NB> struct GemmStage {
 // consecutive rows hit 16 distinct bank groups.  All LDS operands of a stage
 // are read first; group barriers then interleave one MFMA with a few VALU of
 // the dequantization so the two pipes overlap.
-template <int FMT, int NW, int TPW, int DEPTH, int MB, int NB, bool ALL>
+template <int FMT, int NW, int TPW, int DEPTH, int MB, int NB, bool ALL, int CP = 1>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   using F = Fmt<FMT>;
   using S = GemmStage<FMT, MB, NB>;
@@ -1275,8 +1275,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   // own waits for the code registers then need no merge over branches).
   // Otherwise (splits that leave waves with few or no tiles) a wave issues
   // only its own stages.
-  u4 bq[DEPTH][S::CH][NB];   // code chunks of the stages in flight
-  auto issue_stage = [&](int st) {
+  static_assert(CP == 1 || (CP == 2 && DEPTH == 1), "codes one stage ahead of x: one x stage in flight");
+  constexpr int BQ = DEPTH > CP ? DEPTH : CP;
+  constexpr int CL = S::CH * NB;                          // code loads per stage
+  u4 bq[BQ][S::CH][NB];   // code chunks of the stages in flight
+  auto issue_x = [&](int st) {
     const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG, j = hj % SEG;
     const int kt = min(wt0 + t, a.wordtiles - 1);
     uint8_t* dst = wbuf + (st % DEPTH) * S::SB;
@@ -1296,11 +1299,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
             (const void __attribute__((address_space(1)))*)(src + voff[q]),
             (void __attribute__((address_space(3)))*)(dst + (p * 2 * MB + q) * 1024), 16, 0, 0);
     }
+  };
+  auto issue_codes = [&](int st) {
+    const int t = st / S::STAGES, hj = st % S::STAGES, h = hj / SEG;
+    const int kt = min(wt0 + t, a.wordtiles - 1);
 #pragma unroll
     for (int c = 0; c < S::CH; ++c)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        bq[st % DEPTH][c][nb] = *reinterpret_cast<const u4*>(cb[nb] + (int64_t)kt * 1024 + (h + c) * 512);
+        bq[st % BQ][c][nb] = *reinterpret_cast<const u4*>(cb[nb] + (int64_t)kt * 1024 + (h + c) * 512);
+  };
+  auto issue_stage = [&](int st) {
+    issue_x(st);
+    issue_codes(st);
     __builtin_amdgcn_sched_barrier(0);   // stages stay in issue order (the waits count them)
   };
 
@@ -1337,7 +1348,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
       const int gi = min(max((kseg >> lg) - gw0, 0), gwn - 1);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        bt[c][nb] = bq[st % DEPTH][c][nb];
+        bt[c][nb] = bq[st % BQ][c][nb];
         szv[c][nb] = szl[(nb * 32 + (lane & 31)) * SZS + gi];
       }
     }
@@ -1409,11 +1420,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
     if (d < lim) issue_stage(d);
+  if (CP == 2 && 1 < lim) {   // the next stage's codes behind the first stage
+    issue_codes(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // the table is written with the stages still in flight: its stores are
   // plain ds_write_b32 in asm, since the compiler would otherwise wait for
   // every outstanding global->LDS load before an LDS store it cannot tell
   // apart from them (the table lies outside every wave's ring)
-  {
+  if (CP == 2) {
+    if (lim >= 2) wait_vm<(CP == 2 ? S::DMA + CL : 0)>();
+    else if (lim == 1) wait_vm<S::DMA>();
+    else wait_vm<0>();
+  } else {
     const int ist = min(DEPTH, lim);
     if (ist >= 3) wait_vm<(DEPTH >= 3 ? 3 : 0) * S::DMA>();
     else if (ist == 2) wait_vm<(DEPTH >= 2 ? 2 : 0) * S::DMA>();
@@ -1434,7 +1453,31 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs a) {
   __builtin_amdgcn_s_barrier();
 
   // 5. the K loop: wait for stage st (newer stages may stay in flight),
-  //    compute it, refill its buffer with stage st + DEPTH
+  //    compute it, refill its buffer with stage st + DEPTH.  CP = 2: the
+  //    codes of stage st + 1 are already in flight behind stage st's x, so
+  //    their HBM latency hides under stage st's compute
+  if constexpr (CP == 2) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (st < lim) {
+        if (st + 1 < lim) wait_vm<CL>();   // all but the next stage's codes
+        else wait_vm<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (!ALL || st < nst) compute_stage(st);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 1 < lim) {
+          wait_lgkm0();  // this buffer's reads are back
+          __builtin_amdgcn_sched_barrier(0);
+          issue_x(st + 1);
+        }
+        // the waits above count the code loads as the newest: keep them behind
+        // every x load of the stage
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 2 < lim) issue_codes(st + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
     if (st < lim) {
@@ -1706,18 +1749,22 @@ static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, int rows, hipStr
 
 // grid: x = column tiles, y = row tiles, z = K splits; MB x NB blocks of 32 x 32.
 // Two stages in flight per wave where that measured faster (32 x 32 tiles,
-// q8_0), one elsewhere (the 64-row tiles' rings then leave the L2 path less
-// crowded).  TPW is the fewest word tiles per wave (1, 2, 4, or 8 on 32 x 32
+// q8_0), one elsewhere (a second x stage per wave adds L2 traffic at the
+// start and no bandwidth: every CU of an XCD pulls its stage at once, at the
+// L2's rate); with one x stage in flight the codes of the next stage are
+// already loading (their HBM latency hides under the current stage's
+// compute).  TPW is the fewest word tiles per wave (1, 2, 4, or 8 on 32 x 32
 // tiles) that cover the split, since every wave issues all TPW * STAGES stages.
 template <int FMT, int D, int MB, int NB, int TPW>
 static void launch_gemm_tpw(const GemmArgs& a, const Plan& p, hipStream_t s) {
   const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.splits), block(GEMM_THREADS);
   constexpr int NW = GEMM_THREADS / 64;
+  constexpr int CP = D == 1 ? 2 : 1;   // one x stage in flight: the codes run a stage ahead
   // issue every stage in every wave when that wastes at most an eighth of them
   if ((int64_t)8 * (NW * TPW - p.tps) <= NW * TPW)
-    hipLaunchKernelGGL((gemm_kernel<FMT, NW, TPW, D, MB, NB, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<FMT, NW, TPW, D, MB, NB, true, CP>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<FMT, NW, TPW, D, MB, NB, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<FMT, NW, TPW, D, MB, NB, false, CP>), grid, block, 0, s, a);
 }
 
 template <int FMT, int D, int MB, int NB>
