@@ -5,11 +5,12 @@
 A step is one qgemm call of the decode workload: INT4 asymmetric, group 128,
 M=1, N=6144, K=2048 (the fused QKV of a D=2048 block).  Each step reads a
 different copy of the packed weight, scales and zero points; the copies add
-up to more than twice the 256 MB on-die cache, and a 512 MiB write evicts that
+up to more than twice the 256 MB on-die cache, and a 512 MiB read evicts that
 cache before every timed replay, so every timed step streams its weight bytes
 from HBM whatever K is.  The K timed steps are captured once in a HIP graph
-and replayed (median of several replays), bracketed by events on the stream
-the kernels run on.
+between two device clock stamps on the stream the kernels run on, and
+replayed (median of several replays); HIP events around the same replays are
+reported beside them.
 
 One JSON line is printed: value = weight GB/s at M=1, plus the roofline of the
 GEMV kernel against the published HBM peak and against the ceilings measured
@@ -45,12 +46,20 @@ _EVICT = {}
 
 
 def evict(torch):
-    """Write 512 MiB (twice the on-die cache) so that no weight bytes stay
-    cached from earlier work; issued on the current stream, outside any graph."""
+    """Read 512 MiB (twice the on-die cache) so that no weight bytes stay
+    cached from earlier work; issued on the current stream, outside any graph.
+    Reading, not writing: an eviction by writes leaves the cache full of dirty
+    lines, whose write-back to HBM then competes with the timed reads that
+    displace them (about 28 us per timed replay of 20 decode steps)."""
     buf = _EVICT.get("buf")
     if buf is None:
-        buf = _EVICT["buf"] = torch.empty(2 * MALL_BYTES // 2, dtype=torch.float16, device="cuda")
-    buf.fill_(1.0)
+        buf = _EVICT["buf"] = torch.ones(2 * MALL_BYTES // 2, dtype=torch.float16, device="cuda")
+        for _ in range(2):   # the writes above leave dirty lines: read them out once
+            torch.sum(buf, dtype=torch.float32)
+        torch.cuda.synchronize()
+    torch.sum(buf, dtype=torch.float32)
+
+
 KERNEL_SRC = os.path.join(ROOT, "bit_weight_only_dequant_amd", "csrc", "kernels.hip")
 
 
@@ -106,21 +115,54 @@ class Leg:
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                self.step(i)
-        g.replay()  # first replay uploads the graph; not timed
-        torch.cuda.synchronize()
-        self.replay_ms = replay_times(torch, g, steps, replays)
+        g, stamps = capture(self.qgm, torch, self.step, steps)
+        self.replay_ms, self.replay_ms_events = replay_times(torch, g, steps, replays, stamps)
         return float(np.median(self.replay_ms))
 
 
-def replay_times(torch, g, steps, replays):
+class Stamps:
+    """Two device clock stamps (qg_clock_stamp) around the steps of a graph."""
+
+    def __init__(self, qgm, torch):
+        self.qgm = qgm
+        self.buf = torch.zeros(2, dtype=torch.int64, device="cuda")
+        self.khz = qgm.clock_rate_khz(torch.cuda.current_device())
+
+    def first(self):
+        self.qgm.clock_stamp(self.buf[0:1])
+
+    def last(self):
+        self.qgm.clock_stamp(self.buf[1:2])
+
+    def span_ms(self):
+        t = self.buf.cpu().tolist()
+        return (t[1] - t[0]) / self.khz
+
+
+def capture(qgm, torch, step, steps):
+    """`steps` calls of step(i) captured in one HIP graph between two device
+    clock stamps; the first replay (which uploads the graph) is not timed."""
+    stamps = Stamps(qgm, torch)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stamps.first()
+        for i in range(steps):
+            step(i)
+        stamps.last()
+    g.replay()
+    torch.cuda.synchronize()
+    return g, stamps
+
+
+def replay_times(torch, g, steps, replays, stamps):
     """ms per step of each of `replays` timed replays of graph g, the on-die
-    cache evicted before each."""
+    cache evicted before each: from the device clock stamps inside the graph
+    (exactly the steps), and from HIP events recorded on the stream around the
+    replay (the steps plus the graph's own launch latency, about 11 us per
+    replay on this runtime, which only an event recorded inside the graph could
+    exclude, and the runtime refuses event records during capture)."""
     stream = torch.cuda.current_stream()
-    out = []
+    inner, events = [], []
     for _ in range(replays):
         evict(torch)
         start = torch.cuda.Event(enable_timing=True)
@@ -129,8 +171,9 @@ def replay_times(torch, g, steps, replays):
         g.replay()
         stop.record(stream)
         stop.synchronize()
-        out.append(start.elapsed_time(stop) / steps)
-    return out
+        events.append(start.elapsed_time(stop) / steps)
+        inner.append(stamps.span_ms() / steps)
+    return inner, events
 
 
 FORMAT_NAMES = ("int4_asym", "int2_asym", "q4_0", "q8_0", "q4k")
@@ -368,15 +411,12 @@ def stream_leg(qgm, torch, nbytes, steps, replays, grids=(256, 512, 1024, 2048))
         for i in range(4):
             step(i)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                step(i)
-        g.replay()
-        torch.cuda.synchronize()
-        ms = float(np.median(replay_times(torch, g, steps, replays)))
+        g, stamps = capture(qgm, torch, step, steps)
+        inner, events = replay_times(torch, g, steps, replays, stamps)
+        ms = float(np.median(inner))
         gbs = nbytes / (ms * 1e-3) / 1e9
-        rows.append(dict(workgroups=wg, us_per_launch=round(ms * 1e3, 3), GBps=round(gbs, 1)))
+        rows.append(dict(workgroups=wg, us_per_launch=round(ms * 1e3, 3), GBps=round(gbs, 1),
+                         us_per_launch_events=round(float(np.median(events)) * 1e3, 3)))
         if best is None or gbs > best["GBps"]:
             best = rows[-1]
         del g
@@ -388,14 +428,10 @@ def empty_floor(qgm, torch, workgroups, threads, steps, replays):
     for _ in range(4):
         qgm.empty_launch(workgroups, threads)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(steps):
-            qgm.empty_launch(workgroups, threads)
-    g.replay()
-    torch.cuda.synchronize()
-    ms = float(np.median(replay_times(torch, g, steps, replays)))
-    return dict(workgroups=workgroups, threads=threads, us_per_launch=round(ms * 1e3, 3))
+    g, stamps = capture(qgm, torch, lambda i: qgm.empty_launch(workgroups, threads), steps)
+    inner, events = replay_times(torch, g, steps, replays, stamps)
+    return dict(workgroups=workgroups, threads=threads, us_per_launch=round(float(np.median(inner)) * 1e3, 3),
+                us_per_launch_events=round(float(np.median(events)) * 1e3, 3))
 
 
 def mfma_peaks(qgm, torch):
@@ -428,16 +464,12 @@ def mfma_peaks(qgm, torch):
 def graph_time(torch, step, steps, warmup):
     """ms per step of `step(i)`, captured once in a HIP graph and replayed
     once after an eviction of the on-die cache."""
+    import bit_weight_only_dequant_amd as qgm
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(steps):
-            step(i)
-    g.replay()
-    torch.cuda.synchronize()
-    return replay_times(torch, g, steps, 1)[0]
+    g, stamps = capture(qgm, torch, step, steps)
+    return replay_times(torch, g, steps, 1, stamps)[0][0]
 
 
 def fp16_leg(qgm, torch, synth, Ms=(1, 8, 32, 128, 512, 2048)):
@@ -590,6 +622,7 @@ def main():
         print(json.dumps(main_r), flush=True)
         return
     replay_ms = list(leg.replay_ms)
+    ms_events = float(np.median(leg.replay_ms_events))
     wbytes, copies = leg.wbytes, leg.copies
     del leg
     torch.cuda.empty_cache()
@@ -644,6 +677,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
+        "ms_per_step_events": round(ms_events, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -653,10 +687,14 @@ def main():
                    "M": 1, "N": 6144, "K": 2048, "group": 128, "format": "int4_asym",
                    "weight_bytes_per_step": wbytes, "weight_copies": copies,
                    "weight_bytes_per_replay": wbytes * args.steps, "on_die_cache_bytes": MALL_BYTES,
-                   "timing": f"K steps captured in one HIP graph; median of {MAIN_REPLAYS} timed replays, "
-                             "each after a 512 MiB write that evicts the on-die cache",
+                   "timing": f"K steps captured in one HIP graph between two device clock stamps "
+                             f"(qg_clock_stamp, stream order); ms_per_step = stamp span / K, the median of "
+                             f"{MAIN_REPLAYS} timed replays, each after a 512 MiB read that evicts the on-die cache; "
+                             "ms_per_step_events = HIP events on the stream around the same replays, which also "
+                             "hold the graph's own launch latency (events cannot be recorded inside a graph here)",
                    "replay_ms_per_step": [round(v, 6) for v in replay_ms]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "achieved_events": round(wbytes / (ms_events * 1e-3) / 1e9, 1),
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": gemv_kernel_name(qgm, main_case),

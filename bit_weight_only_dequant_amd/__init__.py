@@ -64,6 +64,8 @@ _SIGS = {
     "qg_empty_launch": ([_I, _I, _P], _I),
     "qg_mfma_probe": ([_P, _I, _I, _P], _I),
     "qg_device_info": ([_I] + [ctypes.POINTER(_I)] * 4, _I),
+    "qg_clock_stamp": ([_P, _P], _I),
+    "qg_clock_rate": ([_I, ctypes.POINTER(_I)], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -469,6 +471,23 @@ def mfma_probe(out, workgroups: int, iters: int, stream=None):
     if out.dtype != torch.float32 or out.numel() < workgroups * 256:
         raise ValueError("out must be float32 with workgroups * 256 elements")
     _check(_lib.qg_mfma_probe(_ptr(out), workgroups, iters, _stream(out.device, stream)), "qg_mfma_probe")
+
+
+def clock_stamp(out, stream=None):
+    """The device's constant-rate clock into out[0] (an int64 device tensor),
+    in stream order: two stamps bracket exactly the launches between them."""
+    _dev(out, "out")
+    torch = _torch()
+    if out.dtype != torch.int64 or out.numel() < 1:
+        raise ValueError("out must be an int64 device tensor with at least one element")
+    _check(_lib.qg_clock_stamp(_ptr(out), _stream(out.device, stream)), "qg_clock_stamp")
+
+
+def clock_rate_khz(device: int = 0) -> int:
+    """Rate of the clock clock_stamp reads, in kHz."""
+    v = _I()
+    _check(_lib.qg_clock_rate(device, ctypes.byref(v)), "qg_clock_rate")
+    return v.value
 
 
 def device_info(device: int = 0) -> dict:

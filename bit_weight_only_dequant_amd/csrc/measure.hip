@@ -7,7 +7,12 @@
 //   qg_empty_launch - an empty kernel: the launch floor of a grid;
 //   qg_mfma_probe   - back-to-back independent v_mfma_f32_16x16x32_f16 on
 //                     every SIMD: the sustained dense fp16 matrix rate;
-//   qg_device_info  - compute units and clocks as the runtime reports them.
+//   qg_device_info  - compute units and clocks as the runtime reports them;
+//   qg_clock_stamp  - the device's constant-rate clock, stored by one wave in
+//                     stream order: two stamps bracket the launches between
+//                     them on the device (a graph's own launch latency, which
+//                     events around the graph would include, stays outside);
+//   qg_clock_rate   - that clock's rate.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,6 +53,13 @@ __global__ __launch_bounds__(STREAM_THREADS) void stream_read_kernel(const mu4* 
 }
 
 __global__ void empty_kernel() {}
+
+// The stamp is read as the wave starts; stream order puts it after every
+// earlier launch has completed and before any later one starts.
+__global__ void clock_stamp_kernel(uint64_t* __restrict__ out) {
+  const uint64_t t = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) out[0] = t;
+}
 
 // Every wave keeps 8 independent accumulators so that each MFMA waits for no
 // earlier result; the sum of one element per accumulator is written per lane.
@@ -94,6 +106,25 @@ extern "C" int qg_empty_launch(int workgroups, int threads, void* stream) {
   if (workgroups <= 0 || threads <= 0 || threads > 1024) return QG_E_ARG;
   hipLaunchKernelGGL(empty_kernel, dim3(workgroups), dim3(threads), 0, reinterpret_cast<hipStream_t>(stream));
   return hip_status(hipGetLastError());
+}
+
+extern "C" int qg_clock_stamp(uint64_t* out, void* stream) {
+  if (!out) return QG_E_ARG;
+  if (reinterpret_cast<uintptr_t>(out) % 8 != 0) return QG_E_ALIGN;
+  hipLaunchKernelGGL(clock_stamp_kernel, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), out);
+  return hip_status(hipGetLastError());
+}
+
+extern "C" int qg_clock_rate(int device, int* khz) {
+  if (!khz) return QG_E_ARG;
+  int v = 0;
+  const int st = hip_status(hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, device));
+  if (st != QG_OK) {
+    clear_pending_error();
+    return st;
+  }
+  *khz = v;
+  return QG_OK;
 }
 
 extern "C" int qg_mfma_probe(float* out, int workgroups, int iters, void* stream) {

@@ -332,6 +332,22 @@ int qg_mfma_probe(float* out, int workgroups, int iters, void* stream);
 int qg_device_info(int device, int* compute_units, int* clock_khz, int* memory_clock_khz,
                    int* memory_bus_bits);
 
+/* One wave stores the device's constant-rate clock (the counter that
+ * qg_clock_rate reports) into out[0], in stream order: it runs after every
+ * earlier launch on `stream` has completed and before any later one starts,
+ * so two stamps bracket exactly the launches between them on the device.
+ * Inside a captured graph this keeps the graph's own launch latency out of
+ * the bracket, which events recorded around the graph would include (events
+ * cannot be recorded inside a graph on this runtime).  Follows the phase
+ * timings of the TinyLoop README, "Quick CLI Tour", "Benchmark".
+ * out [device, out] uint64 [1], 8-byte aligned; written asynchronously.
+ * Errors: QG_E_ARG (NULL), QG_E_ALIGN, QG_E_DEVICE. */
+int qg_clock_stamp(uint64_t* out, void* stream);
+
+/* Rate (kHz) of the clock qg_clock_stamp reads, as the HIP runtime reports it.
+ * Errors: QG_E_ARG (NULL pointer), QG_E_DEVICE. */
+int qg_clock_rate(int device, int* khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -336,3 +336,11 @@ def test_noalloc_refuses_oversized_plans_before_any_hip_call():
     assert lib.qgemm_noalloc(A, 14336, A, A, None, None, 4096, 512, 4096, 14336, 32, 2, A, 4096, None) == E_WS
     assert lib.qgemm_noalloc(A, 128, A, A, A, None, 16, 0, 16, 128, 32, 0, A, 16, None) == OK   # M = 0: no-op
     assert lib.qgemm_noalloc(A + 2, 128, A, A, A, None, 16, 1, 16, 128, 32, 0, A, 16, None) == E_ALIGN
+
+
+def test_clock_helpers_validate_before_any_hip_call():
+    # the in-graph timing stamps of bench.py: NULL and misaligned outputs are
+    # refused on the host
+    assert lib.qg_clock_stamp(None, None) == E_ARG
+    assert lib.qg_clock_stamp(A + 4, None) == E_ALIGN
+    assert lib.qg_clock_rate(0, None) == E_ARG

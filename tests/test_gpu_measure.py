@@ -32,3 +32,32 @@ def test_mfma_probe_runs_and_rejects_a_small_output():
     assert torch.isfinite(out).all()
     with pytest.raises(ValueError):
         qgm.mfma_probe(out, 9, 3)
+
+
+def test_clock_stamps_bracket_the_launches_between_them():
+    # two stamps in a graph around launches of known duration: the span grows
+    # with the work between them, and agrees with events around a long run
+    khz = qgm.clock_rate_khz(0)
+    assert 1_000 <= khz <= 10_000_000
+    out = torch.empty(64 * 256, dtype=torch.float32, device="cuda")
+    ts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    spans = []
+    for iters in (200, 2000):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            qgm.clock_stamp(ts[0:1])
+            qgm.mfma_probe(out, 64, iters)
+            qgm.clock_stamp(ts[1:2])
+        for _ in range(2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            b.synchronize()
+        t = ts.cpu().tolist()
+        span_ms = (t[1] - t[0]) / khz
+        assert 0.0 < span_ms <= a.elapsed_time(b) * 1.05 + 0.02
+        spans.append(span_ms)
+    assert spans[1] > 5.0 * spans[0]   # ten times the MFMA rounds between the stamps
+    with pytest.raises(ValueError):
+        qgm.clock_stamp(torch.zeros(2, dtype=torch.int32, device="cuda"))
