@@ -102,17 +102,24 @@ def kernel_bytes(outdir, leg, key, cal, algo):
 
 def loop_segments(outdir, run, name, L=8):
     """Per-dispatch values of counter `name` in the loop_prof run `run`, split
-    at the eviction fills: (dispatches per loop k, the resident loops 1..L as
-    an L x k array, the L loops that each follow an eviction as L x k).  Only
-    the qGEMM kernels count, not the weight repack or torch's copies."""
+    at the evictions: (dispatches per loop k, the resident loops 1..L as an
+    L x k array, the L loops that each follow an eviction as L x k).  Only the
+    qGEMM kernels count, not the weight repack or torch's copies.  An
+    eviction is a torch reduction over 512 MiB (the first one also fills its
+    buffer and reads it twice); eviction kernels with no qGEMM dispatch
+    between them are one boundary."""
     seq = counter(outdir, run, name)
     cur, segs = [], []
+    after_evict = False
     for k, v in seq:
-        if "Fill" in k:          # an eviction (torch fill of 512 MiB)
-            segs.append(cur)
-            cur = []
+        if "reduce_kernel" in k or "FillFunctor" in k:
+            if not after_evict:
+                segs.append(cur)
+                cur = []
+            after_evict = True
         elif "qg::" in k and "pack" not in k:
             cur.append(v)
+            after_evict = False
     segs.append(cur)
     k = len(segs[0])                 # dispatches per loop (the warm-up loop)
     if k == 0 or len(segs) != L + 2 or len(segs[1]) != L * k or any(len(x) != k for x in segs[2:]):

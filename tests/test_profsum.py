@@ -17,6 +17,8 @@ COPY = "void at::native::direct_copy_kernel_cuda(at::TensorIteratorBase&)"
 GEMM = "void qg::gemm_kernel<0, 4, 4, 8, 2, 4>(qg::GemmArgs)"
 GEMV = "void qg::gemv_half_kernel<0, 8, 2, 1>(qg::GemvArgs)"
 PACK = "qg::qpack_kernel(unsigned int const*, unsigned int*, int, int, int, int, long)"
+REDUCE = "void at::native::reduce_kernel<512, 1, at::native::ReduceOp<c10::Half, at::native::func_wrapper_t<float> > >"
+ZERO = "__amd_rocclr_fillBufferAligned"
 
 
 def write(path, cols, rows):
@@ -116,3 +118,25 @@ def test_trace_stats(tmp_path):
     s = profsum.stats_us(profsum.select(items, "gemv"))
     assert s["n"] == 10 and s["avg"] == 5.5 and s["min"] == 1.0 and s["max"] == 10.0
     assert s["p50"] == pytest.approx(float(np.percentile(np.arange(1, 11), 50)))
+
+
+def test_loop_split_at_read_evictions(tmp_path):
+    # the eviction is a reduction over 512 MiB; its first call also fills the
+    # buffer and reads it twice: one boundary, however many kernels
+    out = str(tmp_path)
+    cal = dict(fetch_factor=2.0, write_factor=1.0)
+    L, k = 8, 4
+    setup = [(FILL, 0.0)] + [(ZERO, 0.0), (REDUCE, 9.0)] * 3
+    fetch = [(PACK, 1.0)] * 4 + [(GEMM, 10.0)] * k + [(COPY, 50.0)] + setup
+    for i in range(L):
+        fetch += [(GEMM, 100.0 if i == 0 else 3.0)] * k
+    for i in range(L):
+        fetch += [(COPY, 50.0), (ZERO, 0.0), (REDUCE, 9.0)] + [(GEMM, 100.0)] * k
+    write_seq = [(kname, 0.5 if "qg::gemm" in kname else 7.0) for kname, _ in fetch]
+    pmc(out, "pmc_loop1_FETCH_SIZE", "FETCH_SIZE", fetch)
+    pmc(out, "pmc_loop1_WRITE_SIZE", "WRITE_SIZE", write_seq)
+    r = profsum.loop_bytes(out, "loop1", cal, L=L)
+    per = lambda f: k * (f * 1024 * 2 + 0.5 * 1024)
+    assert r["dispatches_per_loop"] == k
+    assert r["resident_loop_bytes"] == [int(per(100.0))] + [int(per(3.0))] * (L - 1)
+    assert r["evict_each_loop_bytes"] == [int(per(100.0))] * L
