@@ -30,6 +30,14 @@ step() {   # step NAME LIMIT_S ROCPROF_ARGS... -- BENCH_ARGS...
 # first import of torch on a fresh machine pages the image in: not profiled
 timeout -k 10 300 python3 -c "import torch; print(torch.__version__)"
 
+# the traced legs once without the profiler, on this machine: the step times
+# the traced durations are read against
+for leg in main gemm floor; do
+  echo "== plain_$leg: python3 bench.py --only $leg"
+  timeout -k 10 300 python3 "$R/bench.py" --only "$leg" > "$OUT/plain_$leg.json" 2> "$OUT/plain_$leg.log"
+  echo "   done"
+done
+
 step trace_main 300 --kernel-trace --stats -- --only main
 step trace_gemm 300 --kernel-trace --stats -- --only gemm
 step trace_stream 300 --kernel-trace --stats -- --only stream

@@ -177,6 +177,24 @@ def persistent_residency(outdir, cal, L=8, reps=3):
                 latency_L_loops_cycles=round(lL, 1))
 
 
+def plain_step_us(outdir, leg):
+    """us per step of `bench.py --only leg` run without the profiler on the
+    same machine (profile.sh runs it first), or None when it is absent."""
+    try:
+        lines = open(os.path.join(outdir, f"plain_{leg}.json")).read().strip().splitlines()
+        r = json.loads(lines[-1])
+    except Exception:
+        return None
+    return r.get("us_per_call", r.get("us_per_launch"))
+
+
+def plain_note(step_us, avg_us, what):
+    if step_us is None:
+        return ""
+    return (f"  Without the profiler, on the same machine just before (`bench.py --only {what}`, device clock "
+            f"stamps inside the graph), one step takes {step_us} us; the traced average is {avg_us} us.")
+
+
 def md_trace(title, cmd_note, rows):
     out = [f"# {title}", "", "Commands (GPU host, repository root):", "", "```", PROFILE_CMD, SUMMARY_CMD, "```", "",
            cmd_note, "", "| kernel | dispatches | avg us | p10 | p50 | p90 | min | max |", "|---|---|---|---|---|---|---|---|"]
@@ -217,13 +235,20 @@ def main():
     gemv = stats_us(select(tm, "gemv"))
     gemm = stats_us(select(tg, "gemm_kernel"))
     empty = stats_us(select(tf, "empty_kernel"))
+    p_main, p_gemm, p_floor = (plain_step_us(a.outdir, leg) for leg in ("main", "gemm", "floor"))
+    for st, p in ((gemv, p_main), (gemm, p_gemm), (empty, p_floor)):
+        if p is not None:
+            st["bench_step_us_same_machine"] = p
     files["dispatch.json"] = json.dumps(dict(kernel_src_sha=sha, gemv_int4_m1=gemv, gemm_int4_m128=gemm,
                                              empty_kernel=empty), indent=1) + "\n"
     files["empty_kernel_launch_floor_kernel_trace.md"] = md_trace(
         "Kernel trace: the empty kernel of the decode GEMV's grid (768 x 512), graph-replayed",
         "Run `trace_floor` (`... -- python3 bench.py --only floor`): bench.py times the same graph at its "
         "launch floor per step; the traced duration of each dispatch also carries what the profiler adds "
-        "to every dispatch, the same for every kernel of the other traces.",
+        "to every dispatch, the same for every kernel of the other traces." +
+        plain_note(p_floor, empty["avg"], "floor") +
+        ("  The difference is the tracer's own cost per dispatch on this machine; it weighs most on the "
+         "shortest kernels." if p_floor is not None else ""),
         [(short(n), stats_us([d for k, d in tf if k == n])) for n in dict.fromkeys(k for k, _ in tf)
          if "empty_kernel" in n])
     files["gemv_int4_g128_m1_n6144_k2048_kernel_trace.md"] = md_trace(
@@ -231,12 +256,14 @@ def main():
         f"Run `trace_main` (`rocprofv3 --kernel-trace --stats -- python3 bench.py --only main`): every dispatch "
         f"of the headline leg (warm-up, graph upload and the timed replays; the cache is evicted before each "
         f"timed replay).  Kernel sources sha256[:16] = `{sha}`.  Algorithmic bytes per launch {GEMV_BYTES}: "
-        f"{GEMV_BYTES / (gemv['avg'] * 1e3):.1f} GB/s at the average duration.", per_kernel(tm))
+        f"{GEMV_BYTES / (gemv['avg'] * 1e3):.1f} GB/s at the average duration." +
+        plain_note(p_main, gemv["avg"], "main"), per_kernel(tm))
     files["gemm_int4_g128_m128_n8192_k2048_kernel_trace.md"] = md_trace(
         "Kernel trace: prefill GEMM, INT4 g128, M=128, N=8192, K=2048",
         f"Run `trace_gemm` (`... -- python3 bench.py --only gemm`).  Kernel sources sha256[:16] = `{sha}`.  "
         f"2*M*N*K = {2 * 128 * 8192 * 2048} flops per launch: "
-        f"{2 * 128 * 8192 * 2048 / (gemm['avg'] * 1e3) / 1e3:.1f} TFLOP/s at the average duration.", per_kernel(tg))
+        f"{2 * 128 * 8192 * 2048 / (gemm['avg'] * 1e3) / 1e3:.1f} TFLOP/s at the average duration." +
+        plain_note(p_gemm, gemm["avg"], "gemm"), per_kernel(tg))
     files["stream_read_6684672B_kernel_trace.md"] = md_trace(
         "Kernel trace: streaming read of 6684672 bytes per launch (the decode weight bytes)",
         f"Run `trace_stream` (`... -- python3 bench.py --only stream`): four grids (256, 512, 1024, 2048 "

@@ -140,3 +140,16 @@ def test_loop_split_at_read_evictions(tmp_path):
     assert r["dispatches_per_loop"] == k
     assert r["resident_loop_bytes"] == [int(per(100.0))] + [int(per(3.0))] * (L - 1)
     assert r["evict_each_loop_bytes"] == [int(per(100.0))] * L
+
+
+def test_plain_step_times_are_read_beside_the_traces(tmp_path):
+    out = str(tmp_path)
+    with open(os.path.join(out, "plain_main.json"), "w") as f:
+        f.write("noise\n" + json.dumps(dict(leg="decode_int4_g128_M1", us_per_call=3.92)) + "\n")
+    with open(os.path.join(out, "plain_floor.json"), "w") as f:
+        f.write(json.dumps(dict(workgroups=768, threads=512, us_per_launch=1.54)) + "\n")
+    assert profsum.plain_step_us(out, "main") == 3.92
+    assert profsum.plain_step_us(out, "floor") == 1.54
+    assert profsum.plain_step_us(out, "gemm") is None
+    assert "3.92 us" in profsum.plain_note(3.92, 4.1, "main")
+    assert profsum.plain_note(None, 4.1, "main") == ""
