@@ -461,10 +461,9 @@ def mfma_peaks(qgm, torch):
                 probe=f"{wg} workgroups x 4 waves x {iters} rounds of 16 independent v_mfma_f32_16x16x32_f16")
 
 
-def graph_time(torch, step, steps, warmup):
+def graph_time(qgm, torch, step, steps, warmup):
     """ms per step of `step(i)`, captured once in a HIP graph and replayed
     once after an eviction of the on-die cache."""
-    import bit_weight_only_dequant_amd as qgm
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -504,8 +503,8 @@ def fp16_leg(qgm, torch, synth, Ms=(1, 8, 32, 128, 512, 2048)):
         def f16_step(i, x=x, y=y):
             torch.matmul(x, w16s[i % n16].t(), out=y)
 
-        t_deq = graph_time(torch, deq_step, steps, 10)
-        t_f16 = graph_time(torch, f16_step, steps, 10)
+        t_deq = graph_time(qgm, torch, deq_step, steps, 10)
+        t_f16 = graph_time(qgm, torch, f16_step, steps, 10)
         fl = 2.0 * M * N * K
         rows.append(dict(M=M, fused_us=round(t_fused * 1e3, 2), dequant_then_fp16_us=round(t_deq * 1e3, 2),
                          fp16_resident_us=round(t_f16 * 1e3, 2),
