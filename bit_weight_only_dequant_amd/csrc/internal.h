@@ -29,7 +29,7 @@ constexpr int GEMM_SMALL_M = 32;         // M <= this: 32 x 32 tiles; M <= 2x th
 constexpr int GEMM_TPW = 2;              // word tiles per wave (K per workgroup <= 16 tiles)
 constexpr int GEMM_TPW_Q8 = 4;           // q8_0: a tile is 64 wide, so 4 per wave (256 of K)
 constexpr int GEMM_TPW_SMALL = 8;        // 32 x 32 tiles (two stages in flight): long K unsplit
-constexpr int GEMM_DEPTH = 2;            // x/code stages in flight per wave
+constexpr int GEMM_DEPTH = 2;            // x stages in flight per wave on 32 x 32 tiles for M > 32
 constexpr int GEMM_GCAP = 64;            // quantization groups per workgroup, at most
 constexpr int GEMM_TARGET_WG = 256;      // one workgroup per compute unit
 

@@ -1748,12 +1748,11 @@ static bool launch_gemv_f(const GemvArgs& a, int mmax, int tps, int rows, hipStr
 }
 
 // grid: x = column tiles, y = row tiles, z = K splits; MB x NB blocks of 32 x 32.
-// Two stages in flight per wave where that measured faster (32 x 32 tiles,
-// q8_0), one elsewhere (a second x stage per wave adds L2 traffic at the
-// start and no bandwidth: every CU of an XCD pulls its stage at once, at the
-// L2's rate); with one x stage in flight the codes of the next stage are
-// already loading (their HBM latency hides under the current stage's
-// compute).  TPW is the fewest word tiles per wave (1, 2, 4, or 8 on 32 x 32
+// D x stages in flight per wave (launch_gemm_tiles picks it).  A second x
+// stage adds L2 traffic at the start and no bandwidth on 64-row tiles: every
+// CU of an XCD pulls its stage at once, at the L2's rate.  With one x stage in
+// flight the codes of the next stage are already loading (their HBM latency
+// hides under the current stage's compute).  TPW is the fewest word tiles per wave (1, 2, 4, or 8 on 32 x 32
 // tiles) that cover the split, since every wave issues all TPW * STAGES stages.
 template <int FMT, int D, int MB, int NB, int TPW>
 static void launch_gemm_tpw(const GemmArgs& a, const Plan& p, hipStream_t s) {
@@ -1779,16 +1778,30 @@ static void launch_gemm_fmt(const GemmArgs& a, const Plan& p, hipStream_t s) {
   else launch_gemm_tpw<FMT, D, MB, NB, TMAX>(a, p, s);
 }
 
-template <int MB, int NB>
-static void launch_gemm_tiles(const GemmArgs& a, const Plan& p, int fmt, hipStream_t s) {
-  constexpr int D = MB * NB == 1 ? GEMM_DEPTH : 1;
+template <int MB, int NB, int D>
+static void launch_gemm_depth(const GemmArgs& a, const Plan& p, int fmt, hipStream_t s) {
   switch (fmt) {
     case QG_INT4_ASYM: launch_gemm_fmt<INT4_ASYM, D, MB, NB>(a, p, s); break;
     case QG_INT2_ASYM: launch_gemm_fmt<INT2_ASYM, D, MB, NB>(a, p, s); break;
-    case QG_Q8_0: launch_gemm_fmt<Q8_0, GEMM_DEPTH, MB, NB>(a, p, s); break;
+    case QG_Q8_0: launch_gemm_fmt<Q8_0, D, MB, NB>(a, p, s); break;
     case QG_Q4K: launch_gemm_fmt<Q4K, D, MB, NB>(a, p, s); break;
     default: launch_gemm_fmt<Q4_0, D, MB, NB>(a, p, s); break;
   }
+}
+
+// One x stage in flight per wave, with the codes a stage ahead, on 64-row
+// tiles and on 32 x 32 tiles up to M = 32; two x stages on 32 x 32 tiles for
+// larger M, where that measured faster (the looped block's down projection,
+// 128 x 2048 x 8192: 14.9 against 15.4 us).
+template <int MB, int NB>
+static void launch_gemm_tiles(const GemmArgs& a, const Plan& p, int fmt, hipStream_t s) {
+  if constexpr (MB * NB == 1) {
+    if (a.M > 32) {
+      launch_gemm_depth<MB, NB, GEMM_DEPTH>(a, p, fmt, s);
+      return;
+    }
+  }
+  launch_gemm_depth<MB, NB, 1>(a, p, fmt, s);
 }
 
 // QGEMM_CHECK=1: every device pointer of a call must be device (or managed)
