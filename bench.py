@@ -72,11 +72,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=810)
     ap.add_argument("--warmup", type=int, default=81)
-    ap.add_argument("--only", choices=["all", "main", "gemm", "loop", "loop_prof", "loop_prof_persistent", "fp16", "copy",
-                                       "stream", "floor"],
+    ap.add_argument("--only", choices=["all", "main", "gemm", "int2", "loop", "loop_prof", "loop_prof_persistent", "fp16",
+                                       "copy", "stream", "floor"],
                     default="all",
-                    help="main/gemm/loop/fp16/stream/floor: run one leg (for profiler runs); copy: the calibration "
-                         "copy; loop_prof: the looped block resident and with the cache evicted between loops")
+                    help="main/gemm/int2/loop/fp16/stream/floor: run one leg (for profiler runs; int2: INT2 g64 at "
+                         "M=1); copy: the calibration copy; loop_prof: the looped block resident and with the cache "
+                         "evicted between loops")
     ap.add_argument("--loop-m", type=int, default=128, help="M of --only loop / loop_prof")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5, help="oracle timings per workload and thread count")
@@ -593,6 +594,12 @@ def main():
         leg = Leg(qgm, torch, c, 128)
         ms = leg.time(max(64, args.steps // 8), 8, replays=SECONDARY_REPLAYS)
         print(json.dumps(leg_result("prefill_int4_g128_M128", leg, ms, 128, SECONDARY_REPLAYS)), flush=True)
+        return
+    if args.only == "int2":
+        c = synth.workload("int2_g64")
+        leg = Leg(qgm, torch, c, 1)
+        ms = leg.time(args.steps, args.warmup, replays=SECONDARY_REPLAYS)
+        print(json.dumps(leg_result("int2_g64_M1", leg, ms, 1, SECONDARY_REPLAYS)), flush=True)
         return
     if args.only == "loop":
         print(json.dumps(loop_leg(qgm, torch, synth, M=args.loop_m)), flush=True)

@@ -6,6 +6,9 @@
 #   bash bit_weight_only_dequant_amd/profile.sh OUTDIR
 #   python3 -m bit_weight_only_dequant_amd.profsum OUTDIR --write profiles
 #
+# With a second argument `valu` only the instruction-count passes of the M = 1
+# GEMVs run (summarised by profsum ... --part valu).
+#
 # Every step runs under its own time limit and the script stops at the first
 # failure.
 set -eo pipefail
@@ -29,6 +32,16 @@ step() {   # step NAME LIMIT_S ROCPROF_ARGS... -- BENCH_ARGS...
 
 # first import of torch on a fresh machine pages the image in: not profiled
 timeout -k 10 300 python3 -c "import torch; print(torch.__version__)"
+
+# instructions issued and cycles waited per wave by the M = 1 GEMVs (INT4
+# decode shape; INT2 g64, N = 8192): seven SQ counters, one pass each
+VALU_COUNTERS=(SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INSTS_LDS SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAVE_CYCLES)
+step pmc_main_valu 180 --pmc "${VALU_COUNTERS[@]}" -- --only main --steps 81 --warmup 8
+step pmc_int2_valu 180 --pmc "${VALU_COUNTERS[@]}" -- --only int2 --steps 103 --warmup 8
+if [ "$2" = "valu" ]; then
+  echo "profile runs complete: $OUT"
+  exit 0
+fi
 
 # the traced legs once without the profiler, on this machine: the step times
 # the traced durations are read against

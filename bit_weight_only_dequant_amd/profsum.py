@@ -220,13 +220,61 @@ def per_kernel(items):
     return [(short(n), stats_us([d for k, d in items if k == n])) for n in names]
 
 
+VALU_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                 "SQ_WAVE_CYCLES")
+
+
+def valu_counters(outdir, run, key):
+    """Medians over the GEMV dispatches of the SQ counters of `run`, and the
+    same per wave."""
+    med = {c: float(np.median(select(counter(outdir, run, c), key))) for c in VALU_COUNTERS}
+    n = len(select(counter(outdir, run, "SQ_WAVES"), key))
+    waves = med["SQ_WAVES"]
+    per = {c: round(med[c] / waves, 1) for c in VALU_COUNTERS if c != "SQ_WAVES"}
+    return dict(dispatches=n, median=med, per_wave=per,
+                wait_share=round(med["SQ_WAIT_ANY"] / med["SQ_WAVE_CYCLES"], 3),
+                issue_wait_share=round(med["SQ_WAIT_INST_ANY"] / med["SQ_WAVE_CYCLES"], 3))
+
+
+def valu_file(outdir, sha):
+    rows = []
+    for label, run, chunks in (("INT4 g128, M=1, N=6144, K=2048 (decode)", "pmc_main_valu", 6144 * 2048 // 32),
+                               ("INT2 g64, M=1, N=8192, K=2048", "pmc_int2_valu", 8192 * 2048 // 64)):
+        v = valu_counters(outdir, run, "gemv")
+        m, pw = v["median"], v["per_wave"]
+        rows.append(f"| {label} | {v['dispatches']} | {m['SQ_WAVES']:.0f} | {pw['SQ_INSTS_VALU']} | "
+                    f"{m['SQ_INSTS_VALU'] * 64 / chunks:.1f} | {pw['SQ_INSTS_VMEM_RD']} | {pw['SQ_INSTS_LDS']} | "
+                    f"{v['wait_share']} | {v['issue_wait_share']} |")
+    return "\n".join([
+        "# Instruction counters: the M = 1 GEMVs (rocprofv3 --pmc, per dispatch)", "",
+        "Commands (GPU host, repository root):", "", "```", "bash bit_weight_only_dequant_amd/profile.sh OUTDIR valu",
+        "python3 -m bit_weight_only_dequant_amd.profsum OUTDIR --part valu --write profiles", "```", "",
+        f"Runs `pmc_main_valu` (`rocprofv3 --pmc {' '.join(VALU_COUNTERS)} -- python3 bench.py --only main "
+        f"--steps 81 --warmup 8`) and `pmc_int2_valu` (the same counters, `--only int2 --steps 103 --warmup 8`).  "
+        f"Kernel sources sha256[:16] = `{sha}`; medians over the GEMV dispatches.  A chunk is one lane's "
+        f"16-byte code load (32 INT4 or 64 INT2 codes); VALU per chunk = the VALU instructions one lane issues "
+        f"per chunk it dequantizes (SQ_INSTS_VALU counts wave instructions: x 64 lanes / chunks per launch), "
+        f"with the staging, lane sums and epilogue included; waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES, the "
+        f"share of a wave's life spent waiting (loads in flight, LDS, barriers); issue waits = "
+        f"SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, the share spent ready but waiting for an instruction to issue.",
+        "", "| launch | dispatches | waves | VALU per wave | VALU per chunk | vector-memory reads per wave | "
+        "LDS instructions per wave | waiting | issue waits |", "|---|---|---|---|---|---|---|---|---|", *rows,
+        ""]) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("outdir")
     ap.add_argument("--write", default=None)
+    ap.add_argument("--part", choices=["all", "valu"], default="all",
+                    help="valu: only the instruction counters of the M = 1 GEMVs (profile.sh OUTDIR valu)")
     a = ap.parse_args()
     sha = kernel_hash()
     files = {}
+    files["gemv_m1_valu_counters.md"] = valu_file(a.outdir, sha)
+    if a.part == "valu":
+        write_files(files, a.write)
+        return 0
 
     tm = trace(a.outdir, "trace_main")
     tg = trace(a.outdir, "trace_gemm")
@@ -365,11 +413,16 @@ def main():
         f"MFMA busy share = busy SIMD-cycles / (1024 SIMDs x the kernel's average duration in cycles at 2.4 GHz, "
         f"{gemm['avg']} us from `trace_gemm`) = {100 * busy:.1f} %.", ""]) + "\n"
 
-    if a.write:
-        os.makedirs(a.write, exist_ok=True)
+    write_files(files, a.write)
+    return 0
+
+
+def write_files(files, dest):
+    if dest:
+        os.makedirs(dest, exist_ok=True)
         for n, txt in files.items():
-            open(os.path.join(a.write, n), "w").write(txt)
-            print("wrote", os.path.join(a.write, n))
+            open(os.path.join(dest, n), "w").write(txt)
+            print("wrote", os.path.join(dest, n))
     else:
         for n, txt in files.items():
             print(f"---- {n}\n{txt}")

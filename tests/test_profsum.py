@@ -153,3 +153,22 @@ def test_plain_step_times_are_read_beside_the_traces(tmp_path):
     assert profsum.plain_step_us(out, "gemm") is None
     assert "3.92 us" in profsum.plain_note(3.92, 4.1, "main")
     assert profsum.plain_note(None, 4.1, "main") == ""
+
+
+def test_valu_counters_per_wave(tmp_path):
+    out = str(tmp_path)
+    vals = dict(SQ_WAVES=6144.0, SQ_INSTS_VALU=6144.0 * 130, SQ_INSTS_VMEM_RD=6144.0 * 4, SQ_INSTS_LDS=6144.0 * 20,
+                SQ_WAIT_ANY=400.0, SQ_WAIT_INST_ANY=100.0, SQ_WAVE_CYCLES=1000.0)
+    for run in ("pmc_main_valu", "pmc_int2_valu"):
+        rows, d = [], 0
+        for c, v in vals.items():   # a non-GEMV dispatch, then three GEMV ones (the middle one doubled)
+            for j, (k, f) in enumerate(((PACK, 9.0), (GEMV, 1.0), (GEMV, 2.0), (GEMV, 1.0))):
+                rows.append(dict(Dispatch_Id=j + 1, Kernel_Name=k, Counter_Name=c, Counter_Value=v * f))
+        write(os.path.join(out, run, "host", "1", f"{run}_counter_collection.csv"), PMC_COLS, rows)
+    v = profsum.valu_counters(out, "pmc_main_valu", "gemv")
+    assert v["dispatches"] == 3
+    assert v["per_wave"]["SQ_INSTS_VALU"] == 130.0 and v["per_wave"]["SQ_INSTS_VMEM_RD"] == 4.0
+    assert v["wait_share"] == 0.4 and v["issue_wait_share"] == 0.1
+    md = profsum.valu_file(out, "0" * 16)
+    # VALU per chunk: 130 per wave x 6144 waves x 64 lanes over 6144 * 2048 / 32 chunks of 32 INT4 codes
+    assert "| 130.0 | 130.0 |" in md
