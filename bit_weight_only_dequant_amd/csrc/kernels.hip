@@ -418,11 +418,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
     }
   }
   const int om = tid >> 5, orow = tid & 15;   // output of thread tid < 32 MMAX (final sum)
-  uint32_t res = 0u;                           // residual, fp16 bits
-  if (a.resid && a.splits == 1) {
-    const int mm = min(om, a.M - 1), nc = min(rb * 16 + orow, a.N - 1);
-    res = reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)mm * a.ldr + nc];
-  }
+  // residual, fp16 bits: loaded unconditionally (from x when there is none,
+  // dropped at the store), since a load under a branch made the compiler
+  // wait for it, and for every load before it, ahead of the x and code loads
+  const bool has_res = a.resid && a.splits == 1;
+  const uint32_t res = has_res ? reinterpret_cast<const uint16_t*>(a.resid)[(int64_t)min(om, a.M - 1) * a.ldr +
+                                                                           min(rb * 16 + orow, a.N - 1)]
+                               : reinterpret_cast<const uint16_t*>(a.x)[0];
   __builtin_amdgcn_sched_barrier(0);
   u4 xr[NXC];
 #pragma unroll
@@ -549,7 +551,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs a) {
   if (tid & 16) return;
   const int on = rb * 16 + orow;
   if (a.splits == 1) {
-    if (om < a.M && on < a.N) a.y[(int64_t)om * a.ldy + on] = (f16)(total + (float)__builtin_bit_cast(f16, (uint16_t)res));
+    if (om < a.M && on < a.N)
+      a.y[(int64_t)om * a.ldy + on] = (f16)(has_res ? total + (float)__builtin_bit_cast(f16, (uint16_t)res) : total);
     return;
   }
   // split-K: this split's partial; gemv_reduce_kernel sums the splits in order
@@ -638,15 +641,19 @@ __device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by
     }
   }
   const int om = (tid >> 4) % MMAX;   // output row of thread tid < 16 MMAX (final sum)
-  uint32_t res = 0u;                  // its residual, fp16 bits (no branch, no wait here)
-  if (a.resid && a.splits == 1) {
-    const uint16_t* rp = reinterpret_cast<const uint16_t*>(a.resid) + (int64_t)min(om, a.M - 1) * a.ldr +
-                         min(row0 + (tid & 7), a.N - 1);
-    if constexpr (COHERENT_IN)
-      res = __hip_atomic_load(reinterpret_cast<const unsigned short*>(rp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      res = *rp;
-  }
+  // its residual, fp16 bits: loaded unconditionally (from x when there is
+  // none, dropped at the store), since a load under a branch made the
+  // compiler wait for it, and for every load before it, ahead of the x and
+  // code loads
+  const bool has_res = a.resid && a.splits == 1;
+  const uint16_t* rp = has_res ? reinterpret_cast<const uint16_t*>(a.resid) + (int64_t)min(om, a.M - 1) * a.ldr +
+                                     min(row0 + (tid & 7), a.N - 1)
+                               : reinterpret_cast<const uint16_t*>(a.x);
+  uint32_t res;
+  if constexpr (COHERENT_IN)
+    res = __hip_atomic_load(reinterpret_cast<const unsigned short*>(rp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    res = *rp;
   __builtin_amdgcn_sched_barrier(0);
   u4 xr[NXC];
 #pragma unroll
@@ -773,7 +780,7 @@ __device__ __forceinline__ void gemv_half_body(const GemvArgs& a, int bx, int by
   const int on = row0 + (tid & 7);
   if (a.splits == 1) {
     if (om < a.M && on < a.N) {
-      const f16 v = (f16)(total + (float)__builtin_bit_cast(f16, (uint16_t)res));
+      const f16 v = (f16)(has_res ? total + (float)__builtin_bit_cast(f16, (uint16_t)res) : total);
       if constexpr (COHERENT)
         __hip_atomic_store(reinterpret_cast<unsigned short*>(a.y) + (int64_t)om * a.ldy + on,
                            __builtin_bit_cast(unsigned short, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
