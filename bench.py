@@ -324,6 +324,7 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
         if int(status[0]) != 0:
             raise RuntimeError("qloop_block_persistent (one launch): a grid barrier gave up")
         res["persistent_one_launch_total"] = ev[0].elapsed_time(ev[1])
+    graph = loop_graph_times(qgm, torch, x, x0, lins, L, scratch)
     wbytes = sum(l.weight_bytes for l in lins)
     flops = 2.0 * M * (D * 3 * D + D * D + D * F + F * D)
     cold, warm = res["cold"], res["warm"]
@@ -347,10 +348,48 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
                    persistent_loops2_L_ms=round(float(np.median(pc[1:])), 4),
                    persistent_evict_each_loop_median_ms=round(float(np.median(pe)), 4))
         out["persistent_one_launch_ms_per_loop"] = round(res["persistent_one_launch_total"] / L, 4)
+    out["graph"] = dict(graph, TFLOPs_loops2_L=round(flops / (graph["loops2_L_us"] * 1e-6) / 1e12, 2),
+                        weight_GBps_loop1_cold=round(wbytes / (graph["loop1_cold_us"] * 1e-6) / 1e9, 1))
     hb = load_loop_traffic(name)
     if hb is not None:
         out["residency_counters"] = hb   # L2 fetch bytes and latency per loop (profiles/loop_traffic.json)
     return out
+
+
+def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5):
+    """Per-loop GPU time of the looped block with no host launch cost in it:
+    L loops, one loop and no loop each captured in a HIP graph between two
+    device clock stamps, every replay after x is reset and the on-die cache
+    evicted (outside the graph).  Loop 1 (cold: weights from HBM, the same as
+    a loop after an eviction) = T_1 - T_0; loops 2..L (weights where loop 1
+    left them) = (T_L - T_1) / (L - 1); medians over the replays.  The eager
+    per-loop events above also time the host's launches, which at M = 1 take
+    about as long as the four GEMVs."""
+    def cap(nloops):
+        stamps = Stamps(qgm, torch)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            stamps.first()
+            if nloops:
+                qgm.loop_block(x, lins, nloops, scratch=scratch)
+            stamps.last()
+        x.copy_(x0)
+        g.replay()
+        torch.cuda.synchronize()
+        return g, stamps
+    graphs = {n: cap(n) for n in (0, 1, L)}
+    t = {n: [] for n in graphs}
+    for _ in range(replays):
+        for n, (g, st) in graphs.items():
+            x.copy_(x0)
+            evict(torch)
+            g.replay()
+            torch.cuda.synchronize()
+            t[n].append(st.span_ms() * 1e3)
+    t0, t1, tl = (np.asarray(t[n]) for n in (0, 1, L))
+    return dict(loop1_cold_us=round(float(np.median(t1 - t0)), 3),
+                loops2_L_us=round(float(np.median((tl - t1) / (L - 1))), 3),
+                stamp_pair_us=round(float(np.median(t0)), 3), replays=replays)
 
 
 def loop_prof(qgm, torch, synth, L=8, M=128):
