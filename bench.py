@@ -348,8 +348,9 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
                    persistent_loops2_L_ms=round(float(np.median(pc[1:])), 4),
                    persistent_evict_each_loop_median_ms=round(float(np.median(pe)), 4))
         out["persistent_one_launch_ms_per_loop"] = round(res["persistent_one_launch_total"] / L, 4)
-    out["graph"] = dict(graph, TFLOPs_loops2_L=round(flops / (graph["loops2_L_us"] * 1e-6) / 1e12, 2),
-                        weight_GBps_loop1_cold=round(wbytes / (graph["loop1_cold_us"] * 1e-6) / 1e9, 1))
+    out["graph"] = dict(graph, weight_GBps_loop1_cold=round(wbytes / (graph["loop1_cold_us"] * 1e-6) / 1e9, 1))
+    if graph["loops2_L_us"]:
+        out["graph"]["TFLOPs_loops2_L"] = round(flops / (graph["loops2_L_us"] * 1e-6) / 1e12, 2)
     hb = load_loop_traffic(name)
     if hb is not None:
         out["residency_counters"] = hb   # L2 fetch bytes and latency per loop (profiles/loop_traffic.json)
@@ -377,7 +378,7 @@ def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5):
         g.replay()
         torch.cuda.synchronize()
         return g, stamps
-    graphs = {n: cap(n) for n in (0, 1, L)}
+    graphs = {n: cap(n) for n in sorted({0, 1, L})}
     t = {n: [] for n in graphs}
     for _ in range(replays):
         for n, (g, st) in graphs.items():
@@ -387,9 +388,10 @@ def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5):
             torch.cuda.synchronize()
             t[n].append(st.span_ms() * 1e3)
     t0, t1, tl = (np.asarray(t[n]) for n in (0, 1, L))
-    return dict(loop1_cold_us=round(float(np.median(t1 - t0)), 3),
-                loops2_L_us=round(float(np.median((tl - t1) / (L - 1))), 3),
-                stamp_pair_us=round(float(np.median(t0)), 3), replays=replays)
+    out = dict(loop1_cold_us=round(float(np.median(t1 - t0)), 3), stamp_pair_us=round(float(np.median(t0)), 3),
+               replays=replays)
+    out["loops2_L_us"] = round(float(np.median((tl - t1) / (L - 1))), 3) if L > 1 else None
+    return out
 
 
 def loop_prof(qgm, torch, synth, L=8, M=128):
