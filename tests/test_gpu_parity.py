@@ -764,6 +764,35 @@ def test_loop_block_full_size(M):
     check_close(x.cpu().numpy(), ref[-1], "loop x_8 full size")
 
 
+@pytest.mark.parametrize("M", [1, 128])
+def test_loop_block_graph_replays_match_eager(M):
+    # the benchmark times the looped block as loops captured in a HIP graph:
+    # every replay (x reset outside the graph, eager work in between) must give
+    # the eager block's bits
+    D, F, L = 256, 512, 3
+    say(f"loop graph replay M={M} D={D} F={F} L={L}")
+    cases = [synth.random_case(4200 + i, 0, 128, N, K, 1)
+             for i, (N, K) in enumerate(((3 * D, D), (D, D), (F, D), (D, F)))]
+    lins = [qgm.QuantLinear.from_case(c, DEV) for c in cases]
+    x0 = dev_half(synth.draw_x(np.random.default_rng(4300 + M), M, D))
+    scratch = torch.empty(M * (3 * D + D + F), dtype=torch.float16, device=DEV)
+    x = x0.clone()
+    qgm.loop_block(x, lins, L, scratch=scratch)
+    torch.cuda.synchronize()
+    eager = x.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qgm.loop_block(x, lins, L, scratch=scratch)
+    for rep in range(4):
+        x.copy_(x0)
+        other = x0.clone()
+        qgm.loop_block(other, lins, 1)     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+
+
 def test_dequant_into_caller_buffer_feeds_an_fp16_gemm():
     # the dequantize-at-load comparison path: qg_dequant into a caller-owned
     # fp16 [N, K] buffer (same bits as `dequant`), then a plain fp32 product
