@@ -9,8 +9,9 @@ up to more than twice the 256 MB on-die cache, and a 512 MiB read evicts that
 cache before every timed replay, so every timed step streams its weight bytes
 from HBM whatever K is.  The K timed steps are captured once in a HIP graph
 between two device clock stamps on the stream the kernels run on, and
-replayed (median of several replays); HIP events around the same replays are
-reported beside them.
+replayed (median of several replays); the span of an empty stamp pair (the
+first stamp's own step) is taken off, so a step's time does not depend on K.
+HIP events around the same replays are reported beside them.
 
 One JSON line is printed: value = weight GB/s at M=1, plus the roofline of the
 GEMV kernel against the published HBM peak and against the ceilings measured
@@ -155,13 +156,35 @@ def capture(qgm, torch, step, steps):
     return g, stamps
 
 
+_STAMP_PAIR = {}
+
+
+def stamp_pair_ms(qgm, torch, replays=9):
+    """Span of the two clock stamps with nothing between them, under the same
+    protocol (median of `replays` replays, each after an eviction): the first
+    stamp's own step (its kernel and the launch gap after it), which every
+    stamp span holds once on top of its K steps.  Measured once per process."""
+    if "ms" not in _STAMP_PAIR:
+        g, stamps = capture(qgm, torch, lambda i: None, 0)
+        spans = []
+        for _ in range(replays):
+            evict(torch)
+            g.replay()
+            torch.cuda.synchronize()
+            spans.append(stamps.span_ms())
+        _STAMP_PAIR["ms"] = float(np.median(spans))
+    return _STAMP_PAIR["ms"]
+
+
 def replay_times(torch, g, steps, replays, stamps):
     """ms per step of each of `replays` timed replays of graph g, the on-die
     cache evicted before each: from the device clock stamps inside the graph
-    (exactly the steps), and from HIP events recorded on the stream around the
-    replay (the steps plus the graph's own launch latency, about 11 us per
-    replay on this runtime, which only an event recorded inside the graph could
-    exclude, and the runtime refuses event records during capture)."""
+    (the stamp span less the span of an empty stamp pair, so exactly the K
+    steps), and from HIP events recorded on the stream around the replay (the
+    steps plus the first stamp and the graph's own launch latency, about 11 us
+    per replay on this runtime, which only an event recorded inside the graph
+    could exclude, and the runtime refuses event records during capture)."""
+    pair = stamp_pair_ms(stamps.qgm, torch)
     stream = torch.cuda.current_stream()
     inner, events = [], []
     for _ in range(replays):
@@ -173,7 +196,7 @@ def replay_times(torch, g, steps, replays, stamps):
         stop.record(stream)
         stop.synchronize()
         events.append(start.elapsed_time(stop) / steps)
-        inner.append(stamps.span_ms() / steps)
+        inner.append((stamps.span_ms() - pair) / steps)
     return inner, events
 
 
@@ -734,8 +757,10 @@ def main():
                    "M": 1, "N": 6144, "K": 2048, "group": 128, "format": "int4_asym",
                    "weight_bytes_per_step": wbytes, "weight_copies": copies,
                    "weight_bytes_per_replay": wbytes * args.steps, "on_die_cache_bytes": MALL_BYTES,
+                   "stamp_pair_ms": round(_STAMP_PAIR.get("ms", float("nan")), 6),
                    "timing": f"K steps captured in one HIP graph between two device clock stamps "
-                             f"(qg_clock_stamp, stream order); ms_per_step = stamp span / K, the median of "
+                             f"(qg_clock_stamp, stream order); ms_per_step = (stamp span - the span of an "
+                             f"empty stamp pair, stamp_pair_ms) / K, the median of "
                              f"{MAIN_REPLAYS} timed replays, each after a 512 MiB read that evicts the on-die cache; "
                              "ms_per_step_events = HIP events on the stream around the same replays, which also "
                              "hold the graph's own launch latency (events cannot be recorded inside a graph here)",
