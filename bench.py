@@ -9,8 +9,10 @@ up to more than twice the 256 MB on-die cache, and a 512 MiB read evicts that
 cache before every timed replay, so every timed step streams its weight bytes
 from HBM whatever K is.  The K timed steps are captured once in a HIP graph
 between two device clock stamps on the stream the kernels run on, and
-replayed (median of several replays); the span of an empty stamp pair (the
-first stamp's own step) is taken off, so a step's time does not depend on K.
+replayed (median of several replays); four untimed steps on the last copies
+open each graph, before the first stamp (the first kernel after the eviction
+pays about 2 us on its own), and the span of an empty stamp pair (the first
+stamp's own step) is taken off, so a step's time does not depend on K.
 HIP events around the same replays are reported beside them.
 
 One JSON line is printed: value = weight GB/s at M=1, plus the roofline of the
@@ -141,12 +143,24 @@ class Stamps:
         return (t[1] - t[0]) / self.khz
 
 
-def capture(qgm, torch, step, steps):
+WARM_STEPS = 4   # untimed steps inside each graph, before its first stamp
+
+
+def capture(qgm, torch, step, steps, warm=WARM_STEPS):
     """`steps` calls of step(i) captured in one HIP graph between two device
-    clock stamps; the first replay (which uploads the graph) is not timed."""
+    clock stamps; the first replay (which uploads the graph) is not timed.
+    Before the first stamp the graph runs `warm` untimed calls step(-1),
+    step(-2), ...: the steps rotate over copies (i % copies), so these read
+    the last copies, far from the first timed ones, and the timed steps still
+    find their weights evicted.  They take up what the first kernel after the
+    eviction pays on its own (its code and arguments come back from HBM too):
+    about 2 us more than a running call (decode GEMV: 6.0 against 3.84 us at
+    one step), which would otherwise make a step's time depend on K."""
     stamps = Stamps(qgm, torch)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
+        for j in range(warm):
+            step(-1 - j)
         stamps.first()
         for i in range(steps):
             step(i)
@@ -165,7 +179,7 @@ def stamp_pair_ms(qgm, torch, replays=9):
     stamp's own step (its kernel and the launch gap after it), which every
     stamp span holds once on top of its K steps.  Measured once per process."""
     if "ms" not in _STAMP_PAIR:
-        g, stamps = capture(qgm, torch, lambda i: None, 0)
+        g, stamps = capture(qgm, torch, lambda i: None, 0, warm=0)
         spans = []
         for _ in range(replays):
             evict(torch)
@@ -383,16 +397,32 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
 def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5):
     """Per-loop GPU time of the looped block with no host launch cost in it:
     L loops, one loop and no loop each captured in a HIP graph between two
-    device clock stamps, every replay after x is reset and the on-die cache
-    evicted (outside the graph).  Loop 1 (cold: weights from HBM, the same as
+    device clock stamps (after one untimed loop on a copy of the weights),
+    every replay after x is reset and the on-die cache evicted (outside the
+    graph).  Loop 1 (cold: weights from HBM, the same as
     a loop after an eviction) = T_1 - T_0; loops 2..L (weights where loop 1
     left them) = (T_L - T_1) / (L - 1); medians over the replays.  The eager
     per-loop events above also time the host's launches, which at M = 1 take
     about as long as the four GEMVs."""
+    # one untimed loop on a copy of the block's weights opens every graph, so
+    # the first timed kernel does not pay for code and arguments evicted with
+    # the cache (see capture); the block's own weights stay evicted
+    warm_lins = []
+    for l in lins:
+        w = object.__new__(type(l))
+        w.__dict__.update(l.__dict__)
+        w.packed = l.packed.clone()
+        w.scales = l.scales.clone()
+        w.zeros = None if l.zeros is None else l.zeros.clone()
+        warm_lins.append(w)
+    warm_x = x0.clone()
+    warm_scratch = torch.empty_like(scratch)
+
     def cap(nloops):
         stamps = Stamps(qgm, torch)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
+            qgm.loop_block(warm_x, warm_lins, 1, scratch=warm_scratch)
             stamps.first()
             if nloops:
                 qgm.loop_block(x, lins, nloops, scratch=scratch)
@@ -406,6 +436,7 @@ def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5):
     for _ in range(replays):
         for n, (g, st) in graphs.items():
             x.copy_(x0)
+            warm_x.copy_(x0)
             evict(torch)
             g.replay()
             torch.cuda.synchronize()
@@ -759,7 +790,9 @@ def main():
                    "weight_bytes_per_replay": wbytes * args.steps, "on_die_cache_bytes": MALL_BYTES,
                    "stamp_pair_ms": round(_STAMP_PAIR.get("ms", float("nan")), 6),
                    "timing": f"K steps captured in one HIP graph between two device clock stamps "
-                             f"(qg_clock_stamp, stream order); ms_per_step = (stamp span - the span of an "
+                             f"(qg_clock_stamp, stream order), after {WARM_STEPS} untimed steps on the last copies "
+                             f"(the first kernel after the eviction pays about 2 us on its own); "
+                             f"ms_per_step = (stamp span - the span of an "
                              f"empty stamp pair, stamp_pair_ms) / K, the median of "
                              f"{MAIN_REPLAYS} timed replays, each after a 512 MiB read that evicts the on-die cache; "
                              "ms_per_step_events = HIP events on the stream around the same replays, which also "
