@@ -152,10 +152,11 @@ def capture(qgm, torch, step, steps, warm=WARM_STEPS):
     Before the first stamp the graph runs `warm` untimed calls step(-1),
     step(-2), ...: the steps rotate over copies (i % copies), so these read
     the last copies, far from the first timed ones, and the timed steps still
-    find their weights evicted.  They take up what the first kernel after the
-    eviction pays on its own (its code and arguments come back from HBM too):
-    about 2 us more than a running call (decode GEMV: 6.0 against 3.84 us at
-    one step), which would otherwise make a step's time depend on K."""
+    find their weights evicted.  They take up what the first kernels after
+    the eviction pay on their own: about 2 us more than a running call
+    (decode GEMV: 6.0 against 3.84 us at one step), whichever kernels they are
+    (after four empty kernels the one timed GEMV takes 4.4 us, after another
+    GEMV 4.0-4.1 us), which would otherwise make a step's time depend on K."""
     stamps = Stamps(qgm, torch)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -405,8 +406,8 @@ def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5):
     per-loop events above also time the host's launches, which at M = 1 take
     about as long as the four GEMVs."""
     # one untimed loop on a copy of the block's weights opens every graph, so
-    # the first timed kernel does not pay for code and arguments evicted with
-    # the cache (see capture); the block's own weights stay evicted
+    # the first timed kernel does not pay what the first kernels after the
+    # eviction pay (see capture); the block's own weights stay evicted
     warm_lins = []
     for l in lins:
         w = object.__new__(type(l))
