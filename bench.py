@@ -352,6 +352,15 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
             if int(status[0]) != 0:
                 raise RuntimeError("qloop_block_persistent: a grid barrier gave up")
             res["persistent_" + mode] = per
+        # both persistent forms timed in graphs too, as the four-launch block is below
+        status.zero_()
+        for key, one in (("graph_persistent", False), ("graph_persistent_one_launch", True)):
+            def run_p(xx, ll, n, sc, one=one):
+                qgm.loop_block_persistent(xx, ll, n, scratch=sc, status=status, one_launch=one)
+            res[key] = loop_graph_times(qgm, torch, x, x0, lins, L, scratch, run=run_p)
+        torch.cuda.synchronize()
+        if int(status[0]) != 0:
+            raise RuntimeError("qloop_block_persistent (graph): a grid barrier gave up")
         # all L loops in one launch (each XCD keeps its rows' weights in its L2)
         x.copy_(x0)
         evict(torch)
@@ -386,6 +395,8 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
                    persistent_loops2_L_ms=round(float(np.median(pc[1:])), 4),
                    persistent_evict_each_loop_median_ms=round(float(np.median(pe)), 4))
         out["persistent_one_launch_ms_per_loop"] = round(res["persistent_one_launch_total"] / L, 4)
+        out["graph_persistent"] = res["graph_persistent"]
+        out["graph_persistent_one_launch"] = res["graph_persistent_one_launch"]
     out["graph"] = dict(graph, weight_GBps_loop1_cold=round(wbytes / (graph["loop1_cold_us"] * 1e-6) / 1e9, 1))
     if graph["loops2_L_us"]:
         out["graph"]["TFLOPs_loops2_L"] = round(flops / (graph["loops2_L_us"] * 1e-6) / 1e12, 2)
@@ -395,7 +406,7 @@ def loop_leg(qgm, torch, synth, L=8, M=128, control=True):
     return out
 
 
-def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5):
+def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5, run=None):
     """Per-loop GPU time of the looped block with no host launch cost in it:
     L loops, one loop and no loop each captured in a HIP graph between two
     device clock stamps (after one untimed loop on a copy of the weights),
@@ -404,7 +415,11 @@ def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5):
     a loop after an eviction) = T_1 - T_0; loops 2..L (weights where loop 1
     left them) = (T_L - T_1) / (L - 1); medians over the replays.  The eager
     per-loop events above also time the host's launches, which at M = 1 take
-    about as long as the four GEMVs."""
+    about as long as the four GEMVs.  run(x, linears, loops, scratch) runs the
+    block (default: loop_block, four launches per loop)."""
+    if run is None:
+        def run(xx, ll, n, sc):
+            qgm.loop_block(xx, ll, n, scratch=sc)
     # one untimed loop on a copy of the block's weights opens every graph, so
     # the first timed kernel does not pay what the first kernels after the
     # eviction pay (see capture); the block's own weights stay evicted
@@ -423,10 +438,10 @@ def loop_graph_times(qgm, torch, x, x0, lins, L, scratch, replays=5):
         stamps = Stamps(qgm, torch)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            qgm.loop_block(warm_x, warm_lins, 1, scratch=warm_scratch)
+            run(warm_x, warm_lins, 1, warm_scratch)
             stamps.first()
             if nloops:
-                qgm.loop_block(x, lins, nloops, scratch=scratch)
+                run(x, lins, nloops, scratch)
             stamps.last()
         x.copy_(x0)
         g.replay()
