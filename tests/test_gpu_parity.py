@@ -340,7 +340,9 @@ def test_gemm_long_k_small_tiles(monkeypatch, fmt, group, K, tpw, all_):
 # Seeded sweep over random shapes, formats and M: every plan branch the
 # shapes reach (GEMV rows, MFMA GEMV chunks, GEMM tiles, word tiles per wave,
 # issue modes, splits) against the oracle, half of the cases with a residual.
-def _random_shape_cases(n=40, seed=20261203):
+# QGEMM_TEST_RANDOM_CASES / QGEMM_TEST_RANDOM_SEED widen it for a longer run.
+def _random_shape_cases(n=int(os.environ.get("QGEMM_TEST_RANDOM_CASES", "40")),
+                        seed=int(os.environ.get("QGEMM_TEST_RANDOM_SEED", "20261203"))):
     rng = np.random.default_rng(seed)
     groups = {0: (32, 64, 128), 1: (32, 64, 128), 2: (32,), 3: (32,), 4: (256,)}
     out = []
